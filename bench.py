@@ -1,0 +1,242 @@
+#!/usr/bin/env python3
+"""Benchmark of the fp16 NT GEMM (D = A * B^T) on one MI355X.
+
+One step = one call of the library on one batch of synthetic operands
+(inputs generated from the workload's seed and already resident in HBM when
+the timed region starts).  Prints one JSON line:
+
+  value       whole-run throughput, TFLOP/s = 2*M*N*K*steps / timed seconds
+  roofline    the GEMM kernel against the dense-fp16 MFMA peak: achieved =
+              2*M*N*K / mean launch duration (HIP events bracketing the timed
+              region on the launch stream, divided by the number of
+              back-to-back launches), traffic = HBM bytes per launch from the
+              committed rocprofv3 counter summary when it matches the
+              current kernel sources, else null
+  cpu_baseline  the CPU oracle timed on the host cores on a bounded sample
+              (a block of full output rows), scaled to TFLOP/s
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
+                       [--workload NAME] [--rung R] [--no-cpu-baseline]
+       python bench.py --copy-calib   (a plain device copy of known size, for
+                                       scaling the HBM byte counters)
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_FP16_TFLOPS = 2516.6   # MI355X dense fp16 MFMA: 256 CU x 2.4 GHz x 4096 FLOP/CU/clk
+HBM_PEAK_GBS = 8000.0
+METRIC = "fp16 GEMM TFLOP/s at M=N=K=4096 (+ % of MI355X dense-fp16 peak)"
+KERNEL_SOURCES = ["common.hpp", "sched.hpp", "ladder.hpp", "ring.hpp", "persistent_ws.hpp", "gemm_f16_nt.hip"]
+RUNG_NAMES = {0: "auto", 1: "r1_single_tile", 2: "r2_kloop", 3: "r3_grid", 4: "r4_ring",
+              5: "r5_persistent_ws"}
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "dense_fp16_gemm_nt_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_record(workload: str, rung_name: str):
+    """HBM bytes per launch from profiles/traffic_<workload>.json if it was
+    taken on the current kernel sources, else None."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("kernel_src_sha") != kernel_source_hash() or rec.get("rung") != rung_name:
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def parse():
+    p = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=10)
+    p.add_argument("--workload", default="square_4096")
+    p.add_argument("--rung", type=int, default=0, help="0 = library choice, 1..5 = ladder rung")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-seconds", type=float, default=12.0, help="target oracle time for the CPU sample")
+    p.add_argument("--copy-calib", action="store_true", help="run only a plain device copy (counter scaling)")
+    return p.parse_args()
+
+
+def copy_calib():
+    import torch
+
+    n = 256 << 20  # bytes
+    src = torch.empty(n // 2, dtype=torch.float16, device="cuda:0").fill_(1.0)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calib_bytes_read": n, "copy_calib_bytes_written": n, "launches": 5}), flush=True)
+
+
+def cpu_baseline(A, B, D_gpu_bits, w, target_s):
+    """Time the oracle on the first R full output rows (R sized to about
+    target_s seconds of work on the host's cores) and check those rows of
+    the GPU result against it."""
+    import numpy as np
+
+    import oracle
+    from tests.parity import compare
+
+    rows = 8
+    t0 = time.perf_counter()
+    _, threads = oracle.gemm_nt(A[:rows], B)
+    dt = time.perf_counter() - t0
+    rows = int(max(8, min(w.M, rows * target_s / max(dt, 1e-6))))
+    t0 = time.perf_counter()
+    ref, threads = oracle.gemm_nt(A[:rows], B)
+    dt = time.perf_counter() - t0
+    ok, worst, nbad, _ = compare(D_gpu_bits[:rows], ref, w.K)
+    flop = 2.0 * rows * w.N * w.K
+    return {
+        "value": round(flop / dt / 1e12, 6),
+        "unit": "TFLOP/s",
+        "cores": int(threads),
+        "kind": "oracle",
+        "sample": f"first {rows} of {w.M} output rows x all {w.N} columns, K={w.K} "
+                  f"({rows * w.N} dot products, fp64 accumulation), {dt:.1f} s",
+        "seconds": round(dt, 3),
+        "gpu_rows_match_oracle": bool(ok),
+        "gpu_rows_worst_err_over_tol": round(worst, 4),
+        "cpu_model": _cpu_model(),
+    }
+
+
+def _cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on exactly one GPU (got --gpus {args.gpus}); "
+              "the GEMM is not sharded across GPUs here.", file=sys.stderr)
+        sys.exit(2)
+    if args.copy_calib:
+        copy_calib()
+        return
+
+    import numpy as np
+    import torch
+
+    import dense_fp16_gemm_nt_amd as g
+    from dense_fp16_gemm_nt_amd import inputs, workloads
+
+    w = workloads.BY_NAME[args.workload]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    print(f"[bench] {w.describe()} rung={RUNG_NAMES[args.rung]} warmup={args.warmup} steps={args.steps}",
+          file=sys.stderr, flush=True)
+    A_np, B_np = inputs.operands(w.M, w.N, w.K, w.seed, w.dist)
+    A = torch.from_numpy(A_np).to(dev)
+    B = torch.from_numpy(B_np).to(dev)
+    D = torch.empty((w.M, w.N), dtype=torch.float16, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    L = g.lib()
+    a_ptr, b_ptr, d_ptr = A.data_ptr(), B.data_ptr(), D.data_ptr()
+    s_ptr = ctypes.c_void_p(stream.cuda_stream)
+    if args.rung == 0:
+        def step():
+            return L.gemm_f16_nt(w.M, w.N, w.K, a_ptr, b_ptr, d_ptr, s_ptr)
+    else:
+        def step():
+            return L.gemm_f16_nt_rung(args.rung, w.M, w.N, w.K, a_ptr, b_ptr, d_ptr, s_ptr)
+
+    for _ in range(args.warmup):
+        if step() != 0:
+            raise SystemExit("gemm_f16_nt returned an error")
+    torch.cuda.synchronize()
+
+    # timed region: bracketed by events on the launch stream, with the
+    # device synchronised on both sides
+    region0 = torch.cuda.Event(enable_timing=True)
+    region1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    region0.record(stream)
+    bad = 0
+    for _ in range(args.steps):
+        bad |= step()
+    region1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    if bad:
+        raise SystemExit("gemm_f16_nt returned an error")
+    region_ms = region0.elapsed_time(region1)
+    kernel_ms = region_ms / args.steps      # mean launch duration over the region
+
+    flop = float(w.flop)
+    value = flop * args.steps / (region_ms * 1e-3) / 1e12
+    achieved = flop / (kernel_ms * 1e-3) / 1e12
+    rung_name = RUNG_NAMES[args.rung]
+    traffic = traffic_record(w.name, rung_name)
+
+    out = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(region_ms / args.steps, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic",
+        "config": {
+            "workload": w.name, "M": w.M, "N": w.N, "K": w.K, "seed": w.seed,
+            "dist": w.dist, "layout": "A MxK row-major, B NxK row-major, D MxN row-major",
+            "accumulate": "f32", "kernel": rung_name,
+        },
+        "pct_of_peak": round(100.0 * value / PEAK_FP16_TFLOPS, 2),
+        "roofline": {
+            "bound": "mfma",
+            "achieved": round(achieved, 2),
+            "peak": PEAK_FP16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(achieved / PEAK_FP16_TFLOPS, 4),
+            "traffic": traffic,
+            "kernel_mean_ms": round(kernel_ms, 5),
+            "kernel_src_sha": kernel_source_hash(),
+        },
+        "wall_s": round(wall, 4),
+    }
+    props = torch.cuda.get_device_properties(dev)
+    out["device"] = {"name": props.name, "cus": props.multi_processor_count,
+                     "arch": getattr(props, "gcnArchName", "?")}
+    if not args.no_cpu_baseline:
+        D_bits = D.cpu().view(torch.int16).numpy().view(np.uint16)
+        out["cpu_baseline"] = cpu_baseline(A_np, B_np, D_bits, w, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

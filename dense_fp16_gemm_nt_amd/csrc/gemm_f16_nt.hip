@@ -1,0 +1,251 @@
+// C-ABI boundary of the fp16 NT GEMM library: argument validation (before
+// any HIP call), device checks, rung dispatch and launch.  The contract of
+// every entry point is in include/gemm_f16_nt.h.
+#include "gemm_f16_nt.h"
+
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cstring>
+#include <mutex>
+
+#include "common.hpp"
+#include "ladder.hpp"
+#include "persistent_ws.hpp"
+#include "ring.hpp"
+#include "sched.hpp"
+
+using namespace g16;
+
+namespace {
+
+// Kernel configurations of the fast rungs.
+using RingCfg = ring::Cfg<256, 256, 64, 2, 1>;
+using WsCfg = ws::Cfg<64, 2, 1>;
+constexpr int kFastTile = 256;
+
+__global__ void fill_zero_kernel(uint16_t* __restrict__ D, int64_t n)
+{
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride) D[i] = 0;
+}
+
+// --------------------------------------------------------------- devices
+constexpr int kMaxDevices = 64;
+struct DeviceInfo {
+    std::atomic<int> state{0};  // 0 unknown, 1 ok, -1 unusable
+    int cu_count = 0;
+};
+DeviceInfo g_dev[kMaxDevices];
+std::mutex g_dev_lock;
+
+int device_info(int* cu_count)
+{
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return GEMM_F16_NT_DEVICE;
+    DeviceInfo& d = g_dev[dev];
+    int st = d.state.load(std::memory_order_acquire);
+    if (st == 0) {
+        std::lock_guard<std::mutex> lock(g_dev_lock);
+        st = d.state.load(std::memory_order_relaxed);
+        if (st == 0) {
+            hipDeviceProp_t prop;
+            int cus = 0;
+            st = -1;
+            if (hipGetDeviceProperties(&prop, dev) == hipSuccess &&
+                std::strncmp(prop.gcnArchName, "gfx950", 6) == 0 &&
+                hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
+                cus > 0) {
+                d.cu_count = cus;
+                st = 1;
+            }
+            d.state.store(st, std::memory_order_release);
+        }
+    }
+    if (st != 1) return GEMM_F16_NT_DEVICE;
+    *cu_count = d.cu_count;
+    return GEMM_F16_NT_OK;
+}
+
+// ------------------------------------------------------------ validation
+bool overlaps(const void* a, int64_t abytes, const void* b, int64_t bbytes)
+{
+    if (abytes <= 0 || bbytes <= 0) return false;
+    const uintptr_t a0 = (uintptr_t)a, b0 = (uintptr_t)b;
+    return a0 < b0 + (uintptr_t)bbytes && b0 < a0 + (uintptr_t)abytes;
+}
+
+int validate(int rung, int64_t M, int64_t N, int64_t K, const void* A, const void* B, const void* D)
+{
+    if (rung < 0 || rung > GEMM_F16_NT_R5_PERSISTENT_WS) return GEMM_F16_NT_INVALID_ARG;
+    if (M < 0 || N < 0 || K < 0) return GEMM_F16_NT_INVALID_ARG;
+    const bool any_out = M > 0 && N > 0;
+    if (any_out && K > 0 && (A == nullptr || B == nullptr)) return GEMM_F16_NT_INVALID_ARG;
+    if (any_out && D == nullptr) return GEMM_F16_NT_INVALID_ARG;
+    if (K % 8 != 0) return GEMM_F16_NT_UNSUPPORTED;
+    // index ranges the kernels are built for: per-lane 32-bit byte offsets
+    // within a 256-row band, 2^31 tiles, 2D grid limits of the 128-tile rungs
+    if (K > (int64_t(1) << 22) || M > (int64_t(1) << 31) || N > (int64_t(1) << 31)) return GEMM_F16_NT_UNSUPPORTED;
+    if (rung == GEMM_F16_NT_R1_SINGLE_TILE && !(M == 128 && N == 128 && K == 64)) return GEMM_F16_NT_UNSUPPORTED;
+    if (rung == GEMM_F16_NT_R2_KLOOP && !(M == 128 && N == 128)) return GEMM_F16_NT_UNSUPPORTED;
+    if (rung == GEMM_F16_NT_R3_GRID && (N + 127) / 128 > 65535) return GEMM_F16_NT_UNSUPPORTED;
+    if (!any_out) return GEMM_F16_NT_OK;
+    if (K > 0 && (((uintptr_t)A & 15) || ((uintptr_t)B & 15))) return GEMM_F16_NT_UNSUPPORTED;
+    if ((uintptr_t)D & 15) return GEMM_F16_NT_UNSUPPORTED;
+    const int64_t dbytes = M * N * 2;
+    if (K > 0 && (overlaps(A, M * K * 2, D, dbytes) || overlaps(B, N * K * 2, D, dbytes)))
+        return GEMM_F16_NT_INVALID_ARG;
+    return GEMM_F16_NT_OK;
+}
+
+int launched()
+{
+    return hipGetLastError() == hipSuccess ? GEMM_F16_NT_OK : GEMM_F16_NT_LAUNCH;
+}
+
+int launch_fill_zero(void* D, int64_t n, hipStream_t s)
+{
+    const int64_t blocks = (n + 255) / 256;
+    const unsigned grid = (unsigned)(blocks < 4096 ? blocks : 4096);
+    hipLaunchKernelGGL(fill_zero_kernel, dim3(grid), dim3(256), 0, s, (uint16_t*)D, n);
+    return launched();
+}
+
+int launch_ring(int64_t M, int64_t N, int64_t K, const f16* A, const f16* B, f16* D, hipStream_t s)
+{
+    const int64_t tm = (M + kFastTile - 1) / kFastTile, tn = (N + kFastTile - 1) / kFastTile;
+    const bool edge = (M % kFastTile) || (N % kFastTile) || (K % RingCfg::BK) || (N % 4);
+    if (edge)
+        hipLaunchKernelGGL((ring::ring_kernel<RingCfg, true>), dim3((unsigned)(tm * tn)), dim3(RingCfg::THREADS), 0,
+                           s, A, B, D, M, N, K, tm, tn);
+    else
+        hipLaunchKernelGGL((ring::ring_kernel<RingCfg, false>), dim3((unsigned)(tm * tn)), dim3(RingCfg::THREADS), 0,
+                           s, A, B, D, M, N, K, tm, tn);
+    return launched();
+}
+
+int launch_ws(int64_t M, int64_t N, int64_t K, const f16* A, const f16* B, f16* D, int64_t grid,
+              hipStream_t s)
+{
+    const int64_t tm = (M + kFastTile - 1) / kFastTile, tn = (N + kFastTile - 1) / kFastTile;
+    const bool edge = (M % kFastTile) || (N % kFastTile) || (K % WsCfg::BK) || (N % 4);
+    if (grid > tm * tn) grid = tm * tn;
+    if (edge)
+        hipLaunchKernelGGL((ws::ws_kernel<WsCfg, true>), dim3((unsigned)grid), dim3(WsCfg::THREADS), 0, s, A, B, D,
+                           M, N, K, tm, tn);
+    else
+        hipLaunchKernelGGL((ws::ws_kernel<WsCfg, false>), dim3((unsigned)grid), dim3(WsCfg::THREADS), 0, s, A, B, D,
+                           M, N, K, tm, tn);
+    return launched();
+}
+
+int run(int rung, int64_t M, int64_t N, int64_t K, const void* A, const void* B, void* D, int64_t grid_override,
+        void* stream)
+{
+    int st = validate(rung, M, N, K, A, B, D);
+    if (st != GEMM_F16_NT_OK) return st;
+    if (M == 0 || N == 0) return GEMM_F16_NT_OK;
+    int cus = 0;
+    st = device_info(&cus);
+    if (st != GEMM_F16_NT_OK) return st;
+    hipStream_t s = (hipStream_t)stream;
+    if (K == 0) return launch_fill_zero(D, M * N, s);
+    const f16* a = (const f16*)A;
+    const f16* b = (const f16*)B;
+    f16* d = (f16*)D;
+    switch (rung) {
+    case GEMM_F16_NT_R1_SINGLE_TILE:
+        hipLaunchKernelGGL(ladder::r1_single_tile, dim3(1), dim3(ladder::THREADS), 0, s, a, b, d);
+        return launched();
+    case GEMM_F16_NT_R2_KLOOP:
+    case GEMM_F16_NT_R3_GRID: {
+        const dim3 grid((unsigned)((M + 127) / 128), (unsigned)((N + 127) / 128));
+        hipLaunchKernelGGL(ladder::r23_kloop_grid, grid, dim3(ladder::THREADS), 0, s, a, b, d, M, N, K);
+        return launched();
+    }
+    case GEMM_F16_NT_R4_RING:
+        return launch_ring(M, N, K, a, b, d, s);
+    case GEMM_F16_NT_R5_PERSISTENT_WS:
+        return launch_ws(M, N, K, a, b, d, grid_override > 0 ? grid_override : cus, s);
+    default:  // 0: the library's choice
+        return launch_ring(M, N, K, a, b, d, s);
+    }
+}
+
+}  // namespace
+
+extern "C" {
+
+int gemm_f16_nt(int64_t M, int64_t N, int64_t K, const void* A, const void* B, void* D, void* stream)
+{
+    return run(0, M, N, K, A, B, D, 0, stream);
+}
+
+int gemm_f16_nt_rung(int rung, int64_t M, int64_t N, int64_t K, const void* A, const void* B, void* D,
+                     void* stream)
+{
+    if (rung < 1) return GEMM_F16_NT_INVALID_ARG;
+    return run(rung, M, N, K, A, B, D, 0, stream);
+}
+
+int gemm_f16_nt_persistent(int64_t M, int64_t N, int64_t K, const void* A, const void* B, void* D,
+                           int64_t num_workgroups, void* stream)
+{
+    if (num_workgroups < 1 || num_workgroups > (int64_t(1) << 31) - 1) return GEMM_F16_NT_INVALID_ARG;
+    return run(GEMM_F16_NT_R5_PERSISTENT_WS, M, N, K, A, B, D, num_workgroups, stream);
+}
+
+int gemm_f16_nt_check(int rung, int64_t M, int64_t N, int64_t K, const void* A, const void* B, const void* D)
+{
+    return validate(rung, M, N, K, A, B, D);
+}
+
+const char* gemm_f16_nt_status_string(int status)
+{
+    switch (status) {
+    case GEMM_F16_NT_OK: return "ok";
+    case GEMM_F16_NT_INVALID_ARG: return "invalid argument";
+    case GEMM_F16_NT_UNSUPPORTED: return "unsupported shape, alignment or rung";
+    case GEMM_F16_NT_LAUNCH: return "kernel launch failed";
+    case GEMM_F16_NT_DEVICE: return "no usable gfx950 device";
+    default: return "unknown status";
+    }
+}
+
+int64_t gemm_f16_nt_schedule(int64_t M, int64_t N, int64_t num_workgroups, int64_t* wg, int64_t* tile_m,
+                             int64_t* tile_n, int64_t capacity)
+{
+    if (M < 0 || N < 0 || num_workgroups < 1 || capacity < 0) return GEMM_F16_NT_INVALID_ARG;
+    if (capacity > 0 && (wg == nullptr || tile_m == nullptr || tile_n == nullptr)) return GEMM_F16_NT_INVALID_ARG;
+    const int64_t tm = (M + kFastTile - 1) / kFastTile, tn = (N + kFastTile - 1) / kFastTile;
+    const int64_t total = tm * tn;
+    const int64_t grid = num_workgroups < total ? num_workgroups : (total > 0 ? total : 1);
+    int64_t n = 0;
+    for (int64_t w = 0; w < grid; ++w)
+        for (int64_t i = 0;; ++i) {
+            const int64_t t = persistent_tile(w, i, grid);
+            if (t >= total) break;
+            const TileCoord c = grouped_tile(t, tm, tn);
+            if (n < capacity) {
+                wg[n] = w;
+                tile_m[n] = c.m_idx;
+                tile_n[n] = c.n_idx;
+            }
+            ++n;
+        }
+    return n;
+}
+
+int gemm_f16_nt_ring_plan(int depth, int64_t steps, int* stage, int64_t* lap, int64_t* refill)
+{
+    if (depth < 1 || steps < 0) return GEMM_F16_NT_INVALID_ARG;
+    if (steps > 0 && (stage == nullptr || lap == nullptr || refill == nullptr)) return GEMM_F16_NT_INVALID_ARG;
+    for (int64_t k = 0; k < steps; ++k) {
+        stage[k] = ring_stage(k, depth);
+        lap[k] = ring_lap(k, depth);
+        refill[k] = ring_refill_after(k, depth, steps);
+    }
+    return GEMM_F16_NT_OK;
+}
+
+}  // extern "C"

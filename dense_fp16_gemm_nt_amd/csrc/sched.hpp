@@ -1,0 +1,91 @@
+// Tile scheduling and ring bookkeeping, host+device so the CPU tests can
+// evaluate exactly what the kernels run.
+//
+// Tile decomposition: output tile (m_idx, n_idx) covers
+// D[m_idx*BM .. +BM, n_idx*BN .. +BN], reads A rows m_idx*BM.. and B rows
+// n_idx*BN.. ("TIRx GEMM detailed technical notes", V3 "Spatial Tiling with
+// Multiple CTAs": m_st = bx*BLK_M, n_st = by*BLK_N).
+//
+// Grouped order: the persistent scheduler of the same notes (V6 "Better L2
+// Locality") visits tiles in groups of 8 along M so that neighbouring tiles
+// share A row bands and B row bands in L2.  The notes give no formula; the
+// reading used here walks a group of (up to) 8 tile rows column by column.
+//
+// XCD remap: a gfx950 device dispatches consecutive workgroups round-robin
+// over its 8 XCDs, each with a private L2.  Workgroup w is given slot
+// xcd_slot(w) so that the workgroups resident on one XCD take a contiguous
+// run of the grouped order.  Both maps are bijections for any grid size, so
+// the result never depends on them (only the L2 hit rate does).
+#pragma once
+
+#include <stdint.h>
+
+#ifndef __HIPCC__
+#define __host__
+#define __device__
+#define __forceinline__ inline
+#endif
+
+namespace g16 {
+
+constexpr int kGroupM = 8;
+constexpr int kNumXcd = 8;
+
+struct TileCoord {
+    int64_t m_idx, n_idx;
+};
+
+// Linear tile id t (grouped order) -> tile coordinates.
+__host__ __device__ __forceinline__ TileCoord grouped_tile(int64_t t, int64_t tiles_m, int64_t tiles_n)
+{
+    const int64_t per_group = (int64_t)kGroupM * tiles_n;
+    const int64_t g = t / per_group;
+    const int64_t first_m = g * kGroupM;
+    const int64_t rem = tiles_m - first_m;
+    const int64_t gm = rem < kGroupM ? rem : kGroupM;
+    const int64_t r = t - g * per_group;
+    TileCoord c;
+    c.m_idx = first_m + r % gm;
+    c.n_idx = r / gm;
+    return c;
+}
+
+// Workgroup id -> slot in [0, grid) such that the workgroups dispatched to
+// one XCD (w mod 8 equal) own one contiguous range of slots.
+__host__ __device__ __forceinline__ int64_t xcd_slot(int64_t w, int64_t grid)
+{
+    const int64_t x = w % kNumXcd;
+    const int64_t j = w / kNumXcd;
+    const int64_t q = grid / kNumXcd;
+    const int64_t r = grid % kNumXcd;
+    return x * q + (x < r ? x : r) + j;
+}
+
+// The i-th tile visited by workgroup w of a persistent grid of `grid`
+// workgroups, as a linear grouped-order id; >= total when done.
+__host__ __device__ __forceinline__ int64_t persistent_tile(int64_t w, int64_t i, int64_t grid)
+{
+    return xcd_slot(w, grid) + i * grid;
+}
+
+// Ring bookkeeping for a ring of `depth` stages fed with k-steps 0, 1, ...:
+// step k lives in stage k % depth and is the (k / depth)-th use of that
+// stage ("lap"; the pages' phase bit is lap & 1).  With one counter per ring
+// that never resets, a wait always names the current lap, including across
+// tile boundaries of the persistent kernels.
+__host__ __device__ __forceinline__ int ring_stage(int64_t k, int depth) { return (int)(k % depth); }
+__host__ __device__ __forceinline__ int64_t ring_lap(int64_t k, int depth) { return k / depth; }
+
+// Refill rule of the software pipeline ("TIRx GEMM detailed technical
+// notes", V5 "Main-Loop Schedule"): once step k has been consumed, its stage
+// is refilled with step k + depth, if that step exists.  Returns -1 when
+// nothing is left.  The kernels issue this refill at the barrier that opens
+// step k + 1 (k = -1 there stands for the prologue, which fills steps
+// 0 .. depth-2 before the loop, so step depth-1 is issued on entry).
+__host__ __device__ __forceinline__ int64_t ring_refill_after(int64_t k, int depth, int64_t total)
+{
+    const int64_t p = k + depth;
+    return p < total ? p : -1;
+}
+
+}  // namespace g16

@@ -1,0 +1,100 @@
+/*
+ * gemm_f16_nt -- dense fp16 GEMM  D = A * B^T  on AMD Instinct MI355X (gfx950).
+ *
+ * The operation ("GEMM I - the tiled baseline", problem statement; "TIRx GEMM
+ * detailed technical notes", V3 "Spatial Tiling with Multiple CTAs" and V8
+ * "Operand Partition"):
+ *
+ *     D[m][n] = fp16( sum_k A[m][k] * B[n][k] ),   0 <= m < M, 0 <= n < N
+ *
+ *   A  M x K fp16, row-major (leading dimension K)
+ *   B  N x K fp16, row-major (leading dimension K) -- B is stored N x K so
+ *      both operands stream as K-contiguous row bands
+ *   D  M x N fp16, row-major (leading dimension N), fully overwritten
+ *
+ * Products accumulate in fp32 and are rounded to fp16 once, at writeback,
+ * round-to-nearest-even; magnitudes >= 65520 become +-inf.  D is
+ * overwritten, never accumulated into (the first K step starts the sum,
+ * "GEMM I", Step 1 "Why accum=False").  The fp32 summation order is the
+ * kernel's own and is not part of the contract.
+ *
+ * Pointers: A, B and D are device pointers (HIP device memory of the current
+ * device).  The caller owns them; the library never frees, retains or
+ * allocates memory.  A and B must be 16-byte aligned.  D must not overlap A
+ * or B.  `stream` is a hipStream_t (NULL = the null stream).
+ *
+ * Calls are asynchronous and stream-ordered: they validate, enqueue and
+ * return.  Validation happens before any HIP call, so an invalid call
+ * launches nothing and leaves D untouched.  Faults inside a kernel surface
+ * at the caller's next synchronisation of the stream.
+ *
+ * Shapes: M, N >= 0; K >= 0 and K % 8 == 0 (every row starts 16-byte
+ * aligned).  M = 0 or N = 0 is a no-op; K = 0 writes +0.0 to all of D.
+ *
+ * Return value: GEMM_F16_NT_OK (0) or a negative status below.
+ */
+#ifndef GEMM_F16_NT_H
+#define GEMM_F16_NT_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define GEMM_F16_NT_OK 0
+#define GEMM_F16_NT_INVALID_ARG (-1) /* negative size, null pointer with data, unknown rung, overlap */
+#define GEMM_F16_NT_UNSUPPORTED (-2) /* K % 8 != 0, misaligned A/B, shape a rung does not implement */
+#define GEMM_F16_NT_LAUNCH (-3)      /* the HIP launch itself failed */
+#define GEMM_F16_NT_DEVICE (-4)      /* no usable device / device query failed / not gfx950 */
+
+/* The ladder of kernels ("GEMM I", Steps 1-3; "GEMM III", Step 7; "TIRx
+ * GEMM detailed technical notes", V1-V7).  Every rung computes the same D. */
+#define GEMM_F16_NT_R1_SINGLE_TILE 1 /* M = N = 128, K = 64 only, one workgroup */
+#define GEMM_F16_NT_R2_KLOOP 2       /* M = N = 128, any K: K-loop into one accumulator */
+#define GEMM_F16_NT_R3_GRID 3        /* any shape: 2D grid of 128 x 128 tiles */
+#define GEMM_F16_NT_R4_RING 4        /* any shape: 256 x 256 tiles, direct-to-LDS pipelined ring */
+#define GEMM_F16_NT_R5_PERSISTENT_WS 5 /* any shape: persistent, producer/consumer waves */
+
+/* D = A * B^T with the library's choice of kernel for the shape. */
+int gemm_f16_nt(int64_t M, int64_t N, int64_t K, const void* A, const void* B, void* D, void* stream);
+
+/* The same product on one named rung of the ladder (for tests and the
+ * bench).  Returns GEMM_F16_NT_UNSUPPORTED if the rung does not implement
+ * the shape (R1 and R2 are single-tile rungs). */
+int gemm_f16_nt_rung(int rung, int64_t M, int64_t N, int64_t K, const void* A, const void* B, void* D,
+                     void* stream);
+
+/* Persistent rung R5 with an explicit number of workgroups (>= 1) instead
+ * of one per compute unit.  The result must not depend on it; tests use it
+ * to check that every grid size gives identical bits. */
+int gemm_f16_nt_persistent(int64_t M, int64_t N, int64_t K, const void* A, const void* B, void* D,
+                           int64_t num_workgroups, void* stream);
+
+/* Validation only, no HIP call: the status the call above would return for
+ * these arguments before launching anything (rung 0 = gemm_f16_nt). */
+int gemm_f16_nt_check(int rung, int64_t M, int64_t N, int64_t K, const void* A, const void* B,
+                      const void* D);
+
+/* Static description of a status code (never NULL). */
+const char* gemm_f16_nt_status_string(int status);
+
+/* Host evaluation of the persistent rung's tile schedule, no HIP call.  For
+ * a grid of `num_workgroups` on an M x N output (256 x 256 tiles), writes
+ * one entry per (workgroup, visit) in workgroup-major visit order:
+ * wg[i], tile_m[i], tile_n[i].  Returns the number of entries (the tile
+ * count) or a negative status; writes at most `capacity` entries. */
+int64_t gemm_f16_nt_schedule(int64_t M, int64_t N, int64_t num_workgroups, int64_t* wg, int64_t* tile_m,
+                             int64_t* tile_n, int64_t capacity);
+
+/* Host evaluation of the operand ring's bookkeeping for `depth` stages and
+ * `steps` k steps: stage[k], lap[k] (the pages' phase is lap & 1) and
+ * refill[k] = the step loaded into stage[k] once step k is consumed (-1 if
+ * none).  Returns 0 or a negative status. */
+int gemm_f16_nt_ring_plan(int depth, int64_t steps, int* stage, int64_t* lap, int64_t* refill);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GEMM_F16_NT_H */

@@ -1,0 +1,158 @@
+"""C-ABI library on the CPU: it loads, exports every declared symbol,
+validates before any HIP call, and its host-side schedule / ring logic
+matches the pages' printed tables and is a bijection over tiles."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import dense_fp16_gemm_nt_amd as g
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gemm_f16_nt.h")
+GOLDEN = os.path.join(ROOT, "tests", "golden")
+
+
+def _golden(name):
+    rows = []
+    with open(os.path.join(GOLDEN, name)) as f:
+        for line in f:
+            line = line.strip()
+            if line and not line.startswith("#"):
+                rows.append([int(x) for x in line.split()])
+    return np.array(rows, dtype=np.int64)
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(gemm_f16_nt\w*)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    names = declared_functions()
+    assert "gemm_f16_nt" in names and len(names) >= 7
+    L = ctypes.CDLL(g.LIB_PATH)
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_status_strings():
+    assert g.status_string(0) == "ok"
+    for s in (g.INVALID_ARG, g.UNSUPPORTED, g.LAUNCH, g.DEVICE, 12345):
+        assert isinstance(g.status_string(s), str) and g.status_string(s)
+
+
+A0, B0, D0 = 0x10000, 0x20000000, 0x40000000   # fake, 16-byte aligned, disjoint
+
+
+@pytest.mark.parametrize("args,want", [
+    ((0, 64, 64, 64, A0, B0, D0), g.OK),
+    ((0, -1, 64, 64, A0, B0, D0), g.INVALID_ARG),
+    ((0, 64, -1, 64, A0, B0, D0), g.INVALID_ARG),
+    ((0, 64, 64, -8, A0, B0, D0), g.INVALID_ARG),
+    ((0, 64, 64, 64, 0, B0, D0), g.INVALID_ARG),
+    ((0, 64, 64, 64, A0, 0, D0), g.INVALID_ARG),
+    ((0, 64, 64, 64, A0, B0, 0), g.INVALID_ARG),
+    ((0, 64, 64, 12, A0, B0, D0), g.UNSUPPORTED),          # K % 8
+    ((0, 64, 64, 64, A0 + 2, B0, D0), g.UNSUPPORTED),      # misaligned A
+    ((0, 64, 64, 64, A0, B0 + 8, D0), g.UNSUPPORTED),      # misaligned B
+    ((0, 64, 64, 64, A0, B0, D0 + 4), g.UNSUPPORTED),      # misaligned D
+    ((0, 64, 64, 64, A0, B0, A0 + 4096), g.INVALID_ARG),   # D overlaps A
+    ((0, 64, 64, 64, A0, B0, B0), g.INVALID_ARG),          # D overlaps B
+    ((6, 64, 64, 64, A0, B0, D0), g.INVALID_ARG),          # unknown rung
+    ((-1, 64, 64, 64, A0, B0, D0), g.INVALID_ARG),
+    ((1, 128, 128, 64, A0, B0, D0), g.OK),
+    ((1, 128, 128, 128, A0, B0, D0), g.UNSUPPORTED),       # R1 is one 128x128x64 tile
+    ((2, 128, 128, 4096, A0, B0, D0), g.OK),
+    ((2, 256, 128, 64, A0, B0, D0), g.UNSUPPORTED),        # R2 is one tile
+    ((3, 1000, 333, 72, A0, B0, D0), g.OK),
+    ((4, 1, 1, 8, A0, B0, D0), g.OK),
+    ((5, 5000, 7, 8, A0, B0, D0), g.OK),
+    ((0, 0, 64, 64, 0, 0, 0), g.OK),                       # empty output: nothing needed
+    ((0, 64, 64, 0, 0, 0, D0), g.OK),                      # K = 0: D only
+    ((0, 64, 64, 1 << 23, A0, B0, D0), g.UNSUPPORTED),     # beyond the kernels' index range
+])
+def test_validation(args, want):
+    assert g.check(*args) == want
+
+
+def test_invalid_call_returns_before_any_device_work():
+    L = g.lib()
+    assert L.gemm_f16_nt(-1, 4, 8, A0, B0, D0, None) == g.INVALID_ARG
+    assert L.gemm_f16_nt_rung(0, 4, 4, 8, A0, B0, D0, None) == g.INVALID_ARG
+    assert L.gemm_f16_nt_persistent(4, 4, 8, A0, B0, D0, 0, None) == g.INVALID_ARG
+    assert L.gemm_f16_nt(0, 4, 8, 0, 0, 0, None) == g.OK     # empty: no-op
+
+
+@pytest.mark.skipif(os.environ.get("HIP_VISIBLE_DEVICES") is None and os.path.exists("/dev/kfd"),
+                    reason="a GPU may be present")
+def test_valid_call_without_gpu_fails_loudly():
+    # no device here: a well-formed call must report DEVICE, not pretend
+    assert g.lib().gemm_f16_nt(64, 64, 64, A0, B0, D0, None) == g.DEVICE
+
+
+def test_ring_plan_matches_printed_phase_table():
+    gold = _golden("ring_schedule_depth2.txt")
+    stage, lap, _ = g.ring_plan(2, len(gold))
+    assert np.array_equal(stage, gold[:, 1])
+    assert np.array_equal(lap & 1, gold[:, 2])
+
+
+def test_ring_plan_refill_schedule_ktiles5():
+    gold = _golden("ring_refill_ktiles5.txt")
+    stage, _, refill = g.ring_plan(2, 5)
+    assert np.array_equal(stage, gold[:, 1])
+    assert np.array_equal(refill, gold[:, 2])
+
+
+@pytest.mark.parametrize("depth,steps", [(1, 7), (2, 64), (3, 10), (4, 129)])
+def test_ring_plan_invariants(depth, steps):
+    stage, lap, refill = g.ring_plan(depth, steps)
+    for k in range(steps):
+        assert stage[k] == k % depth and lap[k] == k // depth
+        if refill[k] >= 0:
+            # a refill reuses the stage just consumed, one lap later
+            assert stage[refill[k]] == stage[k] and lap[refill[k]] == lap[k] + 1
+    # every step except the prologue's is loaded by exactly one refill
+    loaded = sorted(int(r) for r in refill if r >= 0)
+    assert loaded == list(range(min(depth, steps), steps))
+
+
+@pytest.mark.parametrize("M,N,grid", [
+    (4096, 4096, 256), (8192, 8192, 256), (32768, 1024, 256), (256, 256, 256),
+    (4096, 4096, 1), (4096, 4096, 7), (4096, 4096, 512), (1000, 3000, 37), (1, 1, 3),
+    (8192, 8192, 148),
+])
+def test_schedule_is_a_bijection(M, N, grid):
+    wg, tm, tn = g.schedule(M, N, grid)
+    T_m, T_n = -(-M // 256), -(-N // 256)
+    assert len(wg) == T_m * T_n
+    assert np.all((tm >= 0) & (tm < T_m) & (tn >= 0) & (tn < T_n))
+    ids = tm * T_n + tn
+    assert len(np.unique(ids)) == T_m * T_n
+    counts = np.bincount(wg)
+    assert counts.max() - counts.min() <= 1          # balanced to one tile
+
+
+def test_schedule_matches_printed_persistent_arithmetic():
+    M, N, tile, tiles, grid, mean_x10 = _golden("persistent_grid_4096.txt")[0]
+    # same tile count with this build's 256 x 256 tiles at twice the size
+    scale = 256 // tile
+    wg, _, _ = g.schedule(M * scale, N * scale, grid)
+    assert len(wg) == tiles
+    counts = np.bincount(wg, minlength=grid)
+    assert round(10 * counts.mean()) == mean_x10
+    assert set(counts.tolist()) == {tiles // grid, tiles // grid + 1}
+
+
+def test_schedule_xcd_locality():
+    # one tile per workgroup at 4096^2: the 32 workgroups of one XCD
+    # (w mod 8 equal) own a compact block of tiles (8 tile rows x 4 columns)
+    wg, tm, tn = g.schedule(4096, 4096, 256)
+    for x in range(8):
+        sel = (wg % 8) == x
+        assert sel.sum() == 32
+        assert len(np.unique(tm[sel])) == 8 and len(np.unique(tn[sel])) == 4

@@ -1,0 +1,273 @@
+"""GPU parity: every rung of the HIP ladder against the CPU oracle, through
+the C-ABI, on seeded inputs (tolerance and exact pins as documented in
+tests/parity.py and tests/test_oracle_pins.py).
+
+All tests here need an MI355X; each prints the case it is about to run
+before touching the GPU.
+"""
+import sys
+
+import numpy as np
+import pytest
+
+import dense_fp16_gemm_nt_amd as g
+import oracle
+from dense_fp16_gemm_nt_amd import inputs, workloads
+from tests.parity import as_f64, assert_parity
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+DEV = "cuda:0"
+ALL_RUNGS = [1, 2, 3, 4, 5]
+
+
+def say(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def dev(x: np.ndarray):
+    return torch.from_numpy(np.ascontiguousarray(x)).to(DEV)
+
+
+def host_bits(t) -> np.ndarray:
+    return t.cpu().view(torch.int16).numpy().view(np.uint16)
+
+
+def run(rung, A, B, D=None):
+    """rung 0 = gemm_f16_nt (the library's choice)."""
+    if rung == 0:
+        out = g.gemm_f16_nt(A, B, D)
+    else:
+        out = g.gemm_f16_nt_rung(rung, A, B, D)
+    torch.cuda.synchronize()
+    return out
+
+
+def supported(rung, M, N, K):
+    if rung == 1:
+        return (M, N, K) == (128, 128, 64)
+    if rung == 2:
+        return (M, N) == (128, 128)
+    return True
+
+
+def rand_case(M, N, K, seed, dist=workloads.U11):
+    A, B = inputs.operands(M, N, K, seed, dist)
+    return A, B
+
+
+# ------------------------------------------------------------ small shapes
+
+SMALL = [(w.M, w.N, w.K, w.seed, w.dist) for w in workloads.WORKLOADS[:2]] + [(128, 128, 512, 21, workloads.U11)]
+
+
+@pytest.mark.parametrize("rung", [0] + ALL_RUNGS)
+@pytest.mark.parametrize("case", SMALL, ids=lambda c: f"{c[0]}x{c[1]}x{c[2]}")
+def test_small_workloads(rung, case):
+    M, N, K, seed, dist = case
+    if not supported(rung, M, N, K):
+        pytest.skip("rung does not implement this shape")
+    A, B = rand_case(M, N, K, seed, dist)
+    ref, _ = oracle.gemm_nt(A, B)
+    say(f"[gpu] rung={rung} M={M} N={N} K={K} seed={seed}")
+    D = run(rung, dev(A), dev(B))
+    worst = assert_parity(host_bits(D), ref, K, f"rung {rung} {M}x{N}x{K}")
+    say(f"      worst err/tol = {worst:.3f}")
+
+
+RAGGED = [
+    (1, 1, 8), (3, 5, 16), (33, 17, 24), (128, 4, 64), (130, 130, 72), (255, 257, 136),
+    (256, 256, 8), (300, 260, 200), (257, 513, 520), (511, 129, 1000), (640, 384, 64 * 9 + 8),
+    (64, 7, 40), (5, 3, 8),
+]
+
+
+@pytest.mark.parametrize("rung", [0, 3, 4, 5])
+@pytest.mark.parametrize("shape", RAGGED, ids=lambda s: "x".join(map(str, s)))
+def test_ragged_shapes(rung, shape):
+    M, N, K = shape
+    A, B = rand_case(M, N, K, 100 + M + N + K)
+    ref, _ = oracle.gemm_nt(A, B)
+    say(f"[gpu] ragged rung={rung} M={M} N={N} K={K}")
+    D = run(rung, dev(A), dev(B))
+    assert_parity(host_bits(D), ref, K, f"rung {rung} {M}x{N}x{K}")
+
+
+# -------------------------------------------------------------- exact pins
+
+@pytest.mark.parametrize("rung", [0] + ALL_RUNGS)
+def test_selection_matrix_bitwise(rung):
+    M, N, K = (128, 128, 64) if rung in (1,) else ((128, 128, 512) if rung == 2 else (384, 320, 192))
+    rng = np.random.default_rng(5)
+    pick = rng.integers(0, K, M)
+    A = np.zeros((M, K), np.float16)
+    A[np.arange(M), pick] = 1
+    B = (rng.uniform(-60000, 60000, (N, K))).astype(np.float16)
+    say(f"[gpu] selection rung={rung} M={M} N={N} K={K}")
+    D = run(rung, dev(A), dev(B))
+    assert np.array_equal(host_bits(D), B[:, pick].T.view(np.uint16))
+
+
+@pytest.mark.parametrize("rung", [0, 3, 4, 5])
+@pytest.mark.parametrize("K", [64, 512, 4096, 8192])
+def test_all_ones_equals_k(rung, K):
+    A = np.ones((256, K), np.float16)
+    B = np.ones((256, K), np.float16)
+    say(f"[gpu] all-ones rung={rung} K={K}")
+    D = run(rung, dev(A), dev(B))
+    assert np.all(as_f64(host_bits(D)) == K)
+
+
+@pytest.mark.parametrize("rung", [0, 3, 4, 5])
+def test_small_integers_bitwise(rung):
+    rng = np.random.default_rng(14)
+    for (M, N, K, lo, hi) in [(256, 192, 8192, -4, 5), (264, 256, 768, 0, 5)]:
+        A = rng.integers(lo, hi, (M, K)).astype(np.float16)
+        B = rng.integers(lo, hi, (N, K)).astype(np.float16)
+        ref, _ = oracle.gemm_nt(A, B)
+        say(f"[gpu] small-int rung={rung} M={M} N={N} K={K}")
+        D = run(rung, dev(A), dev(B))
+        got = host_bits(D)
+        assert np.array_equal(got, ref), f"{np.sum(got != ref)} mismatches"
+
+
+@pytest.mark.parametrize("rung", [0, 3, 4, 5])
+def test_designed_rows(rung):
+    """Exact sums on a tie, on the overflow threshold and on the subnormal
+    grid: round-half-even, +inf at 65520, gradual underflow."""
+    K = 64
+    A = np.zeros((128, K), np.float16)
+    B = np.zeros((128, K), np.float16)
+    A[0, :2] = [1, 1]
+    A[1, 0] = 2.0 ** -12
+    B[0, :2] = [2048, 1]
+    B[1, :2] = [2048, 3]
+    B[2, :2] = [65504, 16]
+    B[3, 0] = 2.0 ** -12
+    B[4, 0] = 2.0 ** -13
+    B[5, :2] = [-65504, -16]
+    say(f"[gpu] designed rows rung={rung}")
+    D = host_bits(run(rung, dev(A), dev(B)))
+    assert [int(x) for x in D[0, :3]] == [0x6800, 0x6802, 0x7C00]
+    assert int(D[0, 5]) == 0xFC00
+    assert int(D[1, 3]) == 0x0001, hex(int(D[1, 3]))   # 2^-24, smallest subnormal
+    assert int(D[1, 4]) == 0x0000                       # 2^-25 ties to zero
+
+
+# ------------------------------------------------------- degenerate shapes
+
+@pytest.mark.parametrize("rung", [0, 3, 4, 5])
+def test_k_zero_writes_zeros(rung):
+    D = torch.full((70, 90), float("nan"), dtype=torch.float16, device=DEV)
+    A = torch.empty((70, 0), dtype=torch.float16, device=DEV)
+    B = torch.empty((90, 0), dtype=torch.float16, device=DEV)
+    say(f"[gpu] K=0 rung={rung}")
+    run(rung, A, B, D)
+    assert torch.all(D == 0).item()
+
+
+def test_empty_outputs_are_noops():
+    A = torch.ones((0, 64), dtype=torch.float16, device=DEV)
+    B = torch.ones((32, 64), dtype=torch.float16, device=DEV)
+    say("[gpu] empty M")
+    D = g.gemm_f16_nt(A, B)
+    torch.cuda.synchronize()
+    assert D.shape == (0, 32)
+
+
+def test_error_paths_launch_nothing():
+    A = torch.ones((128, 64), dtype=torch.float16, device=DEV)
+    B = torch.ones((128, 64), dtype=torch.float16, device=DEV)
+    D = torch.full((128, 128), 7.0, dtype=torch.float16, device=DEV)
+    say("[gpu] error paths")
+    with pytest.raises(g.GemmError) as e:
+        g.gemm_f16_nt_rung(1, A[:, :56].contiguous(), B[:, :56].contiguous(), D)   # R1 needs K = 64
+    assert e.value.status == g.UNSUPPORTED
+    L = g.lib()
+    st = L.gemm_f16_nt(128, 128, 60, A.data_ptr(), B.data_ptr(), D.data_ptr(), None)
+    assert st == g.UNSUPPORTED
+    st = L.gemm_f16_nt(128, 128, 64, A.data_ptr() + 2, B.data_ptr(), D.data_ptr(), None)
+    assert st == g.UNSUPPORTED
+    torch.cuda.synchronize()
+    assert torch.all(D == 7.0).item()
+
+
+# ----------------------------------------------- invariants of the schedule
+
+def test_poisoned_output_is_fully_overwritten():
+    M, N, K = 520, 700, 256
+    A, B = rand_case(M, N, K, 77)
+    ref, _ = oracle.gemm_nt(A, B)
+    for rung in (0, 3, 4, 5):
+        D = torch.full((M, N), float("nan"), dtype=torch.float16, device=DEV)
+        say(f"[gpu] poison rung={rung}")
+        run(rung, dev(A), dev(B), D)
+        assert_parity(host_bits(D), ref, K, f"poison rung {rung}")
+
+
+def test_repeatable_and_grid_size_invariant():
+    M, N, K = 1280, 1536, 1024
+    A, B = rand_case(M, N, K, 78)
+    dA, dB = dev(A), dev(B)
+    say("[gpu] repeatability rung 4 / auto")
+    first = host_bits(run(4, dA, dB))
+    for _ in range(2):
+        assert np.array_equal(host_bits(run(4, dA, dB)), first)
+    base = None
+    for grid in (1, 7, 256, 512):
+        say(f"[gpu] persistent grid={grid}")
+        D = g.gemm_f16_nt_persistent(dA, dB, grid)
+        torch.cuda.synchronize()
+        bits = host_bits(D)
+        if base is None:
+            base = bits
+            ref, _ = oracle.gemm_nt(A, B)
+            assert_parity(bits, ref, K, "persistent")
+        assert np.array_equal(bits, base), f"grid {grid} differs"
+
+
+def test_non_default_stream_and_interleaving():
+    M, N, K = 512, 512, 512
+    A, B = rand_case(M, N, K, 79)
+    ref, _ = oracle.gemm_nt(A, B)
+    s = torch.cuda.Stream(device=DEV)
+    with torch.cuda.stream(s):
+        dA, dB = dev(A), dev(B)
+        say("[gpu] side stream")
+        X = torch.randn(2048, 2048, device=DEV)
+        for rung in (0, 4, 5):
+            D = g.gemm_f16_nt(dA, dB) if rung == 0 else g.gemm_f16_nt_rung(rung, dA, dB)
+            X = X * 1.0001          # unrelated work queued on the same stream
+            s.synchronize()
+            assert_parity(host_bits(D), ref, K, f"stream rung {rung}")
+
+
+# ------------------------------------------- full sizes, sampled outputs
+
+def sample_positions(M, N, count, seed):
+    rng = np.random.default_rng(seed)
+    rows = [0, M - 1, 255, 256, M // 2, M - 256] + list(rng.integers(0, M, count))
+    cols = [0, N - 1, 256, 255, N // 2, N - 257] + list(rng.integers(0, N, count))
+    return np.clip(np.array(rows), 0, M - 1), np.clip(np.array(cols), 0, N - 1)
+
+
+@pytest.mark.parametrize("name", ["square_4096", "square_8192", "tall_32768x1024x8192"])
+def test_full_size_workloads_sampled(name):
+    w = workloads.BY_NAME[name]
+    A, B = inputs.operands(w.M, w.N, w.K, w.seed, w.dist)
+    say(f"[gpu] full size {w.describe()} (library choice)")
+    dA, dB = dev(A), dev(B)
+    D = run(0, dA, dB)
+    rows, cols = sample_positions(w.M, w.N, 3000, w.seed)
+    ref, _ = oracle.gemm_nt_sampled(A, B, rows, cols)
+    got = host_bits(D[torch.from_numpy(rows).to(DEV), torch.from_numpy(cols).to(DEV)])
+    worst = assert_parity(got, ref, w.K, name)
+    say(f"      worst err/tol = {worst:.3f}")
+    # whole output: finite everywhere (the workloads cannot overflow)
+    assert torch.isfinite(D).all().item()
+    if name == "square_4096":
+        say("[gpu] full size square_4096 on rung 5")
+        D5 = run(5, dA, dB)
+        got5 = host_bits(D5[torch.from_numpy(rows).to(DEV), torch.from_numpy(cols).to(DEV)])
+        assert_parity(got5, ref, w.K, name + " rung 5")
