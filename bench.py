@@ -24,7 +24,6 @@ from __future__ import annotations
 
 import argparse
 import ctypes
-import hashlib
 import json
 import os
 import sys
@@ -36,23 +35,22 @@ sys.path.insert(0, ROOT)
 PEAK_FP16_TFLOPS = 2516.6   # MI355X dense fp16 MFMA: 256 CU x 2.4 GHz x 4096 FLOP/CU/clk
 HBM_PEAK_GBS = 8000.0
 METRIC = "fp16 GEMM TFLOP/s at M=N=K=4096 (+ % of MI355X dense-fp16 peak)"
-KERNEL_SOURCES = ["common.hpp", "sched.hpp", "ladder.hpp", "ring.hpp", "persistent_ws.hpp", "gemm_f16_nt.hip"]
 RUNG_NAMES = {0: "auto", 1: "r1_single_tile", 2: "r2_kloop", 3: "r3_grid", 4: "r4_ring",
               5: "r5_persistent_ws"}
 
 
 def kernel_source_hash() -> str:
-    h = hashlib.sha256()
-    for name in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, "dense_fp16_gemm_nt_amd", "csrc", name), "rb") as f:
-            h.update(f.read())
-    return h.hexdigest()[:16]
+    from dense_fp16_gemm_nt_amd.profiling import kernel_source_hash as h
+
+    return h()
 
 
 def traffic_record(workload: str, rung_name: str):
-    """HBM bytes per launch from profiles/traffic_<workload>.json if it was
-    taken on the current kernel sources, else None."""
-    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
+    """HBM bytes per launch from profiles/traffic_<rung>_<workload>.txt (a
+    JSON record written by dense_fp16_gemm_nt_amd.profiling from two
+    rocprofv3 counter passes) if it was taken on the current kernel
+    sources, else None."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{rung_name}_{workload}.txt")
     if not os.path.exists(path):
         return None
     with open(path) as f:

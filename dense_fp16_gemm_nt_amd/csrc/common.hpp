@@ -84,21 +84,21 @@ __device__ __forceinline__ void store_block(f16* __restrict__ D, int64_t ldd, in
 // ---------------------------------------------------------------------------
 // LDS tiles: a tile of R rows x BK fp16 is stored row-major with
 // CH = BK/8 16-byte chunks per row; chunk c of row r sits at physical chunk
-// c ^ swz(r).  The XOR spreads the 32 rows a fragment read touches (same
-// logical chunk) over distinct bank groups.  SWZ selects the row bits used.
+// c ^ swz(r).  A fragment read has 32 lanes read 32 consecutive rows at the
+// same logical chunk; the XOR spreads the rows that the LDS serves together
+// over distinct banks.  SWZ names the bank window the pattern is built for:
 //   SWZ 0: no swizzle
-//   SWZ 1: swz(r) = r mod CH                 (8 consecutive rows distinct)
-//   SWZ 2: swz(r) = (r / 2) mod CH for CH=8, (r / 4) mod 4 for CH=4
-//          (16 consecutive rows distinct when two rows share a 256-byte
-//           bank window)
+//   SWZ 1: 128-byte window (32 banks x 4 bytes, 8 lanes of 16 bytes per
+//          cycle): swz(r) = (r / rows_per_128B) mod CH
+//   SWZ 2: 256-byte window (64 banks): swz(r) = (r / rows_per_256B) mod CH
 // ---------------------------------------------------------------------------
 template <int CH, int SWZ>
 __host__ __device__ __forceinline__ int swz_of_row(int r)
 {
+    constexpr int ROW_BYTES = CH * 16;
     if (SWZ == 0) return 0;
-    if (SWZ == 1) return r & (CH - 1);
-    if (CH == 8) return (r >> 1) & 7;
-    return (r >> 2) & (CH - 1);
+    if (SWZ == 1) return (r / (128 / ROW_BYTES > 0 ? 128 / ROW_BYTES : 1)) & (CH - 1);
+    return (r / (256 / ROW_BYTES)) & (CH - 1);
 }
 
 template <int CH, int SWZ>
@@ -137,5 +137,26 @@ __device__ __forceinline__ void load_lds_16(const void* gptr, void* lds)
 {
     __builtin_amdgcn_global_load_lds((const G16_GLOBAL void*)gptr, (G16_LDS void*)lds, 16, 0, 0);
 }
+
+// Buffer resource over a byte range (raw buffer, 32-bit data format so the
+// descriptor is valid for untyped loads).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+// Direct-to-LDS 16-byte buffer load: lane i reads base + voff + soff and
+// its 16 bytes land at lds + 16*i (lds wave-uniform, goes to M0).
+__device__ __forceinline__ void buffer_load_lds_16(__amdgpu_buffer_rsrc_t r, void* lds, uint32_t voff,
+                                                   uint32_t soff)
+{
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (G16_LDS void*)lds, 16, (int)voff, (int)soff, 0, 0);
+}
+
+// Scheduling-group masks for __builtin_amdgcn_sched_group_barrier.
+constexpr int kSchedMfma = 0x008;
+constexpr int kSchedVmem = 0x010;
+constexpr int kSchedDsRead = 0x100;
+constexpr int kSchedDsWrite = 0x200;
 
 }  // namespace g16

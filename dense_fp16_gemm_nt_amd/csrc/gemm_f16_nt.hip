@@ -19,9 +19,13 @@ using namespace g16;
 
 namespace {
 
-// Kernel configurations of the fast rungs.
-using RingCfg = ring::Cfg<256, 256, 64, 2, 1>;
-using WsCfg = ws::Cfg<64, 2, 1>;
+// Kernel configurations of the fast rungs (measured on MI355X; see the
+// bench): rung 4 = 256 x 256 tile, 64-wide k steps, 2-stage ring, 8 waves of
+// 128 x 64 (two per SIMD), loads issued in the first sub-step, 2 MFMAs ahead
+// of each barrier, LDS-staged epilogue; rung 5 = 32-wide k steps, 4 stages.
+using RingCfg = ring::Cfg<256, 256, 64, 2, 2, 2, 4>;
+constexpr int kRingPre = 2, kRingLsplit = 1;
+using WsCfg = ws::Cfg<32, 4, 2>;
 constexpr int kFastTile = 256;
 
 __global__ void fill_zero_kernel(uint16_t* __restrict__ D, int64_t n)
@@ -116,11 +120,11 @@ int launch_ring(int64_t M, int64_t N, int64_t K, const f16* A, const f16* B, f16
     const int64_t tm = (M + kFastTile - 1) / kFastTile, tn = (N + kFastTile - 1) / kFastTile;
     const bool edge = (M % kFastTile) || (N % kFastTile) || (K % RingCfg::BK) || (N % 4);
     if (edge)
-        hipLaunchKernelGGL((ring::ring_kernel<RingCfg, true>), dim3((unsigned)(tm * tn)), dim3(RingCfg::THREADS), 0,
-                           s, A, B, D, M, N, K, tm, tn);
+        hipLaunchKernelGGL((ring::ring_kernel<RingCfg, true, kRingPre, kRingLsplit, true>), dim3((unsigned)(tm * tn)),
+                           dim3(RingCfg::THREADS), 0, s, A, B, D, M, N, K, tm, tn);
     else
-        hipLaunchKernelGGL((ring::ring_kernel<RingCfg, false>), dim3((unsigned)(tm * tn)), dim3(RingCfg::THREADS), 0,
-                           s, A, B, D, M, N, K, tm, tn);
+        hipLaunchKernelGGL((ring::ring_kernel<RingCfg, false, kRingPre, kRingLsplit, true>), dim3((unsigned)(tm * tn)),
+                           dim3(RingCfg::THREADS), 0, s, A, B, D, M, N, K, tm, tn);
     return launched();
 }
 

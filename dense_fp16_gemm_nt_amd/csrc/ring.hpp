@@ -1,20 +1,32 @@
 // Rung 4: pipelined LDS ring fed by direct-to-LDS loads.
 //
-// The pages' step 4/5 replace the threads' copy with an asynchronous copy
-// engine and then double-buffer the operand tiles so the next K tile
-// streams in while the current one is multiplied ("TIRx GEMM detailed
-// technical notes", V4 "TMA Async Load and Store" and V5 "Software Pipeline
-// with Double-Buffered SMEM").  On gfx950 the copy engine is the
-// direct-to-LDS form of the vector memory load (global_load_lds_dwordx4):
-// each lane names a 16-byte global source and the data lands in LDS without
-// passing through registers; completion is the issuing wave's vmcnt.
+// The pages' steps 4-5 replace the threads' copy with an asynchronous copy
+// engine and then multi-buffer the operand tiles so the next K tile streams
+// in while the current one is multiplied ("TIRx GEMM detailed technical
+// notes", V4 "TMA Async Load and Store" and V5 "Software Pipeline with
+// Double-Buffered SMEM").  On gfx950 the copy engine is the direct-to-LDS
+// form of the buffer load (buffer_load_dwordx4 ... lds): each lane names a
+// 16-byte global source and the data lands in LDS without passing through
+// registers; completion is the issuing wave's vmcnt.
 //
-// Workgroup tile BM x BN (256 x 256), BK-wide k steps, STAGES-deep ring.
-// 4 waves (one per SIMD), 2 x 2, each owning a (BM/2) x (BN/2) = 128 x 128
-// accumulator (16 blocks of 32x32, 256 fp32 per lane).  Every wave issues
-// its share of the loads and then multiplies; one workgroup barrier per k
-// step both publishes step k and releases the stage of step k-1.
+// Workgroup tile BM x BN (256 x 256), BK-wide k steps, a STAGES-deep ring
+// in LDS, WAVES_M x WAVES_N waves each owning a (BM/WAVES_M) x (BN/WAVES_N)
+// accumulator in registers.  Every wave issues its share of the loads and
+// multiplies; one workgroup barrier per k step both publishes step k+1 and
+// releases the stage of step k.  Schedule of one k step j:
+//  * sub-steps 0 .. KSUB-2: the fragments of sub-step kk+1 are read from LDS
+//    while the MFMAs of sub-step kk run (two register buffers), and during
+//    the first LSPLIT sub-steps this wave's loads of step j + STAGES - 1 go
+//    out one per MFMA (into the stage the barrier of step j-1 released);
+//  * last sub-step: wait until this wave's LDS reads of step j are complete
+//    and its loads of step j+1 have landed, issue PRE MFMAs so the matrix
+//    core stays busy, cross the barrier, read the first fragments of step
+//    j+1, finish the MFMAs of step j.
+// The loop body has no branch on the accumulators (the last step is peeled)
+// so they stay in place across iterations.
 #pragma once
+
+#include <type_traits>
 
 #include "common.hpp"
 #include "sched.hpp"
@@ -26,10 +38,11 @@ __device__ __attribute__((aligned(64))) uint32_t g_zero_line[16] = {0};
 
 namespace ring {
 
-template <int BM_, int BN_, int BK_, int STAGES_, int SWZ_>
+template <int BM_, int BN_, int BK_, int STAGES_, int SWZ_, int WM_ = 2, int WN_ = 2>
 struct Cfg {
     static constexpr int BM = BM_, BN = BN_, BK = BK_, STAGES = STAGES_, SWZ = SWZ_;
-    static constexpr int WAVES = 4, THREADS = 256;
+    static constexpr int WAVES_M = WM_, WAVES_N = WN_;     // wave grid over the tile
+    static constexpr int WAVES = WM_ * WN_, THREADS = 64 * WAVES;
     static constexpr int CH = BK / 8;                 // 16-byte chunks per LDS row
     static constexpr int ROW_BYTES = BK * 2;
     static constexpr int ROWS_PER_LOAD = 1024 / ROW_BYTES;  // one wave load = 1 KiB
@@ -39,7 +52,7 @@ struct Cfg {
     static constexpr int A_LOADS = A_BYTES / 1024 / WAVES;  // per wave per step
     static constexpr int B_LOADS = B_BYTES / 1024 / WAVES;
     static constexpr int LPW = A_LOADS + B_LOADS;
-    static constexpr int WTM = BM / 2, WTN = BN / 2;  // wave tile
+    static constexpr int WTM = BM / WAVES_M, WTN = BN / WAVES_N;  // wave tile
     static constexpr int FM = WTM / 32, FN = WTN / 32;
     static constexpr int KSUB = BK / 16;
     static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
@@ -92,31 +105,85 @@ __device__ __forceinline__ f16x8 frag(const char* tile, int row, int chunk)
     return *reinterpret_cast<const f16x8*>(tile + lds_chunk_offset<C::CH, C::SWZ>(row, chunk));
 }
 
-// Multiply one staged k step into the wave's accumulators.
+// Fragment registers of one 16-wide k sub-step: FM A rows-blocks and FN
+// B row-blocks, one 16-byte LDS read each.
 template <class C>
-__device__ __forceinline__ void mma_stage(const char* As, const char* Bs, int wm, int wn, int lane,
-                                          f32x16 (&acc)[C::FM][C::FN])
+__device__ __forceinline__ void read_frags(const char* st, int wm, int wn, int lane, int kk,
+                                           f16x8 (&a)[C::FM], f16x8 (&b)[C::FN])
+{
+    const int chunk = 2 * kk + (lane >> 5);
+#pragma unroll
+    for (int i = 0; i < C::FM; ++i) a[i] = frag<C>(st, wm + 32 * i + (lane & 31), chunk);
+#pragma unroll
+    for (int j = 0; j < C::FN; ++j) b[j] = frag<C>(st + C::A_BYTES, wn + 32 * j + (lane & 31), chunk);
+}
+
+// MFMAs [first, last) of one sub-step, in (i, j) row-major order.
+template <class C, int FIRST, int LAST>
+__device__ __forceinline__ void mfma_range(const f16x8 (&a)[C::FM], const f16x8 (&b)[C::FN],
+                                           f32x16 (&acc)[C::FM][C::FN])
 {
 #pragma unroll
-    for (int kk = 0; kk < C::KSUB; ++kk) {
-        const int chunk = 2 * kk + (lane >> 5);
-        f16x8 a[C::FM], b[C::FN];
-#pragma unroll
-        for (int i = 0; i < C::FM; ++i) a[i] = frag<C>(As, wm + 32 * i + (lane & 31), chunk);
-#pragma unroll
-        for (int j = 0; j < C::FN; ++j) b[j] = frag<C>(Bs, wn + 32 * j + (lane & 31), chunk);
-#pragma unroll
-        for (int i = 0; i < C::FM; ++i)
-#pragma unroll
-            for (int j = 0; j < C::FN; ++j) acc[i][j] = mfma_32x32x16(b[j], a[i], acc[i][j]);
+    for (int q = FIRST; q < LAST; ++q) {
+        const int i = q / C::FN, j = q % C::FN;
+        acc[i][j] = mfma_32x32x16(b[j], a[i], acc[i][j]);
     }
 }
 
-template <class C, bool EDGE>
-__global__ __launch_bounds__(256, 1) void ring_kernel(const f16* __restrict__ A, const f16* __restrict__ B,
-                                                      f16* __restrict__ D, int64_t M, int64_t N, int64_t K,
-                                                      int64_t tiles_m, int64_t tiles_n)
+// Interleave hint for one sub-step: NQ MFMAs, each followed by up to one LDS
+// read and one vector-memory load while any remain.
+// (nr, nl are compile-time constants once the callers' loops are unrolled.)
+template <int NQ>
+__device__ __forceinline__ void interleave_hint(int nr, int nl)
 {
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) {
+        __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+        if (q < nr) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
+        if (q < nl) __builtin_amdgcn_sched_group_barrier(kSchedVmem, 1, 0);
+    }
+}
+
+// Epilogue: round a wave's (FM*32) x (FN*32) accumulator tile to fp16, stage
+// it in LDS and write it to D with 16-byte stores that cover whole 128-byte
+// lines (the registers hold 4 consecutive columns per lane, which would
+// otherwise mean partial-line 8-byte stores).  Row r of the staged tile is FN*64 bytes;
+// 16-byte chunk c of row r sits at chunk c ^ (r mod CPR).
+template <class C>
+__device__ __forceinline__ void epilogue_lds(char* lds, f16* __restrict__ D, int64_t ldd, int64_t row0,
+                                             int64_t col0, const f32x16 (&acc)[C::FM][C::FN], int lane)
+{
+    constexpr int ROWB = C::FN * 64;      // bytes per staged row
+    constexpr int CPR = ROWB / 16;        // chunks per row
+#pragma unroll
+    for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+        for (int j = 0; j < C::FN; ++j)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const int r = 32 * i + (lane & 31);
+                const int c = 4 * j + g;
+                const int off = r * ROWB + ((c ^ (r % CPR)) << 4) + ((lane >> 5) << 3);
+                *reinterpret_cast<f16x4*>(lds + off) =
+                    cvt4(acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]);
+            }
+    wait_lgkmcnt0();
+    constexpr int ROWS_PER_STORE = 64 / CPR;
+#pragma unroll
+    for (int q = 0; q < C::FM * 32 / ROWS_PER_STORE; ++q) {
+        const int r = q * ROWS_PER_STORE + lane / CPR;
+        const int c = lane % CPR;
+        const u32x4 v = *reinterpret_cast<const u32x4*>(lds + r * ROWB + ((c ^ (r % CPR)) << 4));
+        *reinterpret_cast<u32x4*>(D + (row0 + r) * ldd + col0 + 8 * c) = v;
+    }
+}
+
+template <class C, bool EDGE, int PRE, int LSPLIT, bool EPI_LDS>
+__global__ __launch_bounds__(C::THREADS, 1) void ring_kernel(const f16* __restrict__ A, const f16* __restrict__ B,
+                                                       f16* __restrict__ D, int64_t M, int64_t N, int64_t K,
+                                                       int64_t tiles_m, int64_t tiles_n)
+{
+    static_assert(LSPLIT >= 1 && LSPLIT < C::KSUB && C::LPW % LSPLIT == 0, "load split");
     __shared__ __attribute__((aligned(1024))) char smem[C::LDS_BYTES];
     const int t = threadIdx.x, lane = t & 63;
     const int w = __builtin_amdgcn_readfirstlane(t >> 6);
@@ -133,13 +200,31 @@ __global__ __launch_bounds__(256, 1) void ring_kernel(const f16* __restrict__ A,
     lane_offsets<C, C::A_LOADS>(w, lane, ldb, a_off, a_row, a_kc);
     lane_offsets<C, C::B_LOADS>(w, lane, ldb, b_off, b_row, b_kc);
     const int64_t a_rows = M - m0, b_rows = N - n0;
+    const __amdgpu_buffer_rsrc_t a_rsrc = make_rsrc(a_base, (uint32_t)(C::BM * ldb));
+    const __amdgpu_buffer_rsrc_t b_rsrc = make_rsrc(b_base, (uint32_t)(C::BN * ldb));
 
-    const int64_t KT = (K + C::BK - 1) / C::BK;
-    auto issue = [&](int64_t step) {
+    // load q (0 .. LPW-1) of this wave for k step `step`
+    auto load_one = [&](int64_t step, int q) {
         char* st = smem + (int)(step % C::STAGES) * C::STAGE_BYTES;
         const int64_t k0 = step * C::BK;
-        issue_loads<C, C::A_LOADS, EDGE>(a_base, a_off, a_row, a_kc, a_rows, K, k0, st, w);
-        issue_loads<C, C::B_LOADS, EDGE>(b_base, b_off, b_row, b_kc, b_rows, K, k0, st + C::A_BYTES, w);
+        if (q < C::A_LOADS) {
+            char* d = st + (w * C::A_LOADS + q) * 1024;
+            if (EDGE) {
+                const bool ok = a_row[q] < a_rows && k0 + a_kc[q] < K;
+                load_lds_16(ok ? (const void*)(a_base + k0 * 2 + a_off[q]) : (const void*)g_zero_line, d);
+            } else {
+                buffer_load_lds_16(a_rsrc, d, a_off[q], (uint32_t)(k0 * 2));
+            }
+        } else {
+            const int qb = q - C::A_LOADS;
+            char* d = st + C::A_BYTES + (w * C::B_LOADS + qb) * 1024;
+            if (EDGE) {
+                const bool ok = b_row[qb] < b_rows && k0 + b_kc[qb] < K;
+                load_lds_16(ok ? (const void*)(b_base + k0 * 2 + b_off[qb]) : (const void*)g_zero_line, d);
+            } else {
+                buffer_load_lds_16(b_rsrc, d, b_off[qb], (uint32_t)(k0 * 2));
+            }
+        }
     };
 
     f32x16 acc[C::FM][C::FN];
@@ -148,38 +233,87 @@ __global__ __launch_bounds__(256, 1) void ring_kernel(const f16* __restrict__ A,
 #pragma unroll
         for (int j = 0; j < C::FN; ++j) acc[i][j] = f32x16{};
 
+    const int64_t KT = (K + C::BK - 1) / C::BK;
     // prologue: steps 0 .. STAGES-2
 #pragma unroll
     for (int s = 0; s < C::STAGES - 1; ++s)
-        if (s < KT) issue(s);
+        if (s < KT)
+#pragma unroll
+            for (int q = 0; q < C::LPW; ++q) load_one(s, q);
+    if (KT >= C::STAGES - 1)
+        wait_vmcnt<(C::STAGES - 2) * C::LPW>();
+    else
+        wait_vmcnt<0>();
+    wg_barrier();
 
-    const int wm = (w >> 1) * C::WTM, wn = (w & 1) * C::WTN;
-    for (int64_t kt = 0; kt < KT; ++kt) {
-        // this wave's loads of step kt have landed
-        if (kt + C::STAGES - 2 < KT)
+    const int wm = (w / C::WAVES_N) * C::WTM, wn = (w % C::WAVES_N) * C::WTN;
+    constexpr int NQ = C::FM * C::FN;
+    constexpr int NR = C::FM + C::FN;
+    constexpr int LPS = C::LPW / LSPLIT;   // loads per loading sub-step
+    constexpr int LB = (C::KSUB - 1) & 1;
+    f16x8 fa[2][C::FM], fb[2][C::FN];
+    read_frags<C>(smem, wm, wn, lane, 0, fa[0], fb[0]);
+
+    // sub-steps 0 .. KSUB-2 of step j; LOADS: issue step j+STAGES-1
+    auto substeps = [&](int64_t j, auto loads_tag) {
+        constexpr bool LOADS = decltype(loads_tag)::value;
+        const char* st = smem + (int)(j % C::STAGES) * C::STAGE_BYTES;
+#pragma unroll
+        for (int kk = 0; kk < C::KSUB - 1; ++kk) {
+            read_frags<C>(st, wm, wn, lane, kk + 1, fa[(kk + 1) & 1], fb[(kk + 1) & 1]);
+            if (LOADS && kk < LSPLIT) {
+#pragma unroll
+                for (int q = 0; q < LPS; ++q) load_one(j + C::STAGES - 1, kk * LPS + q);
+            }
+            mfma_range<C, 0, NQ>(fa[kk & 1], fb[kk & 1], acc);
+            interleave_hint<NQ>(NR, (LOADS && kk < LSPLIT) ? LPS : 0);
+        }
+    };
+    // last sub-step of step j with the handoff to step j+1
+    auto handoff = [&](int64_t j, auto exact_tag) {
+        constexpr bool EXACT = decltype(exact_tag)::value;
+        wait_lgkmcnt0();
+        mfma_range<C, 0, PRE>(fa[LB], fb[LB], acc);
+        if (EXACT)
             wait_vmcnt<(C::STAGES - 2) * C::LPW>();
         else
             wait_vmcnt<0>();
-        // every wave's loads of step kt are visible, and every wave has
-        // finished reading the stage of step kt-1
         wg_barrier();
-        const int64_t nk = ring_refill_after(kt - 1, C::STAGES, KT);
-        if (nk >= 0) issue(nk);
-        const char* st = smem + (int)(kt % C::STAGES) * C::STAGE_BYTES;
-        mma_stage<C>(st, st + C::A_BYTES, wm, wn, lane, acc);
-    }
+        read_frags<C>(smem + (int)((j + 1) % C::STAGES) * C::STAGE_BYTES, wm, wn, lane, 0, fa[0], fb[0]);
+        mfma_range<C, PRE, NQ>(fa[LB], fb[LB], acc);
+        interleave_hint<NQ - PRE>(NR, 0);
+    };
+    using True_ = std::integral_constant<bool, true>;
+    using False_ = std::integral_constant<bool, false>;
 
-    const bool full = !EDGE || (m0 + C::BM <= M && n0 + C::BN <= N && N % 4 == 0);
+    const int64_t j_loads_end = KT - C::STAGES + 1;  // steps j < this issue loads
+    int64_t j = 0;
+    for (; j < j_loads_end && j + 1 < KT; ++j) {
+        substeps(j, True_{});
+        handoff(j, True_{});
+    }
+    for (; j + 1 < KT; ++j) {
+        substeps(j, False_{});
+        handoff(j, False_{});
+    }
+    substeps(KT - 1, False_{});
+    mfma_range<C, 0, NQ>(fa[LB], fb[LB], acc);
+    if (!EDGE && EPI_LDS) {
+        wg_barrier();  // every wave is done reading the ring
+        epilogue_lds<C>(smem + w * (C::FM * 32 * C::FN * 64), D, N, m0 + wm, n0 + wn, acc, lane);
+    } else {
+        const bool full = !EDGE || (m0 + C::BM <= M && n0 + C::BN <= N && N % 4 == 0);
 #pragma unroll
-    for (int i = 0; i < C::FM; ++i)
+        for (int i = 0; i < C::FM; ++i)
 #pragma unroll
-        for (int j = 0; j < C::FN; ++j) {
-            const int64_t mb = m0 + wm + 32 * i, nb = n0 + wn + 32 * j;
-            if (full)
-                store_block<true>(D, N, M, N, mb, nb, acc[i][j], lane);
-            else
-                store_block<false>(D, N, M, N, mb, nb, acc[i][j], lane);
-        }
+            for (int jj = 0; jj < C::FN; ++jj) {
+                const int64_t mb = m0 + wm + 32 * i, nb = n0 + wn + 32 * jj;
+                if (full)
+                    store_block<true>(D, N, M, N, mb, nb, acc[i][jj], lane);
+                else
+                    store_block<false>(D, N, M, N, mb, nb, acc[i][jj], lane);
+            }
+    }
 }
 
 }  // namespace ring

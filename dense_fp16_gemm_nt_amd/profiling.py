@@ -1,0 +1,125 @@
+"""Summaries of rocprofv3 output for the GEMM kernels (short text files).
+
+  python -m dense_fp16_gemm_nt_amd.profiling stats  --dir D --kernel SUBSTR --command CMD --out FILE
+      per-kernel dispatch count and mean/min/max duration from a
+      `rocprofv3 --kernel-trace --stats --output-format csv` run
+  python -m dense_fp16_gemm_nt_amd.profiling traffic --fetch D1 --write D2 --copy-fetch D3 --copy-write D4
+      --copy-bytes N --kernel SUBSTR --workload NAME --rung NAME --command CMD --out FILE
+      HBM bytes per dispatch of the kernel from FETCH_SIZE / WRITE_SIZE
+      passes (KiB per dispatch), each scaled by what the same counter reads
+      for a device copy of known size
+"""
+from __future__ import annotations
+
+import argparse
+import csv
+import glob
+import hashlib
+import json
+import os
+import statistics
+import sys
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+KERNEL_SOURCES = ["common.hpp", "sched.hpp", "ladder.hpp", "ring.hpp", "persistent_ws.hpp", "gemm_f16_nt.hip"]
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "dense_fp16_gemm_nt_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def _find(d: str, pattern: str) -> str:
+    hits = sorted(glob.glob(os.path.join(d, "**", pattern), recursive=True))
+    if not hits:
+        raise FileNotFoundError(f"no {pattern} under {d}")
+    return hits[0]
+
+
+def kernel_stats(d: str, substr: str):
+    rows = list(csv.DictReader(open(_find(d, "*kernel_trace.csv"))))
+    durs = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3 for r in rows if substr in r["Kernel_Name"]]
+    names = sorted({r["Kernel_Name"] for r in rows if substr in r["Kernel_Name"]})
+    return names, durs
+
+
+def counter_per_dispatch(d: str, counter: str, substr: str) -> float:
+    rows = list(csv.DictReader(open(_find(d, "*counter_collection.csv"))))
+    per = {}
+    for r in rows:
+        if substr in r["Kernel_Name"] and r["Counter_Name"] == counter:
+            per.setdefault(r["Dispatch_Id"], 0.0)
+            per[r["Dispatch_Id"]] += float(r["Counter_Value"])
+    if not per:
+        raise ValueError(f"{counter} for {substr!r} not found in {d}")
+    return statistics.mean(per.values())
+
+
+def cmd_stats(a):
+    names, durs = kernel_stats(a.dir, a.kernel)
+    lines = [f"# rocprofv3 kernel trace summary: {a.kernel}",
+             f"command: {a.command}",
+             f"kernels: {', '.join(names)}",
+             f"dispatches: {len(durs)}",
+             f"mean_us: {statistics.mean(durs):.3f}",
+             f"median_us: {statistics.median(durs):.3f}",
+             f"min_us: {min(durs):.3f}",
+             f"max_us: {max(durs):.3f}",
+             f"kernel_src_sha: {kernel_source_hash()}"]
+    stats_csv = glob.glob(os.path.join(a.dir, "**", "*kernel_stats.csv"), recursive=True)
+    if stats_csv:
+        lines.append("")
+        lines.append("## rocprofv3 --stats (kernel_stats.csv rows)")
+        for r in csv.DictReader(open(stats_csv[0])):
+            lines.append(", ".join(f"{k}={v}" for k, v in r.items()))
+    open(a.out, "w").write("\n".join(lines) + "\n")
+    print("\n".join(lines[:9]))
+
+
+def cmd_traffic(a):
+    fetch_k = counter_per_dispatch(a.fetch, "FETCH_SIZE", a.kernel)
+    write_k = counter_per_dispatch(a.write, "WRITE_SIZE", a.kernel)
+    copy_fetch_k = counter_per_dispatch(a.copy_fetch, "FETCH_SIZE", a.copy_kernel)
+    copy_write_k = counter_per_dispatch(a.copy_write, "WRITE_SIZE", a.copy_kernel)
+    f_scale = a.copy_bytes / (copy_fetch_k * 1024.0)
+    w_scale = a.copy_bytes / (copy_write_k * 1024.0)
+    rec = {
+        "workload": a.workload, "rung": a.rung, "kernel": a.kernel,
+        "fetch_kib_per_dispatch": fetch_k, "write_kib_per_dispatch": write_k,
+        "copy_bytes": a.copy_bytes, "copy_fetch_kib": copy_fetch_k, "copy_write_kib": copy_write_k,
+        "fetch_scale": f_scale, "write_scale": w_scale,
+        "hbm_bytes_per_launch": fetch_k * 1024.0 * f_scale + write_k * 1024.0 * w_scale,
+        "kernel_src_sha": kernel_source_hash(),
+        "command": a.command,
+    }
+    open(a.out, "w").write(json.dumps(rec, indent=1) + "\n")
+    print(json.dumps(rec, indent=1))
+
+
+def main(argv=None):
+    p = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    sub = p.add_subparsers(dest="cmd", required=True)
+    s = sub.add_parser("stats")
+    s.add_argument("--dir", required=True)
+    s.add_argument("--kernel", required=True)
+    s.add_argument("--command", required=True)
+    s.add_argument("--out", required=True)
+    t = sub.add_parser("traffic")
+    for k in ("fetch", "write", "copy_fetch", "copy_write"):
+        t.add_argument("--" + k.replace("_", "-"), dest=k, required=True)
+    t.add_argument("--copy-bytes", type=float, required=True)
+    t.add_argument("--copy-kernel", default="copy")
+    t.add_argument("--kernel", required=True)
+    t.add_argument("--workload", required=True)
+    t.add_argument("--rung", required=True)
+    t.add_argument("--command", required=True)
+    t.add_argument("--out", required=True)
+    a = p.parse_args(argv)
+    {"stats": cmd_stats, "traffic": cmd_traffic}[a.cmd](a)
+
+
+if __name__ == "__main__":
+    sys.exit(main())
