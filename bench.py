@@ -63,8 +63,8 @@ def traffic_record(workload: str, rung_name: str):
 def parse():
     p = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=50)
-    p.add_argument("--warmup", type=int, default=10)
+    p.add_argument("--steps", type=int, default=1000)
+    p.add_argument("--warmup", type=int, default=100)
     p.add_argument("--workload", default="square_4096")
     p.add_argument("--rung", type=int, default=0, help="0 = library choice, 1..5 = ladder rung")
     p.add_argument("--no-cpu-baseline", action="store_true")

@@ -57,6 +57,10 @@ def lib() -> ctypes.CDLL:
             L.gemm_f16_nt_rung.argtypes = [i32, i64, i64, i64, vp, vp, vp, vp]
             L.gemm_f16_nt_persistent.restype = i32
             L.gemm_f16_nt_persistent.argtypes = [i64, i64, i64, vp, vp, vp, i64, vp]
+            L.gemm_f16_nt_strided_batched.restype = i32
+            L.gemm_f16_nt_strided_batched.argtypes = [i64, i64, i64, vp, i64, i64, vp, i64, i64, vp, i64, i64, i64, vp]
+            L.gemm_f16_nt_check_strided.restype = i32
+            L.gemm_f16_nt_check_strided.argtypes = [i64, i64, i64, vp, i64, i64, vp, i64, i64, vp, i64, i64, i64]
             L.gemm_f16_nt_check.restype = i32
             L.gemm_f16_nt_check.argtypes = [i32, i64, i64, i64, vp, vp, vp]
             L.gemm_f16_nt_status_string.restype = ctypes.c_char_p
@@ -130,9 +134,95 @@ def gemm_f16_nt_persistent(A, B, num_workgroups: int, D=None):
     return D
 
 
+def _as_batched(X, name):
+    """(batch or None, rows, cols, ld, stride) of a 2D or 3D fp16 device tensor
+    whose last dimension is contiguous."""
+    import torch
+
+    if X.dtype != torch.float16 or not X.is_cuda:
+        raise TypeError(f"{name} must be a float16 device tensor")
+    if X.dim() == 2:
+        if X.stride(1) != 1:
+            raise ValueError(f"{name}: last dimension must be contiguous")
+        return None, X.shape[0], X.shape[1], X.stride(0), 0
+    if X.dim() == 3:
+        if X.stride(2) != 1:
+            raise ValueError(f"{name}: last dimension must be contiguous")
+        return X.shape[0], X.shape[1], X.shape[2], X.stride(1), X.stride(0)
+    raise ValueError(f"{name} must be 2D or 3D")
+
+
+def gemm_f16_nt_strided_batched(A, B, D=None):
+    """D[b] = A[b] @ B[b].T for 3D (or 2D, broadcast) fp16 tensors whose last
+    dimension is contiguous; any leading dimension / batch stride the C-ABI
+    accepts.  D defaults to a new contiguous (batch, M, N) tensor."""
+    import torch
+
+    ba, M, K, lda, sa = _as_batched(A, "A")
+    bb, N, Kb, ldb, sb = _as_batched(B, "B")
+    if Kb != K:
+        raise ValueError(f"inner dimensions differ: {K} and {Kb}")
+    if ba is not None and bb is not None and ba != bb:
+        raise ValueError(f"batch sizes differ: {ba} and {bb}")
+    batch = ba if ba is not None else (bb if bb is not None else 1)
+    if A.device != B.device:
+        raise ValueError("A and B on different devices")
+    if D is None:
+        D = torch.empty((batch, M, N), dtype=torch.float16, device=A.device)
+    bd, Md, Nd, ldd, sd = _as_batched(D if D.dim() == 3 else D.unsqueeze(0), "D")
+    if (bd, Md, Nd) != (batch, M, N):
+        raise ValueError(f"D must be {batch} x {M} x {N}")
+    st = lib().gemm_f16_nt_strided_batched(M, N, K, A.data_ptr(), lda, sa, B.data_ptr(), ldb, sb,
+                                           D.data_ptr(), ldd, sd, batch, _stream(A))
+    if st != OK:
+        raise GemmError(st, "gemm_f16_nt_strided_batched")
+    return D
+
+
+def attention_scores(Q, Kt):
+    """Unscaled attention scores S = Q @ K^T per head: Q (..., Sq, d) and
+    K (..., Sk, d) with equal leading dimensions -> S (..., Sq, Sk), fp16
+    (fp32 accumulation, one rounding), on the strided-batched kernel.  No
+    scaling or softmax is applied."""
+    import torch
+
+    if Q.shape[:-2] != Kt.shape[:-2] or Q.shape[-1] != Kt.shape[-1]:
+        raise ValueError(f"shapes {tuple(Q.shape)} and {tuple(Kt.shape)} do not match")
+    lead = tuple(Q.shape[:-2])
+    Sq, Sk = Q.shape[-2], Kt.shape[-2]
+    S = torch.empty(lead + (Sq, Sk), dtype=torch.float16, device=Q.device)
+
+    def as3(X):
+        # collapse the leading dimensions when one stride describes them
+        if X.dim() == 2:
+            return X.unsqueeze(0)
+        try:
+            return X.view(-1, X.shape[-2], X.shape[-1])
+        except RuntimeError:
+            return None
+
+    q3, k3, s3 = as3(Q), as3(Kt), as3(S)
+    if q3 is not None and k3 is not None:
+        gemm_f16_nt_strided_batched(q3, k3, s3)
+        return S
+    # leading dimensions not collapsible (e.g. heads interleaved in the
+    # rows): one batched call per index of the outer dimensions
+    for idx in torch.cartesian_prod(*[torch.arange(n) for n in lead[:-1]]).reshape(-1, len(lead) - 1).tolist() \
+            if len(lead) > 1 else [[]]:
+        sl = tuple(idx)
+        gemm_f16_nt_strided_batched(Q[sl], Kt[sl], S[sl])
+    return S
+
+
 def check(rung: int, M: int, N: int, K: int, A_ptr: int, B_ptr: int, D_ptr: int) -> int:
     """Validation status for raw arguments (no HIP call)."""
     return lib().gemm_f16_nt_check(int(rung), int(M), int(N), int(K), A_ptr, B_ptr, D_ptr)
+
+
+def check_strided(M, N, K, A_ptr, lda, sa, B_ptr, ldb, sb, D_ptr, ldd, sd, batch) -> int:
+    """Validation status of the strided form for raw arguments (no HIP call)."""
+    return lib().gemm_f16_nt_check_strided(int(M), int(N), int(K), A_ptr, int(lda), int(sa), B_ptr, int(ldb),
+                                           int(sb), D_ptr, int(ldd), int(sd), int(batch))
 
 
 def schedule(M: int, N: int, num_workgroups: int):

@@ -57,10 +57,13 @@ __device__ __forceinline__ f16x4 cvt4(float a, float b, float c, float d)
 }
 
 // Write one 32x32 accumulator block whose top-left output is (m0, n0).
-// FULL: the block lies inside D and N % 4 == 0 (8-byte aligned stores).
+// FULL: the block lies inside D and every row start is 8-byte aligned.
+// Otherwise rows >= M and columns >= N are skipped, and 8-byte stores are
+// used only where `vec` says row starts are 8-byte aligned.
 template <bool FULL>
 __device__ __forceinline__ void store_block(f16* __restrict__ D, int64_t ldd, int64_t M, int64_t N,
-                                            int64_t m0, int64_t n0, const f32x16& acc, int lane)
+                                            int64_t m0, int64_t n0, const f32x16& acc, int lane,
+                                            bool vec = true)
 {
     const int64_t m = m0 + acc_row(lane);
 #pragma unroll
@@ -70,7 +73,7 @@ __device__ __forceinline__ void store_block(f16* __restrict__ D, int64_t ldd, in
         if (FULL) {
             *reinterpret_cast<f16x4*>(D + m * ldd + n) = h;
         } else if (m < M) {
-            if (n + 3 < N && (ldd % 4) == 0) {
+            if (vec && n + 3 < N) {
                 *reinterpret_cast<f16x4*>(D + m * ldd + n) = h;
             } else {
 #pragma unroll
@@ -137,6 +140,20 @@ __device__ __forceinline__ void load_lds_16(const void* gptr, void* lds)
 {
     __builtin_amdgcn_global_load_lds((const G16_GLOBAL void*)gptr, (G16_LDS void*)lds, 16, 0, 0);
 }
+
+// Problem description passed to the tiled kernels by value.  Leading
+// dimensions and batch strides are in elements; batch b reads
+// A + b*sa, B + b*sb and writes D + b*sd.
+struct GemmArgs {
+    const f16* A;
+    const f16* B;
+    f16* D;
+    int64_t M, N, K;
+    int64_t lda, ldb, ldd;
+    int64_t sa, sb, sd;
+    int64_t batch;
+    int64_t tiles_m, tiles_n;  // output tiles per batch entry
+};
 
 // Buffer resource over a byte range (raw buffer, 32-bit data format so the
 // descriptor is valid for untyped loads).

@@ -102,6 +102,47 @@ int validate(int rung, int64_t M, int64_t N, int64_t K, const void* A, const voi
     return GEMM_F16_NT_OK;
 }
 
+// Extent in elements of a batch of row-major matrices, for the overlap check.
+int64_t span_elems(int64_t rows, int64_t cols, int64_t ld, int64_t stride, int64_t batch)
+{
+    if (rows <= 0 || cols <= 0 || batch <= 0) return 0;
+    return (batch - 1) * stride + (rows - 1) * ld + cols;
+}
+
+int validate_strided(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, int64_t sa, const void* B,
+                     int64_t ldb, int64_t sb, const void* D, int64_t ldd, int64_t sd, int64_t batch)
+{
+    if (M < 0 || N < 0 || K < 0 || batch < 0) return GEMM_F16_NT_INVALID_ARG;
+    if (lda < K || ldb < K || ldd < N || sa < 0 || sb < 0 || sd < 0) return GEMM_F16_NT_INVALID_ARG;
+    const bool any_out = M > 0 && N > 0 && batch > 0;
+    if (!any_out) return GEMM_F16_NT_OK;
+    if (D == nullptr || (K > 0 && (A == nullptr || B == nullptr))) return GEMM_F16_NT_INVALID_ARG;
+    // batch entries of D must not overlap each other (they are written concurrently)
+    if (batch > 1 && sd < (M - 1) * ldd + N) return GEMM_F16_NT_INVALID_ARG;
+    if (K % 8 != 0 || lda % 8 != 0 || ldb % 8 != 0 || sa % 8 != 0 || sb % 8 != 0) return GEMM_F16_NT_UNSUPPORTED;
+    if (K > (int64_t(1) << 22) || lda > (int64_t(1) << 22) || ldb > (int64_t(1) << 22) || M > (int64_t(1) << 31) ||
+        N > (int64_t(1) << 31) || batch > (int64_t(1) << 31))
+        return GEMM_F16_NT_UNSUPPORTED;
+    if (K > 0 && (((uintptr_t)A & 15) || ((uintptr_t)B & 15))) return GEMM_F16_NT_UNSUPPORTED;
+    if ((uintptr_t)D & 15) return GEMM_F16_NT_UNSUPPORTED;
+    const int64_t dbytes = span_elems(M, N, ldd, sd, batch) * 2;
+    if (K > 0 && (overlaps(A, span_elems(M, K, lda, sa, batch) * 2, D, dbytes) ||
+                  overlaps(B, span_elems(N, K, ldb, sb, batch) * 2, D, dbytes)))
+        return GEMM_F16_NT_INVALID_ARG;
+    return GEMM_F16_NT_OK;
+}
+
+__global__ void fill_zero_strided_kernel(uint16_t* __restrict__ D, int64_t M, int64_t N, int64_t ldd, int64_t sd,
+                                         int64_t batch)
+{
+    const int64_t per = M * N, n = per * batch;
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride) {
+        const int64_t b = i / per, r = (i - b * per) / N, c = i - b * per - r * N;
+        D[b * sd + r * ldd + c] = 0;
+    }
+}
+
 int launched()
 {
     return hipGetLastError() == hipSuccess ? GEMM_F16_NT_OK : GEMM_F16_NT_LAUNCH;
@@ -115,17 +156,39 @@ int launch_fill_zero(void* D, int64_t n, hipStream_t s)
     return launched();
 }
 
-int launch_ring(int64_t M, int64_t N, int64_t K, const f16* A, const f16* B, f16* D, hipStream_t s)
+int launch_ring(const GemmArgs& g0, hipStream_t s)
 {
-    const int64_t tm = (M + kFastTile - 1) / kFastTile, tn = (N + kFastTile - 1) / kFastTile;
-    const bool edge = (M % kFastTile) || (N % kFastTile) || (K % RingCfg::BK) || (N % 4);
+    GemmArgs g = g0;
+    g.tiles_m = (g.M + kFastTile - 1) / kFastTile;
+    g.tiles_n = (g.N + kFastTile - 1) / kFastTile;
+    const int64_t blocks = g.tiles_m * g.tiles_n * g.batch;
+    if (blocks > 0x7fffffff) return GEMM_F16_NT_UNSUPPORTED;
+    // the fast variant needs whole tiles and 16-byte aligned rows of D
+    const bool edge = (g.M % kFastTile) || (g.N % kFastTile) || (g.K % RingCfg::BK) || (g.ldd % 8) || (g.sd % 8);
     if (edge)
-        hipLaunchKernelGGL((ring::ring_kernel<RingCfg, true, kRingPre, kRingLsplit, true>), dim3((unsigned)(tm * tn)),
-                           dim3(RingCfg::THREADS), 0, s, A, B, D, M, N, K, tm, tn);
+        hipLaunchKernelGGL((ring::ring_kernel<RingCfg, true, kRingPre, kRingLsplit, true>), dim3((unsigned)blocks),
+                           dim3(RingCfg::THREADS), 0, s, g);
     else
-        hipLaunchKernelGGL((ring::ring_kernel<RingCfg, false, kRingPre, kRingLsplit, true>), dim3((unsigned)(tm * tn)),
-                           dim3(RingCfg::THREADS), 0, s, A, B, D, M, N, K, tm, tn);
+        hipLaunchKernelGGL((ring::ring_kernel<RingCfg, false, kRingPre, kRingLsplit, true>), dim3((unsigned)blocks),
+                           dim3(RingCfg::THREADS), 0, s, g);
     return launched();
+}
+
+GemmArgs contiguous_args(int64_t M, int64_t N, int64_t K, const void* A, const void* B, void* D)
+{
+    GemmArgs g{};
+    g.A = (const f16*)A;
+    g.B = (const f16*)B;
+    g.D = (f16*)D;
+    g.M = M;
+    g.N = N;
+    g.K = K;
+    g.lda = K;
+    g.ldb = K;
+    g.ldd = N;
+    g.sa = g.sb = g.sd = 0;
+    g.batch = 1;
+    return g;
 }
 
 int launch_ws(int64_t M, int64_t N, int64_t K, const f16* A, const f16* B, f16* D, int64_t grid,
@@ -168,11 +231,11 @@ int run(int rung, int64_t M, int64_t N, int64_t K, const void* A, const void* B,
         return launched();
     }
     case GEMM_F16_NT_R4_RING:
-        return launch_ring(M, N, K, a, b, d, s);
+        return launch_ring(contiguous_args(M, N, K, A, B, D), s);
     case GEMM_F16_NT_R5_PERSISTENT_WS:
         return launch_ws(M, N, K, a, b, d, grid_override > 0 ? grid_override : cus, s);
     default:  // 0: the library's choice
-        return launch_ring(M, N, K, a, b, d, s);
+        return launch_ring(contiguous_args(M, N, K, A, B, D), s);
     }
 }
 
@@ -197,6 +260,47 @@ int gemm_f16_nt_persistent(int64_t M, int64_t N, int64_t K, const void* A, const
 {
     if (num_workgroups < 1 || num_workgroups > (int64_t(1) << 31) - 1) return GEMM_F16_NT_INVALID_ARG;
     return run(GEMM_F16_NT_R5_PERSISTENT_WS, M, N, K, A, B, D, num_workgroups, stream);
+}
+
+int gemm_f16_nt_strided_batched(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, int64_t stride_a,
+                                const void* B, int64_t ldb, int64_t stride_b, void* D, int64_t ldd,
+                                int64_t stride_d, int64_t batch, void* stream)
+{
+    int st = validate_strided(M, N, K, A, lda, stride_a, B, ldb, stride_b, D, ldd, stride_d, batch);
+    if (st != GEMM_F16_NT_OK) return st;
+    if (M == 0 || N == 0 || batch == 0) return GEMM_F16_NT_OK;
+    int cus = 0;
+    st = device_info(&cus);
+    if (st != GEMM_F16_NT_OK) return st;
+    hipStream_t s = (hipStream_t)stream;
+    if (K == 0) {
+        const int64_t n = M * N * batch, blocks = (n + 255) / 256;
+        hipLaunchKernelGGL(fill_zero_strided_kernel, dim3((unsigned)(blocks < 4096 ? blocks : 4096)), dim3(256), 0, s,
+                           (uint16_t*)D, M, N, ldd, stride_d, batch);
+        return launched();
+    }
+    GemmArgs g{};
+    g.A = (const f16*)A;
+    g.B = (const f16*)B;
+    g.D = (f16*)D;
+    g.M = M;
+    g.N = N;
+    g.K = K;
+    g.lda = lda;
+    g.ldb = ldb;
+    g.ldd = ldd;
+    g.sa = stride_a;
+    g.sb = stride_b;
+    g.sd = stride_d;
+    g.batch = batch;
+    return launch_ring(g, s);
+}
+
+int gemm_f16_nt_check_strided(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, int64_t stride_a,
+                              const void* B, int64_t ldb, int64_t stride_b, const void* D, int64_t ldd,
+                              int64_t stride_d, int64_t batch)
+{
+    return validate_strided(M, N, K, A, lda, stride_a, B, ldb, stride_b, D, ldd, stride_d, batch);
 }
 
 int gemm_f16_nt_check(int rung, int64_t M, int64_t N, int64_t K, const void* A, const void* B, const void* D)

@@ -130,7 +130,7 @@ __global__ __launch_bounds__(THREADS) void r23_kloop_grid(const f16* __restrict_
             if (full)
                 store_block<true>(D, N, M, N, m_st + wm + 32 * i, n_st + wn + 32 * j, acc[i][j], lane);
             else
-                store_block<false>(D, N, M, N, m_st + wm + 32 * i, n_st + wn + 32 * j, acc[i][j], lane);
+                store_block<false>(D, N, M, N, m_st + wm + 32 * i, n_st + wn + 32 * j, acc[i][j], lane, N % 4 == 0);
         }
 }
 

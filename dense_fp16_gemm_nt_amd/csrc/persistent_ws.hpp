@@ -153,7 +153,7 @@ __global__ __launch_bounds__(768, 1) void ws_kernel(const f16* __restrict__ A, c
                 if (full)
                     store_block<true>(D, N, M, N, mb, nb, acc[a][b], lane);
                 else
-                    store_block<false>(D, N, M, N, mb, nb, acc[a][b], lane);
+                    store_block<false>(D, N, M, N, mb, nb, acc[a][b], lane, N % 4 == 0);
             }
     }
 }

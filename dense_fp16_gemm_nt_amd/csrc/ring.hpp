@@ -179,29 +179,33 @@ __device__ __forceinline__ void epilogue_lds(char* lds, f16* __restrict__ D, int
 }
 
 template <class C, bool EDGE, int PRE, int LSPLIT, bool EPI_LDS>
-__global__ __launch_bounds__(C::THREADS, 1) void ring_kernel(const f16* __restrict__ A, const f16* __restrict__ B,
-                                                       f16* __restrict__ D, int64_t M, int64_t N, int64_t K,
-                                                       int64_t tiles_m, int64_t tiles_n)
+__global__ __launch_bounds__(C::THREADS, 1) void ring_kernel(const GemmArgs g)
 {
     static_assert(LSPLIT >= 1 && LSPLIT < C::KSUB && C::LPW % LSPLIT == 0, "load split");
     __shared__ __attribute__((aligned(1024))) char smem[C::LDS_BYTES];
     const int t = threadIdx.x, lane = t & 63;
     const int w = __builtin_amdgcn_readfirstlane(t >> 6);
 
-    const int64_t total = tiles_m * tiles_n;
-    const TileCoord tc = grouped_tile(xcd_slot(blockIdx.x, total), tiles_m, tiles_n);
+    // workgroup -> (batch entry, tile): the XCD remap and grouped order run
+    // over all batch entries' tiles, batch-major
+    const int64_t per_batch = g.tiles_m * g.tiles_n;
+    const int64_t slot = xcd_slot(blockIdx.x, per_batch * g.batch);
+    const int64_t bidx = slot / per_batch;
+    const TileCoord tc = grouped_tile(slot - bidx * per_batch, g.tiles_m, g.tiles_n);
     const int64_t m0 = tc.m_idx * C::BM, n0 = tc.n_idx * C::BN;
+    const int64_t M = g.M, N = g.N, K = g.K, ldd = g.ldd;
+    f16* __restrict__ D = g.D + bidx * g.sd;
 
-    const int64_t ldb = K * 2;
-    const char* a_base = reinterpret_cast<const char*>(A) + m0 * ldb;
-    const char* b_base = reinterpret_cast<const char*>(B) + n0 * ldb;
+    const int64_t lda_b = g.lda * 2, ldb_b = g.ldb * 2;
+    const char* a_base = reinterpret_cast<const char*>(g.A + bidx * g.sa) + m0 * lda_b;
+    const char* b_base = reinterpret_cast<const char*>(g.B + bidx * g.sb) + n0 * ldb_b;
     uint32_t a_off[C::A_LOADS], b_off[C::B_LOADS];
     int a_row[C::A_LOADS], b_row[C::B_LOADS], a_kc[C::A_LOADS], b_kc[C::B_LOADS];
-    lane_offsets<C, C::A_LOADS>(w, lane, ldb, a_off, a_row, a_kc);
-    lane_offsets<C, C::B_LOADS>(w, lane, ldb, b_off, b_row, b_kc);
+    lane_offsets<C, C::A_LOADS>(w, lane, lda_b, a_off, a_row, a_kc);
+    lane_offsets<C, C::B_LOADS>(w, lane, ldb_b, b_off, b_row, b_kc);
     const int64_t a_rows = M - m0, b_rows = N - n0;
-    const __amdgpu_buffer_rsrc_t a_rsrc = make_rsrc(a_base, (uint32_t)(C::BM * ldb));
-    const __amdgpu_buffer_rsrc_t b_rsrc = make_rsrc(b_base, (uint32_t)(C::BN * ldb));
+    const __amdgpu_buffer_rsrc_t a_rsrc = make_rsrc(a_base, (uint32_t)(C::BM * lda_b));
+    const __amdgpu_buffer_rsrc_t b_rsrc = make_rsrc(b_base, (uint32_t)(C::BN * ldb_b));
 
     // load q (0 .. LPW-1) of this wave for k step `step`
     auto load_one = [&](int64_t step, int q) {
@@ -300,18 +304,20 @@ __global__ __launch_bounds__(C::THREADS, 1) void ring_kernel(const f16* __restri
     mfma_range<C, 0, NQ>(fa[LB], fb[LB], acc);
     if (!EDGE && EPI_LDS) {
         wg_barrier();  // every wave is done reading the ring
-        epilogue_lds<C>(smem + w * (C::FM * 32 * C::FN * 64), D, N, m0 + wm, n0 + wn, acc, lane);
+        epilogue_lds<C>(smem + w * (C::FM * 32 * C::FN * 64), D, ldd, m0 + wm, n0 + wn, acc, lane);
     } else {
-        const bool full = !EDGE || (m0 + C::BM <= M && n0 + C::BN <= N && N % 4 == 0);
+        // 8-byte stores need every row start of this batch entry aligned
+        const bool vec = ldd % 4 == 0 && g.sd % 4 == 0;
+        const bool full = !EDGE || (m0 + C::BM <= M && n0 + C::BN <= N && vec);
 #pragma unroll
         for (int i = 0; i < C::FM; ++i)
 #pragma unroll
             for (int jj = 0; jj < C::FN; ++jj) {
                 const int64_t mb = m0 + wm + 32 * i, nb = n0 + wn + 32 * jj;
                 if (full)
-                    store_block<true>(D, N, M, N, mb, nb, acc[i][jj], lane);
+                    store_block<true>(D, ldd, M, N, mb, nb, acc[i][jj], lane);
                 else
-                    store_block<false>(D, N, M, N, mb, nb, acc[i][jj], lane);
+                    store_block<false>(D, ldd, M, N, mb, nb, acc[i][jj], lane, vec);
             }
     }
 }

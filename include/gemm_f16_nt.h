@@ -71,6 +71,32 @@ int gemm_f16_nt_rung(int rung, int64_t M, int64_t N, int64_t K, const void* A, c
 int gemm_f16_nt_persistent(int64_t M, int64_t N, int64_t K, const void* A, const void* B, void* D,
                            int64_t num_workgroups, void* stream);
 
+/* Strided, batched form (general leading dimensions; "GEMM I" claims any
+ * M, N, K, and the batch covers per-head products such as attention
+ * scores Q*K^T, the bridge to attention at the end of "GEMM III"):
+ *
+ *   for b in [0, batch):  D_b = A_b * B_b^T
+ *     A_b = A + b*stride_a, M x K, row r at A_b + r*lda
+ *     B_b = B + b*stride_b, N x K, row r at B_b + r*ldb
+ *     D_b = D + b*stride_d, M x N, row r at D_b + r*ldd
+ *
+ * All leading dimensions and strides are in elements (fp16).  lda, ldb >= K
+ * and multiples of 8 (16-byte rows); stride_a, stride_b multiples of 8 (0
+ * repeats one operand for every batch entry); ldd >= N, any value; stride_d
+ * any value, and for batch > 1 at least (M-1)*ldd + N so the outputs do not
+ * overlap.  D needs 16-byte alignment of its base only: rows that are not
+ * 8-byte aligned are written element by element.  Same precision, rounding,
+ * ownership and error behaviour as gemm_f16_nt; the library's kernel choice
+ * (rung 4). */
+int gemm_f16_nt_strided_batched(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, int64_t stride_a,
+                                const void* B, int64_t ldb, int64_t stride_b, void* D, int64_t ldd,
+                                int64_t stride_d, int64_t batch, void* stream);
+
+/* Validation only for the strided form, no HIP call. */
+int gemm_f16_nt_check_strided(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, int64_t stride_a,
+                              const void* B, int64_t ldb, int64_t stride_b, const void* D, int64_t ldd,
+                              int64_t stride_d, int64_t batch);
+
 /* Validation only, no HIP call: the status the call above would return for
  * these arguments before launching anything (rung 0 = gemm_f16_nt). */
 int gemm_f16_nt_check(int rung, int64_t M, int64_t N, int64_t K, const void* A, const void* B,

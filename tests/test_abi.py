@@ -156,3 +156,23 @@ def test_schedule_xcd_locality():
         sel = (wg % 8) == x
         assert sel.sum() == 32
         assert len(np.unique(tm[sel])) == 8 and len(np.unique(tn[sel])) == 4
+
+
+@pytest.mark.parametrize("args,want", [
+    # M, N, K, A, lda, sa, B, ldb, sb, D, ldd, sd, batch
+    ((64, 64, 64, A0, 64, 4096, B0, 64, 4096, D0, 64, 4096, 3), g.OK),
+    ((64, 64, 64, A0, 72, 0, B0, 64, 0, D0, 64, 4096, 3), g.OK),           # broadcast A and B
+    ((64, 64, 64, A0, 56, 0, B0, 64, 0, D0, 64, 4096, 1), g.INVALID_ARG),  # lda < K
+    ((64, 64, 64, A0, 64, 0, B0, 64, 0, D0, 60, 4096, 1), g.INVALID_ARG),  # ldd < N
+    ((64, 64, 64, A0, 68, 0, B0, 64, 0, D0, 64, 4096, 1), g.UNSUPPORTED),  # lda % 8
+    ((64, 64, 64, A0, 64, 4, B0, 64, 0, D0, 64, 4096, 2), g.UNSUPPORTED),  # stride_a % 8
+    ((64, 64, 64, A0, 64, 0, B0, 64, 0, D0, 66, 8192, 2), g.OK),           # odd row pitch of D
+    ((64, 64, 64, A0, 64, 0, B0, 64, 0, D0, 64, 4097, 2), g.OK),           # odd batch stride of D
+    ((64, 64, 64, A0, 64, 0, B0, 64, 0, D0, 64, 4000, 2), g.INVALID_ARG),  # outputs overlap
+    ((64, 64, 64, A0, 64, 0, B0, 64, 0, D0, 64, 0, 2), g.INVALID_ARG),     # all batches on one D
+    ((64, 64, 64, A0, 64, 0, B0, 64, 0, D0, 64, 4096, 0), g.OK),           # empty batch
+    ((64, 64, 64, A0, 64, 0, B0, 64, 0, D0, 64, 4096, -1), g.INVALID_ARG),
+    ((64, 64, 64, A0, 64, 0, B0, 64, 0, A0 + 64, 64, 4096, 1), g.INVALID_ARG),  # D overlaps A
+])
+def test_strided_validation(args, want):
+    assert g.check_strided(*args) == want

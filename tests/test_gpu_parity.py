@@ -271,3 +271,80 @@ def test_full_size_workloads_sampled(name):
         D5 = run(5, dA, dB)
         got5 = host_bits(D5[torch.from_numpy(rows).to(DEV), torch.from_numpy(cols).to(DEV)])
         assert_parity(got5, ref, w.K, name + " rung 5")
+
+
+# ------------------------------------------------- strided / batched form
+
+def _padded(X: np.ndarray, ld: int):
+    """Device tensor holding X (rows x cols) with row pitch ld (ld >= cols)."""
+    rows, cols = X.shape
+    buf = torch.zeros((rows, ld), dtype=torch.float16)
+    buf[:, :cols] = torch.from_numpy(X)
+    return buf.to(DEV)[:, :cols]
+
+
+@pytest.mark.parametrize("case", [
+    # batch, M, N, K, pad_a, pad_b, pad_d, broadcast_b
+    (3, 300, 260, 136, 8, 24, 4, False),
+    (2, 512, 512, 256, 0, 0, 0, False),      # whole tiles: the fast variant
+    (2, 256, 256, 64, 64, 0, 0, False),      # whole tiles with padded A rows
+    (4, 130, 70, 40, 16, 8, 12, True),       # B shared by every batch entry
+    (1, 1, 1, 8, 0, 0, 0, False),
+], ids=lambda c: "b{}_{}x{}x{}".format(*c[:4]))
+def test_strided_batched(case):
+    batch, M, N, K, pa, pb, pd, bcast = case
+    rng = np.random.default_rng(batch * 1000 + M + N + K)
+    As = [rng.uniform(-1, 1, (M, K)).astype(np.float16) for _ in range(batch)]
+    Bs = [rng.uniform(-1, 1, (N, K)).astype(np.float16) for _ in range(1 if bcast else batch)]
+    A = torch.stack([_padded(a, K + pa) for a in As])
+    B = torch.stack([_padded(b, K + pb) for b in Bs])
+    if bcast:
+        B = B[0]
+    Dfull = torch.full((batch, M, N + pd), float("nan"), dtype=torch.float16, device=DEV)
+    D = Dfull[:, :, :N]
+    say(f"[gpu] strided batch={batch} M={M} N={N} K={K} pads=({pa},{pb},{pd}) bcast={bcast}")
+    g.gemm_f16_nt_strided_batched(A, B, D)
+    torch.cuda.synchronize()
+    for b in range(batch):
+        ref, _ = oracle.gemm_nt(As[b], Bs[0 if bcast else b])
+        assert_parity(host_bits(D[b].contiguous()), ref, K, f"batch {b}")
+    if pd:  # the padding columns of D are never written
+        assert torch.isnan(Dfull[:, :, N:]).all().item()
+
+
+@pytest.mark.parametrize("layout", ["bhsd", "bshd"])
+def test_attention_scores(layout):
+    B_, H, Sq, Sk, d = 2, 3, 200, 264, 64
+    rng = np.random.default_rng(7 if layout == "bhsd" else 8)
+    q = rng.uniform(-1, 1, (B_, H, Sq, d)).astype(np.float16)
+    k = rng.uniform(-1, 1, (B_, H, Sk, d)).astype(np.float16)
+    if layout == "bhsd":
+        Q, Kt = dev(q), dev(k)
+    else:  # heads interleaved in the rows: (B, S, H, d) storage viewed as (B, H, S, d)
+        Q = dev(np.ascontiguousarray(q.transpose(0, 2, 1, 3))).transpose(1, 2)
+        Kt = dev(np.ascontiguousarray(k.transpose(0, 2, 1, 3))).transpose(1, 2)
+    say(f"[gpu] attention scores layout={layout}")
+    S = g.attention_scores(Q, Kt)
+    torch.cuda.synchronize()
+    assert S.shape == (B_, H, Sq, Sk)
+    for b in range(B_):
+        for h in range(H):
+            ref, _ = oracle.gemm_nt(q[b, h], k[b, h])
+            assert_parity(host_bits(S[b, h].contiguous()), ref, d, f"b{b} h{h}")
+
+
+def test_strided_unaligned_output_rows():
+    """Row pitch and batch stride of D that leave rows 2-byte aligned only."""
+    batch, M, N, K = 2, 260, 257, 64
+    rng = np.random.default_rng(31)
+    As = [rng.uniform(-1, 1, (M, K)).astype(np.float16) for _ in range(batch)]
+    Bs = [rng.uniform(-1, 1, (N, K)).astype(np.float16) for _ in range(batch)]
+    ldd, sd = N + 3, (M - 1) * (N + 3) + N + 5
+    flat = torch.full((sd * batch + 16,), float("nan"), dtype=torch.float16, device=DEV)
+    D = flat.as_strided((batch, M, N), (sd, ldd, 1))
+    say(f"[gpu] strided unaligned D ldd={ldd} sd={sd}")
+    g.gemm_f16_nt_strided_batched(torch.stack([dev(a) for a in As]), torch.stack([dev(b) for b in Bs]), D)
+    torch.cuda.synchronize()
+    for b in range(batch):
+        ref, _ = oracle.gemm_nt(As[b], Bs[b])
+        assert_parity(host_bits(D[b].contiguous()), ref, K, f"batch {b}")
