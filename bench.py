@@ -67,6 +67,8 @@ def parse():
     p.add_argument("--warmup", type=int, default=100)
     p.add_argument("--workload", default="square_4096")
     p.add_argument("--rung", type=int, default=0, help="0 = library choice, 1..5 = ladder rung")
+    p.add_argument("--splitk", type=int, default=-1,
+                   help="time gemm_f16_nt_splitk with this many K slices (0 = library choice)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="target oracle time for the CPU sample")
     p.add_argument("--copy-calib", action="store_true", help="run only a plain device copy (counter scaling)")
@@ -149,7 +151,8 @@ def main():
     w = workloads.BY_NAME[args.workload]
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    print(f"[bench] {w.describe()} rung={RUNG_NAMES[args.rung]} warmup={args.warmup} steps={args.steps}",
+    print(f"[bench] {w.describe()} rung={RUNG_NAMES[args.rung]} splitk={args.splitk} warmup={args.warmup} "
+          f"steps={args.steps}",
           file=sys.stderr, flush=True)
     A_np, B_np = inputs.operands(w.M, w.N, w.K, w.seed, w.dist)
     A = torch.from_numpy(A_np).to(dev)
@@ -160,7 +163,14 @@ def main():
     L = g.lib()
     a_ptr, b_ptr, d_ptr = A.data_ptr(), B.data_ptr(), D.data_ptr()
     s_ptr = ctypes.c_void_p(stream.cuda_stream)
-    if args.rung == 0:
+    if args.splitk >= 0:
+        ws_bytes = max(16, g.splitk_workspace_bytes(w.M, w.N, w.K, args.splitk))
+        ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+
+        def step():
+            return L.gemm_f16_nt_splitk(w.M, w.N, w.K, a_ptr, b_ptr, d_ptr, args.splitk, ws.data_ptr(), ws_bytes,
+                                        s_ptr)
+    elif args.rung == 0:
         def step():
             return L.gemm_f16_nt(w.M, w.N, w.K, a_ptr, b_ptr, d_ptr, s_ptr)
     else:
@@ -193,7 +203,7 @@ def main():
     flop = float(w.flop)
     value = flop * args.steps / (region_ms * 1e-3) / 1e12
     achieved = flop / (kernel_ms * 1e-3) / 1e12
-    rung_name = RUNG_NAMES[args.rung]
+    rung_name = RUNG_NAMES[args.rung] if args.splitk < 0 else f"splitk{args.splitk}"
     traffic = traffic_record(w.name, rung_name)
 
     out = {

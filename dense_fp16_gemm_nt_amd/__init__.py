@@ -61,6 +61,10 @@ def lib() -> ctypes.CDLL:
             L.gemm_f16_nt_strided_batched.argtypes = [i64, i64, i64, vp, i64, i64, vp, i64, i64, vp, i64, i64, i64, vp]
             L.gemm_f16_nt_check_strided.restype = i32
             L.gemm_f16_nt_check_strided.argtypes = [i64, i64, i64, vp, i64, i64, vp, i64, i64, vp, i64, i64, i64]
+            L.gemm_f16_nt_splitk.restype = i32
+            L.gemm_f16_nt_splitk.argtypes = [i64, i64, i64, vp, vp, vp, i32, vp, i64, vp]
+            L.gemm_f16_nt_splitk_workspace.restype = i64
+            L.gemm_f16_nt_splitk_workspace.argtypes = [i64, i64, i64, i32]
             L.gemm_f16_nt_check.restype = i32
             L.gemm_f16_nt_check.argtypes = [i32, i64, i64, i64, vp, vp, vp]
             L.gemm_f16_nt_status_string.restype = ctypes.c_char_p
@@ -212,6 +216,29 @@ def attention_scores(Q, Kt):
         sl = tuple(idx)
         gemm_f16_nt_strided_batched(Q[sl], Kt[sl], S[sl])
     return S
+
+
+def splitk_workspace_bytes(M: int, N: int, K: int, splits: int = 0) -> int:
+    n = lib().gemm_f16_nt_splitk_workspace(int(M), int(N), int(K), int(splits))
+    if n < 0:
+        raise GemmError(int(n), "gemm_f16_nt_splitk_workspace")
+    return int(n)
+
+
+def gemm_f16_nt_splitk(A, B, D=None, splits: int = 0, workspace=None):
+    """D = A @ B.T with K cut into slices (fp32 partials in `workspace`, a
+    byte tensor on A's device; allocated here when not given)."""
+    import torch
+
+    M, N, K, D = _operands(A, B, D)
+    need = splitk_workspace_bytes(M, N, K, splits)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=A.device)
+    st = lib().gemm_f16_nt_splitk(M, N, K, A.data_ptr(), B.data_ptr(), D.data_ptr(), int(splits),
+                                  workspace.data_ptr(), workspace.numel() * workspace.element_size(), _stream(A))
+    if st != OK:
+        raise GemmError(st, "gemm_f16_nt_splitk")
+    return D
 
 
 def check(rung: int, M: int, N: int, K: int, A_ptr: int, B_ptr: int, D_ptr: int) -> int:

@@ -153,6 +153,11 @@ struct GemmArgs {
     int64_t sa, sb, sd;
     int64_t batch;
     int64_t tiles_m, tiles_n;  // output tiles per batch entry
+    // split-K mode (k_chunk > 0): batch entry b is K slice
+    // [b*k_chunk, min(K, (b+1)*k_chunk)) of one product, whose fp32 partial
+    // sums go to P + b*M*N (row pitch N); A, B and D are not offset by b
+    int64_t k_chunk;
+    float* P;
 };
 
 // Buffer resource over a byte range (raw buffer, 32-bit data format so the

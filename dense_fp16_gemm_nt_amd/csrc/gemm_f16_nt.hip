@@ -174,6 +174,79 @@ int launch_ring(const GemmArgs& g0, hipStream_t s)
     return launched();
 }
 
+// ------------------------------------------------------------- split-K
+// Slices of K for a tile-starved product: enough to give every CU a
+// workgroup, but at least kMinStepsPerSlice 64-wide steps per slice (a
+// slice pays a prologue, a partial-sum write and its share of the
+// reduction; measured on MI355X, K = 512 on one 256 x 256 tile is faster
+// unsplit) and at most kMaxSplits slices.
+constexpr int64_t kMaxSplits = 64;
+constexpr int64_t kMinStepsPerSlice = 8;
+
+int64_t choose_splits(int64_t M, int64_t N, int64_t K, int cus)
+{
+    const int64_t tiles = ((M + kFastTile - 1) / kFastTile) * ((N + kFastTile - 1) / kFastTile);
+    const int64_t kt = (K + RingCfg::BK - 1) / RingCfg::BK;
+    if (tiles * 2 >= cus) return 1;
+    int64_t s = cus / tiles;
+    s = s < kt / kMinStepsPerSlice ? s : kt / kMinStepsPerSlice;
+    s = s < kMaxSplits ? s : kMaxSplits;
+    return s > 1 ? s : 1;
+}
+
+// k elements per slice (a whole number of 64-wide steps) and the slice count
+void split_plan(int64_t K, int64_t splits, int64_t* k_chunk, int64_t* n_slices)
+{
+    const int64_t kt = (K + RingCfg::BK - 1) / RingCfg::BK;
+    const int64_t steps = (kt + splits - 1) / splits;
+    *k_chunk = steps * RingCfg::BK;
+    *n_slices = (K + *k_chunk - 1) / *k_chunk;
+}
+
+int launch_splitk(int64_t M, int64_t N, int64_t K, const void* A, const void* B, void* D, int64_t splits,
+                  float* P, hipStream_t s)
+{
+    int64_t k_chunk = 0, n_slices = 0;
+    split_plan(K, splits, &k_chunk, &n_slices);
+    GemmArgs g{};
+    g.A = (const f16*)A;
+    g.B = (const f16*)B;
+    g.D = (f16*)D;
+    g.M = M;
+    g.N = N;
+    g.K = K;
+    g.lda = K;
+    g.ldb = K;
+    g.ldd = N;
+    g.batch = n_slices;
+    g.k_chunk = k_chunk;
+    g.P = P;
+    g.tiles_m = (M + kFastTile - 1) / kFastTile;
+    g.tiles_n = (N + kFastTile - 1) / kFastTile;
+    const int64_t blocks = g.tiles_m * g.tiles_n * n_slices;
+    if (blocks > 0x7fffffff) return GEMM_F16_NT_UNSUPPORTED;
+    const bool edge = (M % kFastTile) || (N % kFastTile) || (K % RingCfg::BK);
+    if (edge)
+        hipLaunchKernelGGL((ring::ring_kernel<RingCfg, true, kRingPre, kRingLsplit, false, false, true>),
+                           dim3((unsigned)blocks), dim3(RingCfg::THREADS), 0, s, g);
+    else
+        hipLaunchKernelGGL((ring::ring_kernel<RingCfg, false, kRingPre, kRingLsplit, false, false, true>),
+                           dim3((unsigned)blocks), dim3(RingCfg::THREADS), 0, s, g);
+    int st = launched();
+    if (st != GEMM_F16_NT_OK) return st;
+    const bool vec = N % 4 == 0;
+    const int64_t items = vec ? M * N / 4 : M * N;
+    const int64_t rblocks = (items + 255) / 256;
+    const unsigned rgrid = (unsigned)(rblocks < 8192 ? rblocks : 8192);
+    if (vec)
+        hipLaunchKernelGGL(ring::splitk_reduce_kernel<true>, dim3(rgrid), dim3(256), 0, s, P, (f16*)D, M, N, N,
+                           n_slices);
+    else
+        hipLaunchKernelGGL(ring::splitk_reduce_kernel<false>, dim3(rgrid), dim3(256), 0, s, P, (f16*)D, M, N, N,
+                           n_slices);
+    return launched();
+}
+
 GemmArgs contiguous_args(int64_t M, int64_t N, int64_t K, const void* A, const void* B, void* D)
 {
     GemmArgs g{};
@@ -294,6 +367,46 @@ int gemm_f16_nt_strided_batched(int64_t M, int64_t N, int64_t K, const void* A, 
     g.sd = stride_d;
     g.batch = batch;
     return launch_ring(g, s);
+}
+
+int64_t gemm_f16_nt_splitk_workspace(int64_t M, int64_t N, int64_t K, int splits)
+{
+    if (M < 0 || N < 0 || K < 0 || splits < 0 || splits > kMaxSplits) return GEMM_F16_NT_INVALID_ARG;
+    int64_t s = splits;
+    if (s == 0) {
+        int cus = 0;
+        if (device_info(&cus) != GEMM_F16_NT_OK) return GEMM_F16_NT_DEVICE;
+        s = choose_splits(M, N, K, cus);
+    }
+    if (s <= 1 || K == 0) return 0;
+    int64_t k_chunk = 0, n_slices = 0;
+    split_plan(K, s, &k_chunk, &n_slices);
+    return n_slices > 1 ? n_slices * M * N * 4 : 0;
+}
+
+int gemm_f16_nt_splitk(int64_t M, int64_t N, int64_t K, const void* A, const void* B, void* D, int splits,
+                       void* workspace, int64_t workspace_bytes, void* stream)
+{
+    if (splits < 0 || splits > kMaxSplits || workspace_bytes < 0) return GEMM_F16_NT_INVALID_ARG;
+    int st = validate(0, M, N, K, A, B, D);
+    if (st != GEMM_F16_NT_OK) return st;
+    if (M == 0 || N == 0) return GEMM_F16_NT_OK;
+    int cus = 0;
+    st = device_info(&cus);
+    if (st != GEMM_F16_NT_OK) return st;
+    hipStream_t s = (hipStream_t)stream;
+    if (K == 0) return launch_fill_zero(D, M * N, s);
+    const int64_t want = splits == 0 ? choose_splits(M, N, K, cus) : splits;
+    int64_t k_chunk = 0, n_slices = 1;
+    if (want > 1) split_plan(K, want, &k_chunk, &n_slices);
+    if (n_slices <= 1) return launch_ring(contiguous_args(M, N, K, A, B, D), s);
+    const int64_t need = n_slices * M * N * 4;
+    if (workspace == nullptr || workspace_bytes < need) return GEMM_F16_NT_INVALID_ARG;
+    if ((uintptr_t)workspace & 15) return GEMM_F16_NT_UNSUPPORTED;
+    if (overlaps(workspace, need, A, M * K * 2) || overlaps(workspace, need, B, N * K * 2) ||
+        overlaps(workspace, need, D, M * N * 2))
+        return GEMM_F16_NT_INVALID_ARG;
+    return launch_splitk(M, N, K, A, B, D, want, (float*)workspace, s);
 }
 
 int gemm_f16_nt_check_strided(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, int64_t stride_a,

@@ -130,16 +130,23 @@ __device__ __forceinline__ void mfma_range(const f16x8 (&a)[C::FM], const f16x8 
     }
 }
 
-// Interleave hint for one sub-step: NQ MFMAs, each followed by up to one LDS
-// read and one vector-memory load while any remain.
+// Interleave hint for one sub-step: NQ MFMAs, each followed by up to one
+// vector-memory load while any remain; the nr LDS reads either go one per
+// MFMA (READS_FIRST false) or all ahead of the MFMAs (true), which gives the
+// last read a whole sub-step of MFMAs to land in.
 // (nr, nl are compile-time constants once the callers' loops are unrolled.)
-template <int NQ>
+template <int NQ, bool READS_FIRST = false>
 __device__ __forceinline__ void interleave_hint(int nr, int nl)
 {
+    if (READS_FIRST) {
+#pragma unroll
+        for (int q = 0; q < NQ; ++q)
+            if (q < nr) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
+    }
 #pragma unroll
     for (int q = 0; q < NQ; ++q) {
         __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
-        if (q < nr) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
+        if (!READS_FIRST && q < nr) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
         if (q < nl) __builtin_amdgcn_sched_group_barrier(kSchedVmem, 1, 0);
     }
 }
@@ -178,7 +185,28 @@ __device__ __forceinline__ void epilogue_lds(char* lds, f16* __restrict__ D, int
     }
 }
 
-template <class C, bool EDGE, int PRE, int LSPLIT, bool EPI_LDS>
+// Write one 32x32 accumulator block as fp32 partial sums (16-byte stores of
+// four consecutive columns; element stores where vec is false or at edges).
+__device__ __forceinline__ void store_block_f32(float* __restrict__ P, int64_t ldp, int64_t M, int64_t N,
+                                                int64_t m0, int64_t n0, const f32x16& acc, int lane, bool vec)
+{
+    const int64_t m = m0 + acc_row(lane);
+    if (m >= M) return;
+#pragma unroll
+    for (int g4 = 0; g4 < 4; ++g4) {
+        const int64_t n = n0 + acc_col(lane, g4);
+        if (vec && n + 3 < N) {
+            *reinterpret_cast<f32x4*>(P + m * ldp + n) =
+                f32x4{acc[4 * g4], acc[4 * g4 + 1], acc[4 * g4 + 2], acc[4 * g4 + 3]};
+        } else {
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                if (n + r < N) P[m * ldp + n + r] = acc[4 * g4 + r];
+        }
+    }
+}
+
+template <class C, bool EDGE, int PRE, int LSPLIT, bool EPI_LDS, bool READS_FIRST = false, bool SPLITK = false>
 __global__ __launch_bounds__(C::THREADS, 1) void ring_kernel(const GemmArgs g)
 {
     static_assert(LSPLIT >= 1 && LSPLIT < C::KSUB && C::LPW % LSPLIT == 0, "load split");
@@ -193,12 +221,15 @@ __global__ __launch_bounds__(C::THREADS, 1) void ring_kernel(const GemmArgs g)
     const int64_t bidx = slot / per_batch;
     const TileCoord tc = grouped_tile(slot - bidx * per_batch, g.tiles_m, g.tiles_n);
     const int64_t m0 = tc.m_idx * C::BM, n0 = tc.n_idx * C::BN;
-    const int64_t M = g.M, N = g.N, K = g.K, ldd = g.ldd;
-    f16* __restrict__ D = g.D + bidx * g.sd;
+    const int64_t M = g.M, N = g.N, ldd = g.ldd;
+    // split-K: this workgroup contracts K slice bidx of the one product
+    const int64_t k_begin = SPLITK ? bidx * g.k_chunk : 0;
+    const int64_t K = SPLITK ? (g.K - k_begin < g.k_chunk ? g.K - k_begin : g.k_chunk) : g.K;
+    f16* __restrict__ D = g.D + (SPLITK ? 0 : bidx * g.sd);
 
     const int64_t lda_b = g.lda * 2, ldb_b = g.ldb * 2;
-    const char* a_base = reinterpret_cast<const char*>(g.A + bidx * g.sa) + m0 * lda_b;
-    const char* b_base = reinterpret_cast<const char*>(g.B + bidx * g.sb) + n0 * ldb_b;
+    const char* a_base = reinterpret_cast<const char*>(g.A + (SPLITK ? k_begin : bidx * g.sa)) + m0 * lda_b;
+    const char* b_base = reinterpret_cast<const char*>(g.B + (SPLITK ? k_begin : bidx * g.sb)) + n0 * ldb_b;
     uint32_t a_off[C::A_LOADS], b_off[C::B_LOADS];
     int a_row[C::A_LOADS], b_row[C::B_LOADS], a_kc[C::A_LOADS], b_kc[C::B_LOADS];
     lane_offsets<C, C::A_LOADS>(w, lane, lda_b, a_off, a_row, a_kc);
@@ -270,7 +301,7 @@ __global__ __launch_bounds__(C::THREADS, 1) void ring_kernel(const GemmArgs g)
                 for (int q = 0; q < LPS; ++q) load_one(j + C::STAGES - 1, kk * LPS + q);
             }
             mfma_range<C, 0, NQ>(fa[kk & 1], fb[kk & 1], acc);
-            interleave_hint<NQ>(NR, (LOADS && kk < LSPLIT) ? LPS : 0);
+            interleave_hint<NQ, READS_FIRST>(NR, (LOADS && kk < LSPLIT) ? LPS : 0);
         }
     };
     // last sub-step of step j with the handoff to step j+1
@@ -285,7 +316,7 @@ __global__ __launch_bounds__(C::THREADS, 1) void ring_kernel(const GemmArgs g)
         wg_barrier();
         read_frags<C>(smem + (int)((j + 1) % C::STAGES) * C::STAGE_BYTES, wm, wn, lane, 0, fa[0], fb[0]);
         mfma_range<C, PRE, NQ>(fa[LB], fb[LB], acc);
-        interleave_hint<NQ - PRE>(NR, 0);
+        interleave_hint<NQ - PRE, READS_FIRST>(NR, 0);
     };
     using True_ = std::integral_constant<bool, true>;
     using False_ = std::integral_constant<bool, false>;
@@ -302,7 +333,15 @@ __global__ __launch_bounds__(C::THREADS, 1) void ring_kernel(const GemmArgs g)
     }
     substeps(KT - 1, False_{});
     mfma_range<C, 0, NQ>(fa[LB], fb[LB], acc);
-    if (!EDGE && EPI_LDS) {
+    if (SPLITK) {
+        float* __restrict__ P = g.P + bidx * M * N;
+        const bool vec = N % 4 == 0;
+#pragma unroll
+        for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+            for (int jj = 0; jj < C::FN; ++jj)
+                store_block_f32(P, N, M, N, m0 + wm + 32 * i, n0 + wn + 32 * jj, acc[i][jj], lane, vec);
+    } else if (!EDGE && EPI_LDS) {
         wg_barrier();  // every wave is done reading the ring
         epilogue_lds<C>(smem + w * (C::FM * 32 * C::FN * 64), D, ldd, m0 + wm, n0 + wn, acc, lane);
     } else {
@@ -319,6 +358,31 @@ __global__ __launch_bounds__(C::THREADS, 1) void ring_kernel(const GemmArgs g)
                 else
                     store_block<false>(D, ldd, M, N, mb, nb, acc[i][jj], lane, vec);
             }
+    }
+}
+
+// Split-K reduction: D = fp16(sum over slices s = 0, 1, ... of P[s]), in
+// slice order, rounded once (round-to-nearest-even).  Four outputs per
+// thread when N % 4 == 0, else one.
+template <bool VEC>
+__global__ void splitk_reduce_kernel(const float* __restrict__ P, f16* __restrict__ D, int64_t M, int64_t N,
+                                     int64_t ldd, int64_t splits)
+{
+    const int64_t MN = M * N;
+    const int64_t per = VEC ? 4 : 1;
+    const int64_t n_items = MN / per;
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t it = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; it < n_items; it += stride) {
+        const int64_t e = it * per, row = e / N, col = e - row * N;
+        if (VEC) {
+            f32x4 s = *reinterpret_cast<const f32x4*>(P + e);
+            for (int64_t k = 1; k < splits; ++k) s += *reinterpret_cast<const f32x4*>(P + k * MN + e);
+            *reinterpret_cast<f16x4*>(D + row * ldd + col) = cvt4(s[0], s[1], s[2], s[3]);
+        } else {
+            float s = P[e];
+            for (int64_t k = 1; k < splits; ++k) s += P[k * MN + e];
+            D[row * ldd + col] = (f16)s;
+        }
     }
 }
 

@@ -92,6 +92,26 @@ int gemm_f16_nt_strided_batched(int64_t M, int64_t N, int64_t K, const void* A, 
                                 const void* B, int64_t ldb, int64_t stride_b, void* D, int64_t ldd,
                                 int64_t stride_d, int64_t batch, void* stream);
 
+/* Split-K form for products with fewer output tiles than compute units
+ * (the persistent scheduler of "TIRx GEMM detailed technical notes", V6,
+ * has nothing to balance when a shape has a handful of tiles): K is cut
+ * into `splits` slices of whole 64-wide steps (0 = the library's choice,
+ * at most 64), each slice's fp32 partial sums go to `workspace`, and a
+ * second kernel adds the slices in slice order and rounds once to fp16 --
+ * the single rounding at writeback is kept.  The fp32 summation order
+ * differs from gemm_f16_nt's (any order is within the contract).
+ * `workspace` is caller-owned device memory of at least
+ * gemm_f16_nt_splitk_workspace(M, N, K, splits) bytes, 16-byte aligned,
+ * not overlapping A, B or D; its contents are scratch.  When one slice
+ * suffices the call is gemm_f16_nt and the workspace is not touched. */
+int gemm_f16_nt_splitk(int64_t M, int64_t N, int64_t K, const void* A, const void* B, void* D, int splits,
+                       void* workspace, int64_t workspace_bytes, void* stream);
+
+/* Bytes of workspace gemm_f16_nt_splitk needs (0 if it will not split), or
+ * a negative status.  With splits = 0 this queries the current device's
+ * compute-unit count (the only HIP call). */
+int64_t gemm_f16_nt_splitk_workspace(int64_t M, int64_t N, int64_t K, int splits);
+
 /* Validation only for the strided form, no HIP call. */
 int gemm_f16_nt_check_strided(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, int64_t stride_a,
                               const void* B, int64_t ldb, int64_t stride_b, const void* D, int64_t ldd,

@@ -176,3 +176,25 @@ def test_schedule_xcd_locality():
 ])
 def test_strided_validation(args, want):
     assert g.check_strided(*args) == want
+
+
+def test_splitk_workspace_sizes():
+    L = g.lib()
+    # K = 512 is 8 steps of 64; 4 slices of 2 steps; fp32 partials
+    assert L.gemm_f16_nt_splitk_workspace(256, 256, 512, 4) == 4 * 256 * 256 * 4
+    # 3 requested slices of 8 steps -> 3 steps each -> slices of 192, 192, 128
+    assert L.gemm_f16_nt_splitk_workspace(256, 256, 512, 3) == 3 * 256 * 256 * 4
+    # more slices than steps: one step per slice
+    assert L.gemm_f16_nt_splitk_workspace(100, 60, 130, 16) == 3 * 100 * 60 * 4
+    assert L.gemm_f16_nt_splitk_workspace(256, 256, 512, 1) == 0
+    assert L.gemm_f16_nt_splitk_workspace(256, 256, 0, 4) == 0
+    assert L.gemm_f16_nt_splitk_workspace(256, 256, 512, 65) == g.INVALID_ARG
+    assert L.gemm_f16_nt_splitk_workspace(-1, 256, 512, 2) == g.INVALID_ARG
+
+
+def test_splitk_argument_errors_before_any_device_work():
+    L = g.lib()
+    assert L.gemm_f16_nt_splitk(256, 256, 512, A0, B0, D0, -1, None, 0, None) == g.INVALID_ARG
+    assert L.gemm_f16_nt_splitk(256, 256, 512, A0, B0, D0, 65, None, 0, None) == g.INVALID_ARG
+    assert L.gemm_f16_nt_splitk(256, 256, 500, A0, B0, D0, 2, None, 0, None) == g.UNSUPPORTED
+    assert L.gemm_f16_nt_splitk(0, 256, 512, A0, B0, D0, 2, None, 0, None) == g.OK

@@ -348,3 +348,56 @@ def test_strided_unaligned_output_rows():
     for b in range(batch):
         ref, _ = oracle.gemm_nt(As[b], Bs[b])
         assert_parity(host_bits(D[b].contiguous()), ref, K, f"batch {b}")
+
+
+# ------------------------------------------------------------ split-K form
+
+@pytest.mark.parametrize("case", [
+    (256, 256, 512, 0), (256, 256, 512, 2), (256, 256, 512, 4), (256, 256, 512, 8),
+    (300, 260, 520, 3), (200, 130, 200, 2), (128, 64, 64, 4), (512, 256, 2048, 16), (1, 1, 8, 2),
+    (256, 256, 65536, 0), (256, 256, 8192, 64),
+], ids=lambda c: "{}x{}x{}_s{}".format(*c))
+def test_splitk(case):
+    M, N, K, splits = case
+    A, B = rand_case(M, N, K, 500 + M + N + K + splits)
+    ref, _ = oracle.gemm_nt(A, B)
+    dA, dB = dev(A), dev(B)
+    D = torch.full((M, N), float("nan"), dtype=torch.float16, device=DEV)
+    say(f"[gpu] split-K M={M} N={N} K={K} splits={splits}")
+    g.gemm_f16_nt_splitk(dA, dB, D, splits=splits)
+    torch.cuda.synchronize()
+    assert_parity(host_bits(D), ref, K, f"split-K {case}")
+    first = host_bits(D)
+    g.gemm_f16_nt_splitk(dA, dB, D, splits=splits)
+    torch.cuda.synchronize()
+    assert np.array_equal(host_bits(D), first)        # fixed slice order: repeatable
+
+
+def test_splitk_exact_pins():
+    """Small integers: every fp32 partial and their sum are exact, so the
+    split result equals the oracle bit for bit; all-ones gives K."""
+    rng = np.random.default_rng(44)
+    M, N, K = 256, 192, 4096
+    A = rng.integers(-4, 5, (M, K)).astype(np.float16)
+    B = rng.integers(-4, 5, (N, K)).astype(np.float16)
+    ref, _ = oracle.gemm_nt(A, B)
+    say("[gpu] split-K small integers")
+    D = g.gemm_f16_nt_splitk(dev(A), dev(B), splits=8)
+    torch.cuda.synchronize()
+    assert np.array_equal(host_bits(D), ref)
+    ones = torch.ones((256, 8192), dtype=torch.float16, device=DEV)
+    D = g.gemm_f16_nt_splitk(ones, ones, splits=16)
+    torch.cuda.synchronize()
+    assert torch.all(D.float() == 8192).item()
+
+
+def test_splitk_rejects_small_workspace():
+    A = torch.ones((256, 512), dtype=torch.float16, device=DEV)
+    ws = torch.empty(1024, dtype=torch.uint8, device=DEV)
+    D = torch.full((256, 256), 7.0, dtype=torch.float16, device=DEV)
+    say("[gpu] split-K small workspace")
+    with pytest.raises(g.GemmError) as e:
+        g.gemm_f16_nt_splitk(A, A, D, splits=4, workspace=ws)
+    assert e.value.status == g.INVALID_ARG
+    torch.cuda.synchronize()
+    assert torch.all(D == 7.0).item()
