@@ -13,6 +13,7 @@
 #include "ladder.hpp"
 #include "persistent_ws.hpp"
 #include "ring.hpp"
+#include "ring4.hpp"
 #include "sched.hpp"
 
 using namespace g16;
@@ -22,11 +23,15 @@ namespace {
 // Kernel configurations of the fast rungs (measured on MI355X; see the
 // bench): rung 4 = 256 x 256 tile, 64-wide k steps, 2-stage ring, 8 waves of
 // 128 x 64 (two per SIMD), loads issued in the first sub-step, 2 MFMAs ahead
-// of each barrier, LDS-staged epilogue; rung 5 = 32-wide k steps, 4 stages.
+// of each barrier, LDS-staged epilogue; rung 5 = 32-wide k steps, 4 stages;
+// rung 6 = rung 4's ring with 4 waves of 128 x 128 on 16x16x32 MFMAs and a
+// generated instruction schedule, persistent (ring4.hpp), for whole tiles.
 using RingCfg = ring::Cfg<256, 256, 64, 2, 2, 2, 4>;
 constexpr int kRingPre = 2, kRingLsplit = 1;
 using WsCfg = ws::Cfg<32, 4, 2>;
 constexpr int kFastTile = 256;
+// the library's choice takes the four-wave scheduled ring where it applies
+constexpr bool kDefaultRing4 = true;
 
 __global__ void fill_zero_kernel(uint16_t* __restrict__ D, int64_t n)
 {
@@ -79,9 +84,16 @@ bool overlaps(const void* a, int64_t abytes, const void* b, int64_t bbytes)
     return a0 < b0 + (uintptr_t)bbytes && b0 < a0 + (uintptr_t)abytes;
 }
 
+// Shapes the four-wave scheduled ring implements: whole 256 x 256 tiles and
+// at least two 64-wide k steps (M = 0 or N = 0 is a no-op everywhere).
+bool ring4_shape(int64_t M, int64_t N, int64_t K)
+{
+    return M % ring4::C::BM == 0 && N % ring4::C::BN == 0 && K % ring4::C::BK == 0 && K >= 2 * ring4::C::BK;
+}
+
 int validate(int rung, int64_t M, int64_t N, int64_t K, const void* A, const void* B, const void* D)
 {
-    if (rung < 0 || rung > GEMM_F16_NT_R5_PERSISTENT_WS) return GEMM_F16_NT_INVALID_ARG;
+    if (rung < 0 || rung > GEMM_F16_NT_R6_RING4) return GEMM_F16_NT_INVALID_ARG;
     if (M < 0 || N < 0 || K < 0) return GEMM_F16_NT_INVALID_ARG;
     const bool any_out = M > 0 && N > 0;
     if (any_out && K > 0 && (A == nullptr || B == nullptr)) return GEMM_F16_NT_INVALID_ARG;
@@ -93,6 +105,7 @@ int validate(int rung, int64_t M, int64_t N, int64_t K, const void* A, const voi
     if (rung == GEMM_F16_NT_R1_SINGLE_TILE && !(M == 128 && N == 128 && K == 64)) return GEMM_F16_NT_UNSUPPORTED;
     if (rung == GEMM_F16_NT_R2_KLOOP && !(M == 128 && N == 128)) return GEMM_F16_NT_UNSUPPORTED;
     if (rung == GEMM_F16_NT_R3_GRID && (N + 127) / 128 > 65535) return GEMM_F16_NT_UNSUPPORTED;
+    if (rung == GEMM_F16_NT_R6_RING4 && !ring4_shape(M, N, K)) return GEMM_F16_NT_UNSUPPORTED;
     if (!any_out) return GEMM_F16_NT_OK;
     if (K > 0 && (((uintptr_t)A & 15) || ((uintptr_t)B & 15))) return GEMM_F16_NT_UNSUPPORTED;
     if ((uintptr_t)D & 15) return GEMM_F16_NT_UNSUPPORTED;
@@ -156,8 +169,32 @@ int launch_fill_zero(void* D, int64_t n, hipStream_t s)
     return launched();
 }
 
-int launch_ring(const GemmArgs& g0, hipStream_t s)
+// Whether the four-wave scheduled ring covers this problem: whole tiles and
+// 16-byte aligned output rows in every batch entry.
+bool ring4_fits(const GemmArgs& g)
 {
+    return ring4_shape(g.M, g.N, g.K) && g.ldd % 8 == 0 && g.sd % 8 == 0;
+}
+
+// Persistent launch: one workgroup per compute unit (fewer when there are
+// fewer tiles); every workgroup walks its share of the tiles.
+int launch_ring4(const GemmArgs& g0, hipStream_t s)
+{
+    GemmArgs g = g0;
+    g.tiles_m = g.M / ring4::C::BM;
+    g.tiles_n = g.N / ring4::C::BN;
+    const int64_t tiles = g.tiles_m * g.tiles_n * g.batch;
+    int cus = 0;
+    const int st = device_info(&cus);
+    if (st != GEMM_F16_NT_OK) return st;
+    const int64_t grid = tiles < cus ? tiles : cus;
+    hipLaunchKernelGGL(ring4::ring4_kernel, dim3((unsigned)grid), dim3(ring4::C::THREADS), 0, s, g);
+    return launched();
+}
+
+int launch_ring(const GemmArgs& g0, hipStream_t s, bool allow_ring4 = false)
+{
+    if (allow_ring4 && ring4_fits(g0)) return launch_ring4(g0, s);
     GemmArgs g = g0;
     g.tiles_m = (g.M + kFastTile - 1) / kFastTile;
     g.tiles_n = (g.N + kFastTile - 1) / kFastTile;
@@ -307,8 +344,10 @@ int run(int rung, int64_t M, int64_t N, int64_t K, const void* A, const void* B,
         return launch_ring(contiguous_args(M, N, K, A, B, D), s);
     case GEMM_F16_NT_R5_PERSISTENT_WS:
         return launch_ws(M, N, K, a, b, d, grid_override > 0 ? grid_override : cus, s);
+    case GEMM_F16_NT_R6_RING4:
+        return launch_ring4(contiguous_args(M, N, K, A, B, D), s);
     default:  // 0: the library's choice
-        return launch_ring(contiguous_args(M, N, K, A, B, D), s);
+        return launch_ring(contiguous_args(M, N, K, A, B, D), s, kDefaultRing4);
     }
 }
 
@@ -366,7 +405,7 @@ int gemm_f16_nt_strided_batched(int64_t M, int64_t N, int64_t K, const void* A, 
     g.sb = stride_b;
     g.sd = stride_d;
     g.batch = batch;
-    return launch_ring(g, s);
+    return launch_ring(g, s, kDefaultRing4);
 }
 
 int64_t gemm_f16_nt_splitk_workspace(int64_t M, int64_t N, int64_t K, int splits)
@@ -399,7 +438,7 @@ int gemm_f16_nt_splitk(int64_t M, int64_t N, int64_t K, const void* A, const voi
     const int64_t want = splits == 0 ? choose_splits(M, N, K, cus) : splits;
     int64_t k_chunk = 0, n_slices = 1;
     if (want > 1) split_plan(K, want, &k_chunk, &n_slices);
-    if (n_slices <= 1) return launch_ring(contiguous_args(M, N, K, A, B, D), s);
+    if (n_slices <= 1) return launch_ring(contiguous_args(M, N, K, A, B, D), s, kDefaultRing4);
     const int64_t need = n_slices * M * N * 4;
     if (workspace == nullptr || workspace_bytes < need) return GEMM_F16_NT_INVALID_ARG;
     if ((uintptr_t)workspace & 15) return GEMM_F16_NT_UNSUPPORTED;

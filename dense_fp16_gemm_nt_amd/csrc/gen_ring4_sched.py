@@ -1,0 +1,308 @@
+"""Generate the instruction schedule of the 4-wave ring kernel (ring4.hpp).
+
+The k loop of that kernel is one inline-assembly block so that the order of
+matrix-core instructions, LDS fragment reads, direct-to-LDS loads and the
+exact wait counts is fixed by construction instead of by the compiler's
+scheduler.  This script writes that block as a C string macro into
+ring4_sched.inc; the kernel supplies the operands.  Run it after changing
+the schedule parameters:
+
+    python gen_ring4_sched.py            # writes ring4_sched.inc
+
+Pipeline (the pages' software pipeline with a double-buffered operand ring,
+"TIRx GEMM detailed technical notes", V4-V5, on gfx950 direct-to-LDS loads):
+
+  * workgroup tile 256 x 256, 64-wide k steps, 2 LDS stages of 64 KiB
+    (A rows at +0, B rows at +32 KiB; 128-byte rows, 16-byte chunk c of
+    row r at chunk c ^ ((r / 2) mod 8)), 4 waves in a 2 x 2 grid, each wave
+    owning 128 x 128 outputs = 8 x 8 blocks of v_mfma_f32_16x16x32_f16.
+    Block (i, j) (A rows 16i.., B rows 16j..) accumulates in operand
+    %[cB], B = 8i + j (64 AGPR quadruples: all 256 accumulation registers).  The 16x16x32 form is used
+    because it holds a higher clock than 32x32x16 at the same work per cycle
+    (it reads and writes half the accumulator bytes per FLOP);
+  * a k step is 2 sub-steps of 32 k; the 16 fragments (8 A blocks, 8 B
+    blocks, one 16-byte LDS read each) of sub-step 1 are read while sub-step
+    0 runs, into the second of two fragment buffers (F0 = v[128:191],
+    F1 = v[192:255]);
+  * a wave's 16 loads of a step (8 A, 8 B row groups of 1 KiB) are split:
+    the first n_hand of step j+2 go out right after step j's barrier (which
+    frees the stage step j+2 refills), the rest during step j+1, so every
+    load has more than a step to land and the loads do not come in bursts;
+  * sub-step 1 waits for its own loads (vmcnt) and LDS reads (lgkmcnt),
+    crosses the one barrier of the step (which publishes step j+1 and frees
+    step j's stage), then reads step j+1's sub-step-0 fragments into F0;
+  * the prologue loads steps 0 and 1 (both stages are free), so step 0
+    issues no body loads; the last two steps issue no handoff loads and the
+    last step has no barrier.
+
+MFMA operand roles: the B block feeds srcA and the A block srcB, so lane l
+of block (i, j) holds output row 16i + l%16 and the four consecutive output
+columns 16j + 4*(l/16) + 0..3.
+
+Operands expected by the block (see ring4.hpp): accumulators %[c0] ..
+%[c63] (AGPR, written: the first k step starts from 0), load offsets
+%[aoQ], %[boQ] (VGPR), fragment-read addresses %[raSK], %[rbSK] for stage S
+and sub-step K (VGPR), buffer resources %[rsa], %[rsb], the wave's LDS load
+base %[lb], the byte offsets %[ko] and %[kh] of the next two steps to load
+and the count %[rem] of k steps (SGPR, all modified; %[kh] is scratch).
+"""
+from __future__ import annotations
+
+import os
+import sys
+
+FRAG_BASE = 128
+NB = 8           # 16-row blocks per wave tile side
+NQ = NB * NB     # MFMAs per sub-step
+KSUB = 2         # 32-wide sub-steps per 64-wide k step
+NLOAD = 16       # direct-to-LDS loads per wave per k step
+# fragment read order inside a buffer: a0, b0..b7, a1..a7 (MFMA q = 8i + j
+# needs a_i and b_j, so the reads land in the order the MFMAs use them)
+READ_ORDER = [("a", 0)] + [("b", j) for j in range(NB)] + [("a", i) for i in range(1, NB)]
+
+
+def freg(buf: int, op: str, idx: int) -> str:
+    base = FRAG_BASE + 64 * buf + (0 if op == "a" else 32) + 4 * idx
+    return f"v[{base}:{base + 3}]"
+
+
+def areg(i: int, j: int) -> str:
+    """Accumulator operand of block (i, j): %[cB], B = 8i + j (an AGPR
+    quadruple chosen by the compiler)."""
+    return f"%[c{NB * i + j}]"
+
+
+class Emitter:
+    def __init__(self) -> None:
+        self.lines: list[str] = []
+        self.lgkm: list[tuple] = []   # outstanding LDS reads, in issue order
+
+    def op(self, s: str) -> None:
+        self.lines.append(s)
+
+    def label(self, s: str) -> None:
+        self.lines.append(s + ":")
+
+    # --- LDS fragment reads ------------------------------------------------
+    def read(self, buf: int, op: str, idx: int, stage: int, kk: int) -> None:
+        self.op(f"ds_read_b128 {freg(buf, op, idx)}, %[r{op}{stage}{kk}] offset:{2048 * idx}")
+        self.lgkm.append((buf, op, idx))
+
+    def wait_frag(self, *need: tuple) -> None:
+        """lgkmcnt wait for the reads in `need` (LDS reads complete in
+        order, so the count is the number issued after the newest one)."""
+        pos = [self.lgkm.index(n) for n in need if n in self.lgkm]
+        if not pos:
+            return
+        p = max(pos)
+        after = len(self.lgkm) - 1 - p
+        if after > 15:  # the counter field is 4 bits: wait for more
+            p = len(self.lgkm) - 1 - 15
+            after = 15
+        self.op(f"s_waitcnt lgkmcnt({after})")
+        del self.lgkm[: p + 1]
+
+    def wait_all(self) -> None:
+        self.op("s_waitcnt vmcnt(0) lgkmcnt(0)")
+        self.lgkm.clear()
+
+    # --- direct-to-LDS loads -----------------------------------------------
+    def load(self, n: int, stage: int, ahead: bool = False) -> None:
+        """Load n (0..15) of this wave into `stage`: even n are A loads, odd
+        n are B loads (row group n // 2 of the wave's share).  The global
+        k offset is %[ko], or %[kh] (= %[ko] + 128, the step after) when
+        ahead.  No immediate offset: for a direct-to-LDS load it would be
+        added to the LDS destination as well."""
+        q = n // 2
+        if n % 2 == 0:
+            dst = stage * 65536 + q * 1024
+            voff, rsrc = f"%[ao{q}]", "%[rsa]"
+        else:
+            dst = stage * 65536 + 32768 + q * 1024
+            voff, rsrc = f"%[bo{q}]", "%[rsb]"
+        self.op(f"s_add_u32 m0, %[lb], {dst}")
+        self.op("s_nop 0")  # M0 write -> LDS-DMA read of M0
+        koff = "%[kh]" if ahead else "%[ko]"
+        self.op(f"buffer_load_dwordx4 {voff}, {rsrc}, {koff} offen lds")
+
+    # --- MFMA ----------------------------------------------------------------
+    def mfma(self, buf: int, i: int, j: int, first: bool) -> None:
+        self.wait_frag((buf, "a", i), (buf, "b", j))
+        c = areg(i, j)
+        self.op(f"v_mfma_f32_16x16x32_f16 {c}, {freg(buf, 'b', j)}, {freg(buf, 'a', i)}, {'0' if first else c}")
+
+
+def spread(n: int, start: int, every: int) -> list[int]:
+    return [start + every * k for k in range(n)]
+
+
+def emit_step(e: Emitter, stage: int, first: bool, body_loads: bool, hand_loads: bool, last: bool,
+              p: dict) -> None:
+    """One 64-wide k step j reading `stage`.
+
+    The 16 loads of a step are split: loads 0 .. n_hand-1 of step j+2 go out
+    right after step j's barrier (the barrier frees `stage`, which step j+2
+    refills), loads n_hand .. 15 of step j+1 go out during step j's body
+    (into the other stage, freed by step j-1's barrier).  body_loads /
+    hand_loads say whether those steps exist.  first: the accumulators
+    start from 0.  last: no handoff (no barrier, no next-step reads)."""
+    n_hand = len(p["hand_slots"])
+    body = [(n_hand + k, g) for k, g in enumerate(p["body_slots"])] if body_loads else []
+    nb = 0
+    nr = len(READ_ORDER)
+    hand: list[tuple[int, int]] = []
+    nh = 0
+    for kk in range(KSUB):
+        cur = kk & 1
+        if kk == 0:
+            # sub-step 1's fragments, from this stage, into F1
+            reads = [(1, op, idx, stage, 1) for (op, idx) in READ_ORDER]
+            slots = spread(nr, p["read_start"], p["read_every"])
+        else:
+            reads, slots = [], []
+        r_next = 0
+        for q in range(NQ):
+            i, j = q // NB, q % NB
+            g = kk * NQ + q
+            if kk == KSUB - 1 and not last and q == p["pre"]:
+                # handoff: this wave's reads of the stage and its loads of
+                # the next step are complete; the barrier publishes the
+                # next step and frees this stage for the step after it
+                e.wait_all()
+                e.op("s_barrier")
+                reads = [(0, op, idx, stage ^ 1, 0) for (op, idx) in READ_ORDER]
+                slots = spread(nr, q + p["post_start"], p["post_every"])
+                r_next = 0
+                if hand_loads:
+                    hand = [(k, q + off) for k, off in enumerate(p["hand_slots"])]
+            e.mfma(cur, i, j, first and kk == 0)
+            while r_next < len(reads) and slots[r_next] <= q:
+                e.read(*reads[r_next])
+                r_next += 1
+            if kk == KSUB - 1:
+                while nh < len(hand) and hand[nh][1] <= q:
+                    e.load(hand[nh][0], stage, ahead=True)  # step j+2 -> this stage
+                    nh += 1
+            while nb < len(body) and body[nb][1] <= g:
+                e.load(body[nb][0], stage ^ 1)          # step j+1 -> other stage
+                nb += 1
+        # whatever did not fit the MFMA slots goes out at the end
+        while r_next < len(reads):
+            e.read(*reads[r_next])
+            r_next += 1
+    while nh < len(hand):
+        e.load(hand[nh][0], stage, ahead=True)
+        nh += 1
+    assert nb == len(body), "body load slots beyond the step"
+    if not last:
+        e.op("s_add_u32 %[ko], %[ko], 128")   # %[ko] is the offset of step j+1 during step j
+        e.op("s_add_u32 %[kh], %[kh], 128")   # %[kh] that of step j+2
+
+
+def generate(p: dict) -> str:
+    """The k loop.  During step j, %[ko] is the byte offset of step j+1
+    (body loads) and %[kh] that of step j+2 (handoff loads)."""
+    assert len(p["hand_slots"]) + len(p["body_slots"]) == NLOAD
+    e = Emitter()
+    # prologue: steps 0 and 1 into stages 0 and 1
+    for n in range(NLOAD):
+        e.load(n, 0)
+    e.op("s_add_u32 %[ko], %[ko], 128")
+    for n in range(NLOAD):
+        e.load(n, 1)
+    # %[ko] = offset of step 1 while step 0 runs, %[kh] that of step 2
+    e.op("s_add_u32 %[kh], %[ko], 128")
+    e.op(f"s_waitcnt vmcnt({NLOAD})")
+    e.op("s_barrier")
+    for (op, idx) in READ_ORDER:
+        e.read(0, op, idx, 0, 0)
+    after_handoff = None
+
+    def step(stage, first, body_loads, hand_loads, last):
+        nonlocal after_handoff
+        if after_handoff is not None:
+            e.lgkm = list(after_handoff)
+        emit_step(e, stage, first, body_loads, hand_loads, last, p)
+        if not last:
+            if after_handoff is None:
+                after_handoff = list(e.lgkm)
+            assert e.lgkm == after_handoff, "step entry state differs between paths"
+
+    # step 0 (stage 0): KT == 2 has no step 2 to load
+    e.op("s_cmp_eq_u32 %[rem], 2")
+    e.op("s_cbranch_scc1 5f")
+    step(0, True, False, True, False)
+    e.op("s_sub_u32 %[rem], %[rem], 1")
+    e.op("s_branch 1f")
+    e.label("5")
+    step(0, True, False, False, False)
+    e.op("s_sub_u32 %[rem], %[rem], 1")
+    e.op("s_branch 2f")
+    # steps in stage 1 (rem >= 2 here)
+    e.label("1")
+    e.op("s_cmp_eq_u32 %[rem], 2")
+    e.op("s_cbranch_scc1 6f")
+    step(1, False, True, True, False)
+    e.op("s_sub_u32 %[rem], %[rem], 1")
+    e.op("s_branch 7f")
+    e.label("6")
+    step(1, False, True, False, False)
+    e.op("s_sub_u32 %[rem], %[rem], 1")
+    e.op("s_branch 3f")
+    # steps in stage 0 (rem >= 2 here)
+    e.label("7")
+    e.op("s_cmp_eq_u32 %[rem], 2")
+    e.op("s_cbranch_scc1 8f")
+    step(0, False, True, True, False)
+    e.op("s_sub_u32 %[rem], %[rem], 1")
+    e.op("s_branch 1b")
+    e.label("8")
+    step(0, False, True, False, False)
+    e.op("s_sub_u32 %[rem], %[rem], 1")
+    # last step in stage 1
+    e.label("2")
+    step(1, False, False, False, True)
+    e.op("s_branch 4f")
+    # last step in stage 0
+    e.label("3")
+    step(0, False, False, False, True)
+    e.label("4")
+    # the accumulators are read by VALU code after the block: cover the
+    # MFMA write -> VALU read latency
+    e.op("s_nop 7")
+    e.op("s_nop 7")
+    e.op("s_nop 7")
+    return "\n".join(e.lines)
+
+
+DEFAULT = {
+    "pre": 32,            # MFMAs of sub-step 1 before the barrier
+    "read_start": 0,      # sub-step 0: first read after MFMA read_start ...
+    "read_every": 2,      # ... then one every read_every MFMAs
+    "post_start": 0,      # after the barrier: first read after MFMA pre + post_start ...
+    "post_every": 1,      # ... then one every post_every MFMAs
+    "hand_slots": spread(8, 0, 4),     # loads 0-7 of step j+2 after step j's barrier
+    "body_slots": spread(8, 2, 8),     # loads 8-15 of step j+1 during step j
+}
+
+
+def as_macro(name: str, text: str) -> str:
+    body = [f'    "{ln}\\n"' for ln in text.split("\n")]
+    return f"#define {name} \\\n" + " \\\n".join(body) + "\n"
+
+
+def main(argv: list[str]) -> int:
+    here = os.path.dirname(os.path.abspath(__file__))
+    out = os.path.join(here, "ring4_sched.inc")
+    text = generate(DEFAULT)
+    hdr = ("// Generated by gen_ring4_sched.py from the schedule parameters\n// "
+           + ", ".join(f"{k}={v}" for k, v in DEFAULT.items()) + ".\n// Do not edit.\n")
+    with open(out, "w") as f:
+        f.write(hdr)
+        f.write(as_macro("G16_RING4_KLOOP", text))
+    print(out, len(text.split("\n")), "lines")
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main(sys.argv[1:]))

@@ -21,7 +21,8 @@ import statistics
 import sys
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-KERNEL_SOURCES = ["common.hpp", "sched.hpp", "ladder.hpp", "ring.hpp", "persistent_ws.hpp", "gemm_f16_nt.hip"]
+KERNEL_SOURCES = ["common.hpp", "sched.hpp", "ladder.hpp", "ring.hpp", "ring4.hpp", "ring4_sched.inc",
+                  "persistent_ws.hpp", "gemm_f16_nt.hip"]
 
 
 def kernel_source_hash() -> str:

@@ -1,0 +1,231 @@
+"""Host checks of the generated k-loop schedule of the four-wave ring kernel.
+
+The schedule (dense_fp16_gemm_nt_amd/csrc/ring4_sched.inc) is straight-line
+assembly produced by gen_ring4_sched.py.  These tests execute its control
+flow on the CPU for a range of k-step counts and check the ring protocol
+("TIRx GEMM detailed technical notes", V5 "Software Pipeline with
+Double-Buffered SMEM": a stage is refilled only after every consumer has
+released it, and read only after its load has landed and been published):
+
+  * every k step is loaded exactly once, into stage step % 2, and no load
+    reaches beyond K;
+  * a load into a stage is issued only after the barrier that follows the
+    last read of the stage's previous contents, with no read of that stage
+    since (the LDS write-after-read race across waves);
+  * a fragment read sees a stage whose loads were waited for (vmcnt) and
+    then published by a barrier, with no load into that stage in flight;
+  * every MFMA consumes the fragments of its own k step, sub-step and
+    block, after an lgkmcnt wait that covers their reads (LDS reads
+    complete in issue order), and accumulates into the block's registers,
+    starting from 0 in the first step;
+  * all waves cross the same number of barriers, and the committed include
+    is what the generator writes.
+
+All four waves run the same instruction stream, so one stream stands for
+all of them; the checks treat every barrier as the point where all waves'
+earlier waited-for loads become visible.
+"""
+from __future__ import annotations
+
+import importlib.util
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+CSRC = os.path.join(ROOT, "dense_fp16_gemm_nt_amd", "csrc")
+
+
+def _gen():
+    spec = importlib.util.spec_from_file_location("gen_ring4_sched", os.path.join(CSRC, "gen_ring4_sched.py"))
+    mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mod)
+    return mod
+
+
+GEN = _gen()
+NB = GEN.NB
+
+
+def _regs(spec: str) -> int:
+    """First register number of 'v[a:b]'."""
+    return int(re.match(r"v\[(\d+):\d+\]", spec).group(1))
+
+
+class Sim:
+    """Executes one wave's stream of the generated block for KT k steps."""
+
+    def __init__(self, text: str, kt: int):
+        self.lines = text.split("\n")
+        self.kt = kt
+        self.labels: dict[str, list[int]] = {}
+        for i, ln in enumerate(self.lines):
+            m = re.match(r"^(\d+):$", ln)
+            if m:
+                self.labels.setdefault(m.group(1), []).append(i)
+
+    def target(self, ref: str, pc: int) -> int:
+        n, d = ref[:-1], ref[-1]
+        c = self.labels[n]
+        return min(x for x in c if x > pc) if d == "f" else max(x for x in c if x < pc)
+
+    def run(self) -> dict:
+        kt = self.kt
+        rem, ko, kh, m0, scc = kt, 0, None, None, 0
+        epoch = 0                      # barriers crossed
+        vm: list[tuple] = []           # outstanding loads (step, stage, n), issue order
+        lgkm: list[tuple] = []         # outstanding reads (reg, content)
+        landed: dict[int, dict] = {0: {}, 1: {}}    # stage -> {n: (step, epoch waited)}
+        visible: dict[int, dict] = {0: {}, 1: {}}   # stage -> {n: step} published
+        reads_since_barrier = {0: 0, 1: 0}
+        frag: dict[int, tuple] = {}    # vgpr base -> (step, kk, op, idx) once its read completed
+        acc_started = set()
+        loaded_steps: dict[int, set] = {}
+        mfma = 0
+        pc = 0
+        while pc < len(self.lines):
+            ln = self.lines[pc]
+            if ln.startswith("s_cmp_eq_u32 %[rem], "):
+                scc = int(rem == int(ln.split(",")[1]))
+            elif ln.startswith("s_cbranch_scc1 "):
+                if scc:
+                    pc = self.target(ln.split()[1], pc)
+                    continue
+            elif ln.startswith("s_branch "):
+                pc = self.target(ln.split()[1], pc)
+                continue
+            elif ln.startswith("s_sub_u32 %[rem]"):
+                rem -= 1
+            elif ln.startswith("s_add_u32 %[ko]"):
+                ko += 128
+            elif ln == "s_add_u32 %[kh], %[ko], 128":
+                kh = ko + 128
+            elif ln.startswith("s_add_u32 %[kh], %[kh], "):
+                kh += 128
+            elif ln.startswith("s_add_u32 m0, %[lb], "):
+                m0 = int(ln.split(",")[2])
+            elif ln.startswith("buffer_load_dwordx4"):
+                m = re.match(r"buffer_load_dwordx4 %\[[ab]o\d\], %\[rs[ab]\], %\[(k[oh])\] offen( offset:(\d+))? lds$", ln)
+                assert m, ln
+                imm = int(m.group(3) or 0)
+                # the immediate offset moves the global address and the LDS
+                # destination alike
+                step = ((ko if m.group(1) == "ko" else kh) + imm) // 128
+                assert 0 <= step < kt, f"load of step {step} beyond K (KT={kt})"
+                dst = m0 + imm
+                assert dst % 1024 == 0 and 0 <= dst < 2 * 65536, f"LDS destination {dst}"
+                st = dst // 65536
+                off = dst % 65536
+                n = 2 * ((off % 32768) // 1024) + (1 if off >= 32768 else 0)
+                assert ("%[ao" in ln) == (n % 2 == 0), "A/B operand does not match the LDS region"
+                assert st == step % 2, f"step {step} loaded into stage {st}"
+                assert reads_since_barrier[st] == 0, "load into a stage read since the last barrier"
+                vm.append((step, st, n))
+                loaded_steps.setdefault(step, set()).add(n)
+            elif ln.startswith("s_waitcnt"):
+                m = re.search(r"vmcnt\((\d+)\)", ln)
+                if m:
+                    keep = int(m.group(1))
+                    done, vm = (vm[: len(vm) - keep], vm[len(vm) - keep:]) if keep else (vm, [])
+                    for (step, st, n) in done:
+                        landed[st][n] = (step, epoch)
+                m = re.search(r"lgkmcnt\((\d+)\)", ln)
+                if m:
+                    keep = int(m.group(1))
+                    done, lgkm = (lgkm[: len(lgkm) - keep], lgkm[len(lgkm) - keep:]) if keep else (lgkm, [])
+                    for reg, content in done:
+                        frag[reg] = content
+            elif ln == "s_barrier":
+                assert not lgkm, "barrier with LDS reads in flight"
+                epoch += 1
+                reads_since_barrier = {0: 0, 1: 0}
+                for st in (0, 1):
+                    for n, (step, _) in landed[st].items():
+                        visible[st][n] = step
+                    landed[st] = {}
+            elif ln.startswith("ds_read_b128"):
+                m = re.match(r"ds_read_b128 (v\[\d+:\d+\]), %\[r([ab])(\d)(\d)\] offset:(\d+)", ln)
+                reg, op, st, kk, off = _regs(m.group(1)), m.group(2), int(m.group(3)), int(m.group(4)), int(m.group(5))
+                idx = off // 2048
+                assert not any(s == st for (_, s, _) in vm), "read of a stage with a load in flight"
+                steps = set(visible[st].values())
+                assert len(visible[st]) == 16 and len(steps) == 1, "read of an incompletely published stage"
+                step = steps.pop()
+                reads_since_barrier[st] += 1
+                frag.pop(reg, None)
+                lgkm.append((reg, (step, kk, op, idx)))
+            elif ln.startswith("v_mfma_f32_16x16x32_f16"):
+                m = re.match(r"v_mfma_f32_16x16x32_f16 (%\[c(\d+)\]), (v\[\d+:\d+\]), (v\[\d+:\d+\]), (\S+)$", ln)
+                acc, blk, breg, areg, src_c = m.group(1), int(m.group(2)), _regs(m.group(3)), _regs(m.group(4)), m.group(5)
+                step, kk = mfma // (2 * NB * NB), (mfma // (NB * NB)) % 2
+                i, j = blk // NB, blk % NB
+                assert frag.get(areg) == (step, kk, "a", i), f"MFMA {mfma}: A operand {frag.get(areg)}"
+                assert frag.get(breg) == (step, kk, "b", j), f"MFMA {mfma}: B operand {frag.get(breg)}"
+                if step == 0 and kk == 0:
+                    assert src_c == "0" and blk not in acc_started
+                    acc_started.add(blk)
+                else:
+                    assert src_c == acc and blk in acc_started
+                mfma += 1
+            pc += 1
+        assert not vm and not lgkm, "operations in flight at the end of the block"
+        return {"mfma": mfma, "epoch": epoch, "acc": acc_started, "loaded": loaded_steps}
+
+
+@pytest.mark.parametrize("kt", [2, 3, 4, 5, 6, 7, 8, 9, 16, 33])
+def test_schedule_ring_protocol(kt):
+    res = Sim(GEN.generate(GEN.DEFAULT), kt).run()
+    assert res["mfma"] == 2 * NB * NB * kt          # 128 MFMAs per 64-wide k step
+    assert res["epoch"] == kt                        # prologue barrier + one per handoff
+    assert len(res["acc"]) == NB * NB                # every block accumulated
+    assert sorted(res["loaded"]) == list(range(kt))
+    assert all(v == set(range(16)) for v in res["loaded"].values())
+
+
+@pytest.mark.parametrize("params", [
+    {"pre": 16}, {"pre": 48, "post_every": 1}, {"read_every": 1}, {"read_every": 3},
+    {"hand_slots": [], "body_slots": list(range(0, 64, 4))},
+    {"hand_slots": list(range(0, 32, 2)), "body_slots": []},
+])
+def test_schedule_variants_keep_protocol(params):
+    p = dict(GEN.DEFAULT)
+    p.update(params)
+    for kt in (2, 3, 4, 7):
+        Sim(GEN.generate(p), kt).run()
+
+
+def test_simulator_catches_a_planted_race():
+    """Moving one handoff load ahead of its barrier must be caught."""
+    text = GEN.generate(GEN.DEFAULT).split("\n")
+    bar = text.index("s_barrier", text.index("s_barrier") + 1)   # step 0's handoff barrier
+    ld = next(i for i in range(bar, len(text)) if "%[kh] offen lds" in text[i])
+    planted = text[:bar - 1] + text[ld - 2: ld + 1] + text[bar - 1: ld - 2] + text[ld + 1:]
+    with pytest.raises(AssertionError):
+        Sim("\n".join(planted), 4).run()
+
+
+def test_simulator_catches_an_immediate_offset():
+    """A direct-to-LDS load with an instruction offset lands off its row
+    group in LDS (the offset applies to both addresses)."""
+    text = GEN.generate(GEN.DEFAULT).replace("%[kh] offen lds", "%[ko] offen offset:128 lds", 1)
+    with pytest.raises(AssertionError):
+        Sim(text, 4).run()
+
+
+def test_simulator_catches_a_short_wait():
+    """Weakening an lgkmcnt wait before an MFMA must be caught."""
+    text = GEN.generate(GEN.DEFAULT).split("\n")
+    k = next(i for i, ln in enumerate(text) if ln.startswith("s_waitcnt lgkmcnt(") and "vmcnt" not in ln
+             and int(ln[len("s_waitcnt lgkmcnt("):-1]) < 14)
+    n = int(text[k][len("s_waitcnt lgkmcnt("):-1])
+    text[k] = f"s_waitcnt lgkmcnt({n + 1})"
+    with pytest.raises(AssertionError):
+        Sim("\n".join(text), 4).run()
+
+
+def test_committed_include_matches_generator():
+    text = GEN.generate(GEN.DEFAULT)
+    with open(os.path.join(CSRC, "ring4_sched.inc")) as f:
+        inc = f.read()
+    assert GEN.as_macro("G16_RING4_KLOOP", text) in inc
