@@ -56,9 +56,6 @@ NB = 8           # 16-row blocks per wave tile side
 NQ = NB * NB     # MFMAs per sub-step
 KSUB = 2         # 32-wide sub-steps per 64-wide k step
 NLOAD = 16       # direct-to-LDS loads per wave per k step
-# fragment read order inside a buffer: a0, b0..b7, a1..a7 (MFMA q = 8i + j
-# needs a_i and b_j, so the reads land in the order the MFMAs use them)
-READ_ORDER = [("a", 0)] + [("b", j) for j in range(NB)] + [("a", i) for i in range(1, NB)]
 
 
 def freg(buf: int, op: str, idx: int) -> str:
@@ -132,6 +129,29 @@ class Emitter:
         self.op(f"v_mfma_f32_16x16x32_f16 {c}, {freg(buf, 'b', j)}, {freg(buf, 'a', i)}, {'0' if first else c}")
 
 
+def mfma_block(q: int, order: str) -> tuple[int, int]:
+    """Block (i, j) of the q-th MFMA of a sub-step.  'ij': i outer (runs of
+    8 MFMAs share an A fragment); 'ji': j outer; 'snake': i outer with j
+    reversed on odd rows (the B fragment repeats across a row change)."""
+    if order == "ji":
+        return q % NB, q // NB
+    i, j = q // NB, q % NB
+    if order == "snake" and i % 2 == 1:
+        j = NB - 1 - j
+    return i, j
+
+
+def read_order(order: str) -> list[tuple[str, int]]:
+    """Fragment reads in the order the MFMAs first need them."""
+    seen: list[tuple[str, int]] = []
+    for q in range(NQ):
+        i, j = mfma_block(q, order)
+        for f in (("a", i), ("b", j)):
+            if f not in seen:
+                seen.append(f)
+    return seen
+
+
 def spread(n: int, start: int, every: int) -> list[int]:
     return [start + every * k for k in range(n)]
 
@@ -149,20 +169,21 @@ def emit_step(e: Emitter, stage: int, first: bool, body_loads: bool, hand_loads:
     n_hand = len(p["hand_slots"])
     body = [(n_hand + k, g) for k, g in enumerate(p["body_slots"])] if body_loads else []
     nb = 0
-    nr = len(READ_ORDER)
+    ro = read_order(p.get("order", "ij"))
+    nr = len(ro)
     hand: list[tuple[int, int]] = []
     nh = 0
     for kk in range(KSUB):
         cur = kk & 1
         if kk == 0:
             # sub-step 1's fragments, from this stage, into F1
-            reads = [(1, op, idx, stage, 1) for (op, idx) in READ_ORDER]
+            reads = [(1, op, idx, stage, 1) for (op, idx) in ro]
             slots = spread(nr, p["read_start"], p["read_every"])
         else:
             reads, slots = [], []
         r_next = 0
         for q in range(NQ):
-            i, j = q // NB, q % NB
+            i, j = mfma_block(q, p.get("order", "ij"))
             g = kk * NQ + q
             if kk == KSUB - 1 and not last and q == p["pre"]:
                 # handoff: this wave's reads of the stage and its loads of
@@ -170,7 +191,7 @@ def emit_step(e: Emitter, stage: int, first: bool, body_loads: bool, hand_loads:
                 # next step and frees this stage for the step after it
                 e.wait_all()
                 e.op("s_barrier")
-                reads = [(0, op, idx, stage ^ 1, 0) for (op, idx) in READ_ORDER]
+                reads = [(0, op, idx, stage ^ 1, 0) for (op, idx) in ro]
                 slots = spread(nr, q + p["post_start"], p["post_every"])
                 r_next = 0
                 if hand_loads:
@@ -214,7 +235,7 @@ def generate(p: dict) -> str:
     e.op("s_add_u32 %[kh], %[ko], 128")
     e.op(f"s_waitcnt vmcnt({NLOAD})")
     e.op("s_barrier")
-    for (op, idx) in READ_ORDER:
+    for (op, idx) in read_order(p.get("order", "ij")):
         e.read(0, op, idx, 0, 0)
     after_handoff = None
 
@@ -276,9 +297,10 @@ def generate(p: dict) -> str:
 
 
 DEFAULT = {
+    "order": "snake",     # MFMA order inside a sub-step (see mfma_block)
     "pre": 32,            # MFMAs of sub-step 1 before the barrier
     "read_start": 0,      # sub-step 0: first read after MFMA read_start ...
-    "read_every": 2,      # ... then one every read_every MFMAs
+    "read_every": 1,      # ... then one every read_every MFMAs
     "post_start": 0,      # after the barrier: first read after MFMA pre + post_start ...
     "post_every": 1,      # ... then one every post_every MFMAs
     "hand_slots": spread(8, 0, 4),     # loads 0-7 of step j+2 after step j's barrier
