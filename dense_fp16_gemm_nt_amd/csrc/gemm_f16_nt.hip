@@ -25,7 +25,8 @@ namespace {
 // 128 x 64 (two per SIMD), loads issued in the first sub-step, 2 MFMAs ahead
 // of each barrier, LDS-staged epilogue; rung 5 = 32-wide k steps, 4 stages;
 // rung 6 = rung 4's ring with 4 waves of 128 x 128 on 16x16x32 MFMAs and a
-// generated instruction schedule, persistent (ring4.hpp), for whole tiles.
+// generated instruction schedule, persistent (ring4.hpp), for whole tiles;
+// rung 7 = rung 6 with release and publish barriers per step.
 using RingCfg = ring::Cfg<256, 256, 64, 2, 2, 2, 4>;
 constexpr int kRingPre = 2, kRingLsplit = 1;
 using WsCfg = ws::Cfg<32, 4, 2>;
@@ -93,7 +94,7 @@ bool ring4_shape(int64_t M, int64_t N, int64_t K)
 
 int validate(int rung, int64_t M, int64_t N, int64_t K, const void* A, const void* B, const void* D)
 {
-    if (rung < 0 || rung > GEMM_F16_NT_R6_RING4) return GEMM_F16_NT_INVALID_ARG;
+    if (rung < 0 || rung > GEMM_F16_NT_R7_RING4_2B) return GEMM_F16_NT_INVALID_ARG;
     if (M < 0 || N < 0 || K < 0) return GEMM_F16_NT_INVALID_ARG;
     const bool any_out = M > 0 && N > 0;
     if (any_out && K > 0 && (A == nullptr || B == nullptr)) return GEMM_F16_NT_INVALID_ARG;
@@ -105,7 +106,8 @@ int validate(int rung, int64_t M, int64_t N, int64_t K, const void* A, const voi
     if (rung == GEMM_F16_NT_R1_SINGLE_TILE && !(M == 128 && N == 128 && K == 64)) return GEMM_F16_NT_UNSUPPORTED;
     if (rung == GEMM_F16_NT_R2_KLOOP && !(M == 128 && N == 128)) return GEMM_F16_NT_UNSUPPORTED;
     if (rung == GEMM_F16_NT_R3_GRID && (N + 127) / 128 > 65535) return GEMM_F16_NT_UNSUPPORTED;
-    if (rung == GEMM_F16_NT_R6_RING4 && !ring4_shape(M, N, K)) return GEMM_F16_NT_UNSUPPORTED;
+    if ((rung == GEMM_F16_NT_R6_RING4 || rung == GEMM_F16_NT_R7_RING4_2B) && !ring4_shape(M, N, K))
+        return GEMM_F16_NT_UNSUPPORTED;
     if (!any_out) return GEMM_F16_NT_OK;
     if (K > 0 && (((uintptr_t)A & 15) || ((uintptr_t)B & 15))) return GEMM_F16_NT_UNSUPPORTED;
     if ((uintptr_t)D & 15) return GEMM_F16_NT_UNSUPPORTED;
@@ -178,7 +180,17 @@ bool ring4_fits(const GemmArgs& g)
 
 // Persistent launch: one workgroup per compute unit (fewer when there are
 // fewer tiles); every workgroup walks its share of the tiles.
-int launch_ring4(const GemmArgs& g0, hipStream_t s)
+// Operand bytes beyond which the k loop with release and publish barriers
+// is chosen: below it the operands stay in the 256 MB last-level cache and
+// the single-barrier loop is ~1% faster; above it loads stream from HBM and
+// the earlier, evenly spread loads of the two-barrier loop win (5-9% at
+// 8192^3 and 32768x1024x8192).
+constexpr int64_t kRing4TwoBarrierBytes = int64_t(96) << 20;
+
+// Persistent launch: one workgroup per compute unit (fewer when there are
+// fewer tiles); every workgroup walks its share of the tiles.  form: 1 =
+// one barrier per step, 2 = release + publish barriers, 0 = by size.
+int launch_ring4(const GemmArgs& g0, hipStream_t s, int form = 0)
 {
     GemmArgs g = g0;
     g.tiles_m = g.M / ring4::C::BM;
@@ -188,7 +200,11 @@ int launch_ring4(const GemmArgs& g0, hipStream_t s)
     const int st = device_info(&cus);
     if (st != GEMM_F16_NT_OK) return st;
     const int64_t grid = tiles < cus ? tiles : cus;
-    hipLaunchKernelGGL(ring4::ring4_kernel, dim3((unsigned)grid), dim3(ring4::C::THREADS), 0, s, g);
+    if (form == 0) form = (g.M + g.N) * g.K * 2 * g.batch > kRing4TwoBarrierBytes ? 2 : 1;
+    if (form == 2)
+        hipLaunchKernelGGL(ring4::ring4_kernel<true>, dim3((unsigned)grid), dim3(ring4::C::THREADS), 0, s, g);
+    else
+        hipLaunchKernelGGL(ring4::ring4_kernel<false>, dim3((unsigned)grid), dim3(ring4::C::THREADS), 0, s, g);
     return launched();
 }
 
@@ -345,7 +361,9 @@ int run(int rung, int64_t M, int64_t N, int64_t K, const void* A, const void* B,
     case GEMM_F16_NT_R5_PERSISTENT_WS:
         return launch_ws(M, N, K, a, b, d, grid_override > 0 ? grid_override : cus, s);
     case GEMM_F16_NT_R6_RING4:
-        return launch_ring4(contiguous_args(M, N, K, A, B, D), s);
+        return launch_ring4(contiguous_args(M, N, K, A, B, D), s, 1);
+    case GEMM_F16_NT_R7_RING4_2B:
+        return launch_ring4(contiguous_args(M, N, K, A, B, D), s, 2);
     default:  // 0: the library's choice
         return launch_ring(contiguous_args(M, N, K, A, B, D), s, kDefaultRing4);
     }

@@ -35,6 +35,15 @@ Pipeline (the pages' software pipeline with a double-buffered operand ring,
     issues no body loads; the last two steps issue no handoff loads and the
     last step has no barrier.
 
+A second form (generate2, macro G16_RING4_KLOOP2) splits the handoff in two
+barriers per step: a release barrier right after sub-step 0's fragment reads
+(the stage is dead from there on) and a publish barrier in sub-step 1.  The
+loads of step j+2 then start a whole sub-step earlier and go out evenly, one
+every few MFMAs, instead of in a burst after one barrier: when the operands
+stream from HBM, bursts from all CUs of an XCD queue at its L2 and triple the
+load latency.  It costs one more barrier per step, which does not pay when the
+operands stay in the last-level cache.
+
 MFMA operand roles: the B block feeds srcA and the A block srcB, so lane l
 of block (i, j) holds output row 16i + l%16 and the four consecutive output
 columns 16j + 4*(l/16) + 0..3.
@@ -296,6 +305,151 @@ def generate(p: dict) -> str:
     return "\n".join(e.lines)
 
 
+def emit_step2(e: Emitter, stage: int, first: bool, carried: bool, ahead: bool, last: bool, p: dict) -> None:
+    """One 64-wide k step j in the two-barrier form.
+
+    A release barrier after sub-step 0's reads of this stage (MFMA p["rel"])
+    frees the stage as soon as every wave has its fragments, instead of at
+    the end of the step.  The 16 loads of step j+2 then go out one every
+    p["load_every"] MFMAs from that barrier on; those that fall beyond the
+    step ("carried") go out at the start of step j+1.  A publish barrier in
+    sub-step 1 (MFMA 64 + p["pre"]) waits for step j+1's loads (vmcnt
+    counts only the younger loads of step j+2) and is followed by step
+    j+1's sub-step-0 fragment reads.  carried: step j+1's last loads are
+    issued at the start of this step; ahead: step j+2 exists.  first: the
+    accumulators start from 0.  last: no barriers, no next-step reads."""
+    order = p.get("order", "ij")
+    ro = read_order(order)
+    nr = len(ro)
+    rel, every = p["rel"], p["load_every"]
+    pub = NQ + p["pre"]                                  # MFMA index of the publish barrier
+    slots = [rel + every * n for n in range(NLOAD)]      # step j+2's loads, in step-j MFMA indices
+    own = [(n, g) for n, g in enumerate(slots) if g < 2 * NQ] if (ahead and not last) else []
+    carry = [(n, g - 2 * NQ) for n, g in enumerate(slots) if g >= 2 * NQ] if carried else []
+    n_after_own = None                                   # own loads issued before the publish wait
+    ci = oi = 0
+    reads: list = []
+    rslots: list = []
+    r_next = 0
+    for kk in range(KSUB):
+        cur = kk & 1
+        if kk == 0:
+            reads = [(1, op, idx, stage, 1) for (op, idx) in ro]
+            rslots = spread(nr, p["read_start"], p["read_every"])
+            r_next = 0
+        for q in range(NQ):
+            i, j = mfma_block(q, order)
+            g = kk * NQ + q
+            if not last and g == rel:
+                # release: this wave's reads of the stage are complete
+                while r_next < len(reads):
+                    e.read(*reads[r_next])
+                    r_next += 1
+                e.op("s_waitcnt lgkmcnt(0)")
+                e.lgkm.clear()
+                e.op("s_barrier")
+            if not last and g == pub:
+                # publish: step j+1's loads (all older than the own loads
+                # issued so far) have landed in every wave
+                # (loads issue in slot order; a carried load and an own
+                # load in one slot go carried first)
+                last_c = max([gg for (_, gg) in carry], default=-1)
+                n_young = sum(1 for (_, gg) in own if last_c < gg < pub or (gg == last_c and gg < pub))
+                e.op(f"s_waitcnt vmcnt({n_young}) lgkmcnt(0)")
+                e.lgkm.clear()
+                e.op("s_barrier")
+                reads = [(0, op, idx, stage ^ 1, 0) for (op, idx) in ro]
+                rslots = spread(nr, q + p["post_start"], p["post_every"])
+                r_next = 0
+            e.mfma(cur, i, j, first and kk == 0)
+            while r_next < len(reads) and rslots[r_next] <= q:
+                e.read(*reads[r_next])
+                r_next += 1
+            while ci < len(carry) and carry[ci][1] <= g:
+                e.load(carry[ci][0], stage ^ 1, ahead=False)   # step j+1 -> other stage
+                ci += 1
+            while oi < len(own) and own[oi][1] <= g:
+                e.load(own[oi][0], stage, ahead=True)          # step j+2 -> this stage
+                oi += 1
+        while r_next < len(reads):
+            e.read(*reads[r_next])
+            r_next += 1
+    assert ci == len(carry) and oi == len(own)
+    if not last:
+        e.op("s_add_u32 %[ko], %[ko], 128")
+        e.op("s_add_u32 %[kh], %[kh], 128")
+
+
+def generate2(p: dict) -> str:
+    """The k loop in the two-barrier form (same branch structure and
+    operands as generate())."""
+    assert p["rel"] >= len(read_order(p.get("order", "ij"))) * p["read_every"] - 1 + p["read_start"], \
+        "release barrier before the sub-step-1 reads are issued"
+    assert p["rel"] + p["load_every"] * (NLOAD - 1) < 2 * NQ + NQ + p["pre"], "loads too sparse"
+    e = Emitter()
+    for n in range(NLOAD):
+        e.load(n, 0)
+    e.op("s_add_u32 %[ko], %[ko], 128")
+    for n in range(NLOAD):
+        e.load(n, 1)
+    e.op("s_add_u32 %[kh], %[ko], 128")
+    e.op(f"s_waitcnt vmcnt({NLOAD})")
+    e.op("s_barrier")
+    for (op, idx) in read_order(p.get("order", "ij")):
+        e.read(0, op, idx, 0, 0)
+    after = None
+
+    def step(stage, first, carried, ahead, last):
+        nonlocal after
+        if after is not None:
+            e.lgkm = list(after)
+        emit_step2(e, stage, first, carried, ahead, last, p)
+        if not last:
+            if after is None:
+                after = list(e.lgkm)
+            assert e.lgkm == after, "step entry state differs between paths"
+
+    # step 0: nothing carried (the prologue loaded step 1 whole)
+    e.op("s_cmp_eq_u32 %[rem], 2")
+    e.op("s_cbranch_scc1 5f")
+    step(0, True, False, True, False)
+    e.op("s_sub_u32 %[rem], %[rem], 1")
+    e.op("s_branch 1f")
+    e.label("5")
+    step(0, True, False, False, False)
+    e.op("s_sub_u32 %[rem], %[rem], 1")
+    e.op("s_branch 2f")
+    e.label("1")
+    e.op("s_cmp_eq_u32 %[rem], 2")
+    e.op("s_cbranch_scc1 6f")
+    step(1, False, True, True, False)
+    e.op("s_sub_u32 %[rem], %[rem], 1")
+    e.op("s_branch 7f")
+    e.label("6")
+    step(1, False, True, False, False)
+    e.op("s_sub_u32 %[rem], %[rem], 1")
+    e.op("s_branch 3f")
+    e.label("7")
+    e.op("s_cmp_eq_u32 %[rem], 2")
+    e.op("s_cbranch_scc1 8f")
+    step(0, False, True, True, False)
+    e.op("s_sub_u32 %[rem], %[rem], 1")
+    e.op("s_branch 1b")
+    e.label("8")
+    step(0, False, True, False, False)
+    e.op("s_sub_u32 %[rem], %[rem], 1")
+    e.label("2")
+    step(1, False, False, False, True)
+    e.op("s_branch 4f")
+    e.label("3")
+    step(0, False, False, False, True)
+    e.label("4")
+    e.op("s_nop 7")
+    e.op("s_nop 7")
+    e.op("s_nop 7")
+    return "\n".join(e.lines)
+
+
 DEFAULT = {
     "order": "snake",     # MFMA order inside a sub-step (see mfma_block)
     "pre": 32,            # MFMAs of sub-step 1 before the barrier
@@ -307,22 +461,33 @@ DEFAULT = {
     "body_slots": spread(8, 2, 8),     # loads 8-15 of step j+1 during step j
 }
 
+# two-barrier form (generate2): release after sub-step 0's reads, loads of
+# step j+2 one every 8 MFMAs from there, publish barrier at MFMA 64 + pre
+DEFAULT2 = {k: v for k, v in DEFAULT.items() if k not in ("hand_slots", "body_slots")}
+DEFAULT2.update(rel=24, load_every=8, pre=32)
+
 
 def as_macro(name: str, text: str) -> str:
     body = [f'    "{ln}\\n"' for ln in text.split("\n")]
     return f"#define {name} \\\n" + " \\\n".join(body) + "\n"
 
 
+def params_line(p: dict) -> str:
+    return ", ".join(f"{k}={v}" for k, v in p.items())
+
+
 def main(argv: list[str]) -> int:
     here = os.path.dirname(os.path.abspath(__file__))
     out = os.path.join(here, "ring4_sched.inc")
-    text = generate(DEFAULT)
-    hdr = ("// Generated by gen_ring4_sched.py from the schedule parameters\n// "
-           + ", ".join(f"{k}={v}" for k, v in DEFAULT.items()) + ".\n// Do not edit.\n")
+    text1 = generate(DEFAULT)
+    text2 = generate2(DEFAULT2)
     with open(out, "w") as f:
-        f.write(hdr)
-        f.write(as_macro("G16_RING4_KLOOP", text))
-    print(out, len(text.split("\n")), "lines")
+        f.write("// Generated by gen_ring4_sched.py.  Do not edit.\n")
+        f.write("// G16_RING4_KLOOP: one barrier per k step; " + params_line(DEFAULT) + ".\n")
+        f.write(as_macro("G16_RING4_KLOOP", text1))
+        f.write("// G16_RING4_KLOOP2: release and publish barriers per k step; " + params_line(DEFAULT2) + ".\n")
+        f.write(as_macro("G16_RING4_KLOOP2", text2))
+    print(out, len(text1.split("\n")) + len(text2.split("\n")), "lines")
     return 0
 
 

@@ -57,6 +57,8 @@ extern "C" {
 #define GEMM_F16_NT_R5_PERSISTENT_WS 5 /* any shape: persistent, producer/consumer waves */
 #define GEMM_F16_NT_R6_RING4 6 /* rung 4's ring with 4 waves of 128 x 128 and a fixed instruction
                                   schedule: M, N multiples of 256, K a multiple of 64, K >= 128 */
+#define GEMM_F16_NT_R7_RING4_2B 7 /* rung 6 with a release and a publish barrier per k step (loads start
+                                     earlier and spread evenly); same shapes as rung 6 */
 
 /* D = A * B^T with the library's choice of kernel for the shape. */
 int gemm_f16_nt(int64_t M, int64_t N, int64_t K, const void* A, const void* B, void* D, void* stream);

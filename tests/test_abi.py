@@ -62,7 +62,7 @@ A0, B0, D0 = 0x10000, 0x20000000, 0x40000000   # fake, 16-byte aligned, disjoint
     ((0, 64, 64, 64, A0, B0, D0 + 4), g.UNSUPPORTED),      # misaligned D
     ((0, 64, 64, 64, A0, B0, A0 + 4096), g.INVALID_ARG),   # D overlaps A
     ((0, 64, 64, 64, A0, B0, B0), g.INVALID_ARG),          # D overlaps B
-    ((7, 64, 64, 64, A0, B0, D0), g.INVALID_ARG),          # unknown rung
+    ((8, 64, 64, 64, A0, B0, D0), g.INVALID_ARG),          # unknown rung
     ((-1, 64, 64, 64, A0, B0, D0), g.INVALID_ARG),
     ((1, 128, 128, 64, A0, B0, D0), g.OK),
     ((1, 128, 128, 128, A0, B0, D0), g.UNSUPPORTED),       # R1 is one 128x128x64 tile
@@ -76,6 +76,8 @@ A0, B0, D0 = 0x10000, 0x20000000, 0x40000000   # fake, 16-byte aligned, disjoint
     ((6, 256, 256, 64, A0, B0, D0), g.UNSUPPORTED),        # ... and at least two k steps
     ((6, 256, 256, 136, A0, B0, D0), g.UNSUPPORTED),       # ... of 64
     ((6, 256, 300, 128, A0, B0, D0), g.UNSUPPORTED),
+    ((7, 512, 256, 192, A0, B0, D0), g.OK),
+    ((7, 256, 256, 64, A0, B0, D0), g.UNSUPPORTED),
     ((0, 0, 64, 64, 0, 0, 0), g.OK),                       # empty output: nothing needed
     ((0, 64, 64, 0, 0, 0, D0), g.OK),                      # K = 0: D only
     ((0, 64, 64, 1 << 23, A0, B0, D0), g.UNSUPPORTED),     # beyond the kernels' index range

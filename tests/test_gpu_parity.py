@@ -19,7 +19,7 @@ pytestmark = pytest.mark.gpu
 
 torch = pytest.importorskip("torch")
 DEV = "cuda:0"
-ALL_RUNGS = [1, 2, 3, 4, 5, 6]
+ALL_RUNGS = [1, 2, 3, 4, 5, 6, 7]
 
 
 def say(*a):
@@ -49,7 +49,7 @@ def supported(rung, M, N, K):
         return (M, N, K) == (128, 128, 64)
     if rung == 2:
         return (M, N) == (128, 128)
-    if rung == 6:
+    if rung in (6, 7):
         return M % 256 == 0 and N % 256 == 0 and K % 64 == 0 and K >= 128
     return True
 
@@ -100,7 +100,7 @@ def test_ragged_shapes(rung, shape):
 
 @pytest.mark.parametrize("rung", [0] + ALL_RUNGS)
 def test_selection_matrix_bitwise(rung):
-    M, N, K = {1: (128, 128, 64), 2: (128, 128, 512), 6: (512, 256, 192)}.get(rung, (384, 320, 192))
+    M, N, K = {1: (128, 128, 64), 2: (128, 128, 512), 6: (512, 256, 192), 7: (512, 256, 192)}.get(rung, (384, 320, 192))
     rng = np.random.default_rng(5)
     pick = rng.integers(0, K, M)
     A = np.zeros((M, K), np.float16)
@@ -111,7 +111,7 @@ def test_selection_matrix_bitwise(rung):
     assert np.array_equal(host_bits(D), B[:, pick].T.view(np.uint16))
 
 
-@pytest.mark.parametrize("rung", [0, 3, 4, 5, 6])
+@pytest.mark.parametrize("rung", [0, 3, 4, 5, 6, 7])
 @pytest.mark.parametrize("K", [64, 512, 4096, 8192])
 def test_all_ones_equals_k(rung, K):
     if not supported(rung, 256, 256, K):
@@ -123,11 +123,11 @@ def test_all_ones_equals_k(rung, K):
     assert np.all(as_f64(host_bits(D)) == K)
 
 
-@pytest.mark.parametrize("rung", [0, 3, 4, 5, 6])
+@pytest.mark.parametrize("rung", [0, 3, 4, 5, 6, 7])
 def test_small_integers_bitwise(rung):
     rng = np.random.default_rng(14)
     shapes = [(256, 192, 8192, -4, 5), (264, 256, 768, 0, 5)]
-    if rung == 6:
+    if rung in (6, 7):
         shapes = [(256, 256, 8192, -4, 5), (512, 256, 768, 0, 5)]
     for (M, N, K, lo, hi) in shapes:
         A = rng.integers(lo, hi, (M, K)).astype(np.float16)
@@ -139,11 +139,11 @@ def test_small_integers_bitwise(rung):
         assert np.array_equal(got, ref), f"{np.sum(got != ref)} mismatches"
 
 
-@pytest.mark.parametrize("rung", [0, 3, 4, 5, 6])
+@pytest.mark.parametrize("rung", [0, 3, 4, 5, 6, 7])
 def test_designed_rows(rung):
     """Exact sums on a tie, on the overflow threshold and on the subnormal
     grid: round-half-even, +inf at 65520, gradual underflow."""
-    K, R = (128, 256) if rung == 6 else (64, 128)
+    K, R = (128, 256) if rung in (6, 7) else (64, 128)
     A = np.zeros((R, K), np.float16)
     B = np.zeros((R, K), np.float16)
     A[0, :2] = [1, 1]
@@ -207,7 +207,7 @@ def test_poisoned_output_is_fully_overwritten(shape):
     M, N, K = shape
     A, B = rand_case(M, N, K, 77)
     ref, _ = oracle.gemm_nt(A, B)
-    for rung in (0, 3, 4, 5, 6):
+    for rung in (0, 3, 4, 5, 6, 7):
         if not supported(rung, M, N, K):
             continue
         D = torch.full((M, N), float("nan"), dtype=torch.float16, device=DEV)
@@ -224,9 +224,10 @@ def test_repeatable_and_grid_size_invariant():
     first = host_bits(run(4, dA, dB))
     for _ in range(2):
         assert np.array_equal(host_bits(run(4, dA, dB)), first)
-    first6 = host_bits(run(6, dA, dB))
-    for _ in range(2):
-        assert np.array_equal(host_bits(run(6, dA, dB)), first6)
+    for r in (6, 7):
+        first6 = host_bits(run(r, dA, dB))
+        for _ in range(2):
+            assert np.array_equal(host_bits(run(r, dA, dB)), first6)
     base = None
     for grid in (1, 7, 256, 512):
         say(f"[gpu] persistent grid={grid}")
@@ -240,18 +241,19 @@ def test_repeatable_and_grid_size_invariant():
         assert np.array_equal(bits, base), f"grid {grid} differs"
 
 
-@pytest.mark.parametrize("shape", [(4608, 4608, 256), (8192, 2304, 128), (256, 256, 128)],
+@pytest.mark.parametrize("rung", [6, 7])
+@pytest.mark.parametrize("shape", [(4608, 4608, 256), (8192, 2304, 128), (256, 256, 128), (512, 768, 192)],
                          ids=lambda s: "x".join(map(str, s)))
-def test_ring4_persistent_rounds(shape):
+def test_ring4_persistent_rounds(rung, shape):
     """More tiles than compute units: workgroups of the four-wave ring walk
     several tiles each (the last round partial); every output compared."""
     M, N, K = shape
     A, B = rand_case(M, N, K, 80 + K)
     ref, _ = oracle.gemm_nt(A, B)
     D = torch.full((M, N), float("nan"), dtype=torch.float16, device=DEV)
-    say(f"[gpu] ring4 persistent rounds {M}x{N}x{K}")
-    run(6, dev(A), dev(B), D)
-    assert_parity(host_bits(D), ref, K, f"rung 6 {M}x{N}x{K}")
+    say(f"[gpu] ring4 persistent rounds rung={rung} {M}x{N}x{K}")
+    run(rung, dev(A), dev(B), D)
+    assert_parity(host_bits(D), ref, K, f"rung {rung} {M}x{N}x{K}")
 
 
 def test_non_default_stream_and_interleaving():
@@ -263,7 +265,7 @@ def test_non_default_stream_and_interleaving():
         dA, dB = dev(A), dev(B)
         say("[gpu] side stream")
         X = torch.randn(2048, 2048, device=DEV)
-        for rung in (0, 4, 5, 6):
+        for rung in (0, 4, 5, 6, 7):
             D = g.gemm_f16_nt(dA, dB) if rung == 0 else g.gemm_f16_nt_rung(rung, dA, dB)
             X = X * 1.0001          # unrelated work queued on the same stream
             s.synchronize()
@@ -294,7 +296,7 @@ def test_full_size_workloads_sampled(name):
     # whole output: finite everywhere (the workloads cannot overflow)
     assert torch.isfinite(D).all().item()
     if name == "square_4096":
-        for rung in (4, 5):
+        for rung in (4, 5, 6, 7):
             say(f"[gpu] full size square_4096 on rung {rung}")
             Dr = run(rung, dA, dB)
             gotr = host_bits(Dr[torch.from_numpy(rows).to(DEV), torch.from_numpy(cols).to(DEV)])

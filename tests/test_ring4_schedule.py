@@ -21,6 +21,9 @@ released it, and read only after its load has landed and been published):
   * all waves cross the same number of barriers, and the committed include
     is what the generator writes.
 
+Both forms are checked: one barrier per step (generate) and release and
+publish barriers per step (generate2).
+
 All four waves run the same instruction stream, so one stream stands for
 all of them; the checks treat every barrier as the point where all waves'
 earlier waited-for loads become visible.
@@ -195,6 +198,28 @@ def test_schedule_variants_keep_protocol(params):
         Sim(GEN.generate(p), kt).run()
 
 
+@pytest.mark.parametrize("kt", [2, 3, 4, 5, 6, 7, 8, 9, 16, 33])
+def test_two_barrier_schedule_ring_protocol(kt):
+    res = Sim(GEN.generate2(GEN.DEFAULT2), kt).run()
+    assert res["mfma"] == 2 * NB * NB * kt
+    assert res["epoch"] == 1 + 2 * (kt - 1)          # prologue + release and publish per handoff
+    assert len(res["acc"]) == NB * NB
+    assert sorted(res["loaded"]) == list(range(kt))
+    assert all(v == set(range(16)) for v in res["loaded"].values())
+
+
+@pytest.mark.parametrize("params", [
+    {"rel": 20, "load_every": 6, "pre": 40}, {"rel": 32, "load_every": 8, "pre": 16},
+    {"rel": 24, "load_every": 10, "pre": 48}, {"rel": 16, "load_every": 4, "pre": 32},
+    {"rel": 24, "load_every": 11, "pre": 56},   # look-ahead loads interleave with the next step's own
+])
+def test_two_barrier_variants_keep_protocol(params):
+    p = dict(GEN.DEFAULT2)
+    p.update(params)
+    for kt in (2, 3, 4, 7):
+        Sim(GEN.generate2(p), kt).run()
+
+
 def test_simulator_catches_a_planted_race():
     """Moving one handoff load ahead of its barrier must be caught."""
     text = GEN.generate(GEN.DEFAULT).split("\n")
@@ -225,7 +250,7 @@ def test_simulator_catches_a_short_wait():
 
 
 def test_committed_include_matches_generator():
-    text = GEN.generate(GEN.DEFAULT)
     with open(os.path.join(CSRC, "ring4_sched.inc")) as f:
         inc = f.read()
-    assert GEN.as_macro("G16_RING4_KLOOP", text) in inc
+    assert GEN.as_macro("G16_RING4_KLOOP", GEN.generate(GEN.DEFAULT)) in inc
+    assert GEN.as_macro("G16_RING4_KLOOP2", GEN.generate2(GEN.DEFAULT2)) in inc
