@@ -92,6 +92,18 @@ bool ring4_shape(int64_t M, int64_t N, int64_t K)
     return M % ring4::C::BM == 0 && N % ring4::C::BN == 0 && K % ring4::C::BK == 0 && K >= 2 * ring4::C::BK;
 }
 
+// Operands the 16-byte-load kernels take: every row of A and B starts on a
+// 16-byte boundary (K, leading dimensions and batch strides multiples of 8
+// elements, 16-byte aligned bases) and D's base is 16-byte aligned.  Other
+// operands go to the general kernel (ladder::r3_any).
+bool fast_operands(int64_t K, int64_t lda, int64_t ldb, int64_t sa, int64_t sb, const void* A, const void* B,
+                   const void* D)
+{
+    if (K % 8 || lda % 8 || ldb % 8 || sa % 8 || sb % 8) return false;
+    if (K > 0 && ((((uintptr_t)A) | ((uintptr_t)B)) & 15)) return false;
+    return ((uintptr_t)D & 15) == 0;
+}
+
 int validate(int rung, int64_t M, int64_t N, int64_t K, const void* A, const void* B, const void* D)
 {
     if (rung < 0 || rung > GEMM_F16_NT_R7_RING4_2B) return GEMM_F16_NT_INVALID_ARG;
@@ -99,18 +111,24 @@ int validate(int rung, int64_t M, int64_t N, int64_t K, const void* A, const voi
     const bool any_out = M > 0 && N > 0;
     if (any_out && K > 0 && (A == nullptr || B == nullptr)) return GEMM_F16_NT_INVALID_ARG;
     if (any_out && D == nullptr) return GEMM_F16_NT_INVALID_ARG;
-    if (K % 8 != 0) return GEMM_F16_NT_UNSUPPORTED;
     // index ranges the kernels are built for: per-lane 32-bit byte offsets
     // within a 256-row band, 2^31 tiles, 2D grid limits of the 128-tile rungs
     if (K > (int64_t(1) << 22) || M > (int64_t(1) << 31) || N > (int64_t(1) << 31)) return GEMM_F16_NT_UNSUPPORTED;
+    // rungs other than R3 (and the library's choice) need 16-byte rows
+    const bool general_ok = rung == 0 || rung == GEMM_F16_NT_R3_GRID;
+    if (K % 8 != 0 && !general_ok) return GEMM_F16_NT_UNSUPPORTED;
     if (rung == GEMM_F16_NT_R1_SINGLE_TILE && !(M == 128 && N == 128 && K == 64)) return GEMM_F16_NT_UNSUPPORTED;
     if (rung == GEMM_F16_NT_R2_KLOOP && !(M == 128 && N == 128)) return GEMM_F16_NT_UNSUPPORTED;
     if (rung == GEMM_F16_NT_R3_GRID && (N + 127) / 128 > 65535) return GEMM_F16_NT_UNSUPPORTED;
     if ((rung == GEMM_F16_NT_R6_RING4 || rung == GEMM_F16_NT_R7_RING4_2B) && !ring4_shape(M, N, K))
         return GEMM_F16_NT_UNSUPPORTED;
     if (!any_out) return GEMM_F16_NT_OK;
-    if (K > 0 && (((uintptr_t)A & 15) || ((uintptr_t)B & 15))) return GEMM_F16_NT_UNSUPPORTED;
-    if ((uintptr_t)D & 15) return GEMM_F16_NT_UNSUPPORTED;
+    // fp16 elements are 2-byte aligned; the fast kernels need 16 bytes
+    if ((K > 0 && (((uintptr_t)A & 1) || ((uintptr_t)B & 1))) || ((uintptr_t)D & 1)) return GEMM_F16_NT_UNSUPPORTED;
+    if (!fast_operands(K, K, K, 0, 0, A, B, D)) {
+        if (!general_ok) return GEMM_F16_NT_UNSUPPORTED;
+        if ((N + 127) / 128 > 65535) return GEMM_F16_NT_UNSUPPORTED;   // grid y of the general kernel
+    }
     const int64_t dbytes = M * N * 2;
     if (K > 0 && (overlaps(A, M * K * 2, D, dbytes) || overlaps(B, N * K * 2, D, dbytes)))
         return GEMM_F16_NT_INVALID_ARG;
@@ -134,12 +152,13 @@ int validate_strided(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda
     if (D == nullptr || (K > 0 && (A == nullptr || B == nullptr))) return GEMM_F16_NT_INVALID_ARG;
     // batch entries of D must not overlap each other (they are written concurrently)
     if (batch > 1 && sd < (M - 1) * ldd + N) return GEMM_F16_NT_INVALID_ARG;
-    if (K % 8 != 0 || lda % 8 != 0 || ldb % 8 != 0 || sa % 8 != 0 || sb % 8 != 0) return GEMM_F16_NT_UNSUPPORTED;
     if (K > (int64_t(1) << 22) || lda > (int64_t(1) << 22) || ldb > (int64_t(1) << 22) || M > (int64_t(1) << 31) ||
         N > (int64_t(1) << 31) || batch > (int64_t(1) << 31))
         return GEMM_F16_NT_UNSUPPORTED;
-    if (K > 0 && (((uintptr_t)A & 15) || ((uintptr_t)B & 15))) return GEMM_F16_NT_UNSUPPORTED;
-    if ((uintptr_t)D & 15) return GEMM_F16_NT_UNSUPPORTED;
+    if ((K > 0 && (((uintptr_t)A & 1) || ((uintptr_t)B & 1))) || ((uintptr_t)D & 1)) return GEMM_F16_NT_UNSUPPORTED;
+    // the general kernel's grid: (tiles_m, tiles_n <= 65535, batch <= 65535)
+    if (!fast_operands(K, lda, ldb, sa, sb, A, B, D) && ((N + 127) / 128 > 65535 || batch > 65535))
+        return GEMM_F16_NT_UNSUPPORTED;
     const int64_t dbytes = span_elems(M, N, ldd, sd, batch) * 2;
     if (K > 0 && (overlaps(A, span_elems(M, K, lda, sa, batch) * 2, D, dbytes) ||
                   overlaps(B, span_elems(N, K, ldb, sb, batch) * 2, D, dbytes)))
@@ -300,6 +319,15 @@ int launch_splitk(int64_t M, int64_t N, int64_t K, const void* A, const void* B,
     return launched();
 }
 
+// General operands (any K, strides, 2-byte alignment): R3's structure with
+// element-wise operand copies.
+int launch_any(const GemmArgs& g, hipStream_t s)
+{
+    const dim3 grid((unsigned)((g.M + 127) / 128), (unsigned)((g.N + 127) / 128), (unsigned)g.batch);
+    hipLaunchKernelGGL(ladder::r3_any, grid, dim3(ladder::THREADS), 0, s, g);
+    return launched();
+}
+
 GemmArgs contiguous_args(int64_t M, int64_t N, int64_t K, const void* A, const void* B, void* D)
 {
     GemmArgs g{};
@@ -352,6 +380,7 @@ int run(int rung, int64_t M, int64_t N, int64_t K, const void* A, const void* B,
         return launched();
     case GEMM_F16_NT_R2_KLOOP:
     case GEMM_F16_NT_R3_GRID: {
+        if (!fast_operands(K, K, K, 0, 0, A, B, D)) return launch_any(contiguous_args(M, N, K, A, B, D), s);
         const dim3 grid((unsigned)((M + 127) / 128), (unsigned)((N + 127) / 128));
         hipLaunchKernelGGL(ladder::r23_kloop_grid, grid, dim3(ladder::THREADS), 0, s, a, b, d, M, N, K);
         return launched();
@@ -365,6 +394,7 @@ int run(int rung, int64_t M, int64_t N, int64_t K, const void* A, const void* B,
     case GEMM_F16_NT_R7_RING4_2B:
         return launch_ring4(contiguous_args(M, N, K, A, B, D), s, 2);
     default:  // 0: the library's choice
+        if (!fast_operands(K, K, K, 0, 0, A, B, D)) return launch_any(contiguous_args(M, N, K, A, B, D), s);
         return launch_ring(contiguous_args(M, N, K, A, B, D), s, kDefaultRing4);
     }
 }
@@ -423,6 +453,7 @@ int gemm_f16_nt_strided_batched(int64_t M, int64_t N, int64_t K, const void* A, 
     g.sb = stride_b;
     g.sd = stride_d;
     g.batch = batch;
+    if (!fast_operands(K, lda, ldb, stride_a, stride_b, A, B, D)) return launch_any(g, s);
     return launch_ring(g, s, kDefaultRing4);
 }
 
@@ -435,7 +466,7 @@ int64_t gemm_f16_nt_splitk_workspace(int64_t M, int64_t N, int64_t K, int splits
         if (device_info(&cus) != GEMM_F16_NT_OK) return GEMM_F16_NT_DEVICE;
         s = choose_splits(M, N, K, cus);
     }
-    if (s <= 1 || K == 0) return 0;
+    if (s <= 1 || K == 0 || K % 8 != 0) return 0;
     int64_t k_chunk = 0, n_slices = 0;
     split_plan(K, s, &k_chunk, &n_slices);
     return n_slices > 1 ? n_slices * M * N * 4 : 0;
@@ -453,6 +484,7 @@ int gemm_f16_nt_splitk(int64_t M, int64_t N, int64_t K, const void* A, const voi
     if (st != GEMM_F16_NT_OK) return st;
     hipStream_t s = (hipStream_t)stream;
     if (K == 0) return launch_fill_zero(D, M * N, s);
+    if (!fast_operands(K, K, K, 0, 0, A, B, D)) return launch_any(contiguous_args(M, N, K, A, B, D), s);
     const int64_t want = splits == 0 ? choose_splits(M, N, K, cus) : splits;
     int64_t k_chunk = 0, n_slices = 1;
     if (want > 1) split_plan(K, want, &k_chunk, &n_slices);

@@ -5,7 +5,8 @@
 //
 //  R1  one tile, K = 64, grid 1 x 1       ("GEMM I", Step 1)
 //  R2  one tile, K-loop over 64-wide steps ("GEMM I", Step 2)
-//  R3  2D grid, one workgroup per tile     ("GEMM I", Step 3)
+//  R3  2D grid, one workgroup per tile     ("GEMM I", Step 3); r3_any is
+//      its general-operand form (any K, strides, 2-byte alignment)
 #pragma once
 
 #include "common.hpp"
@@ -132,6 +133,58 @@ __global__ __launch_bounds__(THREADS) void r23_kloop_grid(const f16* __restrict_
             else
                 store_block<false>(D, N, M, N, m_st + wm + 32 * i, n_st + wn + 32 * j, acc[i][j], lane, N % 4 == 0);
         }
+}
+
+
+// General operands on R3's structure: any K, any leading dimensions and
+// batch strides, any 2-byte alignment ("GEMM I" claims any M, N, K; the
+// fast rungs need 16-byte rows).  Each thread fills its 16-byte LDS chunks
+// element by element (zero outside M, N, K), then the R3 K-loop runs on the
+// swizzled tile; D is written element by element unless every row start of
+// every batch entry is 8-byte aligned.  Grid (tiles_m, tiles_n, batch).
+__device__ __forceinline__ void copy_tile_any(const f16* __restrict__ src, int64_t ld, int64_t rows, int64_t K,
+                                              int64_t k0, char* lds, int t)
+{
+#pragma unroll
+    for (int j = 0; j < (BM * CH) / THREADS; ++j) {
+        const int q = t + THREADS * j;
+        const int r = q / CH, c = q % CH;
+        const int64_t gk = k0 + 8 * c;
+        f16x8 v;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] = (r < rows && gk + e < K) ? src[r * ld + gk + e] : (f16)0;
+        *reinterpret_cast<f16x8*>(lds + lds_chunk_offset<CH, SWZ>(r, c)) = v;
+    }
+}
+
+__global__ __launch_bounds__(THREADS) void r3_any(const GemmArgs g)
+{
+    __shared__ __attribute__((aligned(128))) char As[BM * BK * 2];
+    __shared__ __attribute__((aligned(128))) char Bs[BN * BK * 2];
+    const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+    const int64_t m_st = (int64_t)blockIdx.x * BM, n_st = (int64_t)blockIdx.y * BN, b = blockIdx.z;
+    const f16* __restrict__ A = g.A + b * g.sa + m_st * g.lda;
+    const f16* __restrict__ B = g.B + b * g.sb + n_st * g.ldb;
+    f16* __restrict__ D = g.D + b * g.sd;
+    const int wm = 64 * (w >> 1), wn = 64 * (w & 1);
+    f32x16 acc[2][2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) acc[i][j] = f32x16{};
+    for (int64_t k0 = 0; k0 < g.K; k0 += BK) {
+        copy_tile_any(A, g.lda, g.M - m_st, g.K, k0, As, t);
+        copy_tile_any(B, g.ldb, g.N - n_st, g.K, k0, Bs, t);
+        __syncthreads();
+        mma_step(As, Bs, wm, wn, lane, acc);
+        __syncthreads();
+    }
+    const bool vec = ((uintptr_t)g.D & 7) == 0 && g.ldd % 4 == 0 && g.sd % 4 == 0;
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+            store_block<false>(D, g.ldd, g.M, g.N, m_st + wm + 32 * i, n_st + wn + 32 * j, acc[i][j], lane, vec);
 }
 
 }  // namespace ladder

@@ -20,16 +20,19 @@
  *
  * Pointers: A, B and D are device pointers (HIP device memory of the current
  * device).  The caller owns them; the library never frees, retains or
- * allocates memory.  A and B must be 16-byte aligned.  D must not overlap A
- * or B.  `stream` is a hipStream_t (NULL = the null stream).
+ * allocates memory.  They must be 2-byte (fp16) aligned.  D must not
+ * overlap A or B.  `stream` is a hipStream_t (NULL = the null stream).
  *
  * Calls are asynchronous and stream-ordered: they validate, enqueue and
  * return.  Validation happens before any HIP call, so an invalid call
  * launches nothing and leaves D untouched.  Faults inside a kernel surface
  * at the caller's next synchronisation of the stream.
  *
- * Shapes: M, N >= 0; K >= 0 and K % 8 == 0 (every row starts 16-byte
- * aligned).  M = 0 or N = 0 is a no-op; K = 0 writes +0.0 to all of D.
+ * Shapes: M, N, K >= 0.  M = 0 or N = 0 is a no-op; K = 0 writes +0.0 to
+ * all of D.  The fast kernels need every operand row to start on a 16-byte
+ * boundary (K % 8 == 0 and A, B, D 16-byte aligned); other operands run on
+ * a general kernel that copies operands element by element (the library's
+ * choice and rung 3 only; same result contract, several times slower).
  *
  * Return value: GEMM_F16_NT_OK (0) or a negative status below.
  */
@@ -44,7 +47,7 @@ extern "C" {
 
 #define GEMM_F16_NT_OK 0
 #define GEMM_F16_NT_INVALID_ARG (-1) /* negative size, null pointer with data, unknown rung, overlap */
-#define GEMM_F16_NT_UNSUPPORTED (-2) /* K % 8 != 0, misaligned A/B, shape a rung does not implement */
+#define GEMM_F16_NT_UNSUPPORTED (-2) /* shape or alignment a rung does not implement, odd addresses */
 #define GEMM_F16_NT_LAUNCH (-3)      /* the HIP launch itself failed */
 #define GEMM_F16_NT_DEVICE (-4)      /* no usable device / device query failed / not gfx950 */
 
@@ -52,7 +55,7 @@ extern "C" {
  * GEMM detailed technical notes", V1-V7).  Every rung computes the same D. */
 #define GEMM_F16_NT_R1_SINGLE_TILE 1 /* M = N = 128, K = 64 only, one workgroup */
 #define GEMM_F16_NT_R2_KLOOP 2       /* M = N = 128, any K: K-loop into one accumulator */
-#define GEMM_F16_NT_R3_GRID 3        /* any shape: 2D grid of 128 x 128 tiles */
+#define GEMM_F16_NT_R3_GRID 3        /* any shape and alignment: 2D grid of 128 x 128 tiles */
 #define GEMM_F16_NT_R4_RING 4        /* any shape: 256 x 256 tiles, direct-to-LDS pipelined ring */
 #define GEMM_F16_NT_R5_PERSISTENT_WS 5 /* any shape: persistent, producer/consumer waves */
 #define GEMM_F16_NT_R6_RING4 6 /* rung 4's ring with 4 waves of 128 x 128 and a fixed instruction
@@ -84,14 +87,14 @@ int gemm_f16_nt_persistent(int64_t M, int64_t N, int64_t K, const void* A, const
  *     B_b = B + b*stride_b, N x K, row r at B_b + r*ldb
  *     D_b = D + b*stride_d, M x N, row r at D_b + r*ldd
  *
- * All leading dimensions and strides are in elements (fp16).  lda, ldb >= K
- * and multiples of 8 (16-byte rows); stride_a, stride_b multiples of 8 (0
- * repeats one operand for every batch entry); ldd >= N, any value; stride_d
- * any value, and for batch > 1 at least (M-1)*ldd + N so the outputs do not
- * overlap.  D needs 16-byte alignment of its base only: rows that are not
- * 8-byte aligned are written element by element.  Same precision, rounding,
- * ownership and error behaviour as gemm_f16_nt; the library's kernel choice
- * (rung 4). */
+ * All leading dimensions and strides are in elements (fp16).  lda, ldb >= K;
+ * stride_a, stride_b >= 0 (0 repeats one operand for every batch entry);
+ * ldd >= N; stride_d >= 0, and for batch > 1 at least (M-1)*ldd + N so the
+ * outputs do not overlap.  With K, lda, ldb, stride_a, stride_b multiples
+ * of 8 and 16-byte aligned A, B and D the fast kernels run (rows of D that
+ * are not 8-byte aligned are written element by element); otherwise the
+ * general kernel, which also limits batch to 65535.  Same precision,
+ * rounding, ownership and error behaviour as gemm_f16_nt. */
 int gemm_f16_nt_strided_batched(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, int64_t stride_a,
                                 const void* B, int64_t ldb, int64_t stride_b, void* D, int64_t ldd,
                                 int64_t stride_d, int64_t batch, void* stream);
@@ -107,7 +110,8 @@ int gemm_f16_nt_strided_batched(int64_t M, int64_t N, int64_t K, const void* A, 
  * `workspace` is caller-owned device memory of at least
  * gemm_f16_nt_splitk_workspace(M, N, K, splits) bytes, 16-byte aligned,
  * not overlapping A, B or D; its contents are scratch.  When one slice
- * suffices the call is gemm_f16_nt and the workspace is not touched. */
+ * suffices, or the operands need the general kernel (see above), the call
+ * is gemm_f16_nt and the workspace is not touched. */
 int gemm_f16_nt_splitk(int64_t M, int64_t N, int64_t K, const void* A, const void* B, void* D, int splits,
                        void* workspace, int64_t workspace_bytes, void* stream);
 

@@ -56,10 +56,18 @@ A0, B0, D0 = 0x10000, 0x20000000, 0x40000000   # fake, 16-byte aligned, disjoint
     ((0, 64, 64, 64, 0, B0, D0), g.INVALID_ARG),
     ((0, 64, 64, 64, A0, 0, D0), g.INVALID_ARG),
     ((0, 64, 64, 64, A0, B0, 0), g.INVALID_ARG),
-    ((0, 64, 64, 12, A0, B0, D0), g.UNSUPPORTED),          # K % 8
-    ((0, 64, 64, 64, A0 + 2, B0, D0), g.UNSUPPORTED),      # misaligned A
-    ((0, 64, 64, 64, A0, B0 + 8, D0), g.UNSUPPORTED),      # misaligned B
-    ((0, 64, 64, 64, A0, B0, D0 + 4), g.UNSUPPORTED),      # misaligned D
+    ((0, 64, 64, 12, A0, B0, D0), g.OK),                   # K % 8 != 0: the general kernel
+    ((0, 64, 64, 64, A0 + 2, B0, D0), g.OK),               # A rows not 16-byte aligned: general kernel
+    ((0, 64, 64, 64, A0, B0 + 8, D0), g.OK),
+    ((0, 64, 64, 64, A0, B0, D0 + 4), g.OK),
+    ((3, 64, 64, 13, A0, B0, D0), g.OK),                   # R3 takes general operands too
+    ((4, 64, 64, 12, A0, B0, D0), g.UNSUPPORTED),          # the other rungs need 16-byte rows
+    ((4, 64, 64, 64, A0 + 2, B0, D0), g.UNSUPPORTED),
+    ((6, 256, 256, 128, A0, B0, D0 + 8), g.UNSUPPORTED),
+    ((1, 128, 128, 64, A0, B0 + 2, D0), g.UNSUPPORTED),
+    ((0, 64, 64, 64, A0 + 1, B0, D0), g.UNSUPPORTED),      # odd address: not an fp16 array
+    ((0, 64, 64, 64, A0, B0, D0 + 1), g.UNSUPPORTED),
+    ((0, 64, 10_000_000, 12, A0, B0, D0), g.UNSUPPORTED),  # general kernel grid: N/128 > 65535
     ((0, 64, 64, 64, A0, B0, A0 + 4096), g.INVALID_ARG),   # D overlaps A
     ((0, 64, 64, 64, A0, B0, B0), g.INVALID_ARG),          # D overlaps B
     ((8, 64, 64, 64, A0, B0, D0), g.INVALID_ARG),          # unknown rung
@@ -171,8 +179,11 @@ def test_schedule_xcd_locality():
     ((64, 64, 64, A0, 72, 0, B0, 64, 0, D0, 64, 4096, 3), g.OK),           # broadcast A and B
     ((64, 64, 64, A0, 56, 0, B0, 64, 0, D0, 64, 4096, 1), g.INVALID_ARG),  # lda < K
     ((64, 64, 64, A0, 64, 0, B0, 64, 0, D0, 60, 4096, 1), g.INVALID_ARG),  # ldd < N
-    ((64, 64, 64, A0, 68, 0, B0, 64, 0, D0, 64, 4096, 1), g.UNSUPPORTED),  # lda % 8
-    ((64, 64, 64, A0, 64, 4, B0, 64, 0, D0, 64, 4096, 2), g.UNSUPPORTED),  # stride_a % 8
+    ((64, 64, 64, A0, 68, 0, B0, 64, 0, D0, 64, 4096, 1), g.OK),           # lda % 8 != 0: general kernel
+    ((64, 64, 64, A0, 64, 4, B0, 64, 0, D0, 64, 4096, 2), g.OK),           # stride_a % 8 != 0: general kernel
+    ((64, 64, 13, A0, 13, 832, B0, 13, 0, D0, 64, 4096, 2), g.OK),         # K % 8 != 0
+    ((64, 64, 64, A0 + 1, 64, 0, B0, 64, 0, D0, 64, 4096, 1), g.UNSUPPORTED),  # odd address
+    ((64, 64, 64, A0, 68, 0, B0, 64, 0, D0, 64, 4096, 70000), g.UNSUPPORTED),  # general kernel: batch > 65535
     ((64, 64, 64, A0, 64, 0, B0, 64, 0, D0, 66, 8192, 2), g.OK),           # odd row pitch of D
     ((64, 64, 64, A0, 64, 0, B0, 64, 0, D0, 64, 4097, 2), g.OK),           # odd batch stride of D
     ((64, 64, 64, A0, 64, 0, B0, 64, 0, D0, 64, 4000, 2), g.INVALID_ARG),  # outputs overlap
@@ -192,7 +203,9 @@ def test_splitk_workspace_sizes():
     # 3 requested slices of 8 steps -> 3 steps each -> slices of 192, 192, 128
     assert L.gemm_f16_nt_splitk_workspace(256, 256, 512, 3) == 3 * 256 * 256 * 4
     # more slices than steps: one step per slice
-    assert L.gemm_f16_nt_splitk_workspace(100, 60, 130, 16) == 3 * 100 * 60 * 4
+    assert L.gemm_f16_nt_splitk_workspace(100, 60, 136, 16) == 3 * 100 * 60 * 4
+    # K % 8 != 0 runs on the general kernel, never split
+    assert L.gemm_f16_nt_splitk_workspace(100, 60, 130, 16) == 0
     assert L.gemm_f16_nt_splitk_workspace(256, 256, 512, 1) == 0
     assert L.gemm_f16_nt_splitk_workspace(256, 256, 0, 4) == 0
     assert L.gemm_f16_nt_splitk_workspace(256, 256, 512, 65) == g.INVALID_ARG
@@ -203,5 +216,5 @@ def test_splitk_argument_errors_before_any_device_work():
     L = g.lib()
     assert L.gemm_f16_nt_splitk(256, 256, 512, A0, B0, D0, -1, None, 0, None) == g.INVALID_ARG
     assert L.gemm_f16_nt_splitk(256, 256, 512, A0, B0, D0, 65, None, 0, None) == g.INVALID_ARG
-    assert L.gemm_f16_nt_splitk(256, 256, 500, A0, B0, D0, 2, None, 0, None) == g.UNSUPPORTED
+    assert L.gemm_f16_nt_splitk(256, 256, 512, A0 + 1, B0, D0, 2, None, 0, None) == g.UNSUPPORTED
     assert L.gemm_f16_nt_splitk(0, 256, 512, A0, B0, D0, 2, None, 0, None) == g.OK

@@ -192,10 +192,12 @@ def test_error_paths_launch_nothing():
         g.gemm_f16_nt_rung(1, A[:, :56].contiguous(), B[:, :56].contiguous(), D)   # R1 needs K = 64
     assert e.value.status == g.UNSUPPORTED
     L = g.lib()
-    st = L.gemm_f16_nt(128, 128, 60, A.data_ptr(), B.data_ptr(), D.data_ptr(), None)
-    assert st == g.UNSUPPORTED
-    st = L.gemm_f16_nt(128, 128, 64, A.data_ptr() + 2, B.data_ptr(), D.data_ptr(), None)
-    assert st == g.UNSUPPORTED
+    st = L.gemm_f16_nt_rung(4, 128, 128, 60, A.data_ptr(), B.data_ptr(), D.data_ptr(), None)
+    assert st == g.UNSUPPORTED          # the fast rungs need K % 8 == 0
+    st = L.gemm_f16_nt(128, 128, 64, A.data_ptr() + 1, B.data_ptr(), D.data_ptr(), None)
+    assert st == g.UNSUPPORTED          # odd address: not an fp16 array
+    st = L.gemm_f16_nt(128, 128, 64, A.data_ptr(), B.data_ptr(), A.data_ptr() + 64, None)
+    assert st == g.INVALID_ARG          # D overlaps A
     torch.cuda.synchronize()
     assert torch.all(D == 7.0).item()
 
@@ -303,7 +305,58 @@ def test_full_size_workloads_sampled(name):
             assert_parity(gotr, ref, w.K, f"{name} rung {rung}")
 
 
+# ------------------------------------------- general operands (any K, alignment)
+
+GENERAL = [(1, 1, 1), (5, 3, 7), (64, 64, 13), (130, 70, 100), (257, 129, 1001), (300, 260, 9), (128, 128, 66)]
+
+
+@pytest.mark.parametrize("rung", [0, 3])
+@pytest.mark.parametrize("shape", GENERAL, ids=lambda s: "x".join(map(str, s)))
+def test_general_k(rung, shape):
+    """K % 8 != 0: rows are not 16-byte aligned, so the general kernel runs."""
+    M, N, K = shape
+    A, B = rand_case(M, N, K, 200 + M + N + K)
+    ref, _ = oracle.gemm_nt(A, B)
+    say(f"[gpu] general K rung={rung} M={M} N={N} K={K}")
+    D = run(rung, dev(A), dev(B))
+    assert_parity(host_bits(D), ref, K, f"general rung {rung} {M}x{N}x{K}")
+
+
+def _offset_view(X: np.ndarray, off: int):
+    """Contiguous device view of X starting `off` elements into a buffer
+    (2-byte aligned, not 16-byte aligned for odd off)."""
+    buf = torch.zeros(X.size + off + 8, dtype=torch.float16, device=DEV)
+    v = buf[off: off + X.size].view(X.shape)
+    v.copy_(torch.from_numpy(np.ascontiguousarray(X)).to(DEV))
+    return v
+
+
+@pytest.mark.parametrize("offs", [(1, 0, 0), (0, 3, 0), (0, 0, 5), (7, 1, 3)], ids=lambda o: "a{}b{}d{}".format(*o))
+def test_misaligned_operands(offs):
+    M, N, K = 200, 136, 96
+    A, B = rand_case(M, N, K, 301)
+    ref, _ = oracle.gemm_nt(A, B)
+    dA, dB = _offset_view(A, offs[0]), _offset_view(B, offs[1])
+    D = _offset_view(np.zeros((M, N), np.float16), offs[2])
+    say(f"[gpu] misaligned offsets {offs}")
+    run(0, dA, dB, D)
+    assert_parity(host_bits(D), ref, K, f"misaligned {offs}")
+    with pytest.raises(g.GemmError) as e:     # the other rungs refuse them
+        g.gemm_f16_nt_rung(4, dA, dB, D)
+    assert e.value.status == g.UNSUPPORTED
+
+
 # ------------------------------------------------- strided / batched form
+
+def _padded3(Xs, ld: int):
+    """Device (batch, rows, cols) view of the matrices Xs in one buffer with
+    row pitch ld (ld >= cols) and batch stride rows * ld."""
+    rows, cols = Xs[0].shape
+    buf = torch.zeros((len(Xs), rows, ld), dtype=torch.float16)
+    for i, X in enumerate(Xs):
+        buf[i, :, :cols] = torch.from_numpy(X)
+    return buf.to(DEV)[:, :, :cols]
+
 
 def _padded(X: np.ndarray, ld: int):
     """Device tensor holding X (rows x cols) with row pitch ld (ld >= cols)."""
@@ -320,14 +373,17 @@ def _padded(X: np.ndarray, ld: int):
     (2, 256, 256, 64, 64, 0, 0, False),      # whole tiles with padded A rows
     (4, 130, 70, 40, 16, 8, 12, True),       # B shared by every batch entry
     (1, 1, 1, 8, 0, 0, 0, False),
+    (3, 97, 45, 21, 3, 5, 1, False),         # K % 8 != 0, odd pitches: the general kernel
+    (2, 256, 256, 128, 4, 0, 0, True),       # whole tiles but lda % 8 != 0: the general kernel
 ], ids=lambda c: "b{}_{}x{}x{}".format(*c[:4]))
 def test_strided_batched(case):
     batch, M, N, K, pa, pb, pd, bcast = case
     rng = np.random.default_rng(batch * 1000 + M + N + K)
     As = [rng.uniform(-1, 1, (M, K)).astype(np.float16) for _ in range(batch)]
     Bs = [rng.uniform(-1, 1, (N, K)).astype(np.float16) for _ in range(1 if bcast else batch)]
-    A = torch.stack([_padded(a, K + pa) for a in As])
-    B = torch.stack([_padded(b, K + pb) for b in Bs])
+    A = _padded3(As, K + pa)
+    B = _padded3(Bs, K + pb)
+    assert A.stride(1) == K + pa and B.stride(1) == K + pb   # row pitches really padded
     if bcast:
         B = B[0]
     Dfull = torch.full((batch, M, N + pd), float("nan"), dtype=torch.float16, device=DEV)
