@@ -194,7 +194,7 @@ int launch_fill_zero(void* D, int64_t n, hipStream_t s)
 // 16-byte aligned output rows in every batch entry.
 bool ring4_fits(const GemmArgs& g)
 {
-    return ring4_shape(g.M, g.N, g.K) && g.ldd % 8 == 0 && g.sd % 8 == 0;
+    return ring4_shape(g.M, g.N, g.K) && g.ldd % 8 == 0 && g.sd % 8 == 0 && g.ldd < (int64_t(1) << 24);
 }
 
 // Persistent launch: one workgroup per compute unit (fewer when there are

@@ -73,9 +73,47 @@ def freg(buf: int, op: str, idx: int) -> str:
 
 
 def areg(i: int, j: int) -> str:
-    """Accumulator operand of block (i, j): %[cB], B = 8i + j (an AGPR
-    quadruple chosen by the compiler)."""
-    return f"%[c{NB * i + j}]"
+    """Accumulator of block (i, j): a[4B:4B+3], B = 8i + j (the block owns
+    fixed accumulation registers; they never leave the assembly block)."""
+    b = NB * i + j
+    return f"a[{4 * b}:{4 * b + 3}]"
+
+
+# ---------------------------------------------------------------- epilogue
+# In the last k step the output is written while the MFMAs of later rows
+# still run.  Row group i (16 output rows, blocks (i, 0..7)) is final once
+# its 8 MFMAs of the last sub-step are issued and the MFMA results are
+# readable; it is then converted (v_accvgpr_read, v_cvt_pk_f16_f32: round to
+# nearest even), staged in this wave's 4 KiB LDS buffer i % 2 (rows of 256
+# bytes, 16-byte chunk c of row r at chunk c ^ (r mod 16)), read back as
+# whole rows and stored with 16-byte buffer stores, four rows per
+# instruction.  Temporaries live in the first fragment buffer (v128..v191),
+# free once sub-step 0 is done.
+EPI_T = 128   # v128..v159: converted blocks of a group
+EPI_R = 160   # v160..v191: read-back rows, two groups
+
+
+def epilogue_group(i: int) -> list[tuple[str, bool]]:
+    """Instructions of row group i as (text, is_lds_op)."""
+    out: list[tuple[str, bool]] = []
+    off = (i % 2) * 4096
+    for j in range(NB):
+        b = NB * i + j
+        t = EPI_T + 4 * j
+        for r in range(4):
+            out.append((f"v_accvgpr_read_b32 v{t + r}, a{4 * b + r}", False))
+        out.append((f"v_cvt_pk_f16_f32 v{t}, v{t}, v{t + 1}", False))
+        out.append((f"v_cvt_pk_f16_f32 v{t + 1}, v{t + 2}, v{t + 3}", False))
+        out.append((f"ds_write_b64 %[ew{j}], v[{t}:{t + 1}] offset:{off}", True))
+    out.append(("s_waitcnt lgkmcnt(0)", False))
+    rb = EPI_R + 16 * (i % 2)
+    for q in range(4):
+        out.append((f"ds_read_b128 v[{rb + 4 * q}:{rb + 4 * q + 3}], %[er{q}] offset:{off}", True))
+    out.append(("s_waitcnt lgkmcnt(0)", False))
+    for q in range(4):
+        out.append((f"buffer_store_dwordx4 v[{rb + 4 * q}:{rb + 4 * q + 3}], %[so{q}], %[rsd], %[sdo] offen", False))
+    out.append(("s_add_u32 %[sdo], %[sdo], %[gstr]", False))
+    return out
 
 
 class Emitter:
@@ -131,6 +169,43 @@ class Emitter:
         koff = "%[kh]" if ahead else "%[ko]"
         self.op(f"buffer_load_dwordx4 {voff}, {rsrc}, {koff} offen lds")
 
+    # --- epilogue interleaved with the last sub-step -------------------------
+    def epi_start(self, order: str) -> None:
+        # row groups finish in row order only when the MFMAs go row by row
+        assert order in ("ij", "snake"), "the interleaved epilogue needs a row-major MFMA order"
+        self.op("s_mov_b32 %[sdo], 0")
+        self.epi_q: list[tuple[str, bool]] = []
+        self.epi_next = 0          # next row group to queue
+
+    def epi_emit(self, text: str, lds: bool) -> None:
+        self.op(text)
+        if text == "s_waitcnt lgkmcnt(0)":
+            self.lgkm.clear()
+        elif lds:
+            self.lgkm.append(("epi",))
+
+    def epi_after_mfma(self, q: int, per_slot: int, delay: int) -> None:
+        """After MFMA q of the last sub-step: queue the row groups whose
+        MFMAs were all issued at least `delay` MFMAs ago, then emit up to
+        per_slot queued instructions."""
+        while self.epi_next < NB and q >= NB * self.epi_next + NB - 1 + delay:
+            self.epi_q += epilogue_group(self.epi_next)
+            self.epi_next += 1
+        for _ in range(min(per_slot, len(self.epi_q))):
+            self.epi_emit(*self.epi_q.pop(0))
+
+    def epi_finish(self) -> None:
+        """After the last MFMA: MFMA write -> accumulator read latency, then
+        the remaining groups."""
+        self.op("s_nop 7")
+        self.op("s_nop 7")
+        self.op("s_nop 7")
+        while self.epi_next < NB:
+            self.epi_q += epilogue_group(self.epi_next)
+            self.epi_next += 1
+        while self.epi_q:
+            self.epi_emit(*self.epi_q.pop(0))
+
     # --- MFMA ----------------------------------------------------------------
     def mfma(self, buf: int, i: int, j: int, first: bool) -> None:
         self.wait_frag((buf, "a", i), (buf, "b", j))
@@ -139,6 +214,7 @@ class Emitter:
 
 
 def mfma_block(q: int, order: str) -> tuple[int, int]:
+    assert order in ("ij", "ji", "snake")
     """Block (i, j) of the q-th MFMA of a sub-step.  'ij': i outer (runs of
     8 MFMAs share an A fragment); 'ji': j outer; 'snake': i outer with j
     reversed on odd rows (the B fragment repeats across a row change)."""
@@ -205,7 +281,11 @@ def emit_step(e: Emitter, stage: int, first: bool, body_loads: bool, hand_loads:
                 r_next = 0
                 if hand_loads:
                     hand = [(k, q + off) for k, off in enumerate(p["hand_slots"])]
+            if last and kk == KSUB - 1 and q == 0:
+                e.epi_start(p.get("order", "ij"))
             e.mfma(cur, i, j, first and kk == 0)
+            if last and kk == KSUB - 1:
+                e.epi_after_mfma(q, p["epi_slot"], p["epi_delay"])
             while r_next < len(reads) and slots[r_next] <= q:
                 e.read(*reads[r_next])
                 r_next += 1
@@ -223,6 +303,8 @@ def emit_step(e: Emitter, stage: int, first: bool, body_loads: bool, hand_loads:
     while nh < len(hand):
         e.load(hand[nh][0], stage, ahead=True)
         nh += 1
+    if last:
+        e.epi_finish()
     assert nb == len(body), "body load slots beyond the step"
     if not last:
         e.op("s_add_u32 %[ko], %[ko], 128")   # %[ko] is the offset of step j+1 during step j
@@ -297,11 +379,6 @@ def generate(p: dict) -> str:
     e.label("3")
     step(0, False, False, False, True)
     e.label("4")
-    # the accumulators are read by VALU code after the block: cover the
-    # MFMA write -> VALU read latency
-    e.op("s_nop 7")
-    e.op("s_nop 7")
-    e.op("s_nop 7")
     return "\n".join(e.lines)
 
 
@@ -361,7 +438,11 @@ def emit_step2(e: Emitter, stage: int, first: bool, carried: bool, ahead: bool, 
                 reads = [(0, op, idx, stage ^ 1, 0) for (op, idx) in ro]
                 rslots = spread(nr, q + p["post_start"], p["post_every"])
                 r_next = 0
+            if last and kk == KSUB - 1 and q == 0:
+                e.epi_start(p.get("order", "ij"))
             e.mfma(cur, i, j, first and kk == 0)
+            if last and kk == KSUB - 1:
+                e.epi_after_mfma(q, p["epi_slot"], p["epi_delay"])
             while r_next < len(reads) and rslots[r_next] <= q:
                 e.read(*reads[r_next])
                 r_next += 1
@@ -374,6 +455,8 @@ def emit_step2(e: Emitter, stage: int, first: bool, carried: bool, ahead: bool, 
         while r_next < len(reads):
             e.read(*reads[r_next])
             r_next += 1
+    if last:
+        e.epi_finish()
     assert ci == len(carry) and oi == len(own)
     if not last:
         e.op("s_add_u32 %[ko], %[ko], 128")
@@ -444,9 +527,6 @@ def generate2(p: dict) -> str:
     e.label("3")
     step(0, False, False, False, True)
     e.label("4")
-    e.op("s_nop 7")
-    e.op("s_nop 7")
-    e.op("s_nop 7")
     return "\n".join(e.lines)
 
 
@@ -459,6 +539,8 @@ DEFAULT = {
     "post_every": 1,      # ... then one every post_every MFMAs
     "hand_slots": spread(8, 0, 4),     # loads 0-7 of step j+2 after step j's barrier
     "body_slots": spread(8, 2, 8),     # loads 8-15 of step j+1 during step j
+    "epi_slot": 8,        # epilogue instructions per MFMA slot of the last sub-step
+    "epi_delay": 2,       # MFMAs between a row group's last MFMA and its first read
 }
 
 # two-barrier form (generate2): release after sub-step 0's reads, loads of

@@ -18,6 +18,10 @@ released it, and read only after its load has landed and been published):
     block, after an lgkmcnt wait that covers their reads (LDS reads
     complete in issue order), and accumulates into the block's registers,
     starting from 0 in the first step;
+  * the epilogue reads each accumulator once, after the MFMA that finished
+    it and the MFMA-to-read latency, converts consecutive pairs, stages each
+    16-row group in its own LDS buffer, reads it back only after the group's
+    writes completed, and stores every row group once at its own offset;
   * all waves cross the same number of barriers, and the committed include
     is what the generator writes.
 
@@ -87,8 +91,20 @@ class Sim:
         loaded_steps: dict[int, set] = {}
         mfma = 0
         pc = 0
+        final_at: dict[int, int] = {}          # block -> line of its last MFMA
+        since_final: dict[int, int] = {}       # block -> wait states since
+        acc_read: set = set()                  # accumulator registers read
+        vreg: dict[int, tuple] = {}            # epilogue VGPR contents
+        sdo = None
+        epi_pending: list = []                 # staging writes not yet waited: (buf, group, j)
+        staged: dict[int, tuple] = {}          # buf -> (group, set of j) completed
+        stores: list = []
         while pc < len(self.lines):
             ln = self.lines[pc]
+            if not ln.startswith("v_mfma"):
+                nop = re.match(r"s_nop (\d+)$", ln)
+                for b_ in since_final:
+                    since_final[b_] += int(nop.group(1)) + 1 if nop else 1
             if ln.startswith("s_cmp_eq_u32 %[rem], "):
                 scc = int(rem == int(ln.split(",")[1]))
             elif ln.startswith("s_cbranch_scc1 "):
@@ -138,7 +154,17 @@ class Sim:
                     keep = int(m.group(1))
                     done, lgkm = (lgkm[: len(lgkm) - keep], lgkm[len(lgkm) - keep:]) if keep else (lgkm, [])
                     for reg, content in done:
-                        frag[reg] = content
+                        if content[0] == "epi_w":
+                            buf, grp, j = content[1:]
+                            st_ = staged.setdefault(buf, (grp, set()))
+                            if st_[0] != grp:
+                                st_ = (grp, set())
+                            st_[1].add(j)
+                            staged[buf] = st_
+                        elif content[0] == "epi_r":
+                            vreg[reg] = content[1:]
+                        else:
+                            frag[reg] = content
             elif ln == "s_barrier":
                 assert not lgkm, "barrier with LDS reads in flight"
                 epoch += 1
@@ -147,6 +173,47 @@ class Sim:
                     for n, (step, _) in landed[st].items():
                         visible[st][n] = step
                     landed[st] = {}
+            elif ln.startswith("ds_read_b128 ") and "%[er" in ln:
+                m = re.match(r"ds_read_b128 (v\[\d+:\d+\]), %\[er(\d)\] offset:(\d+)$", ln)
+                reg, q, buf = _regs(m.group(1)), int(m.group(2)), int(m.group(3)) // 4096
+                grp, js = staged.get(buf, (None, set()))
+                assert js == set(range(NB)), f"read-back of buffer {buf} before all its writes completed"
+                lgkm.append((reg, ("epi_r", grp, q)))
+            elif ln.startswith("ds_write_b64"):
+                m = re.match(r"ds_write_b64 %\[ew(\d)\], v\[(\d+):(\d+)\] offset:(\d+)$", ln)
+                j, r0, buf = int(m.group(1)), int(m.group(2)), int(m.group(4)) // 4096
+                lo, hi = vreg.get(r0), vreg.get(r0 + 1)
+                assert lo and hi and lo[0] == "pk" and hi[0] == "pk", "staging write of unconverted data"
+                b0 = lo[1] // 4
+                assert lo[1] == 4 * b0 and hi[1] == 4 * b0 + 2, "staging write of the wrong accumulator pairs"
+                grp, jj = b0 // NB, b0 % NB
+                assert jj == j and buf == grp % 2, f"block {b0} staged at column {j}, buffer {buf}"
+                if buf in staged and staged[buf][0] != grp:
+                    del staged[buf]
+                lgkm.append((-1, ("epi_w", buf, grp, j)))
+            elif ln.startswith("v_accvgpr_read_b32"):
+                m = re.match(r"v_accvgpr_read_b32 v(\d+), a(\d+)$", ln)
+                v, a = int(m.group(1)), int(m.group(2))
+                blk = a // 4
+                assert blk in final_at and since_final[blk] >= 11, f"accumulator a{a} read too early"
+                assert a not in acc_read, f"a{a} read twice"
+                acc_read.add(a)
+                vreg[v] = ("acc", a)
+            elif ln.startswith("v_cvt_pk_f16_f32"):
+                m = re.match(r"v_cvt_pk_f16_f32 v(\d+), v(\d+), v(\d+)$", ln)
+                d_, x, y = int(m.group(1)), int(m.group(2)), int(m.group(3))
+                cx, cy = vreg.get(x), vreg.get(y)
+                assert cx and cy and cx[0] == "acc" and cy[0] == "acc" and cy[1] == cx[1] + 1, "conversion pair"
+                vreg[d_] = ("pk", cx[1])
+            elif ln == "s_mov_b32 %[sdo], 0":
+                sdo = 0
+            elif ln == "s_add_u32 %[sdo], %[sdo], %[gstr]":
+                sdo += 1
+            elif ln.startswith("buffer_store_dwordx4"):
+                m = re.match(r"buffer_store_dwordx4 (v\[\d+:\d+\]), %\[so(\d)\], %\[rsd\], %\[sdo\] offen$", ln)
+                reg, q = _regs(m.group(1)), int(m.group(2))
+                assert vreg.get(reg) == (sdo, q), f"store of {vreg.get(reg)} at group {sdo}, rows {q}"
+                stores.append((sdo, q))
             elif ln.startswith("ds_read_b128"):
                 m = re.match(r"ds_read_b128 (v\[\d+:\d+\]), %\[r([ab])(\d)(\d)\] offset:(\d+)", ln)
                 reg, op, st, kk, off = _regs(m.group(1)), m.group(2), int(m.group(3)), int(m.group(4)), int(m.group(5))
@@ -159,9 +226,15 @@ class Sim:
                 frag.pop(reg, None)
                 lgkm.append((reg, (step, kk, op, idx)))
             elif ln.startswith("v_mfma_f32_16x16x32_f16"):
-                m = re.match(r"v_mfma_f32_16x16x32_f16 (%\[c(\d+)\]), (v\[\d+:\d+\]), (v\[\d+:\d+\]), (\S+)$", ln)
-                acc, blk, breg, areg, src_c = m.group(1), int(m.group(2)), _regs(m.group(3)), _regs(m.group(4)), m.group(5)
+                m = re.match(r"v_mfma_f32_16x16x32_f16 (a\[(\d+):\d+\]), (v\[\d+:\d+\]), (v\[\d+:\d+\]), (\S+)$", ln)
+                acc, blk, breg, areg, src_c = m.group(1), int(m.group(2)) // 4, _regs(m.group(3)), _regs(m.group(4)), m.group(5)
                 step, kk = mfma // (2 * NB * NB), (mfma // (NB * NB)) % 2
+                assert not any(4 * blk + r in acc_read for r in range(4)), "MFMA on an accumulator already written out"
+                if step == kt - 1 and kk == 1:
+                    final_at[blk] = pc
+                    since_final[blk] = 0
+                for b_ in since_final:
+                    since_final[b_] += 4       # an MFMA issue is at least 4 wait states
                 i, j = blk // NB, blk % NB
                 assert frag.get(areg) == (step, kk, "a", i), f"MFMA {mfma}: A operand {frag.get(areg)}"
                 assert frag.get(breg) == (step, kk, "b", j), f"MFMA {mfma}: B operand {frag.get(breg)}"
@@ -173,6 +246,8 @@ class Sim:
                 mfma += 1
             pc += 1
         assert not vm and not lgkm, "operations in flight at the end of the block"
+        assert acc_read == set(range(4 * NB * NB)), "accumulators not all written out"
+        assert sorted(stores) == [(i, q) for i in range(NB) for q in range(4)], "output rows not all stored once"
         return {"mfma": mfma, "epoch": epoch, "acc": acc_started, "loaded": loaded_steps}
 
 
@@ -236,6 +311,15 @@ def test_simulator_catches_an_immediate_offset():
     text = GEN.generate(GEN.DEFAULT).replace("%[kh] offen lds", "%[ko] offen offset:128 lds", 1)
     with pytest.raises(AssertionError):
         Sim(text, 4).run()
+
+
+def test_simulator_catches_an_early_epilogue():
+    """Queuing each row group as soon as its MFMAs are issued (no delay)
+    reads accumulators before the MFMA latency has passed."""
+    p = dict(GEN.DEFAULT)
+    p["epi_delay"] = -1
+    with pytest.raises(AssertionError):
+        Sim(GEN.generate(p), 3).run()
 
 
 def test_simulator_catches_a_short_wait():
