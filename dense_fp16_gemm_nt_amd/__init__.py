@@ -29,7 +29,8 @@ R4_RING = 4
 R5_PERSISTENT_WS = 5
 R6_RING4 = 6
 R7_RING4_2B = 7
-RUNGS = (R1_SINGLE_TILE, R2_KLOOP, R3_GRID, R4_RING, R5_PERSISTENT_WS, R6_RING4, R7_RING4_2B)
+R8_RING4_GAP = 8
+RUNGS = (R1_SINGLE_TILE, R2_KLOOP, R3_GRID, R4_RING, R5_PERSISTENT_WS, R6_RING4, R7_RING4_2B, R8_RING4_GAP)
 
 _lock = threading.Lock()
 _lib = None

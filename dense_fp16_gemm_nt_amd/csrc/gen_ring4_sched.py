@@ -242,7 +242,7 @@ def spread(n: int, start: int, every: int) -> list[int]:
 
 
 def emit_step(e: Emitter, stage: int, first: bool, body_loads: bool, hand_loads: bool, last: bool,
-              p: dict) -> None:
+              p: dict, wave: int = 0) -> None:
     """One 64-wide k step j reading `stage`.
 
     The 16 loads of a step are split: loads 0 .. n_hand-1 of step j+2 go out
@@ -250,9 +250,13 @@ def emit_step(e: Emitter, stage: int, first: bool, body_loads: bool, hand_loads:
     refills), loads n_hand .. 15 of step j+1 go out during step j's body
     (into the other stage, freed by step j-1's barrier).  body_loads /
     hand_loads say whether those steps exist.  first: the accumulators
-    start from 0.  last: no handoff (no barrier, no next-step reads)."""
+    start from 0.  last: no handoff (no barrier, no next-step reads).
+    wave: the wave's index; its load slots move by wave * p["hand_shift"]
+    and wave * p["body_shift"] MFMAs, so that the waves of a workgroup do
+    not issue their loads in the same slot."""
     n_hand = len(p["hand_slots"])
-    body = [(n_hand + k, g) for k, g in enumerate(p["body_slots"])] if body_loads else []
+    hs, bs = wave * p.get("hand_shift", 0), wave * p.get("body_shift", 0)
+    body = [(n_hand + k, g + bs) for k, g in enumerate(p["body_slots"])] if body_loads else []
     nb = 0
     ro = read_order(p.get("order", "ij"))
     nr = len(ro)
@@ -280,7 +284,7 @@ def emit_step(e: Emitter, stage: int, first: bool, body_loads: bool, hand_loads:
                 slots = spread(nr, q + p["post_start"], p["post_every"])
                 r_next = 0
                 if hand_loads:
-                    hand = [(k, q + off) for k, off in enumerate(p["hand_slots"])]
+                    hand = [(k, q + off + hs) for k, off in enumerate(p["hand_slots"])]
             if last and kk == KSUB - 1 and q == 0:
                 e.epi_start(p.get("order", "ij"))
             e.mfma(cur, i, j, first and kk == 0)
@@ -311,9 +315,9 @@ def emit_step(e: Emitter, stage: int, first: bool, body_loads: bool, hand_loads:
         e.op("s_add_u32 %[kh], %[kh], 128")   # %[kh] that of step j+2
 
 
-def generate(p: dict) -> str:
-    """The k loop.  During step j, %[ko] is the byte offset of step j+1
-    (body loads) and %[kh] that of step j+2 (handoff loads)."""
+def generate(p: dict, wave: int = 0) -> str:
+    """The k loop of wave `wave`.  During step j, %[ko] is the byte offset
+    of step j+1 (body loads) and %[kh] that of step j+2 (handoff loads)."""
     assert len(p["hand_slots"]) + len(p["body_slots"]) == NLOAD
     e = Emitter()
     # prologue: steps 0 and 1 into stages 0 and 1
@@ -334,7 +338,7 @@ def generate(p: dict) -> str:
         nonlocal after_handoff
         if after_handoff is not None:
             e.lgkm = list(after_handoff)
-        emit_step(e, stage, first, body_loads, hand_loads, last, p)
+        emit_step(e, stage, first, body_loads, hand_loads, last, p, wave)
         if not last:
             if after_handoff is None:
                 after_handoff = list(e.lgkm)
@@ -382,7 +386,8 @@ def generate(p: dict) -> str:
     return "\n".join(e.lines)
 
 
-def emit_step2(e: Emitter, stage: int, first: bool, carried: bool, ahead: bool, last: bool, p: dict) -> None:
+def emit_step2(e: Emitter, stage: int, first: bool, carried: bool, ahead: bool, last: bool, p: dict,
+               wave: int = 0) -> None:
     """One 64-wide k step j in the two-barrier form.
 
     A release barrier after sub-step 0's reads of this stage (MFMA p["rel"])
@@ -394,13 +399,16 @@ def emit_step2(e: Emitter, stage: int, first: bool, carried: bool, ahead: bool, 
     counts only the younger loads of step j+2) and is followed by step
     j+1's sub-step-0 fragment reads.  carried: step j+1's last loads are
     issued at the start of this step; ahead: step j+2 exists.  first: the
-    accumulators start from 0.  last: no barriers, no next-step reads."""
+    accumulators start from 0.  last: no barriers, no next-step reads.
+    wave: the wave's index; its load slots move by wave * p["wave_shift"]
+    MFMAs."""
     order = p.get("order", "ij")
     ro = read_order(order)
     nr = len(ro)
     rel, every = p["rel"], p["load_every"]
     pub = NQ + p["pre"]                                  # MFMA index of the publish barrier
-    slots = [rel + every * n for n in range(NLOAD)]      # step j+2's loads, in step-j MFMA indices
+    shift = wave * p.get("wave_shift", 0)
+    slots = [rel + shift + every * n for n in range(NLOAD)]   # step j+2's loads, in step-j MFMA indices
     own = [(n, g) for n, g in enumerate(slots) if g < 2 * NQ] if (ahead and not last) else []
     carry = [(n, g - 2 * NQ) for n, g in enumerate(slots) if g >= 2 * NQ] if carried else []
     n_after_own = None                                   # own loads issued before the publish wait
@@ -463,12 +471,13 @@ def emit_step2(e: Emitter, stage: int, first: bool, carried: bool, ahead: bool, 
         e.op("s_add_u32 %[kh], %[kh], 128")
 
 
-def generate2(p: dict) -> str:
-    """The k loop in the two-barrier form (same branch structure and
-    operands as generate())."""
+def generate2(p: dict, wave: int = 0) -> str:
+    """The k loop of wave `wave` in the two-barrier form (same branch
+    structure and operands as generate())."""
     assert p["rel"] >= len(read_order(p.get("order", "ij"))) * p["read_every"] - 1 + p["read_start"], \
         "release barrier before the sub-step-1 reads are issued"
-    assert p["rel"] + p["load_every"] * (NLOAD - 1) < 2 * NQ + NQ + p["pre"], "loads too sparse"
+    last_slot = p["rel"] + 3 * p.get("wave_shift", 0) + p["load_every"] * (NLOAD - 1)
+    assert last_slot < 2 * NQ + NQ + p["pre"], "loads too sparse"
     e = Emitter()
     for n in range(NLOAD):
         e.load(n, 0)
@@ -486,7 +495,7 @@ def generate2(p: dict) -> str:
         nonlocal after
         if after is not None:
             e.lgkm = list(after)
-        emit_step2(e, stage, first, carried, ahead, last, p)
+        emit_step2(e, stage, first, carried, ahead, last, p, wave)
         if not last:
             if after is None:
                 after = list(e.lgkm)
@@ -530,6 +539,227 @@ def generate2(p: dict) -> str:
     return "\n".join(e.lines)
 
 
+# ------------------------------------------------------------ third form
+# Release and publish barriers per k step, as in the second form, with at
+# most one instruction besides the MFMA in each MFMA gap.
+#
+# With one wave per SIMD the wave issues about one instruction every four
+# cycles and a 16x16x32 MFMA occupies the matrix core for 16: one other
+# instruction fits between two MFMAs for free, and each further one delays
+# the next MFMA.  This form places every instruction of a step in its own
+# gap (gap g follows MFMA g of the step):
+#
+#   * gaps 0..15: the 16 fragment reads of sub-step 1 (this stage);
+#   * gap rel-1: s_waitcnt lgkmcnt(0) (this wave is done reading the
+#     stage), gap rel: the release barrier - the stage is free for step j+2;
+#   * from gap rel+1, one every load_every gaps: the 16 loads of step j+2
+#     into this stage; those beyond the step go out at the start of step
+#     j+1.  Each 4 loads of an operand share one M0 value: load q lands at
+#     M0 + 1024*(q mod 4) through the instruction offset, which also moves
+#     the global address, so the lane offsets passed for it (%[axQ],
+#     %[bxQ]) are the row-group offsets minus that amount.  This takes 12
+#     of the 16 M0 writes and every s_nop out of the step;
+#   * gap pub-1: s_waitcnt vmcnt(n) for step j+1's loads (n counts the
+#     younger loads of step j+2), gap pub: the publish barrier;
+#   * from gap max(pub+1, f0_start) (sub-step 0 is done with the first
+#     fragment buffer): the 16 fragment reads of step j+1's sub-step 0 (the
+#     other stage), one wait for them f0_lat gaps after the last;
+#   * the step offsets, the step counter and the compare in the last gaps
+#     before MFMA 127, the branches after it.
+#
+# A load has from its issue to the publish barrier of the next step to
+# land: more than 1.5 steps for the first of a step, about half a step for
+# the last, which covers operands streamed from HBM.
+
+
+class Emitter3(Emitter):
+    def load_imm(self, op: str, q: int, stage: int, koff: str = "ko") -> None:
+        """Load q (0..7) of operand op into `stage` with the instruction
+        offset; M0 must hold the base of q's group of 4.  koff: the SGPR
+        with the step's byte offset along K."""
+        imm = 1024 * (q % 4)
+        off = f" offset:{imm}" if imm else ""
+        self.op(f"buffer_load_dwordx4 %[{op}x{q}], %[rs{op}], %[{koff}] offen{off} lds")
+
+    @staticmethod
+    def m0_line(op: str, q: int, stage: int) -> str:
+        base = stage * 65536 + (32768 if op == "b" else 0) + 4096 * (q // 4)
+        return f"s_add_u32 m0, %[lb], {base}"
+
+
+LOAD3 = [("a", q) for q in range(8)] + [("b", q) for q in range(8)]
+
+
+def emit_step3(e: Emitter3, stage: int, first: bool, carried: bool, ahead: bool, has_next: bool, last: bool,
+               tail: list[str], p: dict) -> None:
+    """One 64-wide k step j reading `stage` in the third form.  carried:
+    step j+1's late loads are issued in this step; ahead: this step starts
+    the loads of step j+2; has_next: step j+1 exists (publish barrier, its
+    fragment reads); last: the final step (epilogue).  %[ko] is the byte
+    offset of step j+1 and %[kh] that of step j+2 during the step."""
+    order = p.get("order", "snake")
+    ro = read_order(order)
+    ng = KSUB * NQ
+    gaps: list[list[tuple]] = [[] for _ in range(ng)]
+
+    def free(g: int) -> bool:
+        return 0 <= g < ng and not gaps[g]
+
+    def first_free(g: int) -> int:
+        while not free(g):
+            g += 1
+            assert g < ng, "step too full"
+        return g
+
+    rel, pub, every = p["rel"], p["pub"], p["load_every"]
+    slots = [rel + 1 + every * k for k in range(NLOAD)]          # step j+2's loads, step-j gaps
+    limit = ng - 8                                               # the last gaps hold the tail
+    own = [(k, s) for k, s in enumerate(slots) if s < limit] if ahead else []
+    carry = [(k, max(0, s - ng)) for k, s in enumerate(slots) if s >= limit] if carried else []
+    if not last:
+        br = [t for t in tail if t.startswith(("s_cbranch", "s_branch"))]
+        rest = [t for t in tail if t not in br]
+        assert tail == rest + br, "branches close the tail"
+        for k, t in enumerate(rest):
+            gaps[ng - 1 - len(rest) + k].append(("text", t))
+        for t in br:
+            gaps[ng - 1].append(("text", t))
+    for n, (op, idx) in enumerate(ro):
+        gaps[p["f1_start"] + n * p["f1_every"]].append(("read", (1, op, idx, stage, 1)))
+    assert rel - 1 > p["f1_start"] + (len(ro) - 1) * p["f1_every"]
+    if ahead:
+        gaps[rel - 1].append(("text", "s_waitcnt lgkmcnt(0)", "clear"))
+        gaps[rel].append(("text", "s_barrier"))
+    else:
+        gaps[rel - 1].append(("text", "s_waitcnt lgkmcnt(0)", "clear"))
+    if has_next:
+        # the publish gaps are reserved before the loads are placed
+        gaps[pub - 1].append(("publish_wait",))
+        gaps[pub].append(("text", "s_barrier"))
+    # loads in issue order: step j+1's carried loads (other stage, %[ko]),
+    # then step j+2's own loads (this stage, %[kh]); an M0 write whenever
+    # the group of 4 changes, in a free gap after the previous load
+    seq = [(k, s, stage ^ 1, "ko") for (k, s) in carry] + [(k, s, stage, "kh") for (k, s) in own]
+    prev, cur_m0 = -1, None
+    placed = []
+    for (k, s, st, koff) in seq:
+        op, q = LOAD3[k]
+        g = first_free(max(s, prev + 1))
+        grp = (st, op, q // 4)
+        if grp != cur_m0:
+            m = next((x for x in range(g - 1, prev, -1) if free(x)), None)
+            if m is None:
+                m = first_free(prev + 1)
+                g = first_free(m + 1)
+            gaps[m].append(("text", Emitter3.m0_line(op, q, st)))
+            cur_m0 = grp
+        gaps[g].append(("load", op, q, st, koff))
+        placed.append((g, koff))
+        prev = g
+    assert all(g < ng - 1 - 4 for g, _ in placed), "loads run into the tail"
+    if has_next:
+        # publish: step j+1's loads have landed in every wave; the own loads
+        # of step j+2 issued so far are younger and need not wait
+        n_young = sum(1 for g, koff in placed if koff == "kh" and g < pub - 1)
+        assert not any(koff == "ko" and g >= pub - 1 for g, koff in placed), "carried load after the publish wait"
+        gaps[pub - 1] = [("text", f"s_waitcnt vmcnt({n_young})")]
+        g = max(p["f0_start"], pub + 1)
+        lastr = g
+        for (op, idx) in ro:
+            g = first_free(g)
+            gaps[g].append(("read", (0, op, idx, stage ^ 1, 0)))
+            lastr = g
+            g += 1
+        gaps[first_free(lastr + p["f0_lat"])].append(("text", "s_waitcnt lgkmcnt(0)", "clear"))
+    scc_writers = [g for g in range(ng) for it in gaps[g]
+                   if it[0] == "text" and it[1].startswith(("s_add_u32", "s_sub_u32"))]
+    cmp_at = [g for g in range(ng) for it in gaps[g] if it[0] == "text" and it[1].startswith("s_cmp")]
+    assert not cmp_at or max(scc_writers, default=-1) < min(cmp_at), "SCC clobbered before the branch"
+
+    for g in range(ng):
+        kk, q = divmod(g, NQ)
+        i, j = mfma_block(q, order)
+        if last and kk == KSUB - 1 and q == 0:
+            e.epi_start(order)
+        e.mfma(kk, i, j, first and kk == 0)
+        if last and kk == KSUB - 1:
+            e.epi_after_mfma(q, p["epi_slot"], p["epi_delay"])
+        for it in gaps[g]:
+            if it[0] == "read":
+                e.read(*it[1])
+            elif it[0] == "load":
+                e.load_imm(it[1], it[2], it[3], it[4])
+            else:
+                e.op(it[1])
+                if len(it) > 2:
+                    e.lgkm.clear()
+    if last:
+        e.epi_finish()
+        for t in tail:
+            e.op(t)
+
+
+def generate3(p: dict) -> str:
+    """The k loop in the third form.  During step j, %[ko] is the byte
+    offset of step j+1 (its late loads) and %[kh] that of step j+2."""
+    order = p.get("order", "snake")
+    e = Emitter3()
+    for stage in (0, 1):
+        if stage:
+            e.op("s_add_u32 %[ko], %[ko], 128")
+        for (op, q) in LOAD3:
+            if q % 4 == 0:
+                e.op(Emitter3.m0_line(op, q, stage))
+                e.op("s_nop 0")  # M0 write -> LDS-DMA read of M0
+            e.load_imm(op, q, stage)
+    e.op("s_add_u32 %[kh], %[ko], 128")
+    e.op(f"s_waitcnt vmcnt({NLOAD})")
+    e.op("s_barrier")
+    for (op, idx) in read_order(order):
+        e.read(0, op, idx, 0, 0)
+    e.op("s_waitcnt lgkmcnt(0)")
+    e.lgkm.clear()
+
+    adv = ["s_add_u32 %[ko], %[ko], 128", "s_add_u32 %[kh], %[kh], 128"]
+    sub = "s_sub_u32 %[rem], %[rem], 1"
+    cmp2 = "s_cmp_eq_u32 %[rem], 2"
+
+    def step(stage, first, carried, ahead, has_next, last, tail):
+        e.lgkm = []
+        emit_step3(e, stage, first, carried, ahead, has_next, last, tail, p)
+
+    e.op(cmp2)
+    e.op("s_cbranch_scc1 5f")
+    step(0, True, False, True, True, False, adv + [sub, cmp2, "s_cbranch_scc1 6f"])
+    e.label("1")
+    step(1, False, True, True, True, False, adv + [sub, cmp2, "s_cbranch_scc1 8f"])
+    step(0, False, True, True, True, False, adv + [sub, cmp2, "s_cbranch_scc1 6f", "s_branch 1b"])
+    e.label("5")
+    step(0, True, False, False, True, False, [sub, "s_branch 2f"])               # KT == 2
+    e.label("6")
+    step(1, False, True, False, True, False, [sub, "s_branch 3f"])                # step KT-2 in stage 1
+    e.label("8")
+    step(0, False, True, False, True, False, [sub])                               # step KT-2 in stage 0
+    e.label("2")
+    step(1, False, False, False, False, True, ["s_branch 4f"])                   # last step in stage 1
+    e.label("3")
+    step(0, False, False, False, False, True, [])                                 # last step in stage 0
+    e.label("4")
+    return "\n".join(e.lines)
+
+
+DEFAULT3 = {
+    "order": "snake",
+    "f1_start": 0, "f1_every": 1,
+    "rel": 24,                      # release barrier (its wait one gap earlier)
+    "load_every": 8,                # step j+2's loads from gap rel + 1
+    "pub": 88,                      # publish barrier (its wait one gap earlier)
+    "f0_start": 64,
+    "f0_lat": 12,
+    "epi_slot": 8, "epi_delay": 2,
+}
+
+
 DEFAULT = {
     "order": "snake",     # MFMA order inside a sub-step (see mfma_block)
     "pre": 32,            # MFMAs of sub-step 1 before the barrier
@@ -563,13 +793,16 @@ def main(argv: list[str]) -> int:
     out = os.path.join(here, "ring4_sched.inc")
     text1 = generate(DEFAULT)
     text2 = generate2(DEFAULT2)
+    text3 = generate3(DEFAULT3)
     with open(out, "w") as f:
         f.write("// Generated by gen_ring4_sched.py.  Do not edit.\n")
         f.write("// G16_RING4_KLOOP: one barrier per k step; " + params_line(DEFAULT) + ".\n")
         f.write(as_macro("G16_RING4_KLOOP", text1))
         f.write("// G16_RING4_KLOOP2: release and publish barriers per k step; " + params_line(DEFAULT2) + ".\n")
         f.write(as_macro("G16_RING4_KLOOP2", text2))
-    print(out, len(text1.split("\n")) + len(text2.split("\n")), "lines")
+        f.write("// G16_RING4_KLOOP3: release and publish barriers per k step, one instruction per MFMA gap; " + params_line(DEFAULT3) + ".\n")
+        f.write(as_macro("G16_RING4_KLOOP3", text3))
+    print(out, sum(len(t.split("\n")) for t in (text1, text2, text3)), "lines")
     return 0
 
 

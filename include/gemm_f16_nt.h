@@ -62,6 +62,9 @@ extern "C" {
                                   schedule: M, N multiples of 256, K a multiple of 64, K >= 128 */
 #define GEMM_F16_NT_R7_RING4_2B 7 /* rung 6 with a release and a publish barrier per k step (loads start
                                      earlier and spread evenly); same shapes as rung 6 */
+#define GEMM_F16_NT_R8_RING4_GAP 8 /* rung 7's barriers with at most one instruction between two MFMAs
+                                      (offset loads, 4 M0 writes per step); same shapes as rung 6; the
+                                      library's choice for whole tiles */
 
 /* D = A * B^T with the library's choice of kernel for the shape. */
 int gemm_f16_nt(int64_t M, int64_t N, int64_t K, const void* A, const void* B, void* D, void* stream);

@@ -19,7 +19,8 @@ pytestmark = pytest.mark.gpu
 
 torch = pytest.importorskip("torch")
 DEV = "cuda:0"
-ALL_RUNGS = [1, 2, 3, 4, 5, 6, 7]
+ALL_RUNGS = [1, 2, 3, 4, 5, 6, 7, 8]
+RING4_RUNGS = (6, 7, 8)   # whole 256 x 256 tiles, K a multiple of 64, >= 2 k steps
 
 
 def say(*a):
@@ -49,7 +50,7 @@ def supported(rung, M, N, K):
         return (M, N, K) == (128, 128, 64)
     if rung == 2:
         return (M, N) == (128, 128)
-    if rung in (6, 7):
+    if rung in RING4_RUNGS:
         return M % 256 == 0 and N % 256 == 0 and K % 64 == 0 and K >= 128
     return True
 
@@ -100,7 +101,7 @@ def test_ragged_shapes(rung, shape):
 
 @pytest.mark.parametrize("rung", [0] + ALL_RUNGS)
 def test_selection_matrix_bitwise(rung):
-    M, N, K = {1: (128, 128, 64), 2: (128, 128, 512), 6: (512, 256, 192), 7: (512, 256, 192)}.get(rung, (384, 320, 192))
+    M, N, K = {1: (128, 128, 64), 2: (128, 128, 512), 6: (512, 256, 192), 7: (512, 256, 192), 8: (512, 256, 192)}.get(rung, (384, 320, 192))
     rng = np.random.default_rng(5)
     pick = rng.integers(0, K, M)
     A = np.zeros((M, K), np.float16)
@@ -111,7 +112,7 @@ def test_selection_matrix_bitwise(rung):
     assert np.array_equal(host_bits(D), B[:, pick].T.view(np.uint16))
 
 
-@pytest.mark.parametrize("rung", [0, 3, 4, 5, 6, 7])
+@pytest.mark.parametrize("rung", [0, 3, 4, 5, 6, 7, 8])
 @pytest.mark.parametrize("K", [64, 512, 4096, 8192])
 def test_all_ones_equals_k(rung, K):
     if not supported(rung, 256, 256, K):
@@ -123,11 +124,11 @@ def test_all_ones_equals_k(rung, K):
     assert np.all(as_f64(host_bits(D)) == K)
 
 
-@pytest.mark.parametrize("rung", [0, 3, 4, 5, 6, 7])
+@pytest.mark.parametrize("rung", [0, 3, 4, 5, 6, 7, 8])
 def test_small_integers_bitwise(rung):
     rng = np.random.default_rng(14)
     shapes = [(256, 192, 8192, -4, 5), (264, 256, 768, 0, 5)]
-    if rung in (6, 7):
+    if rung in RING4_RUNGS:
         shapes = [(256, 256, 8192, -4, 5), (512, 256, 768, 0, 5)]
     for (M, N, K, lo, hi) in shapes:
         A = rng.integers(lo, hi, (M, K)).astype(np.float16)
@@ -139,11 +140,11 @@ def test_small_integers_bitwise(rung):
         assert np.array_equal(got, ref), f"{np.sum(got != ref)} mismatches"
 
 
-@pytest.mark.parametrize("rung", [0, 3, 4, 5, 6, 7])
+@pytest.mark.parametrize("rung", [0, 3, 4, 5, 6, 7, 8])
 def test_designed_rows(rung):
     """Exact sums on a tie, on the overflow threshold and on the subnormal
     grid: round-half-even, +inf at 65520, gradual underflow."""
-    K, R = (128, 256) if rung in (6, 7) else (64, 128)
+    K, R = (128, 256) if rung in RING4_RUNGS else (64, 128)
     A = np.zeros((R, K), np.float16)
     B = np.zeros((R, K), np.float16)
     A[0, :2] = [1, 1]
@@ -209,7 +210,7 @@ def test_poisoned_output_is_fully_overwritten(shape):
     M, N, K = shape
     A, B = rand_case(M, N, K, 77)
     ref, _ = oracle.gemm_nt(A, B)
-    for rung in (0, 3, 4, 5, 6, 7):
+    for rung in (0, 3, 4, 5, 6, 7, 8):
         if not supported(rung, M, N, K):
             continue
         D = torch.full((M, N), float("nan"), dtype=torch.float16, device=DEV)
@@ -226,7 +227,7 @@ def test_repeatable_and_grid_size_invariant():
     first = host_bits(run(4, dA, dB))
     for _ in range(2):
         assert np.array_equal(host_bits(run(4, dA, dB)), first)
-    for r in (6, 7):
+    for r in RING4_RUNGS:
         first6 = host_bits(run(r, dA, dB))
         for _ in range(2):
             assert np.array_equal(host_bits(run(r, dA, dB)), first6)
@@ -243,7 +244,7 @@ def test_repeatable_and_grid_size_invariant():
         assert np.array_equal(bits, base), f"grid {grid} differs"
 
 
-@pytest.mark.parametrize("rung", [6, 7])
+@pytest.mark.parametrize("rung", RING4_RUNGS)
 @pytest.mark.parametrize("shape", [(4608, 4608, 256), (8192, 2304, 128), (256, 256, 128), (512, 768, 192)],
                          ids=lambda s: "x".join(map(str, s)))
 def test_ring4_persistent_rounds(rung, shape):
@@ -267,7 +268,7 @@ def test_non_default_stream_and_interleaving():
         dA, dB = dev(A), dev(B)
         say("[gpu] side stream")
         X = torch.randn(2048, 2048, device=DEV)
-        for rung in (0, 4, 5, 6, 7):
+        for rung in (0, 4, 5, 6, 7, 8):
             D = g.gemm_f16_nt(dA, dB) if rung == 0 else g.gemm_f16_nt_rung(rung, dA, dB)
             X = X * 1.0001          # unrelated work queued on the same stream
             s.synchronize()
@@ -298,7 +299,7 @@ def test_full_size_workloads_sampled(name):
     # whole output: finite everywhere (the workloads cannot overflow)
     assert torch.isfinite(D).all().item()
     if name == "square_4096":
-        for rung in (4, 5, 6, 7):
+        for rung in (4, 5, 6, 7, 8):
             say(f"[gpu] full size square_4096 on rung {rung}")
             Dr = run(rung, dA, dB)
             gotr = host_bits(Dr[torch.from_numpy(rows).to(DEV), torch.from_numpy(cols).to(DEV)])

@@ -125,19 +125,25 @@ class Sim:
             elif ln.startswith("s_add_u32 m0, %[lb], "):
                 m0 = int(ln.split(",")[2])
             elif ln.startswith("buffer_load_dwordx4"):
-                m = re.match(r"buffer_load_dwordx4 %\[[ab]o\d\], %\[rs[ab]\], %\[(k[oh])\] offen( offset:(\d+))? lds$", ln)
+                m = re.match(r"buffer_load_dwordx4 %\[([ab])([ox])(\d)\], %\[rs([ab])\], %\[(k[oh])\] offen( offset:(\d+))? lds$", ln)
                 assert m, ln
-                imm = int(m.group(3) or 0)
+                op, kind, q, rop = m.group(1), m.group(2), int(m.group(3)), m.group(4)
+                assert op == rop, "lane offsets of one operand with the other's buffer"
+                imm = int(m.group(7) or 0)
                 # the immediate offset moves the global address and the LDS
-                # destination alike
-                step = ((ko if m.group(1) == "ko" else kh) + imm) // 128
+                # destination alike; the 'x' lane offsets of row group q are
+                # 1024 * (q mod 4) bytes short of the row group's
+                goff = (ko if m.group(5) == "ko" else kh) + imm - (1024 * (q % 4) if kind == "x" else 0)
+                assert goff % 128 == 0, f"global offset {goff} is not a k step"
+                step = goff // 128
                 assert 0 <= step < kt, f"load of step {step} beyond K (KT={kt})"
                 dst = m0 + imm
                 assert dst % 1024 == 0 and 0 <= dst < 2 * 65536, f"LDS destination {dst}"
                 st = dst // 65536
                 off = dst % 65536
                 n = 2 * ((off % 32768) // 1024) + (1 if off >= 32768 else 0)
-                assert ("%[ao" in ln) == (n % 2 == 0), "A/B operand does not match the LDS region"
+                assert (op == "a") == (n % 2 == 0), "A/B operand does not match the LDS region"
+                assert (off % 32768) // 1024 == q, f"row group {q} lands at row group {(off % 32768) // 1024}"
                 assert st == step % 2, f"step {step} loaded into stage {st}"
                 assert reads_since_barrier[st] == 0, "load into a stage read since the last barrier"
                 vm.append((step, st, n))
@@ -295,6 +301,53 @@ def test_two_barrier_variants_keep_protocol(params):
         Sim(GEN.generate2(p), kt).run()
 
 
+@pytest.mark.parametrize("kt", [2, 3, 4, 5, 6, 7, 8, 9, 16, 33, 64])
+def test_third_form_ring_protocol(kt):
+    res = Sim(GEN.generate3(GEN.DEFAULT3), kt).run()
+    assert res["mfma"] == 2 * NB * NB * kt
+    assert res["epoch"] == 2 * (kt - 1)              # prologue, release and publish per step, none in the last
+    assert len(res["acc"]) == NB * NB
+    assert sorted(res["loaded"]) == list(range(kt))
+    assert all(v == set(range(16)) for v in res["loaded"].values())
+
+
+@pytest.mark.parametrize("params", [
+    {"rel": 20, "load_every": 6, "pub": 80}, {"rel": 30, "load_every": 8, "pub": 84},
+    {"rel": 24, "load_every": 4, "pub": 96, "f0_lat": 8}, {"f1_every": 2, "rel": 34, "load_every": 7},
+    {"rel": 24, "load_every": 9, "pub": 92, "f0_lat": 6},    # late loads run past the next release
+])
+def test_third_form_variants_keep_protocol(params):
+    p = dict(GEN.DEFAULT3)
+    p.update(params)
+    for kt in (2, 3, 4, 7):
+        Sim(GEN.generate3(p), kt).run()
+
+
+def test_third_form_one_instruction_per_gap():
+    """In the steady-state steps at most one instruction sits between two
+    MFMAs, except after the last MFMA of a step (the branches)."""
+    lines = GEN.generate3(GEN.DEFAULT3).split("\n")
+    body = lines[lines.index("1:") + 1: lines.index("5:")]
+    runs, n = [], 0
+    for ln in body:
+        if ln.startswith("v_mfma"):
+            runs.append(n)
+            n = 0
+        elif not ln.endswith(":"):
+            n += 1
+    assert runs[0] == 0 and len(runs) == 2 * 2 * NB * NB
+    inner = [r for k, r in enumerate(runs) if k % (2 * NB * NB) != 0]   # gap 127 of a step precedes MFMA 0
+    assert max(inner) <= 1
+
+
+def test_simulator_catches_an_uncompensated_offset():
+    """An instruction offset on lane offsets that were not reduced by it
+    reads the wrong k step."""
+    text = GEN.generate3(GEN.DEFAULT3).replace("%[ax1]", "%[ao1]", 1)
+    with pytest.raises(AssertionError):
+        Sim(text, 4).run()
+
+
 def test_simulator_catches_a_planted_race():
     """Moving one handoff load ahead of its barrier must be caught."""
     text = GEN.generate(GEN.DEFAULT).split("\n")
@@ -338,3 +391,4 @@ def test_committed_include_matches_generator():
         inc = f.read()
     assert GEN.as_macro("G16_RING4_KLOOP", GEN.generate(GEN.DEFAULT)) in inc
     assert GEN.as_macro("G16_RING4_KLOOP2", GEN.generate2(GEN.DEFAULT2)) in inc
+    assert GEN.as_macro("G16_RING4_KLOOP3", GEN.generate3(GEN.DEFAULT3)) in inc
