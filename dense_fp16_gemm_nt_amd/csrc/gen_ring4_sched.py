@@ -669,7 +669,7 @@ def emit_step3(e: Emitter3, stage: int, first: bool, carried: bool, ahead: bool,
             g = first_free(g)
             gaps[g].append(("read", (0, op, idx, stage ^ 1, 0)))
             lastr = g
-            g += 1
+            g += p.get("f0_every", 1)
         gaps[first_free(lastr + p["f0_lat"])].append(("text", "s_waitcnt lgkmcnt(0)", "clear"))
     scc_writers = [g for g in range(ng) for it in gaps[g]
                    if it[0] == "text" and it[1].startswith(("s_add_u32", "s_sub_u32"))]
