@@ -16,10 +16,10 @@ Pipeline (the pages' software pipeline with a double-buffered operand ring,
     (A rows at +0, B rows at +32 KiB; 128-byte rows, 16-byte chunk c of
     row r at chunk c ^ ((r / 2) mod 8)), 4 waves in a 2 x 2 grid, each wave
     owning 128 x 128 outputs = 8 x 8 blocks of v_mfma_f32_16x16x32_f16.
-    Block (i, j) (A rows 16i.., B rows 16j..) accumulates in operand
-    %[cB], B = 8i + j (64 AGPR quadruples: all 256 accumulation registers).  The 16x16x32 form is used
-    because it holds a higher clock than 32x32x16 at the same work per cycle
-    (it reads and writes half the accumulator bytes per FLOP);
+    Block (i, j) (A rows 16i.., B rows 16j..) accumulates in a[4B:4B+3],
+    B = 8i + j (all 256 accumulation registers).  The 16x16x32 form is
+    used because it holds a higher clock than 32x32x16 at the same work per
+    cycle (it reads and writes half the accumulator bytes per FLOP);
   * a k step is 2 sub-steps of 32 k; the 16 fragments (8 A blocks, 8 B
     blocks, one 16-byte LDS read each) of sub-step 1 are read while sub-step
     0 runs, into the second of two fragment buffers (F0 = v[128:191],
@@ -35,25 +35,31 @@ Pipeline (the pages' software pipeline with a double-buffered operand ring,
     issues no body loads; the last two steps issue no handoff loads and the
     last step has no barrier.
 
-A second form (generate2, macro G16_RING4_KLOOP2) splits the handoff in two
+That is the first form (generate, macro G16_RING4_KLOOP).  A second form
+(generate2, macro G16_RING4_KLOOP2) splits the handoff in two
 barriers per step: a release barrier right after sub-step 0's fragment reads
 (the stage is dead from there on) and a publish barrier in sub-step 1.  The
 loads of step j+2 then start a whole sub-step earlier and go out evenly, one
 every few MFMAs, instead of in a burst after one barrier: when the operands
 stream from HBM, bursts from all CUs of an XCD queue at its L2 and triple the
-load latency.  It costs one more barrier per step, which does not pay when the
-operands stay in the last-level cache.
+load latency.  The third form (generate3, macro G16_RING4_KLOOP3, the
+library's choice) keeps those two barriers and places at most one
+instruction between two MFMAs (see its section below).
 
 MFMA operand roles: the B block feeds srcA and the A block srcB, so lane l
 of block (i, j) holds output row 16i + l%16 and the four consecutive output
 columns 16j + 4*(l/16) + 0..3.
 
-Operands expected by the block (see ring4.hpp): accumulators %[c0] ..
-%[c63] (AGPR, written: the first k step starts from 0), load offsets
-%[aoQ], %[boQ] (VGPR), fragment-read addresses %[raSK], %[rbSK] for stage S
-and sub-step K (VGPR), buffer resources %[rsa], %[rsb], the wave's LDS load
-base %[lb], the byte offsets %[ko] and %[kh] of the next two steps to load
-and the count %[rem] of k steps (SGPR, all modified; %[kh] is scratch).
+Operands expected by the block (see ring4.hpp): load offsets %[aoQ],
+%[boQ] and, for the third form, %[axQ], %[bxQ] (the same less 1024*(Q mod
+4)) (VGPR); fragment-read addresses %[raSK], %[rbSK] for stage S and
+sub-step K (VGPR); buffer resources %[rsa], %[rsb]; the wave's LDS load base
+%[lb]; the byte offsets %[ko] and %[kh] of the next two steps to load and
+the count %[rem] of k steps (SGPR, all modified; %[kh] is scratch); and for
+the epilogue the staging and store addresses %[ewJ], %[erQ], %[soQ], the
+output resource %[rsd], the row-group stride %[gstr] and the scratch
+%[sdo].  The accumulators a0..a255 and fragment buffers v128..v255 are
+fixed registers of the block.
 """
 from __future__ import annotations
 
