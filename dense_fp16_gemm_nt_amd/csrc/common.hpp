@@ -60,6 +60,7 @@ __device__ __forceinline__ f16x4 cvt4(float a, float b, float c, float d)
 // FULL: the block lies inside D and every row start is 8-byte aligned.
 // Otherwise rows >= M and columns >= N are skipped, and 8-byte stores are
 // used only where `vec` says row starts are 8-byte aligned.
+// Vector stores are non-temporal: the kernels never read D back.
 template <bool FULL>
 __device__ __forceinline__ void store_block(f16* __restrict__ D, int64_t ldd, int64_t M, int64_t N,
                                             int64_t m0, int64_t n0, const f32x16& acc, int lane,
@@ -71,10 +72,10 @@ __device__ __forceinline__ void store_block(f16* __restrict__ D, int64_t ldd, in
         const int64_t n = n0 + acc_col(lane, g);
         f16x4 h = cvt4(acc[4 * g], acc[4 * g + 1], acc[4 * g + 2], acc[4 * g + 3]);
         if (FULL) {
-            *reinterpret_cast<f16x4*>(D + m * ldd + n) = h;
+            __builtin_nontemporal_store(h, reinterpret_cast<f16x4*>(D + m * ldd + n));
         } else if (m < M) {
             if (vec && n + 3 < N) {
-                *reinterpret_cast<f16x4*>(D + m * ldd + n) = h;
+                __builtin_nontemporal_store(h, reinterpret_cast<f16x4*>(D + m * ldd + n));
             } else {
 #pragma unroll
                 for (int r = 0; r < 4; ++r)

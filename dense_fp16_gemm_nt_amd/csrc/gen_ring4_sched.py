@@ -93,7 +93,9 @@ def areg(i: int, j: int) -> str:
 # nearest even), staged in this wave's 4 KiB LDS buffer i % 2 (rows of 256
 # bytes, 16-byte chunk c of row r at chunk c ^ (r mod 16)), read back as
 # whole rows and stored with 16-byte buffer stores, four rows per
-# instruction.  Temporaries live in the first fragment buffer (v128..v191),
+# instruction.  The stores are non-temporal: the output is not read again
+# by the kernel, and streaming it out as it is written leaves less to write
+# back when the kernel ends (1-2% faster at 4096^3 and 8192^3).  Temporaries live in the first fragment buffer (v128..v191),
 # free once sub-step 0 is done.
 EPI_T = 128   # v128..v159: converted blocks of a group
 EPI_R = 160   # v160..v191: read-back rows, two groups
@@ -117,7 +119,7 @@ def epilogue_group(i: int) -> list[tuple[str, bool]]:
         out.append((f"ds_read_b128 v[{rb + 4 * q}:{rb + 4 * q + 3}], %[er{q}] offset:{off}", True))
     out.append(("s_waitcnt lgkmcnt(0)", False))
     for q in range(4):
-        out.append((f"buffer_store_dwordx4 v[{rb + 4 * q}:{rb + 4 * q + 3}], %[so{q}], %[rsd], %[sdo] offen", False))
+        out.append((f"buffer_store_dwordx4 v[{rb + 4 * q}:{rb + 4 * q + 3}], %[so{q}], %[rsd], %[sdo] offen nt", False))
     out.append(("s_add_u32 %[sdo], %[sdo], %[gstr]", False))
     return out
 

@@ -181,7 +181,8 @@ __device__ __forceinline__ void epilogue_lds(char* lds, f16* __restrict__ D, int
         const int r = q * ROWS_PER_STORE + lane / CPR;
         const int c = lane % CPR;
         const u32x4 v = *reinterpret_cast<const u32x4*>(lds + r * ROWB + ((c ^ (r % CPR)) << 4));
-        *reinterpret_cast<u32x4*>(D + (row0 + r) * ldd + col0 + 8 * c) = v;
+        // non-temporal: D is not read again by the kernel
+        __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(D + (row0 + r) * ldd + col0 + 8 * c));
     }
 }
 

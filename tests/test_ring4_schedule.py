@@ -216,7 +216,7 @@ class Sim:
             elif ln == "s_add_u32 %[sdo], %[sdo], %[gstr]":
                 sdo += 1
             elif ln.startswith("buffer_store_dwordx4"):
-                m = re.match(r"buffer_store_dwordx4 (v\[\d+:\d+\]), %\[so(\d)\], %\[rsd\], %\[sdo\] offen$", ln)
+                m = re.match(r"buffer_store_dwordx4 (v\[\d+:\d+\]), %\[so(\d)\], %\[rsd\], %\[sdo\] offen( nt)?$", ln)
                 reg, q = _regs(m.group(1)), int(m.group(2))
                 assert vreg.get(reg) == (sdo, q), f"store of {vreg.get(reg)} at group {sdo}, rows {q}"
                 stores.append((sdo, q))
