@@ -87,11 +87,14 @@ bool overlaps(const void* a, int64_t abytes, const void* b, int64_t bbytes)
     return a0 < b0 + (uintptr_t)bbytes && b0 < a0 + (uintptr_t)abytes;
 }
 
-// Shapes the four-wave scheduled ring implements: whole 256 x 256 tiles and
-// at least two 64-wide k steps (M = 0 or N = 0 is a no-op everywhere).
+// Shapes the four-wave scheduled ring implements: M, N >= 256 (the last
+// tile row and column are moved back to end at M and N, so every tile is
+// whole), N a multiple of 8 (16-byte stores of the moved column), and at
+// least two whole 64-wide k steps (M = 0 or N = 0 is a no-op everywhere).
 bool ring4_shape(int64_t M, int64_t N, int64_t K)
 {
-    return M % ring4::C::BM == 0 && N % ring4::C::BN == 0 && K % ring4::C::BK == 0 && K >= 2 * ring4::C::BK;
+    return M >= ring4::C::BM && N >= ring4::C::BN && N % 8 == 0 && K % ring4::C::BK == 0 &&
+           K >= 2 * ring4::C::BK;
 }
 
 // Operands the 16-byte-load kernels take: every row of A and B starts on a
@@ -209,8 +212,8 @@ bool ring4_fits(const GemmArgs& g)
 int launch_ring4(const GemmArgs& g0, hipStream_t s, int form = 0)
 {
     GemmArgs g = g0;
-    g.tiles_m = g.M / ring4::C::BM;
-    g.tiles_n = g.N / ring4::C::BN;
+    g.tiles_m = (g.M + ring4::C::BM - 1) / ring4::C::BM;
+    g.tiles_n = (g.N + ring4::C::BN - 1) / ring4::C::BN;
     const int64_t tiles = g.tiles_m * g.tiles_n * g.batch;
     int cus = 0;
     const int st = device_info(&cus);

@@ -59,7 +59,9 @@ extern "C" {
 #define GEMM_F16_NT_R4_RING 4        /* any shape: 256 x 256 tiles, direct-to-LDS pipelined ring */
 #define GEMM_F16_NT_R5_PERSISTENT_WS 5 /* any shape: persistent, producer/consumer waves */
 #define GEMM_F16_NT_R6_RING4 6 /* rung 4's ring with 4 waves of 128 x 128 and a fixed instruction
-                                  schedule: M, N multiples of 256, K a multiple of 64, K >= 128 */
+                                  schedule: M, N >= 256, N a multiple of 8, K a multiple of 64,
+                                  K >= 128 (when M or N is not a multiple of 256 the last tile row
+                                  or column ends at M or N and overlaps its neighbour) */
 #define GEMM_F16_NT_R7_RING4_2B 7 /* rung 6 with a release and a publish barrier per k step (loads start
                                      earlier and spread evenly); same shapes as rung 6 */
 #define GEMM_F16_NT_R8_RING4_GAP 8 /* rung 7's barriers with at most one instruction between two MFMAs

@@ -71,7 +71,7 @@ A0, B0, D0 = 0x10000, 0x20000000, 0x40000000   # fake, 16-byte aligned, disjoint
     ((0, 64, 64, 64, A0, B0, A0 + 4096), g.INVALID_ARG),   # D overlaps A
     ((0, 64, 64, 64, A0, B0, B0), g.INVALID_ARG),          # D overlaps B
     ((9, 64, 64, 64, A0, B0, D0), g.INVALID_ARG),          # unknown rung
-    ((8, 64, 64, 64, A0, B0, D0), g.UNSUPPORTED),          # rung 8: whole 256 x 256 tiles only
+    ((8, 64, 64, 64, A0, B0, D0), g.UNSUPPORTED),          # rung 8: M, N >= 256
     ((-1, 64, 64, 64, A0, B0, D0), g.INVALID_ARG),
     ((1, 128, 128, 64, A0, B0, D0), g.OK),
     ((1, 128, 128, 128, A0, B0, D0), g.UNSUPPORTED),       # R1 is one 128x128x64 tile
@@ -81,10 +81,12 @@ A0, B0, D0 = 0x10000, 0x20000000, 0x40000000   # fake, 16-byte aligned, disjoint
     ((4, 1, 1, 8, A0, B0, D0), g.OK),
     ((5, 5000, 7, 8, A0, B0, D0), g.OK),
     ((6, 256, 512, 128, A0, B0, D0), g.OK),
-    ((6, 64, 64, 64, A0, B0, D0), g.UNSUPPORTED),          # R6 needs whole 256 x 256 tiles
+    ((6, 64, 64, 64, A0, B0, D0), g.UNSUPPORTED),          # R6 needs M, N >= 256
     ((6, 256, 256, 64, A0, B0, D0), g.UNSUPPORTED),        # ... and at least two k steps
     ((6, 256, 256, 136, A0, B0, D0), g.UNSUPPORTED),       # ... of 64
-    ((6, 256, 300, 128, A0, B0, D0), g.UNSUPPORTED),
+    ((6, 256, 300, 128, A0, B0, D0), g.UNSUPPORTED),       # ... N a multiple of 8
+    ((6, 300, 264, 128, A0, B0, D0), g.OK),                # ragged M, N: the last tiles move back
+    ((8, 255, 264, 128, A0, B0, D0), g.UNSUPPORTED),       # ... but not below one tile
     ((7, 512, 256, 192, A0, B0, D0), g.OK),
     ((7, 256, 256, 64, A0, B0, D0), g.UNSUPPORTED),
     ((0, 0, 64, 64, 0, 0, 0), g.OK),                       # empty output: nothing needed

@@ -20,7 +20,7 @@ pytestmark = pytest.mark.gpu
 torch = pytest.importorskip("torch")
 DEV = "cuda:0"
 ALL_RUNGS = [1, 2, 3, 4, 5, 6, 7, 8]
-RING4_RUNGS = (6, 7, 8)   # whole 256 x 256 tiles, K a multiple of 64, >= 2 k steps
+RING4_RUNGS = (6, 7, 8)   # M, N >= 256, N a multiple of 8, K a multiple of 64, >= 2 k steps
 
 
 def say(*a):
@@ -51,7 +51,7 @@ def supported(rung, M, N, K):
     if rung == 2:
         return (M, N) == (128, 128)
     if rung in RING4_RUNGS:
-        return M % 256 == 0 and N % 256 == 0 and K % 64 == 0 and K >= 128
+        return M >= 256 and N >= 256 and N % 8 == 0 and K % 64 == 0 and K >= 128
     return True
 
 
@@ -257,6 +257,35 @@ def test_ring4_persistent_rounds(rung, shape):
     say(f"[gpu] ring4 persistent rounds rung={rung} {M}x{N}x{K}")
     run(rung, dev(A), dev(B), D)
     assert_parity(host_bits(D), ref, K, f"rung {rung} {M}x{N}x{K}")
+
+
+@pytest.mark.parametrize("shape", [(300, 264, 128), (520, 776, 256), (1000, 1032, 192), (4000, 4000, 1024)],
+                         ids=lambda s: "x".join(map(str, s)))
+def test_ring4_ragged_tiles(shape):
+    """M, N not multiples of 256 on the four-wave ring: the last tile row and
+    column move back to end at M and N and overlap their neighbours.  Every
+    output is compared with the oracle, repeated runs are bitwise equal (the
+    shared rows are written twice with the same bits), and the padding
+    columns of a pitched D are never written."""
+    M, N, K = shape
+    A, B = rand_case(M, N, K, 90 + K)
+    ref, _ = oracle.gemm_nt(A, B)
+    dA, dB = dev(A), dev(B)
+    for rung in (0,) + RING4_RUNGS:
+        assert supported(rung, M, N, K)
+        D = torch.full((M, N), float("nan"), dtype=torch.float16, device=DEV)
+        say(f"[gpu] ring4 ragged rung={rung} {M}x{N}x{K}")
+        run(rung, dA, dB, D)
+        first = host_bits(D)
+        assert_parity(first, ref, K, f"rung {rung} {M}x{N}x{K}")
+        for _ in range(2):
+            assert np.array_equal(host_bits(run(rung, dA, dB, D)), first), f"rung {rung} not repeatable"
+    Dfull = torch.full((1, M, N + 8), float("nan"), dtype=torch.float16, device=DEV)
+    say(f"[gpu] ring4 ragged pitched D {M}x{N}x{K}")
+    g.gemm_f16_nt_strided_batched(dA[None], dB[None], Dfull[:, :, :N])
+    torch.cuda.synchronize()
+    assert_parity(host_bits(Dfull[0, :, :N].contiguous()), ref, K, "pitched D")
+    assert torch.isnan(Dfull[:, :, N:]).all().item()
 
 
 def test_non_default_stream_and_interleaving():
