@@ -30,7 +30,9 @@ R5_PERSISTENT_WS = 5
 R6_RING4 = 6
 R7_RING4_2B = 7
 R8_RING4_GAP = 8
-RUNGS = (R1_SINGLE_TILE, R2_KLOOP, R3_GRID, R4_RING, R5_PERSISTENT_WS, R6_RING4, R7_RING4_2B, R8_RING4_GAP)
+R9_RING_SMALL = 9
+RUNGS = (R1_SINGLE_TILE, R2_KLOOP, R3_GRID, R4_RING, R5_PERSISTENT_WS, R6_RING4, R7_RING4_2B, R8_RING4_GAP,
+         R9_RING_SMALL)
 
 _lock = threading.Lock()
 _lib = None
@@ -123,7 +125,7 @@ def gemm_f16_nt(A, B, D=None):
 
 
 def gemm_f16_nt_rung(rung: int, A, B, D=None):
-    """The same product on one rung of the kernel ladder (1..5)."""
+    """The same product on one rung of the kernel ladder (1..9)."""
     M, N, K, D = _operands(A, B, D)
     st = lib().gemm_f16_nt_rung(int(rung), M, N, K, A.data_ptr(), B.data_ptr(), D.data_ptr(), _stream(A))
     if st != OK:

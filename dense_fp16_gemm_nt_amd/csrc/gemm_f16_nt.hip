@@ -28,9 +28,17 @@ namespace {
 // generated instruction schedule, persistent (ring4.hpp), for whole tiles;
 // rung 7 = rung 6 with release and publish barriers per step; rung 8 =
 // rung 7's barriers with at most one instruction between two MFMAs (the
-// library's choice for whole tiles).
+// library's choice when M, N >= 256); rung 9 = rung 4's ring with 128 x 128
+// tiles, 8 waves of 64 x 32 and 4 stages (the library's choice when 256 x
+// 256 tiles would leave most compute units idle).
 using RingCfg = ring::Cfg<256, 256, 64, 2, 2, 2, 4>;
+using RingSmallCfg = ring::Cfg<128, 128, 64, 4, 2, 2, 4>;
 constexpr int kRingPre = 2, kRingLsplit = 1;
+// The library's choice takes 128 x 128 tiles when 256 x 256 tiles would
+// number at most this many per 10 compute units: measured on MI355X, the
+// two tie at ~100 tiles of 256 x 256 on 256 CUs (2560^3), 128 x 128 is
+// 1.6-2.2x faster at 16-64 tiles and 256 x 256 is 1.4x faster at 144.
+constexpr int64_t kSmallTilesPer10Cus = 4;
 using WsCfg = ws::Cfg<32, 4, 2>;
 constexpr int kFastTile = 256;
 // the library's choice takes the four-wave scheduled ring where it applies
@@ -111,7 +119,7 @@ bool fast_operands(int64_t K, int64_t lda, int64_t ldb, int64_t sa, int64_t sb, 
 
 int validate(int rung, int64_t M, int64_t N, int64_t K, const void* A, const void* B, const void* D)
 {
-    if (rung < 0 || rung > GEMM_F16_NT_R8_RING4_GAP) return GEMM_F16_NT_INVALID_ARG;
+    if (rung < 0 || rung > GEMM_F16_NT_R9_RING_SMALL) return GEMM_F16_NT_INVALID_ARG;
     if (M < 0 || N < 0 || K < 0) return GEMM_F16_NT_INVALID_ARG;
     const bool any_out = M > 0 && N > 0;
     if (any_out && K > 0 && (A == nullptr || B == nullptr)) return GEMM_F16_NT_INVALID_ARG;
@@ -229,8 +237,37 @@ int launch_ring4(const GemmArgs& g0, hipStream_t s, int form = 0)
     return launched();
 }
 
+// Rung 4's ring with 128 x 128 tiles (4 stages), one workgroup per tile.
+int launch_ring_small(const GemmArgs& g0, hipStream_t s)
+{
+    using C = RingSmallCfg;
+    GemmArgs g = g0;
+    g.tiles_m = (g.M + C::BM - 1) / C::BM;
+    g.tiles_n = (g.N + C::BN - 1) / C::BN;
+    const int64_t blocks = g.tiles_m * g.tiles_n * g.batch;
+    if (blocks > 0x7fffffff) return GEMM_F16_NT_UNSUPPORTED;
+    const bool edge = (g.M % C::BM) || (g.N % C::BN) || (g.K % C::BK) || (g.ldd % 8) || (g.sd % 8);
+    if (edge)
+        hipLaunchKernelGGL((ring::ring_kernel<C, true, kRingPre, kRingLsplit, true>), dim3((unsigned)blocks),
+                           dim3(C::THREADS), 0, s, g);
+    else
+        hipLaunchKernelGGL((ring::ring_kernel<C, false, kRingPre, kRingLsplit, true>), dim3((unsigned)blocks),
+                           dim3(C::THREADS), 0, s, g);
+    return launched();
+}
+
+// Whether 256 x 256 tiles would leave most compute units idle.
+bool tile_starved(const GemmArgs& g)
+{
+    int cus = 0;
+    if (device_info(&cus) != GEMM_F16_NT_OK) return false;
+    const int64_t tiles = ((g.M + kFastTile - 1) / kFastTile) * ((g.N + kFastTile - 1) / kFastTile) * g.batch;
+    return tiles * 10 <= (int64_t)cus * kSmallTilesPer10Cus;
+}
+
 int launch_ring(const GemmArgs& g0, hipStream_t s, bool allow_ring4 = false)
 {
+    if (allow_ring4 && tile_starved(g0)) return launch_ring_small(g0, s);
     if (allow_ring4 && ring4_fits(g0)) return launch_ring4(g0, s);
     GemmArgs g = g0;
     g.tiles_m = (g.M + kFastTile - 1) / kFastTile;
@@ -397,6 +434,8 @@ int run(int rung, int64_t M, int64_t N, int64_t K, const void* A, const void* B,
         return launch_ring4(contiguous_args(M, N, K, A, B, D), s, 2);
     case GEMM_F16_NT_R8_RING4_GAP:
         return launch_ring4(contiguous_args(M, N, K, A, B, D), s, 3);
+    case GEMM_F16_NT_R9_RING_SMALL:
+        return launch_ring_small(contiguous_args(M, N, K, A, B, D), s);
     default:  // 0: the library's choice
         if (!fast_operands(K, K, K, 0, 0, A, B, D)) return launch_any(contiguous_args(M, N, K, A, B, D), s);
         return launch_ring(contiguous_args(M, N, K, A, B, D), s, kDefaultRing4);
