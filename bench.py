@@ -37,7 +37,7 @@ HBM_PEAK_GBS = 8000.0
 METRIC = "fp16 GEMM TFLOP/s at M=N=K=4096 (+ % of MI355X dense-fp16 peak)"
 RUNG_NAMES = {0: "auto", 1: "r1_single_tile", 2: "r2_kloop", 3: "r3_grid", 4: "r4_ring",
               5: "r5_persistent_ws", 6: "r6_ring4", 7: "r7_ring4_2b", 8: "r8_ring4_gap",
-              9: "r9_ring_small"}
+              9: "r9_ring_small", 10: "r10_ring4_paired"}
 
 
 def kernel_source_hash() -> str:

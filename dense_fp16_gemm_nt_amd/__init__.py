@@ -31,8 +31,9 @@ R6_RING4 = 6
 R7_RING4_2B = 7
 R8_RING4_GAP = 8
 R9_RING_SMALL = 9
+R10_RING4_PAIRED = 10
 RUNGS = (R1_SINGLE_TILE, R2_KLOOP, R3_GRID, R4_RING, R5_PERSISTENT_WS, R6_RING4, R7_RING4_2B, R8_RING4_GAP,
-         R9_RING_SMALL)
+         R9_RING_SMALL, R10_RING4_PAIRED)
 
 _lock = threading.Lock()
 _lib = None
@@ -125,7 +126,7 @@ def gemm_f16_nt(A, B, D=None):
 
 
 def gemm_f16_nt_rung(rung: int, A, B, D=None):
-    """The same product on one rung of the kernel ladder (1..9)."""
+    """The same product on one rung of the kernel ladder (1..10)."""
     M, N, K, D = _operands(A, B, D)
     st = lib().gemm_f16_nt_rung(int(rung), M, N, K, A.data_ptr(), B.data_ptr(), D.data_ptr(), _stream(A))
     if st != OK:

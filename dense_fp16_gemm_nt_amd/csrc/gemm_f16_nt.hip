@@ -27,10 +27,11 @@ namespace {
 // rung 6 = rung 4's ring with 4 waves of 128 x 128 on 16x16x32 MFMAs and a
 // generated instruction schedule, persistent (ring4.hpp), for whole tiles;
 // rung 7 = rung 6 with release and publish barriers per step; rung 8 =
-// rung 7's barriers with at most one instruction between two MFMAs (the
-// library's choice when M, N >= 256); rung 9 = rung 4's ring with 128 x 128
-// tiles, 8 waves of 64 x 32 and 4 stages (the library's choice when 256 x
-// 256 tiles would leave most compute units idle).
+// rung 7's barriers with at most one instruction between two MFMAs; rung 9
+// = rung 4's ring with 128 x 128 tiles, 8 waves of 64 x 32 and 4 stages (the
+// library's choice when 256 x 256 tiles would leave most compute units
+// idle); rung 10 = rung 8 with each block's two sub-steps back to back (the
+// library's choice when M, N >= 256).
 using RingCfg = ring::Cfg<256, 256, 64, 2, 2, 2, 4>;
 using RingSmallCfg = ring::Cfg<128, 128, 64, 4, 2, 2, 4>;
 constexpr int kRingPre = 2, kRingLsplit = 1;
@@ -119,7 +120,7 @@ bool fast_operands(int64_t K, int64_t lda, int64_t ldb, int64_t sa, int64_t sb, 
 
 int validate(int rung, int64_t M, int64_t N, int64_t K, const void* A, const void* B, const void* D)
 {
-    if (rung < 0 || rung > GEMM_F16_NT_R9_RING_SMALL) return GEMM_F16_NT_INVALID_ARG;
+    if (rung < 0 || rung > GEMM_F16_NT_R10_RING4_PAIRED) return GEMM_F16_NT_INVALID_ARG;
     if (M < 0 || N < 0 || K < 0) return GEMM_F16_NT_INVALID_ARG;
     const bool any_out = M > 0 && N > 0;
     if (any_out && K > 0 && (A == nullptr || B == nullptr)) return GEMM_F16_NT_INVALID_ARG;
@@ -133,7 +134,8 @@ int validate(int rung, int64_t M, int64_t N, int64_t K, const void* A, const voi
     if (rung == GEMM_F16_NT_R1_SINGLE_TILE && !(M == 128 && N == 128 && K == 64)) return GEMM_F16_NT_UNSUPPORTED;
     if (rung == GEMM_F16_NT_R2_KLOOP && !(M == 128 && N == 128)) return GEMM_F16_NT_UNSUPPORTED;
     if (rung == GEMM_F16_NT_R3_GRID && (N + 127) / 128 > 65535) return GEMM_F16_NT_UNSUPPORTED;
-    if ((rung == GEMM_F16_NT_R6_RING4 || rung == GEMM_F16_NT_R7_RING4_2B || rung == GEMM_F16_NT_R8_RING4_GAP) &&
+    if ((rung == GEMM_F16_NT_R6_RING4 || rung == GEMM_F16_NT_R7_RING4_2B || rung == GEMM_F16_NT_R8_RING4_GAP ||
+         rung == GEMM_F16_NT_R10_RING4_PAIRED) &&
         !ring4_shape(M, N, K))
         return GEMM_F16_NT_UNSUPPORTED;
     if (!any_out) return GEMM_F16_NT_OK;
@@ -214,9 +216,10 @@ bool ring4_fits(const GemmArgs& g)
 // Persistent launch: one workgroup per compute unit (fewer when there are
 // fewer tiles); every workgroup walks its share of the tiles.  form: the
 // k loop (1 = one barrier per step, 2 = release and publish barriers, 3 =
-// the second form's barriers with one instruction per MFMA gap, 0 = the
-// library's choice, 3: it is the fastest at every size measured, whether
-// the operands stay in the last-level cache or stream from HBM).
+// the second form's barriers with one instruction per MFMA gap, 4 = each
+// block's two sub-steps back to back, 0 = the library's choice, 4: the
+// fastest at every size measured, whether the operands stay in the
+// last-level cache or stream from HBM).
 int launch_ring4(const GemmArgs& g0, hipStream_t s, int form = 0)
 {
     GemmArgs g = g0;
@@ -227,8 +230,10 @@ int launch_ring4(const GemmArgs& g0, hipStream_t s, int form = 0)
     const int st = device_info(&cus);
     if (st != GEMM_F16_NT_OK) return st;
     const int64_t grid = tiles < cus ? tiles : cus;
-    if (form == 0) form = 3;
-    if (form == 3)
+    if (form == 0) form = 4;
+    if (form == 4)
+        hipLaunchKernelGGL(ring4::ring4_kernel<4>, dim3((unsigned)grid), dim3(ring4::C::THREADS), 0, s, g);
+    else if (form == 3)
         hipLaunchKernelGGL(ring4::ring4_kernel<3>, dim3((unsigned)grid), dim3(ring4::C::THREADS), 0, s, g);
     else if (form == 2)
         hipLaunchKernelGGL(ring4::ring4_kernel<2>, dim3((unsigned)grid), dim3(ring4::C::THREADS), 0, s, g);
@@ -436,6 +441,8 @@ int run(int rung, int64_t M, int64_t N, int64_t K, const void* A, const void* B,
         return launch_ring4(contiguous_args(M, N, K, A, B, D), s, 3);
     case GEMM_F16_NT_R9_RING_SMALL:
         return launch_ring_small(contiguous_args(M, N, K, A, B, D), s);
+    case GEMM_F16_NT_R10_RING4_PAIRED:
+        return launch_ring4(contiguous_args(M, N, K, A, B, D), s, 4);
     default:  // 0: the library's choice
         if (!fast_operands(K, K, K, 0, 0, A, B, D)) return launch_any(contiguous_args(M, N, K, A, B, D), s);
         return launch_ring(contiguous_args(M, N, K, A, B, D), s, kDefaultRing4);

@@ -101,20 +101,22 @@ EPI_T = 128   # v128..v159: converted blocks of a group
 EPI_R = 160   # v160..v191: read-back rows, two groups
 
 
-def epilogue_group(i: int) -> list[tuple[str, bool]]:
-    """Instructions of row group i as (text, is_lds_op)."""
+def epilogue_group(i: int, t_base: int = EPI_T, r_base: int = EPI_R) -> list[tuple[str, bool]]:
+    """Instructions of row group i as (text, is_lds_op); t_base and r_base
+    are the first of the 32 VGPRs for converted blocks and for read-back
+    rows."""
     out: list[tuple[str, bool]] = []
     off = (i % 2) * 4096
     for j in range(NB):
         b = NB * i + j
-        t = EPI_T + 4 * j
+        t = t_base + 4 * j
         for r in range(4):
             out.append((f"v_accvgpr_read_b32 v{t + r}, a{4 * b + r}", False))
         out.append((f"v_cvt_pk_f16_f32 v{t}, v{t}, v{t + 1}", False))
         out.append((f"v_cvt_pk_f16_f32 v{t + 1}, v{t + 2}, v{t + 3}", False))
         out.append((f"ds_write_b64 %[ew{j}], v[{t}:{t + 1}] offset:{off}", True))
     out.append(("s_waitcnt lgkmcnt(0)", False))
-    rb = EPI_R + 16 * (i % 2)
+    rb = r_base + 16 * (i % 2)
     for q in range(4):
         out.append((f"ds_read_b128 v[{rb + 4 * q}:{rb + 4 * q + 3}], %[er{q}] offset:{off}", True))
     out.append(("s_waitcnt lgkmcnt(0)", False))
@@ -768,6 +770,271 @@ DEFAULT3 = {
 }
 
 
+# ----------------------------------------------------------- fourth form
+# The two sub-steps of a block back to back: for each block (i, j) of a
+# row, the MFMA of sub-step 0 and then that of sub-step 1 into the same
+# accumulator.  The second reads its accumulator straight from the first
+# (a dependent 16x16x32 MFMA issues back to back without a stall), and the
+# matrix core then spends less energy on accumulator traffic: a
+# measurement of MFMA-only loops under the board's power limit ran 5%
+# faster in this order.
+#
+# Both halves of a step's fragments are then live together, so the
+# registers are laid out by what a row needs:
+#   A(h, i) = v[64 + 32h + 4i]            A block i, sub-step h (one set);
+#   B(p, h, j) = v[128 + 64p + 32h + 4j]  B block j, sub-step h, for the
+#                                         steps of parity p (two sets).
+# During step j the fragments of step j+1 are read from the other stage:
+# its B blocks into the other set, its A blocks of row i once row i of step
+# j is done (rows 6 and 7 at the start of step j+1).  Barriers: a release
+# barrier at gap rel (this stage's last reads, the late A rows, are done;
+# step j+2 may refill it) and a publish barrier at gap pub (step j+1's
+# loads have landed; its fragment reads follow).  Loads and offsets are
+# those of the third form.
+
+def a4(h: int, i: int) -> str:
+    return f"v[{64 + 32 * h + 4 * i}:{64 + 32 * h + 4 * i + 3}]"
+
+
+def b4(p: int, h: int, j: int) -> str:
+    base = 128 + 64 * p + 32 * h + 4 * j
+    return f"v[{base}:{base + 3}]"
+
+
+class Emitter4(Emitter3):
+    def read4(self, op: str, h: int, idx: int, stage: int, p: int) -> None:
+        reg = a4(h, idx) if op == "a" else b4(p, h, idx)
+        self.op(f"ds_read_b128 {reg}, %[r{op}{stage}{h}] offset:{2048 * idx}")
+        self.lgkm.append((op, h, idx, p if op == "b" else None))
+
+    def mfma4(self, p: int, h: int, i: int, j: int, first: bool) -> None:
+        self.wait_frag(("a", h, i, None), ("b", h, j, p))
+        c = areg(i, j)
+        self.op(f"v_mfma_f32_16x16x32_f16 {c}, {b4(p, h, j)}, {a4(h, i)}, {'0' if first else c}")
+
+    def epi_after4(self, g: int, per_slot: int, delay: int, t_base: int, r_base: int) -> None:
+        """After MFMA g of the last step: queue the rows whose MFMAs were all
+        issued at least `delay` MFMAs ago, emit up to per_slot queued
+        instructions."""
+        while self.epi_next < NB and g >= 2 * NB * self.epi_next + 2 * NB - 1 + delay:
+            self.epi_q += epilogue_group(self.epi_next, t_base, r_base)
+            self.epi_next += 1
+        for _ in range(min(per_slot, len(self.epi_q))):
+            self.epi_emit(*self.epi_q.pop(0))
+
+    def epi_finish4(self, t_base: int, r_base: int) -> None:
+        self.op("s_nop 7")
+        self.op("s_nop 7")
+        self.op("s_nop 7")
+        while self.epi_next < NB:
+            self.epi_q += epilogue_group(self.epi_next, t_base, r_base)
+            self.epi_next += 1
+        while self.epi_q:
+            self.epi_emit(*self.epi_q.pop(0))
+
+
+def late_rows4(p: dict) -> list[int]:
+    """Rows whose A fragments of step j+1 are read at the start of step j+1
+    (their row of step j ends too late in the step)."""
+    return [i for i in range(NB) if 2 * NB * i + 2 * NB + p["a_delay"] >= p["read_limit"]]
+
+
+def emit_step4(e: Emitter4, stage: int, first: bool, carried: bool, ahead: bool, has_next: bool, last: bool,
+               tail: list[str], p: dict) -> None:
+    """One 64-wide k step j reading `stage` (B fragments in set stage) in
+    the fourth form; flags as in emit_step3.  The late A rows of this step
+    are read at its start unless `first` (the prologue read them)."""
+    order = p.get("order", "snake")
+    ng = KSUB * NQ
+    par = stage                                  # B fragment set of this step
+    gaps: list[list[tuple]] = [[] for _ in range(ng)]
+    late = late_rows4(p)
+
+    def free(g: int) -> bool:
+        return 0 <= g < ng and not gaps[g]
+
+    def first_free(g: int) -> int:
+        while not free(g):
+            g += 1
+            assert g < ng, "step too full"
+        return g
+
+    rel, pub, every = p["rel"], p["pub"], p["load_every"]
+    if not last:
+        br = [t for t in tail if t.startswith(("s_cbranch", "s_branch"))]
+        rest = [t for t in tail if t not in br]
+        assert tail == rest + br, "branches close the tail"
+        for k, t in enumerate(rest):
+            gaps[ng - 1 - len(rest) + k].append(("text", t))
+        for t in br:
+            gaps[ng - 1].append(("text", t))
+    # this step's late A rows (from this stage)
+    g = 0
+    if not first:
+        for i in late:
+            for h in range(KSUB):
+                g = first_free(g)
+                gaps[g].append(("read", ("a", h, i, stage, par)))
+                g += 1
+    if ahead:
+        assert g < rel - 1, "late reads after the release"
+        gaps[rel - 1].append(("text", "s_waitcnt lgkmcnt(0)", "clear"))
+        gaps[rel].append(("text", "s_barrier"))
+    if has_next:
+        gaps[pub - 1].append(("publish_wait",))
+        gaps[pub].append(("text", "s_barrier"))
+    # loads: as in the third form
+    slots = [rel + 1 + every * k for k in range(NLOAD)]
+    limit = ng - 8
+    own = [(k, s_) for k, s_ in enumerate(slots) if s_ < limit] if ahead else []
+    carry = [(k, max(0, s_ - ng)) for k, s_ in enumerate(slots) if s_ >= limit] if carried else []
+    seq = [(k, s_, stage ^ 1, "ko") for (k, s_) in carry] + [(k, s_, stage, "kh") for (k, s_) in own]
+    prev, cur_m0 = -1, None
+    placed = []
+    for (k, s_, st, koff) in seq:
+        op, q = LOAD3[k]
+        gg = first_free(max(s_, prev + 1))
+        grp = (st, op, q // 4)
+        if grp != cur_m0:
+            m = next((x for x in range(gg - 1, prev, -1) if free(x)), None)
+            if m is None:
+                m = first_free(prev + 1)
+                gg = first_free(m + 1)
+            gaps[m].append(("text", Emitter3.m0_line(op, q, st)))
+            cur_m0 = grp
+        gaps[gg].append(("load", op, q, st, koff))
+        placed.append((gg, koff))
+        prev = gg
+    assert all(gg < ng - 1 - 4 for gg, _ in placed), "loads run into the tail"
+    if has_next:
+        n_young = sum(1 for gg, koff in placed if koff == "kh" and gg < pub - 1)
+        assert not any(koff == "ko" and gg >= pub - 1 for gg, koff in placed), "carried load after the publish wait"
+        # (the late A reads of this step, long done, are waited for too: no
+        # barrier is crossed with LDS reads in flight)
+        gaps[pub - 1] = [("text", f"s_waitcnt vmcnt({n_young}) lgkmcnt(0)", "clear")]
+        # step j+1's fragments (other stage): A row 0, all B blocks, then
+        # the other A rows as their rows of this step finish
+        reads = [("a", h, 0, pub + 1) for h in range(KSUB) if 0 not in late]
+        reads += [("b", h, j, pub + 1) for j in range(NB) for h in range(KSUB)]
+        reads += [("a", h, i, max(pub + 1, 2 * NB * i + 2 * NB + p["a_delay"])) for i in range(1, NB)
+                  if i not in late for h in range(KSUB)]
+        reads.sort(key=lambda r: r[3])
+        gg, lastr = pub + 1, pub + 1
+        for (op, h, idx, earliest) in reads:
+            gg = first_free(max(gg, earliest))
+            assert gg < p["read_limit"], "next-step reads beyond the read limit"
+            gaps[gg].append(("read", (op, h, idx, stage ^ 1, par ^ 1)))
+            lastr = gg
+            gg += p["read_every"]
+        gaps[first_free(lastr + p["f0_lat"])].append(("text", "s_waitcnt lgkmcnt(0)", "clear"))
+    scc_writers = [gg for gg in range(ng) for it in gaps[gg]
+                   if it[0] == "text" and it[1].startswith(("s_add_u32", "s_sub_u32"))]
+    cmp_at = [gg for gg in range(ng) for it in gaps[gg] if it[0] == "text" and it[1].startswith("s_cmp")]
+    assert not cmp_at or max(scc_writers, default=-1) < min(cmp_at), "SCC clobbered before the branch"
+
+    t_base = epi_set4(par)
+    for gg in range(ng):
+        pq, h = divmod(gg, 2)
+        i, j = mfma_block(pq, order)
+        if last and gg == 0:
+            e.epi_start(order)
+        e.mfma4(par, h, i, j, first and gg < 2 * NQ and per_block_first(gg))
+        if last:
+            e.epi_after4(gg, p["epi_slot"], p["epi_delay"], t_base, t_base + 32)
+        for it in gaps[gg]:
+            if it[0] == "read":
+                e.read4(*it[1])
+            elif it[0] == "load":
+                e.load_imm(it[1], it[2], it[3], it[4])
+            else:
+                e.op(it[1])
+                if len(it) > 2:
+                    e.lgkm.clear()
+    if last:
+        e.epi_finish4(t_base, t_base + 32)
+        for t in tail:
+            e.op(t)
+
+
+def epi_set4(par: int) -> int:
+    """First VGPR of the last step's epilogue temporaries: the B set of the
+    other parity, idle in the last step."""
+    return 128 + 64 * (par ^ 1)
+
+
+def per_block_first(gg: int) -> bool:
+    """In the first step, the sub-step-0 MFMA of each block starts it from 0."""
+    return gg % 2 == 0
+
+
+def generate4(p: dict) -> str:
+    """The k loop in the fourth form (same branch structure and offsets as
+    the third)."""
+    order = p.get("order", "snake")
+    e = Emitter4()
+    for stage in (0, 1):
+        if stage:
+            e.op("s_add_u32 %[ko], %[ko], 128")
+        for (op, q) in LOAD3:
+            if q % 4 == 0:
+                e.op(Emitter3.m0_line(op, q, stage))
+                e.op("s_nop 0")  # M0 write -> LDS-DMA read of M0
+            e.load_imm(op, q, stage)
+    e.op("s_add_u32 %[kh], %[ko], 128")
+    e.op(f"s_waitcnt vmcnt({NLOAD})")
+    e.op("s_barrier")
+    # all fragments of step 0, in the order the first MFMAs need them
+    e.read4("a", 0, 0, 0, 0)
+    e.read4("a", 1, 0, 0, 0)
+    for j in range(NB):
+        for h in range(KSUB):
+            e.read4("b", h, j, 0, 0)
+    for i in range(1, NB):
+        for h in range(KSUB):
+            e.read4("a", h, i, 0, 0)
+    pro = list(e.lgkm)
+
+    adv = ["s_add_u32 %[ko], %[ko], 128", "s_add_u32 %[kh], %[kh], 128"]
+    sub = "s_sub_u32 %[rem], %[rem], 1"
+    cmp2 = "s_cmp_eq_u32 %[rem], 2"
+
+    def step(stage, first, carried, ahead, has_next, last, tail):
+        e.lgkm = list(pro) if first else []
+        emit_step4(e, stage, first, carried, ahead, has_next, last, tail, p)
+
+    e.op(cmp2)
+    e.op("s_cbranch_scc1 5f")
+    step(0, True, False, True, True, False, adv + [sub, cmp2, "s_cbranch_scc1 6f"])
+    e.label("1")
+    step(1, False, True, True, True, False, adv + [sub, cmp2, "s_cbranch_scc1 8f"])
+    step(0, False, True, True, True, False, adv + [sub, cmp2, "s_cbranch_scc1 6f", "s_branch 1b"])
+    e.label("5")
+    step(0, True, False, False, True, False, [sub, "s_branch 2f"])               # KT == 2
+    e.label("6")
+    step(1, False, True, False, True, False, [sub, "s_branch 3f"])                # step KT-2 in stage 1
+    e.label("8")
+    step(0, False, True, False, True, False, [sub])                               # step KT-2 in stage 0
+    e.label("2")
+    step(1, False, False, False, False, True, ["s_branch 4f"])                   # last step in stage 1
+    e.label("3")
+    step(0, False, False, False, False, True, [])                                 # last step in stage 0
+    e.label("4")
+    return "\n".join(e.lines)
+
+
+DEFAULT4 = {
+    "order": "snake",
+    "rel": 12,                      # release barrier (its wait one gap earlier)
+    "load_every": 8,                # step j+2's loads from gap rel + 1
+    "pub": 64,                      # publish barrier (its wait one gap earlier)
+    "a_delay": 1,                   # gaps between a row's last MFMA and the next step's read of its A
+    "read_limit": 112,              # next-step reads end before this gap; later A rows move to the next step
+    "read_every": 1,
+    "f0_lat": 8,
+    "epi_slot": 8, "epi_delay": 2,
+}
+
+
 DEFAULT = {
     "order": "snake",     # MFMA order inside a sub-step (see mfma_block)
     "pre": 32,            # MFMAs of sub-step 1 before the barrier
@@ -802,6 +1069,7 @@ def main(argv: list[str]) -> int:
     text1 = generate(DEFAULT)
     text2 = generate2(DEFAULT2)
     text3 = generate3(DEFAULT3)
+    text4 = generate4(DEFAULT4)
     with open(out, "w") as f:
         f.write("// Generated by gen_ring4_sched.py.  Do not edit.\n")
         f.write("// G16_RING4_KLOOP: one barrier per k step; " + params_line(DEFAULT) + ".\n")
@@ -810,7 +1078,9 @@ def main(argv: list[str]) -> int:
         f.write(as_macro("G16_RING4_KLOOP2", text2))
         f.write("// G16_RING4_KLOOP3: release and publish barriers per k step, one instruction per MFMA gap; " + params_line(DEFAULT3) + ".\n")
         f.write(as_macro("G16_RING4_KLOOP3", text3))
-    print(out, sum(len(t.split("\n")) for t in (text1, text2, text3)), "lines")
+        f.write("// G16_RING4_KLOOP4: each block's two sub-steps back to back, release and publish barriers; " + params_line(DEFAULT4) + ".\n")
+        f.write(as_macro("G16_RING4_KLOOP4", text4))
+    print(out, sum(len(t.split("\n")) for t in (text1, text2, text3, text4)), "lines")
     return 0
 
 

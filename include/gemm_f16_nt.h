@@ -65,11 +65,13 @@ extern "C" {
 #define GEMM_F16_NT_R7_RING4_2B 7 /* rung 6 with a release and a publish barrier per k step (loads start
                                      earlier and spread evenly); same shapes as rung 6 */
 #define GEMM_F16_NT_R8_RING4_GAP 8 /* rung 7's barriers with at most one instruction between two MFMAs
-                                      (offset loads, 4 M0 writes per step); same shapes as rung 6; the
-                                      library's choice for those shapes */
+                                      (offset loads, 4 M0 writes per step); same shapes as rung 6 */
 #define GEMM_F16_NT_R9_RING_SMALL 9 /* any shape: rung 4's ring with 128 x 128 tiles, 8 waves of 64 x 32 and
                                        4 stages; the library's choice when 256 x 256 tiles would number
                                        at most 0.4 per compute unit */
+#define GEMM_F16_NT_R10_RING4_PAIRED 10 /* rung 8 with each 16 x 16 block's two 32-wide sub-steps issued
+                                           back to back into its accumulator; same shapes as rung 6;
+                                           the library's choice for those shapes */
 
 /* D = A * B^T with the library's choice of kernel for the shape. */
 int gemm_f16_nt(int64_t M, int64_t N, int64_t K, const void* A, const void* B, void* D, void* stream);

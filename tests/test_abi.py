@@ -70,7 +70,9 @@ A0, B0, D0 = 0x10000, 0x20000000, 0x40000000   # fake, 16-byte aligned, disjoint
     ((0, 64, 10_000_000, 12, A0, B0, D0), g.UNSUPPORTED),  # general kernel grid: N/128 > 65535
     ((0, 64, 64, 64, A0, B0, A0 + 4096), g.INVALID_ARG),   # D overlaps A
     ((0, 64, 64, 64, A0, B0, B0), g.INVALID_ARG),          # D overlaps B
-    ((10, 64, 64, 64, A0, B0, D0), g.INVALID_ARG),         # unknown rung
+    ((11, 64, 64, 64, A0, B0, D0), g.INVALID_ARG),         # unknown rung
+    ((10, 64, 64, 64, A0, B0, D0), g.UNSUPPORTED),         # rung 10: M, N >= 256
+    ((10, 512, 256, 192, A0, B0, D0), g.OK),
     ((9, 64, 64, 64, A0, B0, D0), g.OK),                   # rung 9: any shape
     ((8, 64, 64, 64, A0, B0, D0), g.UNSUPPORTED),          # rung 8: M, N >= 256
     ((-1, 64, 64, 64, A0, B0, D0), g.INVALID_ARG),

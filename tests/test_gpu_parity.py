@@ -19,8 +19,8 @@ pytestmark = pytest.mark.gpu
 
 torch = pytest.importorskip("torch")
 DEV = "cuda:0"
-ALL_RUNGS = [1, 2, 3, 4, 5, 6, 7, 8, 9]
-RING4_RUNGS = (6, 7, 8)   # M, N >= 256, N a multiple of 8, K a multiple of 64, >= 2 k steps
+ALL_RUNGS = [1, 2, 3, 4, 5, 6, 7, 8, 9, 10]
+RING4_RUNGS = (6, 7, 8, 10)   # M, N >= 256, N a multiple of 8, K a multiple of 64, >= 2 k steps
 
 
 def say(*a):
@@ -101,7 +101,7 @@ def test_ragged_shapes(rung, shape):
 
 @pytest.mark.parametrize("rung", [0] + ALL_RUNGS)
 def test_selection_matrix_bitwise(rung):
-    M, N, K = {1: (128, 128, 64), 2: (128, 128, 512), 6: (512, 256, 192), 7: (512, 256, 192), 8: (512, 256, 192)}.get(rung, (384, 320, 192))
+    M, N, K = {1: (128, 128, 64), 2: (128, 128, 512), 6: (512, 256, 192), 7: (512, 256, 192), 8: (512, 256, 192), 10: (512, 256, 192)}.get(rung, (384, 320, 192))
     rng = np.random.default_rng(5)
     pick = rng.integers(0, K, M)
     A = np.zeros((M, K), np.float16)
@@ -112,7 +112,7 @@ def test_selection_matrix_bitwise(rung):
     assert np.array_equal(host_bits(D), B[:, pick].T.view(np.uint16))
 
 
-@pytest.mark.parametrize("rung", [0, 3, 4, 5, 6, 7, 8, 9])
+@pytest.mark.parametrize("rung", [0, 3, 4, 5, 6, 7, 8, 9, 10])
 @pytest.mark.parametrize("K", [64, 512, 4096, 8192])
 def test_all_ones_equals_k(rung, K):
     if not supported(rung, 256, 256, K):
@@ -124,7 +124,7 @@ def test_all_ones_equals_k(rung, K):
     assert np.all(as_f64(host_bits(D)) == K)
 
 
-@pytest.mark.parametrize("rung", [0, 3, 4, 5, 6, 7, 8, 9])
+@pytest.mark.parametrize("rung", [0, 3, 4, 5, 6, 7, 8, 9, 10])
 def test_small_integers_bitwise(rung):
     rng = np.random.default_rng(14)
     shapes = [(256, 192, 8192, -4, 5), (264, 256, 768, 0, 5)]
@@ -140,7 +140,7 @@ def test_small_integers_bitwise(rung):
         assert np.array_equal(got, ref), f"{np.sum(got != ref)} mismatches"
 
 
-@pytest.mark.parametrize("rung", [0, 3, 4, 5, 6, 7, 8, 9])
+@pytest.mark.parametrize("rung", [0, 3, 4, 5, 6, 7, 8, 9, 10])
 def test_designed_rows(rung):
     """Exact sums on a tie, on the overflow threshold and on the subnormal
     grid: round-half-even, +inf at 65520, gradual underflow."""
@@ -210,7 +210,7 @@ def test_poisoned_output_is_fully_overwritten(shape):
     M, N, K = shape
     A, B = rand_case(M, N, K, 77)
     ref, _ = oracle.gemm_nt(A, B)
-    for rung in (0, 3, 4, 5, 6, 7, 8, 9):
+    for rung in (0, 3, 4, 5, 6, 7, 8, 9, 10):
         if not supported(rung, M, N, K):
             continue
         D = torch.full((M, N), float("nan"), dtype=torch.float16, device=DEV)
@@ -297,7 +297,7 @@ def test_non_default_stream_and_interleaving():
         dA, dB = dev(A), dev(B)
         say("[gpu] side stream")
         X = torch.randn(2048, 2048, device=DEV)
-        for rung in (0, 4, 5, 6, 7, 8, 9):
+        for rung in (0, 4, 5, 6, 7, 8, 9, 10):
             D = g.gemm_f16_nt(dA, dB) if rung == 0 else g.gemm_f16_nt_rung(rung, dA, dB)
             X = X * 1.0001          # unrelated work queued on the same stream
             s.synchronize()
@@ -328,7 +328,7 @@ def test_full_size_workloads_sampled(name):
     # whole output: finite everywhere (the workloads cannot overflow)
     assert torch.isfinite(D).all().item()
     if name == "square_4096":
-        for rung in (4, 5, 6, 7, 8, 9):
+        for rung in (4, 5, 6, 7, 8, 9, 10):
             say(f"[gpu] full size square_4096 on rung {rung}")
             Dr = run(rung, dA, dB)
             gotr = host_bits(Dr[torch.from_numpy(rows).to(DEV), torch.from_numpy(cols).to(DEV)])

@@ -88,6 +88,7 @@ class Sim:
         reads_since_barrier = {0: 0, 1: 0}
         frag: dict[int, tuple] = {}    # vgpr base -> (step, kk, op, idx) once its read completed
         acc_started = set()
+        per_block: dict[int, int] = {}  # MFMAs issued per accumulator block
         loaded_steps: dict[int, set] = {}
         mfma = 0
         pc = 0
@@ -99,6 +100,12 @@ class Sim:
         epi_pending: list = []                 # staging writes not yet waited: (buf, group, j)
         staged: dict[int, tuple] = {}          # buf -> (group, set of j) completed
         stores: list = []
+
+        def clobber(v: int) -> None:
+            """A VALU write of v: a fragment held there is gone."""
+            for base in [b for b in frag if b <= v < b + 4]:
+                del frag[base]
+
         while pc < len(self.lines):
             ln = self.lines[pc]
             if not ln.startswith("v_mfma"):
@@ -182,6 +189,8 @@ class Sim:
             elif ln.startswith("ds_read_b128 ") and "%[er" in ln:
                 m = re.match(r"ds_read_b128 (v\[\d+:\d+\]), %\[er(\d)\] offset:(\d+)$", ln)
                 reg, q, buf = _regs(m.group(1)), int(m.group(2)), int(m.group(3)) // 4096
+                for v_ in range(reg, reg + 4):
+                    clobber(v_)
                 grp, js = staged.get(buf, (None, set()))
                 assert js == set(range(NB)), f"read-back of buffer {buf} before all its writes completed"
                 lgkm.append((reg, ("epi_r", grp, q)))
@@ -200,6 +209,7 @@ class Sim:
             elif ln.startswith("v_accvgpr_read_b32"):
                 m = re.match(r"v_accvgpr_read_b32 v(\d+), a(\d+)$", ln)
                 v, a = int(m.group(1)), int(m.group(2))
+                clobber(v)
                 blk = a // 4
                 assert blk in final_at and since_final[blk] >= 11, f"accumulator a{a} read too early"
                 assert a not in acc_read, f"a{a} read twice"
@@ -208,6 +218,7 @@ class Sim:
             elif ln.startswith("v_cvt_pk_f16_f32"):
                 m = re.match(r"v_cvt_pk_f16_f32 v(\d+), v(\d+), v(\d+)$", ln)
                 d_, x, y = int(m.group(1)), int(m.group(2)), int(m.group(3))
+                clobber(d_)
                 cx, cy = vreg.get(x), vreg.get(y)
                 assert cx and cy and cx[0] == "acc" and cy[0] == "acc" and cy[1] == cx[1] + 1, "conversion pair"
                 vreg[d_] = ("pk", cx[1])
@@ -234,7 +245,10 @@ class Sim:
             elif ln.startswith("v_mfma_f32_16x16x32_f16"):
                 m = re.match(r"v_mfma_f32_16x16x32_f16 (a\[(\d+):\d+\]), (v\[\d+:\d+\]), (v\[\d+:\d+\]), (\S+)$", ln)
                 acc, blk, breg, areg, src_c = m.group(1), int(m.group(2)) // 4, _regs(m.group(3)), _regs(m.group(4)), m.group(5)
-                step, kk = mfma // (2 * NB * NB), (mfma // (NB * NB)) % 2
+                # each block accumulates k steps in order, sub-step 0 before
+                # sub-step 1 (whatever the order across blocks)
+                step, kk = divmod(per_block.get(blk, 0), 2)
+                per_block[blk] = per_block.get(blk, 0) + 1
                 assert not any(4 * blk + r in acc_read for r in range(4)), "MFMA on an accumulator already written out"
                 if step == kt - 1 and kk == 1:
                     final_at[blk] = pc
@@ -252,6 +266,7 @@ class Sim:
                 mfma += 1
             pc += 1
         assert not vm and not lgkm, "operations in flight at the end of the block"
+        assert all(n == 2 * kt for n in per_block.values()) and len(per_block) == NB * NB, "MFMAs per block"
         assert acc_read == set(range(4 * NB * NB)), "accumulators not all written out"
         assert sorted(stores) == [(i, q) for i in range(NB) for q in range(4)], "output rows not all stored once"
         return {"mfma": mfma, "epoch": epoch, "acc": acc_started, "loaded": loaded_steps}
@@ -340,6 +355,42 @@ def test_third_form_one_instruction_per_gap():
     assert max(inner) <= 1
 
 
+@pytest.mark.parametrize("kt", [2, 3, 4, 5, 6, 7, 8, 9, 16, 33, 64])
+def test_fourth_form_ring_protocol(kt):
+    res = Sim(GEN.generate4(GEN.DEFAULT4), kt).run()
+    assert res["mfma"] == 2 * NB * NB * kt
+    assert res["epoch"] == 2 * (kt - 1)              # prologue, release and publish per step, none in the last
+    assert len(res["acc"]) == NB * NB
+    assert sorted(res["loaded"]) == list(range(kt))
+    assert all(v == set(range(16)) for v in res["loaded"].values())
+
+
+@pytest.mark.parametrize("params", [
+    {"rel": 16, "pub": 72}, {"rel": 10, "load_every": 7, "pub": 56}, {"read_limit": 100, "a_delay": 2},
+    {"rel": 12, "load_every": 9, "pub": 64, "f0_lat": 6},   # late loads run past the next release
+])
+def test_fourth_form_variants_keep_protocol(params):
+    p = dict(GEN.DEFAULT4)
+    p.update(params)
+    for kt in (2, 3, 4, 7):
+        Sim(GEN.generate4(p), kt).run()
+
+
+def test_fourth_form_pairs_sub_steps():
+    """Each block's sub-step-1 MFMA follows its sub-step-0 MFMA directly."""
+    lines = [ln for ln in GEN.generate4(GEN.DEFAULT4).split("\n") if ln.startswith("v_mfma")]
+    accs = [ln.split()[1].rstrip(",") for ln in lines]
+    assert all(accs[2 * k] == accs[2 * k + 1] for k in range(len(accs) // 2))
+
+
+def test_simulator_catches_epilogue_temporaries_in_live_fragments(monkeypatch):
+    """The last step's epilogue temporaries in the B set its MFMAs still
+    read must be caught."""
+    monkeypatch.setattr(GEN, "epi_set4", lambda par: 128 + 64 * par)
+    with pytest.raises(AssertionError):
+        Sim(GEN.generate4(GEN.DEFAULT4), 3).run()
+
+
 def test_simulator_catches_an_uncompensated_offset():
     """An instruction offset on lane offsets that were not reduced by it
     reads the wrong k step."""
@@ -392,3 +443,4 @@ def test_committed_include_matches_generator():
     assert GEN.as_macro("G16_RING4_KLOOP", GEN.generate(GEN.DEFAULT)) in inc
     assert GEN.as_macro("G16_RING4_KLOOP2", GEN.generate2(GEN.DEFAULT2)) in inc
     assert GEN.as_macro("G16_RING4_KLOOP3", GEN.generate3(GEN.DEFAULT3)) in inc
+    assert GEN.as_macro("G16_RING4_KLOOP4", GEN.generate4(GEN.DEFAULT4)) in inc
