@@ -133,6 +133,21 @@ def _cpu_model():
     return "unknown"
 
 
+def counter_record(workload: str, rung_name: str):
+    """Matrix-core, LDS and HBM figures from profiles/counters_<rung>_<workload>.txt
+    (dense_fp16_gemm_nt_amd.profiling counters) if taken on the current
+    kernel sources, else None."""
+    path = os.path.join(ROOT, "profiles", f"counters_{rung_name}_{workload}.txt")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("kernel_src_sha") != kernel_source_hash() or rec.get("rung") != rung_name:
+        return None
+    keys = ("mfma_busy_pct", "mfma_flop_counted", "lds_bank_conflict_pct", "hbm_gbs")
+    return {k: round(rec[k], 3) for k in keys}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -233,6 +248,7 @@ def main():
             "unit": "TFLOP/s",
             "frac": round(achieved / PEAK_FP16_TFLOPS, 4),
             "traffic": traffic,
+            "counters": counter_record(w.name, rung_name),
             "kernel_mean_ms": round(kernel_ms, 5),
             "kernel_src_sha": kernel_source_hash(),
         },

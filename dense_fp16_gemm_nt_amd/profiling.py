@@ -8,6 +8,13 @@
       HBM bytes per dispatch of the kernel from FETCH_SIZE / WRITE_SIZE
       passes (KiB per dispatch), each scaled by what the same counter reads
       for a device copy of known size
+  python -m dense_fp16_gemm_nt_amd.profiling counters --dir D --trace T --traffic F --flop X --kernel SUBSTR
+      --workload NAME --rung NAME --cus N --command CMD --out FILE
+      matrix-core and LDS figures per dispatch from one counter pass
+      (SQ_VALU_MFMA_BUSY_CYCLES, SQ_INSTS_VALU_MFMA_MOPS_F16,
+      SQ_LDS_BANK_CONFLICT, SQ_LDS_IDX_ACTIVE, SQ_BUSY_CU_CYCLES,
+      GRBM_GUI_ACTIVE), the kernel's mean duration from a kernel trace
+      and its HBM bytes from a traffic record
 """
 from __future__ import annotations
 
@@ -100,6 +107,42 @@ def cmd_traffic(a):
     print(json.dumps(rec, indent=1))
 
 
+COUNTERS = ["SQ_VALU_MFMA_BUSY_CYCLES", "SQ_INSTS_VALU_MFMA_MOPS_F16", "SQ_LDS_BANK_CONFLICT", "SQ_LDS_IDX_ACTIVE",
+            "SQ_BUSY_CU_CYCLES", "GRBM_GUI_ACTIVE"]
+XCDS = 8            # GRBM_GUI_ACTIVE is summed over the 8 XCDs
+SIMDS_PER_CU = 4
+
+
+def cmd_counters(a):
+    c = {name: counter_per_dispatch(a.dir, name, a.kernel) for name in COUNTERS}
+    _, durs = kernel_stats(a.trace, a.kernel)
+    mean_s = statistics.mean(durs) * 1e-6
+    gui = c["GRBM_GUI_ACTIVE"] / XCDS                 # shader-clock cycles of the dispatch
+    simds = a.cus * SIMDS_PER_CU
+    traffic = json.load(open(a.traffic))
+    rec = {
+        "workload": a.workload, "rung": a.rung, "kernel": a.kernel, "flop_per_dispatch": a.flop,
+        "counters_per_dispatch": c,
+        # matrix-core busy cycles over the SIMD-cycles the graphics engine
+        # was active in the dispatch's counter window (GRBM_GUI_ACTIVE: its
+        # cycles span more than the kernel's own duration, so this is a
+        # lower bound on the busy fraction of the kernel itself)
+        "mfma_busy_pct": 100.0 * c["SQ_VALU_MFMA_BUSY_CYCLES"] / (gui * simds),
+        # MFMA FLOPs the hardware counted (equal to 2*M*N*K when every MFMA
+        # of the product ran exactly once)
+        "mfma_flop_counted": c["SQ_INSTS_VALU_MFMA_MOPS_F16"] * 512,
+        "mfma_cycles_per_instruction": c["SQ_VALU_MFMA_BUSY_CYCLES"] / max(c["SQ_INSTS_VALU_MFMA_MOPS_F16"] * 512 / 16384, 1.0),
+        "lds_bank_conflict_pct": 100.0 * c["SQ_LDS_BANK_CONFLICT"] / max(c["SQ_LDS_IDX_ACTIVE"], 1.0),
+        "kernel_mean_us_trace": mean_s * 1e6,
+        "hbm_bytes_per_launch": traffic["hbm_bytes_per_launch"],
+        "hbm_gbs": traffic["hbm_bytes_per_launch"] / mean_s / 1e9,
+        "kernel_src_sha": kernel_source_hash(),
+        "command": a.command,
+    }
+    open(a.out, "w").write(json.dumps(rec, indent=1) + "\n")
+    print(json.dumps(rec, indent=1))
+
+
 def main(argv=None):
     p = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     sub = p.add_subparsers(dest="cmd", required=True)
@@ -118,8 +161,19 @@ def main(argv=None):
     t.add_argument("--rung", required=True)
     t.add_argument("--command", required=True)
     t.add_argument("--out", required=True)
+    c = sub.add_parser("counters")
+    c.add_argument("--dir", required=True)
+    c.add_argument("--trace", required=True)
+    c.add_argument("--traffic", required=True)
+    c.add_argument("--flop", type=float, required=True)
+    c.add_argument("--cus", type=int, required=True)
+    c.add_argument("--kernel", required=True)
+    c.add_argument("--workload", required=True)
+    c.add_argument("--rung", required=True)
+    c.add_argument("--command", required=True)
+    c.add_argument("--out", required=True)
     a = p.parse_args(argv)
-    {"stats": cmd_stats, "traffic": cmd_traffic}[a.cmd](a)
+    {"stats": cmd_stats, "traffic": cmd_traffic, "counters": cmd_counters}[a.cmd](a)
 
 
 if __name__ == "__main__":
