@@ -17,6 +17,11 @@ the timed region starts).  Prints one JSON line:
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
                        [--workload NAME] [--rung R] [--no-cpu-baseline]
+       python bench.py --suite [--only NAME,...] [--seconds S]
+                                      (one JSON line per product beyond the
+                                       five fixed workloads: ragged and
+                                       unaligned shapes, batches, attention
+                                       scores; each against its own roofline)
        python bench.py --copy-calib   (a plain device copy of known size, for
                                        scaling the HBM byte counters)
 """
@@ -73,6 +78,9 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="target oracle time for the CPU sample")
     p.add_argument("--copy-calib", action="store_true", help="run only a plain device copy (counter scaling)")
+    p.add_argument("--suite", action="store_true", help="time the extra products (general shapes, attention scores)")
+    p.add_argument("--only", default="", help="comma-separated extra product names for --suite")
+    p.add_argument("--seconds", type=float, default=0.3, help="timed seconds per extra product")
     return p.parse_args()
 
 
@@ -148,6 +156,102 @@ def counter_record(workload: str, rung_name: str):
     return {k: round(rec[k], 3) for k in keys}
 
 
+def suite(args):
+    """One JSON line per extra product.  Each is timed like the headline
+    (warm-up launches, then back-to-back launches bracketed by events on
+    the launch stream) and placed against the roofline its arithmetic
+    intensity selects: 2*b*M*N*K FLOPs over the compulsory bytes
+    2*b*(MK + NK + MN); below the ridge (peak FLOP/s over 8 TB/s) the
+    bound is HBM."""
+    import numpy as np
+    import torch
+
+    import dense_fp16_gemm_nt_amd as g
+    from dense_fp16_gemm_nt_amd import inputs, workloads
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream(dev)
+    s_ptr = ctypes.c_void_p(stream.cuda_stream)
+    L = g.lib()
+    ridge = PEAK_FP16_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
+    chosen = [n for n in args.only.split(",") if n] or [w.name for w in workloads.EXTRA_WORKLOADS]
+    for name in chosen:
+        w = workloads.EXTRA_BY_NAME[name]
+        print(f"[bench] {w.describe()}", file=sys.stderr, flush=True)
+        A3, B3 = inputs.batched_operands(w.batch, w.M, w.N, w.K, w.seed, w.dist)
+        if w.kind == "heads_rows":
+            # (S, H, d) storage: row s of head h starts at (s*H + h)*d
+            A = torch.from_numpy(np.ascontiguousarray(A3.transpose(1, 0, 2))).to(dev)
+            B = torch.from_numpy(np.ascontiguousarray(B3.transpose(1, 0, 2))).to(dev)
+            lda, sa, ldb, sb = w.batch * w.K, w.K, w.batch * w.K, w.K
+        else:
+            A = torch.from_numpy(A3).to(dev)
+            B = torch.from_numpy(B3).to(dev)
+            lda, sa, ldb, sb = w.K, w.M * w.K, w.K, w.N * w.K
+        D = torch.empty((w.batch, w.M, w.N), dtype=torch.float16, device=dev)
+        a, b, d = A.data_ptr(), B.data_ptr(), D.data_ptr()
+        if w.kind == "gemm":
+            def step():
+                return L.gemm_f16_nt(w.M, w.N, w.K, a, b, d, s_ptr)
+        else:
+            def step():
+                return L.gemm_f16_nt_strided_batched(w.M, w.N, w.K, a, lda, sa, b, ldb, sb, d, w.N, w.M * w.N,
+                                                     w.batch, s_ptr)
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        bad = 0
+        for _ in range(10):
+            bad |= step()
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(10):
+            bad |= step()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        est = e0.elapsed_time(e1) / 10 * 1e-3
+        steps = int(min(5000, max(20, args.seconds / max(est, 1e-6))))
+        for _ in range(steps // 4):
+            bad |= step()
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(steps):
+            bad |= step()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        if bad:
+            raise SystemExit(f"{name}: the library returned an error")
+        launch_s = e0.elapsed_time(e1) * 1e-3 / steps
+        tflops = w.flop / launch_s / 1e12
+        gbs = w.min_bytes / launch_s / 1e9
+        if w.flop / w.min_bytes < ridge:
+            roof = {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                    "frac": round(gbs / HBM_PEAK_GBS, 4)}
+            # context: the same output written by torch's fill kernel (a
+            # plain store stream, no reads), as a practical write ceiling
+            reps = max(5, steps // 4)
+            e0.record(stream)
+            for _ in range(reps):
+                D.fill_(0.0)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            fill_gbs = D.numel() * 2 / (e0.elapsed_time(e1) * 1e-3 / reps) / 1e9
+            roof["fill_gbs_same_output"] = round(fill_gbs, 1)
+        else:
+            roof = {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_FP16_TFLOPS, "unit": "TFLOP/s",
+                    "frac": round(tflops / PEAK_FP16_TFLOPS, 4)}
+        roof["traffic"] = None
+        roof["kernel_src_sha"] = kernel_source_hash()
+        print(json.dumps({
+            "suite": "extra", "workload": w.name, "kind": w.kind, "batch": w.batch, "M": w.M, "N": w.N, "K": w.K,
+            "value": round(tflops, 2), "unit": "TFLOP/s", "us_per_launch": round(launch_s * 1e6, 3),
+            "steps": steps, "compulsory_bytes": w.min_bytes, "compulsory_gbs": round(gbs, 1),
+            "flop_per_byte": round(w.flop / w.min_bytes, 2), "roofline": roof, "dtype": "f16",
+            "data": "synthetic"}), flush=True)
+        del A, B, D
+        torch.cuda.empty_cache()
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -156,6 +260,9 @@ def main():
         sys.exit(2)
     if args.copy_calib:
         copy_calib()
+        return
+    if args.suite:
+        suite(args)
         return
 
     import numpy as np

@@ -106,6 +106,18 @@ bool ring4_shape(int64_t M, int64_t N, int64_t K)
            K >= 2 * ring4::C::BK;
 }
 
+// The fourth form (rung 10, the library's choice) also takes K that is not
+// a multiple of 64, as long as it is a multiple of 8 above 64: its first
+// step is the partial one, whose chunks before a row's first element are
+// moved out of range by a mask that needs every operand band of 256 rows
+// under 2^30 bytes (lda, ldb < 2^21).
+bool ring4_paired_shape(int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb)
+{
+    if (K % ring4::C::BK == 0) return ring4_shape(M, N, K);
+    return M >= ring4::C::BM && N >= ring4::C::BN && N % 8 == 0 && K % 8 == 0 && K > ring4::C::BK &&
+           lda < (int64_t(1) << 21) && ldb < (int64_t(1) << 21);
+}
+
 // Operands the 16-byte-load kernels take: every row of A and B starts on a
 // 16-byte boundary (K, leading dimensions and batch strides multiples of 8
 // elements, 16-byte aligned bases) and D's base is 16-byte aligned.  Other
@@ -134,10 +146,10 @@ int validate(int rung, int64_t M, int64_t N, int64_t K, const void* A, const voi
     if (rung == GEMM_F16_NT_R1_SINGLE_TILE && !(M == 128 && N == 128 && K == 64)) return GEMM_F16_NT_UNSUPPORTED;
     if (rung == GEMM_F16_NT_R2_KLOOP && !(M == 128 && N == 128)) return GEMM_F16_NT_UNSUPPORTED;
     if (rung == GEMM_F16_NT_R3_GRID && (N + 127) / 128 > 65535) return GEMM_F16_NT_UNSUPPORTED;
-    if ((rung == GEMM_F16_NT_R6_RING4 || rung == GEMM_F16_NT_R7_RING4_2B || rung == GEMM_F16_NT_R8_RING4_GAP ||
-         rung == GEMM_F16_NT_R10_RING4_PAIRED) &&
+    if ((rung == GEMM_F16_NT_R6_RING4 || rung == GEMM_F16_NT_R7_RING4_2B || rung == GEMM_F16_NT_R8_RING4_GAP) &&
         !ring4_shape(M, N, K))
         return GEMM_F16_NT_UNSUPPORTED;
+    if (rung == GEMM_F16_NT_R10_RING4_PAIRED && !ring4_paired_shape(M, N, K, K, K)) return GEMM_F16_NT_UNSUPPORTED;
     if (!any_out) return GEMM_F16_NT_OK;
     // fp16 elements are 2-byte aligned; the fast kernels need 16 bytes
     if ((K > 0 && (((uintptr_t)A & 1) || ((uintptr_t)B & 1))) || ((uintptr_t)D & 1)) return GEMM_F16_NT_UNSUPPORTED;
@@ -206,11 +218,12 @@ int launch_fill_zero(void* D, int64_t n, hipStream_t s)
     return launched();
 }
 
-// Whether the four-wave scheduled ring covers this problem: whole tiles and
-// 16-byte aligned output rows in every batch entry.
+// Whether the four-wave scheduled ring (its fourth form) covers this
+// problem: its shapes and 16-byte aligned output rows in every batch entry.
 bool ring4_fits(const GemmArgs& g)
 {
-    return ring4_shape(g.M, g.N, g.K) && g.ldd % 8 == 0 && g.sd % 8 == 0 && g.ldd < (int64_t(1) << 24);
+    return ring4_paired_shape(g.M, g.N, g.K, g.lda, g.ldb) && g.ldd % 8 == 0 && g.sd % 8 == 0 &&
+           g.ldd < (int64_t(1) << 24);
 }
 
 // Persistent launch: one workgroup per compute unit (fewer when there are
@@ -231,6 +244,8 @@ int launch_ring4(const GemmArgs& g0, hipStream_t s, int form = 0)
     if (st != GEMM_F16_NT_OK) return st;
     const int64_t grid = tiles < cus ? tiles : cus;
     if (form == 0) form = 4;
+    // only the fourth form has the partial first step
+    if (form != 4 && g.K % ring4::C::BK != 0) return GEMM_F16_NT_UNSUPPORTED;
     if (form == 4)
         hipLaunchKernelGGL(ring4::ring4_kernel<4>, dim3((unsigned)grid), dim3(ring4::C::THREADS), 0, s, g);
     else if (form == 3)

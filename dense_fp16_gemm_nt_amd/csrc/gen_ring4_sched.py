@@ -58,7 +58,7 @@ sub-step K (VGPR); buffer resources %[rsa], %[rsb]; the wave's LDS load base
 the count %[rem] of k steps (SGPR, all modified; %[kh] is scratch); and for
 the epilogue the staging and store addresses %[ewJ], %[erQ], %[soQ], the
 output resource %[rsd], the row-group stride %[gstr] and the scratch
-%[sdo].  The accumulators a0..a255 and fragment buffers v128..v255 are
+%[sdo]; the fourth form also takes the head masks %[hm0], %[hm1].  The accumulators a0..a255 and fragment buffers v128..v255 are
 fixed registers of the block.
 """
 from __future__ import annotations
@@ -790,7 +790,15 @@ DEFAULT3 = {
 # barrier at gap rel (this stage's last reads, the late A rows, are done;
 # step j+2 may refill it) and a publish barrier at gap pub (step j+1's
 # loads have landed; its fragment reads follow).  Loads and offsets are
-# those of the third form.
+# those of the third form, except step 0's (the head step below).
+#
+# K need not be a multiple of 64 here: the k origin moves back by
+# 64 * steps - K elements so that step 0 is the partial one.  Its chunks
+# that fall before a row's first element get offsets beyond the buffer's
+# size (the head masks %[hm0], %[hm1], one per row-group parity, since the
+# swizzle gives a lane a different chunk in even and odd row groups), so
+# the hardware's range check returns zeros for them instead of reading
+# memory; every later step is whole.
 
 def a4(h: int, i: int) -> str:
     return f"v[{64 + 32 * h + 4 * i}:{64 + 32 * h + 4 * i + 3}]"
@@ -801,7 +809,19 @@ def b4(p: int, h: int, j: int) -> str:
     return f"v[{base}:{base + 3}]"
 
 
+def head_reg(op: str, q: int) -> int:
+    """VGPR holding the head-step lane offset of load q of operand op."""
+    return 64 + (8 if op == "b" else 0) + q
+
+
 class Emitter4(Emitter3):
+    def load_head(self, op: str, q: int) -> None:
+        """Load q of operand op for step 0 (stage 0, %[ko] = 0) from the
+        masked offset in head_reg(op, q), with the instruction offset."""
+        imm = 1024 * (q % 4)
+        off = f" offset:{imm}" if imm else ""
+        self.op(f"buffer_load_dwordx4 v{head_reg(op, q)}, %[rs{op}], %[ko] offen{off} lds")
+
     def read4(self, op: str, h: int, idx: int, stage: int, p: int) -> None:
         reg = a4(h, idx) if op == "a" else b4(p, h, idx)
         self.op(f"ds_read_b128 {reg}, %[r{op}{stage}{h}] offset:{2048 * idx}")
@@ -972,6 +992,13 @@ def generate4(p: dict) -> str:
     the third)."""
     order = p.get("order", "snake")
     e = Emitter4()
+    # step 0 may be a partial step (K not a multiple of 64): its lane
+    # offsets are OR-ed with the head mask of the row group's parity, which
+    # moves the chunks before the row's first element out of the buffer
+    # (they land as zeros); the mask is 0 when K is a multiple of 64.  The
+    # offsets go to v64..v79, free until step 0's fragment reads.
+    for (op, q) in LOAD3:
+        e.op(f"v_or_b32 v{head_reg(op, q)}, %[{op}x{q}], %[hm{q % 2}]")
     for stage in (0, 1):
         if stage:
             e.op("s_add_u32 %[ko], %[ko], 128")
@@ -979,7 +1006,10 @@ def generate4(p: dict) -> str:
             if q % 4 == 0:
                 e.op(Emitter3.m0_line(op, q, stage))
                 e.op("s_nop 0")  # M0 write -> LDS-DMA read of M0
-            e.load_imm(op, q, stage)
+            if stage == 0:
+                e.load_head(op, q)
+            else:
+                e.load_imm(op, q, stage)
     e.op("s_add_u32 %[kh], %[ko], 128")
     e.op(f"s_waitcnt vmcnt({NLOAD})")
     e.op("s_barrier")

@@ -97,3 +97,11 @@ def operands(M: int, N: int, K: int, seed: int, dist: dict):
     """(A, B): A is M x K, B is N x K, both fp16 numpy arrays."""
     return (generate(M, K, seed, STREAM_A, dist),
             generate(N, K, seed, STREAM_B, dist))
+
+
+def batched_operands(batch: int, M: int, N: int, K: int, seed: int, dist: dict):
+    """(A, B) of `batch` products: A is batch x M x K, B is batch x N x K,
+    drawn as one (batch*M) x K and one (batch*N) x K matrix and split into
+    batch entries in order."""
+    A, B = operands(batch * M, batch * N, K, seed, dist)
+    return A.reshape(batch, M, K), B.reshape(batch, N, K)

@@ -46,3 +46,60 @@ WORKLOADS = [
 ]
 BY_NAME = {w.name: w for w in WORKLOADS}
 HEADLINE = BY_NAME["square_4096"]
+
+
+@dataclass(frozen=True)
+class ExtraWorkload:
+    """A product beyond the five fixed workloads, for the general-shape and
+    attention-score entry points: `batch` independent products D[b] =
+    A[b] @ B[b]^T of M x N x K.
+
+    kind  "gemm"       one contiguous product through gemm_f16_nt
+          "strided"    contiguous batch entries through the strided-batched
+                       entry point
+          "heads_rows" attention scores with the heads interleaved in the
+                       rows of Q and K ((S, H, d) storage read as H products
+                       of S x S x d: leading dimension H*d, batch stride d)
+    Operands are drawn as one (batch*M) x K and one (batch*N) x K matrix
+    from the input generator and split into batch entries in order."""
+    name: str
+    kind: str
+    batch: int
+    M: int
+    N: int
+    K: int
+    seed: int
+    dist: dict = field(hash=False, compare=False)
+
+    @property
+    def flop(self) -> int:
+        return 2 * self.batch * self.M * self.N * self.K
+
+    @property
+    def min_bytes(self) -> int:
+        """Compulsory HBM bytes: every operand element read once and every
+        output element written once, 2 bytes each."""
+        return 2 * self.batch * (self.M * self.K + self.N * self.K + self.M * self.N)
+
+    def describe(self) -> str:
+        d = self.dist
+        ds = f"uniform[{d['lo']},{d['hi']}]" if d["kind"] == "uniform" else f"normal(0,{d['sigma']})"
+        return f"{self.name}: {self.kind} batch={self.batch} M={self.M} N={self.N} K={self.K} {ds} seed={self.seed}"
+
+
+EXTRA_WORKLOADS = [
+    # ragged M, N and K (K % 64 != 0): the edge variant of the 8-wave ring
+    ExtraWorkload("ragged_4000", "gemm", 1, 4000, 4000, 4000, 11, U11),
+    # ragged M and N, whole 64-wide k steps: the four-wave ring with clamped edge tiles
+    ExtraWorkload("ragged_mn_4000x4000x4096", "gemm", 1, 4000, 4000, 4096, 12, U11),
+    # K % 8 != 0: operand rows are not 16-byte aligned, so the general kernel runs
+    ExtraWorkload("unaligned_k_4096x4096x4095", "gemm", 1, 4096, 4096, 4095, 13, U11),
+    # a batch of mid-size products, one launch
+    ExtraWorkload("batched_16x1024x1024x4096", "strided", 16, 1024, 1024, 4096, 14, U11),
+    # attention scores S = Q K^T, 32 heads of 4096 x 4096, head dimension 128 and 64
+    ExtraWorkload("attn_scores_h32_s4096_d128", "strided", 32, 4096, 4096, 128, 15, U11),
+    ExtraWorkload("attn_scores_h32_s4096_d64", "strided", 32, 4096, 4096, 64, 16, U11),
+    # the same with the heads interleaved in the rows of Q and K
+    ExtraWorkload("attn_scores_rows_h32_s4096_d128", "heads_rows", 32, 4096, 4096, 128, 17, U11),
+]
+EXTRA_BY_NAME = {w.name: w for w in EXTRA_WORKLOADS}

@@ -73,6 +73,13 @@ A0, B0, D0 = 0x10000, 0x20000000, 0x40000000   # fake, 16-byte aligned, disjoint
     ((11, 64, 64, 64, A0, B0, D0), g.INVALID_ARG),         # unknown rung
     ((10, 64, 64, 64, A0, B0, D0), g.UNSUPPORTED),         # rung 10: M, N >= 256
     ((10, 512, 256, 192, A0, B0, D0), g.OK),
+    ((10, 256, 256, 136, A0, B0, D0), g.OK),               # rung 10: K % 64 != 0, partial first step
+    ((10, 256, 264, 72, A0, B0, D0), g.OK),
+    ((10, 256, 256, 64, A0, B0, D0), g.UNSUPPORTED),       # ... but at least two k steps
+    ((10, 256, 256, 40, A0, B0, D0), g.UNSUPPORTED),
+    ((10, 256, 256, (1 << 21) + 8, A0, B0, D0), g.UNSUPPORTED),  # ... and rows under 2^21 elements
+    ((10, 256, 256, 1 << 21, A0, 1 << 32, 1 << 33), g.OK),  # whole steps: any row length
+    ((8, 256, 256, 136, A0, B0, D0), g.UNSUPPORTED),       # rungs 6-8: whole 64-wide steps only
     ((9, 64, 64, 64, A0, B0, D0), g.OK),                   # rung 9: any shape
     ((8, 64, 64, 64, A0, B0, D0), g.UNSUPPORTED),          # rung 8: M, N >= 256
     ((-1, 64, 64, 64, A0, B0, D0), g.INVALID_ARG),

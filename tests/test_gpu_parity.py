@@ -50,6 +50,8 @@ def supported(rung, M, N, K):
         return (M, N, K) == (128, 128, 64)
     if rung == 2:
         return (M, N) == (128, 128)
+    if rung == 10:   # also a partial first step when K is not a multiple of 64
+        return M >= 256 and N >= 256 and N % 8 == 0 and K % 8 == 0 and K > 64
     if rung in RING4_RUNGS:
         return M >= 256 and N >= 256 and N % 8 == 0 and K % 64 == 0 and K >= 128
     return True
@@ -288,6 +290,44 @@ def test_ring4_ragged_tiles(shape):
     assert torch.isnan(Dfull[:, :, N:]).all().item()
 
 
+@pytest.mark.parametrize("shape", [(256, 256, 72), (512, 256, 136), (520, 776, 200), (300, 264, 1000),
+                                   (1024, 1024, 4040), (256, 512, 120)],
+                         ids=lambda s: "x".join(map(str, s)))
+def test_ring4_partial_first_step(shape):
+    """K not a multiple of 64 on the fourth form (rung 10 and the library's
+    choice): the partial step goes first, its chunks before each row's first
+    element read as zeros.  Every output against the oracle, and bitwise
+    equal to the same product with each operand row padded in front with
+    zeros to whole 64-wide steps (which runs the whole-step path): the
+    padding only adds exact zero products."""
+    M, N, K = shape
+    A, B = rand_case(M, N, K, 140 + K)
+    ref, _ = oracle.gemm_nt(A, B)
+    hk = -K % 64
+    Ap = np.concatenate([np.zeros((M, hk), np.float16), A], axis=1)
+    Bp = np.concatenate([np.zeros((N, hk), np.float16), B], axis=1)
+    say(f"[gpu] ring4 partial first step {M}x{N}x{K} (padded K {K + hk}) rung 10")
+    padded = host_bits(run(10, dev(Ap), dev(Bp)))
+    for rung in (0, 10):
+        assert supported(rung, M, N, K)
+        D = torch.full((M, N), float("nan"), dtype=torch.float16, device=DEV)
+        say(f"[gpu] ring4 partial first step {M}x{N}x{K} rung {rung}")
+        got = host_bits(run(rung, dev(A), dev(B), D))
+        assert_parity(got, ref, K, f"rung {rung} {M}x{N}x{K}")
+        same = (got == padded) | (((got | padded) & 0x7FFF) == 0)   # +0 and -0 alike
+        assert same.all(), f"rung {rung}: {int((~same).sum())} outputs differ from the front-padded product"
+    # operands inside larger rows (leading dimension > K) through the strided form
+    lda, ldb = K + 24, K + 8
+    Apad = torch.zeros((M, lda), dtype=torch.float16)
+    Apad[:, :K] = torch.from_numpy(A)
+    Bpad = torch.zeros((N, ldb), dtype=torch.float16)
+    Bpad[:, :K] = torch.from_numpy(B)
+    say(f"[gpu] ring4 partial first step {M}x{N}x{K} strided lda={lda} ldb={ldb}")
+    Ds = g.gemm_f16_nt_strided_batched(Apad.to(DEV)[:, :K], Bpad.to(DEV)[:, :K])
+    torch.cuda.synchronize()
+    assert_parity(host_bits(Ds[0]), ref, K, f"strided {M}x{N}x{K}")
+
+
 def test_non_default_stream_and_interleaving():
     M, N, K = 512, 512, 512
     A, B = rand_case(M, N, K, 79)
@@ -517,3 +557,37 @@ def test_splitk_rejects_small_workspace():
     assert e.value.status == g.INVALID_ARG
     torch.cuda.synchronize()
     assert torch.all(D == 7.0).item()
+
+
+# ------------------------------- products beyond the five fixed workloads
+
+@pytest.mark.parametrize("name", [w.name for w in workloads.EXTRA_WORKLOADS])
+def test_extra_workloads_sampled(name):
+    """The general-shape, batched and attention-score products that
+    `bench.py --suite` times, at full size and in the same layouts, on
+    sampled outputs of every batch entry; every output element is written
+    (D starts as NaN)."""
+    w = workloads.EXTRA_BY_NAME[name]
+    A3, B3 = inputs.batched_operands(w.batch, w.M, w.N, w.K, w.seed, w.dist)
+    say(f"[gpu] extra product {w.describe()}")
+    D = torch.full((w.batch, w.M, w.N), float("nan"), dtype=torch.float16, device=DEV)
+    if w.kind == "gemm":
+        g.gemm_f16_nt(dev(A3[0]), dev(B3[0]), D[0])
+    elif w.kind == "heads_rows":
+        # (S, H, d) storage read as H products: leading dimension H*d, batch stride d
+        A = dev(A3.transpose(1, 0, 2)).transpose(0, 1)
+        B = dev(B3.transpose(1, 0, 2)).transpose(0, 1)
+        assert A.stride() == (w.K, w.batch * w.K, 1)
+        g.gemm_f16_nt_strided_batched(A, B, D)
+    else:
+        g.gemm_f16_nt_strided_batched(dev(A3), dev(B3), D)
+    torch.cuda.synchronize()
+    assert not torch.isnan(D).any().item(), "output elements left unwritten"
+    per = 3000 if w.batch == 1 else 200
+    worst = 0.0
+    for b in range(w.batch):
+        rows, cols = sample_positions(w.M, w.N, per, w.seed * 100 + b)
+        ref, _ = oracle.gemm_nt_sampled(A3[b], B3[b], rows, cols)
+        got = host_bits(D[b][torch.from_numpy(rows).to(DEV), torch.from_numpy(cols).to(DEV)])
+        worst = max(worst, assert_parity(got, ref, w.K, f"{name} entry {b}"))
+    say(f"      worst err/tol = {worst:.3f}")

@@ -62,3 +62,20 @@ def test_moments(dist, mean, var, bound):
     assert abs(x.var() / var - 1.0) < 0.01
     assert np.abs(x).max() <= bound
     assert np.isfinite(x).all()
+
+
+def test_batched_operands_split_one_draw_in_order():
+    A3, B3 = inputs.batched_operands(3, 4, 5, 16, 9, workloads.U11)
+    A, B = inputs.operands(12, 15, 16, 9, workloads.U11)
+    assert A3.shape == (3, 4, 16) and B3.shape == (3, 5, 16)
+    assert np.array_equal(A3.reshape(12, 16), A) and np.array_equal(B3.reshape(15, 16), B)
+
+
+def test_extra_workloads_are_well_formed():
+    names = [w.name for w in workloads.EXTRA_WORKLOADS]
+    assert len(set(names)) == len(names)
+    for w in workloads.EXTRA_WORKLOADS:
+        assert w.kind in ("gemm", "strided", "heads_rows")
+        assert w.batch >= 1 and min(w.M, w.N, w.K) >= 1
+        assert w.kind != "gemm" or w.batch == 1
+        assert w.flop == 2 * w.batch * w.M * w.N * w.K

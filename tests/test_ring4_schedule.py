@@ -97,6 +97,7 @@ class Sim:
         acc_read: set = set()                  # accumulator registers read
         vreg: dict[int, tuple] = {}            # epilogue VGPR contents
         sdo = None
+        head: dict[int, tuple] = {}            # VGPR -> (op, q) of a head-step lane offset
         epi_pending: list = []                 # staging writes not yet waited: (buf, group, j)
         staged: dict[int, tuple] = {}          # buf -> (group, set of j) completed
         stores: list = []
@@ -131,16 +132,32 @@ class Sim:
                 kh += 128
             elif ln.startswith("s_add_u32 m0, %[lb], "):
                 m0 = int(ln.split(",")[2])
-            elif ln.startswith("buffer_load_dwordx4"):
-                m = re.match(r"buffer_load_dwordx4 %\[([ab])([ox])(\d)\], %\[rs([ab])\], %\[(k[oh])\] offen( offset:(\d+))? lds$", ln)
+            elif ln.startswith("v_or_b32"):
+                # the head step's lane offsets: row group q's reduced offsets
+                # with the head mask of q's parity
+                m = re.match(r"v_or_b32 v(\d+), %\[([ab])x(\d)\], %\[hm(\d)\]$", ln)
                 assert m, ln
-                op, kind, q, rop = m.group(1), m.group(2), int(m.group(3)), m.group(4)
+                v, op, q, par = int(m.group(1)), m.group(2), int(m.group(3)), int(m.group(4))
+                assert par == q % 2, f"row group {q} with the head mask of parity {par}"
+                clobber(v)
+                head[v] = (op, q)
+            elif ln.startswith("buffer_load_dwordx4"):
+                m = re.match(r"buffer_load_dwordx4 (?:%\[([ab])([ox])(\d)\]|v(\d+)), %\[rs([ab])\], %\[(k[oh])\] offen( offset:(\d+))? lds$", ln)
+                assert m, ln
+                if m.group(4) is not None:
+                    v = int(m.group(4))
+                    assert v in head, f"load from v{v}, which holds no head offset"
+                    op, q = head[v]
+                    kind = "x"
+                    assert m.group(6) == "ko" and ko == 0, "a head offset used after step 0"
+                else:
+                    op, kind, q = m.group(1), m.group(2), int(m.group(3))
+                rop, koff, imm = m.group(5), m.group(6), int(m.group(8) or 0)
                 assert op == rop, "lane offsets of one operand with the other's buffer"
-                imm = int(m.group(7) or 0)
                 # the immediate offset moves the global address and the LDS
                 # destination alike; the 'x' lane offsets of row group q are
                 # 1024 * (q mod 4) bytes short of the row group's
-                goff = (ko if m.group(5) == "ko" else kh) + imm - (1024 * (q % 4) if kind == "x" else 0)
+                goff = (ko if koff == "ko" else kh) + imm - (1024 * (q % 4) if kind == "x" else 0)
                 assert goff % 128 == 0, f"global offset {goff} is not a k step"
                 step = goff // 128
                 assert 0 <= step < kt, f"load of step {step} beyond K (KT={kt})"
@@ -397,6 +414,61 @@ def test_simulator_catches_an_uncompensated_offset():
     text = GEN.generate3(GEN.DEFAULT3).replace("%[ax1]", "%[ao1]", 1)
     with pytest.raises(AssertionError):
         Sim(text, 4).run()
+
+
+def test_simulator_catches_a_head_mask_of_the_wrong_parity():
+    """Row group 1 with the even groups' head mask zeroes the wrong chunks
+    when K is not a multiple of 64."""
+    text = GEN.generate4(GEN.DEFAULT4).replace("%[ax1], %[hm1]", "%[ax1], %[hm0]", 1)
+    with pytest.raises(AssertionError):
+        Sim(text, 3).run()
+
+
+def test_simulator_catches_a_swapped_head_offset():
+    """Step 0's load of row group 0 from row group 1's head offset lands
+    the wrong rows."""
+    text = GEN.generate4(GEN.DEFAULT4).replace("buffer_load_dwordx4 v64,", "buffer_load_dwordx4 v65,", 1)
+    with pytest.raises(AssertionError):
+        Sim(text, 3).run()
+
+
+def test_head_step_loads_are_step_zeros_only():
+    """The fourth form reads every step-0 row group through its head
+    offset (and no later step does)."""
+    lines = GEN.generate4(GEN.DEFAULT4).split("\n")
+    ors = [ln for ln in lines if ln.startswith("v_or_b32")]
+    assert len(ors) == GEN.NLOAD
+    head_loads = [ln for ln in lines if re.match(r"buffer_load_dwordx4 v\d+,", ln)]
+    assert len(head_loads) == GEN.NLOAD
+    first_other = next(i for i, ln in enumerate(lines) if ln.startswith("buffer_load_dwordx4 %["))
+    assert all(lines.index(ln) < first_other for ln in head_loads)
+
+
+def _chunk(w: int, lane: int, q: int) -> int:
+    """16-byte chunk of load q of wave w's lane: 8 rows of 8 chunks per
+    load, row r's chunks XOR-swizzled with (r / 2) mod 8."""
+    r = (w * 8 + q) * 8 + lane // 8
+    return (lane % 8) ^ ((r // 2) % 8)
+
+
+def test_head_mask_depends_on_row_group_parity_only():
+    """A lane's chunk in load q depends on q only through its parity, so
+    two head masks serve all 8 row groups; for every partial-step length
+    the masked chunks are exactly those before the row's first element."""
+    for w in range(4):
+        for lane in range(64):
+            for q in range(8):
+                assert _chunk(w, lane, q) == _chunk(0, lane, q % 2)
+    for hk in range(0, 64, 8):
+        for lane in range(64):
+            for q in range(2):
+                c = _chunk(0, lane, q)
+                masked = 8 * c < hk
+                assert masked == all(8 * c + e < hk for e in range(8))
+        # every row of a load has hk / 8 masked chunks
+        for q in range(2):
+            for row in range(8):
+                assert sum(8 * _chunk(0, 8 * row + cl, q) < hk for cl in range(8)) == hk // 8
 
 
 def test_simulator_catches_a_planted_race():
