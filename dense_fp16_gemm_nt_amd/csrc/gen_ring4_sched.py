@@ -815,12 +815,28 @@ def head_reg(op: str, q: int) -> int:
 
 
 class Emitter4(Emitter3):
+    @staticmethod
+    def m0_line4(op: str, q: int, stage: int) -> str:
+        """M0 for the group of 4 loads holding q, in logical stage `stage`
+        (%[lb0], %[lb1]: the wave's load base in the physical stage that
+        holds logical stage 0, 1 of this tile)."""
+        return f"s_add_u32 m0, %[lb{stage}], {(32768 if op == 'b' else 0) + 4096 * (q // 4)}"
+
     def load_head(self, op: str, q: int) -> None:
         """Load q of operand op for step 0 (stage 0, %[ko] = 0) from the
         masked offset in head_reg(op, q), with the instruction offset."""
         imm = 1024 * (q % 4)
         off = f" offset:{imm}" if imm else ""
         self.op(f"buffer_load_dwordx4 v{head_reg(op, q)}, %[rs{op}], %[ko] offen{off} lds")
+
+    @staticmethod
+    def next_load(op: str, q: int) -> str:
+        """Load q of operand op of the next tile's step 0 (its head step)
+        from the masked offset in %[ht], soffset 0, with the instruction
+        offset."""
+        imm = 1024 * (q % 4)
+        off = f" offset:{imm}" if imm else ""
+        return f"buffer_load_dwordx4 %[ht], %[rs{op}n], 0 offen{off} lds"
 
     def read4(self, op: str, h: int, idx: int, stage: int, p: int) -> None:
         reg = a4(h, idx) if op == "a" else b4(p, h, idx)
@@ -860,9 +876,10 @@ def late_rows4(p: dict) -> list[int]:
 
 
 def emit_step4(e: Emitter4, stage: int, first: bool, carried: bool, ahead: bool, has_next: bool, last: bool,
-               tail: list[str], p: dict) -> None:
+               tail: list[str], p: dict, nxt: bool = False) -> None:
     """One 64-wide k step j reading `stage` (B fragments in set stage) in
-    the fourth form; flags as in emit_step3.  The late A rows of this step
+    the fourth form; flags as in emit_step3, and nxt: the last step also
+    loads the next tile's step 0.  The late A rows of this step
     are read at its start unless `first` (the prologue read them)."""
     order = p.get("order", "snake")
     ng = KSUB * NQ
@@ -920,12 +937,30 @@ def emit_step4(e: Emitter4, stage: int, first: bool, carried: bool, ahead: bool,
             if m is None:
                 m = first_free(prev + 1)
                 gg = first_free(m + 1)
-            gaps[m].append(("text", Emitter3.m0_line(op, q, st)))
+            gaps[m].append(("text", Emitter4.m0_line4(op, q, st)))
             cur_m0 = grp
         gaps[gg].append(("load", op, q, st, koff))
         placed.append((gg, koff))
         prev = gg
     assert all(gg < ng - 1 - 4 for gg, _ in placed), "loads run into the tail"
+    if last and nxt:
+        # the next tile's step 0 into the other stage (free since the
+        # previous step's publish barrier: its reads were all waited for
+        # there): M0, the masked offset and the load in gaps of their own,
+        # one load every nxt_every gaps from nxt_start, ahead of most of the
+        # epilogue's stores
+        gl = p["nxt_start"] - p["nxt_every"]
+        for k, (op, q) in enumerate(LOAD3):
+            prev_load = gl
+            gl = first_free(max(prev_load + p["nxt_every"], p["nxt_start"]))
+            before = [x for x in range(gl - 1, prev_load, -1) if free(x)]
+            need = 2 if q % 4 == 0 else 1
+            assert len(before) >= need, "no room for the next-tile load's M0 and offset"
+            gaps[before[0]].append(("text", f"v_or_b32 %[ht], %[{op}x{q}], %[hm{q % 2}]"))
+            if q % 4 == 0:
+                gaps[before[1]].append(("text", Emitter4.m0_line4(op, q, stage ^ 1)))
+            gaps[gl].append(("text", Emitter4.next_load(op, q)))
+        assert gl < ng - 8, "next-tile loads run into the end of the step"
     if has_next:
         n_young = sum(1 for gg, koff in placed if koff == "kh" and gg < pub - 1)
         assert not any(koff == "ko" and gg >= pub - 1 for gg, koff in placed), "carried load after the publish wait"
@@ -953,6 +988,7 @@ def emit_step4(e: Emitter4, stage: int, first: bool, carried: bool, ahead: bool,
     assert not cmp_at or max(scc_writers, default=-1) < min(cmp_at), "SCC clobbered before the branch"
 
     t_base = epi_set4(par)
+    step_at = len(e.lines)
     for gg in range(ng):
         pq, h = divmod(gg, 2)
         i, j = mfma_block(pq, order)
@@ -972,6 +1008,12 @@ def emit_step4(e: Emitter4, stage: int, first: bool, carried: bool, ahead: bool,
                     e.lgkm.clear()
     if last:
         e.epi_finish4(t_base, t_base + 32)
+        if nxt:
+            # stores issued after the last next-tile load: the next tile
+            # waits for its step 0 with them (and its step-1 loads) in flight
+            lines = e.lines[step_at:]
+            last_load = max(n for n, ln in enumerate(lines) if ln.startswith("buffer_load_dwordx4 %[ht]"))
+            e.s_after.append(sum(1 for ln in lines[last_load:] if ln.startswith("buffer_store_dwordx4")))
         for t in tail:
             e.op(t)
 
@@ -992,26 +1034,39 @@ def generate4(p: dict) -> str:
     the third)."""
     order = p.get("order", "snake")
     e = Emitter4()
+    e.s_after = []
     # step 0 may be a partial step (K not a multiple of 64): its lane
     # offsets are OR-ed with the head mask of the row group's parity, which
     # moves the chunks before the row's first element out of the buffer
     # (they land as zeros); the mask is 0 when K is a multiple of 64.  The
-    # offsets go to v64..v79, free until step 0's fragment reads.
+    # offsets go to v64..v79, free until step 0's fragment reads.  A tile
+    # loads its own step 0 here when %[first] != 0; otherwise its step 0
+    # was loaded during the last step of the tile before (that step ran
+    # with %[hasn] != 0), ahead of that tile's output stores.
+    e.op("s_cmp_eq_u32 %[first], 0")
+    e.op("s_cbranch_scc1 11f")
     for (op, q) in LOAD3:
         e.op(f"v_or_b32 v{head_reg(op, q)}, %[{op}x{q}], %[hm{q % 2}]")
-    for stage in (0, 1):
-        if stage:
-            e.op("s_add_u32 %[ko], %[ko], 128")
-        for (op, q) in LOAD3:
-            if q % 4 == 0:
-                e.op(Emitter3.m0_line(op, q, stage))
-                e.op("s_nop 0")  # M0 write -> LDS-DMA read of M0
-            if stage == 0:
-                e.load_head(op, q)
-            else:
-                e.load_imm(op, q, stage)
+    for (op, q) in LOAD3:
+        if q % 4 == 0:
+            e.op(Emitter4.m0_line4(op, q, 0))
+            e.op("s_nop 0")  # M0 write -> LDS-DMA read of M0
+        e.load_head(op, q)
+    e.label("11")
+    e.op("s_add_u32 %[ko], %[ko], 128")
+    for (op, q) in LOAD3:
+        if q % 4 == 0:
+            e.op(Emitter4.m0_line4(op, q, 1))
+            e.op("s_nop 0")
+        e.load_imm(op, q, 1)
     e.op("s_add_u32 %[kh], %[ko], 128")
+    e.op("s_cmp_eq_u32 %[first], 0")
+    e.op("s_cbranch_scc1 12f")
     e.op(f"s_waitcnt vmcnt({NLOAD})")
+    e.op("s_branch 13f")
+    e.label("12")
+    e.op("s_waitcnt vmcnt(@NEXT_WAIT@)")   # step-1 loads and the tile before's late stores
+    e.label("13")
     e.op("s_barrier")
     # all fragments of step 0, in the order the first MFMAs need them
     e.read4("a", 0, 0, 0, 0)
@@ -1028,9 +1083,9 @@ def generate4(p: dict) -> str:
     sub = "s_sub_u32 %[rem], %[rem], 1"
     cmp2 = "s_cmp_eq_u32 %[rem], 2"
 
-    def step(stage, first, carried, ahead, has_next, last, tail):
+    def step(stage, first, carried, ahead, has_next, last, tail, nxt=False):
         e.lgkm = list(pro) if first else []
-        emit_step4(e, stage, first, carried, ahead, has_next, last, tail, p)
+        emit_step4(e, stage, first, carried, ahead, has_next, last, tail, p, nxt)
 
     e.op(cmp2)
     e.op("s_cbranch_scc1 5f")
@@ -1044,12 +1099,25 @@ def generate4(p: dict) -> str:
     step(1, False, True, False, True, False, [sub, "s_branch 3f"])                # step KT-2 in stage 1
     e.label("8")
     step(0, False, True, False, True, False, [sub])                               # step KT-2 in stage 0
+    # the last step, in either stage, with the next tile's step-0 loads
+    # when %[hasn] != 0 and without them otherwise
     e.label("2")
-    step(1, False, False, False, False, True, ["s_branch 4f"])                   # last step in stage 1
+    e.op("s_cmp_eq_u32 %[hasn], 0")
+    e.op("s_cbranch_scc1 14f")
+    step(1, False, False, False, False, True, ["s_branch 4f"], nxt=True)         # last step in stage 1
+    e.label("14")
+    step(1, False, False, False, False, True, ["s_branch 4f"])
     e.label("3")
-    step(0, False, False, False, False, True, [])                                 # last step in stage 0
+    e.op("s_cmp_eq_u32 %[hasn], 0")
+    e.op("s_cbranch_scc1 15f")
+    step(0, False, False, False, False, True, ["s_branch 4f"], nxt=True)         # last step in stage 0
+    e.label("15")
+    step(0, False, False, False, False, True, [])
     e.label("4")
-    return "\n".join(e.lines)
+    assert len(set(e.s_after)) == 1, "both last-step copies leave the same stores after the next-tile loads"
+    wait = NLOAD + e.s_after[0]
+    assert wait < 64, "vmcnt is 6 bits"
+    return "\n".join(e.lines).replace("@NEXT_WAIT@", str(wait))
 
 
 DEFAULT4 = {
@@ -1062,6 +1130,8 @@ DEFAULT4 = {
     "read_every": 1,
     "f0_lat": 8,
     "epi_slot": 8, "epi_delay": 2,
+    "nxt_start": 6,                 # the next tile's step-0 loads in the last step: from this gap ...
+    "nxt_every": 4,                 # ... one every this many gaps
 }
 
 

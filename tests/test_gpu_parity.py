@@ -328,6 +328,34 @@ def test_ring4_partial_first_step(shape):
     assert_parity(host_bits(Ds[0]), ref, K, f"strided {M}x{N}x{K}")
 
 
+@pytest.mark.parametrize("shape", [(8192, 8192, 512), (32768, 4096, 128), (16384, 4096, 192), (8192, 4096, 2040)],
+                         ids=lambda s: "x".join(map(str, s)))
+def test_ring4_consecutive_tiles_bitwise(shape):
+    """Many tiles per workgroup on the fourth form, whose last step loads
+    the next tile's first step (odd step counts swap the stages): every
+    output is bitwise equal to the third form's (rung 8, one tile at a
+    time, the same MFMA sequence per accumulator), on repeated runs."""
+    M, N, K = shape
+    rng = np.random.default_rng(M + N + K)
+    A = torch.from_numpy(rng.uniform(-1, 1, (M, K)).astype(np.float16)).to(DEV)
+    B = torch.from_numpy(rng.uniform(-1, 1, (N, K)).astype(np.float16)).to(DEV)
+    say(f"[gpu] consecutive tiles {M}x{N}x{K}: rung 10 against rung 8")
+    if K % 64 == 0:
+        ref = host_bits(run(8, A, B))
+    else:   # rung 8 needs whole steps: pad each row in front with zeros
+        hk = -K % 64
+        z = torch.zeros((1, hk), dtype=torch.float16, device=DEV)
+        ref = host_bits(run(8, torch.cat([z.expand(M, hk), A], 1).contiguous(), torch.cat([z.expand(N, hk), B], 1).contiguous()))
+    D = torch.full((M, N), float("nan"), dtype=torch.float16, device=DEV)
+    for rep in range(3):
+        got = host_bits(run(10, A, B, D))
+        same = (got == ref) | (((got | ref) & 0x7FFF) == 0)
+        assert same.all(), f"run {rep}: {int((~same).sum())} outputs differ from rung 8"
+    rows, cols = sample_positions(M, N, 500, K)
+    want, _ = oracle.gemm_nt_sampled(A.cpu().numpy(), B.cpu().numpy(), rows, cols)
+    assert_parity(got[rows, cols], want, K, f"{M}x{N}x{K}")
+
+
 def test_non_default_stream_and_interleaving():
     M, N, K = 512, 512, 512
     A, B = rand_case(M, N, K, 79)

@@ -61,11 +61,15 @@ def _regs(spec: str) -> int:
 
 
 class Sim:
-    """Executes one wave's stream of the generated block for KT k steps."""
+    """Executes one wave's stream of the generated block for KT k steps,
+    for `tiles` consecutive tiles of one workgroup (the fourth form carries
+    its ring from tile to tile; the others run one tile)."""
 
-    def __init__(self, text: str, kt: int):
+    def __init__(self, text: str, kt: int, tiles: int = 1, carry: bool = True):
         self.lines = text.split("\n")
         self.kt = kt
+        self.tiles = tiles
+        self.carry = carry      # the fourth form: each last step loads the next tile's step 0
         self.labels: dict[str, list[int]] = {}
         for i, ln in enumerate(self.lines):
             m = re.match(r"^(\d+):$", ln)
@@ -79,213 +83,261 @@ class Sim:
 
     def run(self) -> dict:
         kt = self.kt
-        rem, ko, kh, m0, scc = kt, 0, None, None, 0
-        epoch = 0                      # barriers crossed
-        vm: list[tuple] = []           # outstanding loads (step, stage, n), issue order
-        lgkm: list[tuple] = []         # outstanding reads (reg, content)
-        landed: dict[int, dict] = {0: {}, 1: {}}    # stage -> {n: (step, epoch waited)}
-        visible: dict[int, dict] = {0: {}, 1: {}}   # stage -> {n: step} published
+        # across tiles: the vector-memory queue (loads and stores, issue
+        # order), what each physical stage holds, barriers crossed
+        vm: list[tuple] = []           # ("load", (tile, step), stage, n) | ("store",)
+        landed: dict[int, dict] = {0: {}, 1: {}}    # stage -> {n: (tile, step)} waited for
+        visible: dict[int, dict] = {0: {}, 1: {}}   # stage -> {n: (tile, step)} published
         reads_since_barrier = {0: 0, 1: 0}
-        frag: dict[int, tuple] = {}    # vgpr base -> (step, kk, op, idx) once its read completed
-        acc_started = set()
-        per_block: dict[int, int] = {}  # MFMAs issued per accumulator block
-        loaded_steps: dict[int, set] = {}
+        epoch = 0
         mfma = 0
-        pc = 0
-        final_at: dict[int, int] = {}          # block -> line of its last MFMA
-        since_final: dict[int, int] = {}       # block -> wait states since
-        acc_read: set = set()                  # accumulator registers read
-        vreg: dict[int, tuple] = {}            # epilogue VGPR contents
-        sdo = None
-        head: dict[int, tuple] = {}            # VGPR -> (op, q) of a head-step lane offset
-        epi_pending: list = []                 # staging writes not yet waited: (buf, group, j)
-        staged: dict[int, tuple] = {}          # buf -> (group, set of j) completed
-        stores: list = []
+        loaded_steps: dict[int, set] = {}
+        par = 0                        # physical stage of the tile's logical stage 0
+        first = 1
+        for tile in range(self.tiles):
+            has_next = tile + 1 < self.tiles
+            hasn = int(has_next and self.carry)
+            par_next = par ^ (kt & 1) if hasn else par
+            rem, ko, kh, m0, scc = kt, 0, None, None, 0
+            lgkm: list[tuple] = []         # outstanding reads (reg, content)
+            frag: dict[int, tuple] = {}    # vgpr base -> (tile, step, kk, op, idx) once its read completed
+            acc_started = set()
+            per_block: dict[int, int] = {}  # MFMAs issued per accumulator block
+            pc = 0
+            final_at: dict[int, int] = {}          # block -> line of its last MFMA
+            since_final: dict[int, int] = {}       # block -> wait states since
+            acc_read: set = set()                  # accumulator registers read
+            vreg: dict[int, tuple] = {}            # epilogue VGPR contents
+            sdo = None
+            head: dict = {}                        # VGPR or "ht" -> (op, q) of a step-0 lane offset
+            staged: dict[int, tuple] = {}          # buf -> (group, set of j) completed
+            stores: list = []
 
-        def clobber(v: int) -> None:
-            """A VALU write of v: a fragment held there is gone."""
-            for base in [b for b in frag if b <= v < b + 4]:
-                del frag[base]
+            def clobber(v: int) -> None:
+                """A VALU write of v: a fragment held there is gone."""
+                for base in [b for b in frag if b <= v < b + 4]:
+                    del frag[base]
 
-        while pc < len(self.lines):
-            ln = self.lines[pc]
-            if not ln.startswith("v_mfma"):
-                nop = re.match(r"s_nop (\d+)$", ln)
-                for b_ in since_final:
-                    since_final[b_] += int(nop.group(1)) + 1 if nop else 1
-            if ln.startswith("s_cmp_eq_u32 %[rem], "):
-                scc = int(rem == int(ln.split(",")[1]))
-            elif ln.startswith("s_cbranch_scc1 "):
-                if scc:
+            while pc < len(self.lines):
+                ln = self.lines[pc]
+                if not ln.startswith("v_mfma"):
+                    nop = re.match(r"s_nop (\d+)$", ln)
+                    for b_ in since_final:
+                        since_final[b_] += int(nop.group(1)) + 1 if nop else 1
+                if ln.startswith("s_cmp_eq_u32 %[rem], "):
+                    scc = int(rem == int(ln.split(",")[1]))
+                elif ln == "s_cmp_eq_u32 %[first], 0":
+                    scc = int(first == 0)
+                elif ln == "s_cmp_eq_u32 %[hasn], 0":
+                    scc = int(hasn == 0)
+                elif ln.startswith("s_cbranch_scc1 "):
+                    if scc:
+                        pc = self.target(ln.split()[1], pc)
+                        continue
+                elif ln.startswith("s_branch "):
                     pc = self.target(ln.split()[1], pc)
                     continue
-            elif ln.startswith("s_branch "):
-                pc = self.target(ln.split()[1], pc)
-                continue
-            elif ln.startswith("s_sub_u32 %[rem]"):
-                rem -= 1
-            elif ln.startswith("s_add_u32 %[ko]"):
-                ko += 128
-            elif ln == "s_add_u32 %[kh], %[ko], 128":
-                kh = ko + 128
-            elif ln.startswith("s_add_u32 %[kh], %[kh], "):
-                kh += 128
-            elif ln.startswith("s_add_u32 m0, %[lb], "):
-                m0 = int(ln.split(",")[2])
-            elif ln.startswith("v_or_b32"):
-                # the head step's lane offsets: row group q's reduced offsets
-                # with the head mask of q's parity
-                m = re.match(r"v_or_b32 v(\d+), %\[([ab])x(\d)\], %\[hm(\d)\]$", ln)
-                assert m, ln
-                v, op, q, par = int(m.group(1)), m.group(2), int(m.group(3)), int(m.group(4))
-                assert par == q % 2, f"row group {q} with the head mask of parity {par}"
-                clobber(v)
-                head[v] = (op, q)
-            elif ln.startswith("buffer_load_dwordx4"):
-                m = re.match(r"buffer_load_dwordx4 (?:%\[([ab])([ox])(\d)\]|v(\d+)), %\[rs([ab])\], %\[(k[oh])\] offen( offset:(\d+))? lds$", ln)
-                assert m, ln
-                if m.group(4) is not None:
-                    v = int(m.group(4))
-                    assert v in head, f"load from v{v}, which holds no head offset"
-                    op, q = head[v]
-                    kind = "x"
-                    assert m.group(6) == "ko" and ko == 0, "a head offset used after step 0"
-                else:
-                    op, kind, q = m.group(1), m.group(2), int(m.group(3))
-                rop, koff, imm = m.group(5), m.group(6), int(m.group(8) or 0)
-                assert op == rop, "lane offsets of one operand with the other's buffer"
-                # the immediate offset moves the global address and the LDS
-                # destination alike; the 'x' lane offsets of row group q are
-                # 1024 * (q mod 4) bytes short of the row group's
-                goff = (ko if koff == "ko" else kh) + imm - (1024 * (q % 4) if kind == "x" else 0)
-                assert goff % 128 == 0, f"global offset {goff} is not a k step"
-                step = goff // 128
-                assert 0 <= step < kt, f"load of step {step} beyond K (KT={kt})"
-                dst = m0 + imm
-                assert dst % 1024 == 0 and 0 <= dst < 2 * 65536, f"LDS destination {dst}"
-                st = dst // 65536
-                off = dst % 65536
-                n = 2 * ((off % 32768) // 1024) + (1 if off >= 32768 else 0)
-                assert (op == "a") == (n % 2 == 0), "A/B operand does not match the LDS region"
-                assert (off % 32768) // 1024 == q, f"row group {q} lands at row group {(off % 32768) // 1024}"
-                assert st == step % 2, f"step {step} loaded into stage {st}"
-                assert reads_since_barrier[st] == 0, "load into a stage read since the last barrier"
-                vm.append((step, st, n))
-                loaded_steps.setdefault(step, set()).add(n)
-            elif ln.startswith("s_waitcnt"):
-                m = re.search(r"vmcnt\((\d+)\)", ln)
-                if m:
-                    keep = int(m.group(1))
-                    done, vm = (vm[: len(vm) - keep], vm[len(vm) - keep:]) if keep else (vm, [])
-                    for (step, st, n) in done:
-                        landed[st][n] = (step, epoch)
-                m = re.search(r"lgkmcnt\((\d+)\)", ln)
-                if m:
-                    keep = int(m.group(1))
-                    done, lgkm = (lgkm[: len(lgkm) - keep], lgkm[len(lgkm) - keep:]) if keep else (lgkm, [])
-                    for reg, content in done:
-                        if content[0] == "epi_w":
-                            buf, grp, j = content[1:]
-                            st_ = staged.setdefault(buf, (grp, set()))
-                            if st_[0] != grp:
-                                st_ = (grp, set())
-                            st_[1].add(j)
-                            staged[buf] = st_
-                        elif content[0] == "epi_r":
-                            vreg[reg] = content[1:]
-                        else:
-                            frag[reg] = content
-            elif ln == "s_barrier":
-                assert not lgkm, "barrier with LDS reads in flight"
+                elif ln.startswith("s_sub_u32 %[rem]"):
+                    rem -= 1
+                elif ln.startswith("s_add_u32 %[ko]"):
+                    ko += 128
+                elif ln == "s_add_u32 %[kh], %[ko], 128":
+                    kh = ko + 128
+                elif ln.startswith("s_add_u32 %[kh], %[kh], "):
+                    kh += 128
+                elif ln.startswith("s_add_u32 m0, %[lb], "):
+                    m0 = int(ln.split(",")[2])
+                elif ln.startswith("s_add_u32 m0, %[lb"):
+                    m = re.match(r"s_add_u32 m0, %\[lb([01])\], (\d+)$", ln)
+                    assert m, ln
+                    m0 = (int(m.group(1)) ^ par) * 65536 + int(m.group(2))
+                elif ln.startswith("v_or_b32"):
+                    # a step-0 lane offset: row group q's reduced offsets
+                    # with the head mask of q's parity
+                    m = re.match(r"v_or_b32 (v\d+|%\[ht\]), %\[([ab])x(\d)\], %\[hm(\d)\]$", ln)
+                    assert m, ln
+                    dst, op, q, hp = m.group(1), m.group(2), int(m.group(3)), int(m.group(4))
+                    assert hp == q % 2, f"row group {q} with the head mask of parity {hp}"
+                    if dst.startswith("v"):
+                        clobber(int(dst[1:]))
+                        head[int(dst[1:])] = (op, q)
+                    else:
+                        head["ht"] = (op, q)
+                elif ln.startswith("buffer_load_dwordx4"):
+                    m = re.match(r"buffer_load_dwordx4 (?:%\[([ab])([ox])(\d)\]|v(\d+)|(%\[ht\])), %\[rs([ab])(n?)\], "
+                                 r"(?:%\[(k[oh])\]|(0)) offen( offset:(\d+))? lds$", ln)
+                    assert m, ln
+                    rop, nxt, koff, imm = m.group(6), m.group(7) == "n", m.group(8), int(m.group(11) or 0)
+                    if m.group(4) is not None or m.group(5) is not None:
+                        key = int(m.group(4)) if m.group(4) is not None else "ht"
+                        assert key in head, f"load from {key}, which holds no step-0 offset"
+                        op, q = head[key]
+                        kind = "x"
+                    else:
+                        op, kind, q = m.group(1), m.group(2), int(m.group(3))
+                    assert op == rop, "lane offsets of one operand with the other's buffer"
+                    if nxt:
+                        # the next tile's step 0, from its own buffers, at k offset 0
+                        assert kind == "x" and koff is None and m.group(5) is not None, "next-tile load form"
+                        step, owner = 0, tile + 1
+                    else:
+                        assert koff is not None and m.group(5) is None
+                        if m.group(4) is not None:
+                            assert koff == "ko" and ko == 0, "a step-0 offset used after step 0"
+                        # the immediate offset moves the global address and the
+                        # LDS destination alike; the 'x' lane offsets of row
+                        # group q are 1024 * (q mod 4) bytes short of the row
+                        # group's
+                        goff = (ko if koff == "ko" else kh) + imm - (1024 * (q % 4) if kind == "x" else 0)
+                        assert goff % 128 == 0, f"global offset {goff} is not a k step"
+                        step, owner = goff // 128, tile
+                        assert 0 <= step < kt, f"load of step {step} beyond K (KT={kt})"
+                    dst = m0 + imm
+                    assert dst % 1024 == 0 and 0 <= dst < 2 * 65536, f"LDS destination {dst}"
+                    st = dst // 65536
+                    off = dst % 65536
+                    n = 2 * ((off % 32768) // 1024) + (1 if off >= 32768 else 0)
+                    assert (op == "a") == (n % 2 == 0), "A/B operand does not match the LDS region"
+                    assert (off % 32768) // 1024 == q, f"row group {q} lands at row group {(off % 32768) // 1024}"
+                    want = (par_next if nxt else par) ^ (step % 2)
+                    assert st == want, f"step {step} of tile {owner} loaded into stage {st}, not {want}"
+                    assert reads_since_barrier[st] == 0, "load into a stage read since the last barrier"
+                    assert not nxt or hasn, "next-tile loads in a last step without a next tile"
+                    vm.append(("load", (owner, step), st, n))
+                    if owner == tile:
+                        loaded_steps.setdefault(step, set()).add(n)
+                elif ln.startswith("s_waitcnt"):
+                    m = re.search(r"vmcnt\((\d+)\)", ln)
+                    if m:
+                        keep = int(m.group(1))
+                        done, vm = (vm[: len(vm) - keep], vm[len(vm) - keep:]) if keep else (vm, [])
+                        for op_ in done:
+                            if op_[0] == "load":
+                                landed[op_[2]][op_[3]] = op_[1]
+                    m = re.search(r"lgkmcnt\((\d+)\)", ln)
+                    if m:
+                        keep = int(m.group(1))
+                        done, lgkm = (lgkm[: len(lgkm) - keep], lgkm[len(lgkm) - keep:]) if keep else (lgkm, [])
+                        for reg, content in done:
+                            if content[0] == "epi_w":
+                                buf, grp, j = content[1:]
+                                st_ = staged.setdefault(buf, (grp, set()))
+                                if st_[0] != grp:
+                                    st_ = (grp, set())
+                                st_[1].add(j)
+                                staged[buf] = st_
+                            elif content[0] == "epi_r":
+                                vreg[reg] = content[1:]
+                            else:
+                                frag[reg] = content
+                elif ln == "s_barrier":
+                    assert not lgkm, "barrier with LDS reads in flight"
+                    epoch += 1
+                    reads_since_barrier = {0: 0, 1: 0}
+                    for st in (0, 1):
+                        for n, who in landed[st].items():
+                            visible[st][n] = who
+                        landed[st] = {}
+                elif ln.startswith("ds_read_b128 ") and "%[er" in ln:
+                    m = re.match(r"ds_read_b128 (v\[\d+:\d+\]), %\[er(\d)\] offset:(\d+)$", ln)
+                    reg, q, buf = _regs(m.group(1)), int(m.group(2)), int(m.group(3)) // 4096
+                    for v_ in range(reg, reg + 4):
+                        clobber(v_)
+                    grp, js = staged.get(buf, (None, set()))
+                    assert js == set(range(NB)), f"read-back of buffer {buf} before all its writes completed"
+                    lgkm.append((reg, ("epi_r", grp, q)))
+                elif ln.startswith("ds_write_b64"):
+                    m = re.match(r"ds_write_b64 %\[ew(\d)\], v\[(\d+):(\d+)\] offset:(\d+)$", ln)
+                    j, r0, buf = int(m.group(1)), int(m.group(2)), int(m.group(4)) // 4096
+                    lo, hi = vreg.get(r0), vreg.get(r0 + 1)
+                    assert lo and hi and lo[0] == "pk" and hi[0] == "pk", "staging write of unconverted data"
+                    b0 = lo[1] // 4
+                    assert lo[1] == 4 * b0 and hi[1] == 4 * b0 + 2, "staging write of the wrong accumulator pairs"
+                    grp, jj = b0 // NB, b0 % NB
+                    assert jj == j and buf == grp % 2, f"block {b0} staged at column {j}, buffer {buf}"
+                    if buf in staged and staged[buf][0] != grp:
+                        del staged[buf]
+                    lgkm.append((-1, ("epi_w", buf, grp, j)))
+                elif ln.startswith("v_accvgpr_read_b32"):
+                    m = re.match(r"v_accvgpr_read_b32 v(\d+), a(\d+)$", ln)
+                    v, a = int(m.group(1)), int(m.group(2))
+                    clobber(v)
+                    blk = a // 4
+                    assert blk in final_at and since_final[blk] >= 11, f"accumulator a{a} read too early"
+                    assert a not in acc_read, f"a{a} read twice"
+                    acc_read.add(a)
+                    vreg[v] = ("acc", a)
+                elif ln.startswith("v_cvt_pk_f16_f32"):
+                    m = re.match(r"v_cvt_pk_f16_f32 v(\d+), v(\d+), v(\d+)$", ln)
+                    d_, x, y = int(m.group(1)), int(m.group(2)), int(m.group(3))
+                    clobber(d_)
+                    cx, cy = vreg.get(x), vreg.get(y)
+                    assert cx and cy and cx[0] == "acc" and cy[0] == "acc" and cy[1] == cx[1] + 1, "conversion pair"
+                    vreg[d_] = ("pk", cx[1])
+                elif ln == "s_mov_b32 %[sdo], 0":
+                    sdo = 0
+                elif ln == "s_add_u32 %[sdo], %[sdo], %[gstr]":
+                    sdo += 1
+                elif ln.startswith("buffer_store_dwordx4"):
+                    m = re.match(r"buffer_store_dwordx4 (v\[\d+:\d+\]), %\[so(\d)\], %\[rsd\], %\[sdo\] offen( nt)?$", ln)
+                    reg, q = _regs(m.group(1)), int(m.group(2))
+                    assert vreg.get(reg) == (sdo, q), f"store of {vreg.get(reg)} at group {sdo}, rows {q}"
+                    stores.append((sdo, q))
+                    vm.append(("store",))
+                elif ln.startswith("ds_read_b128"):
+                    m = re.match(r"ds_read_b128 (v\[\d+:\d+\]), %\[r([ab])(\d)(\d)\] offset:(\d+)", ln)
+                    reg, op, ls, kk, off = _regs(m.group(1)), m.group(2), int(m.group(3)), int(m.group(4)), int(m.group(5))
+                    st = ls ^ par
+                    idx = off // 2048
+                    assert not any(o[0] == "load" and o[2] == st for o in vm), \
+                        "read of a stage with a load in flight"
+                    whos = set(visible[st].values())
+                    assert len(visible[st]) == 16 and len(whos) == 1, "read of an incompletely published stage"
+                    who = whos.pop()
+                    assert who[0] == tile, f"tile {tile} reads tile {who}'s data"
+                    reads_since_barrier[st] += 1
+                    frag.pop(reg, None)
+                    lgkm.append((reg, (who[1], kk, op, idx)))
+                elif ln.startswith("v_mfma_f32_16x16x32_f16"):
+                    m = re.match(r"v_mfma_f32_16x16x32_f16 (a\[(\d+):\d+\]), (v\[\d+:\d+\]), (v\[\d+:\d+\]), (\S+)$", ln)
+                    acc, blk, breg, areg, src_c = m.group(1), int(m.group(2)) // 4, _regs(m.group(3)), _regs(m.group(4)), m.group(5)
+                    # each block accumulates k steps in order, sub-step 0 before
+                    # sub-step 1 (whatever the order across blocks)
+                    step, kk = divmod(per_block.get(blk, 0), 2)
+                    per_block[blk] = per_block.get(blk, 0) + 1
+                    assert not any(4 * blk + r in acc_read for r in range(4)), "MFMA on an accumulator already written out"
+                    if step == kt - 1 and kk == 1:
+                        final_at[blk] = pc
+                        since_final[blk] = 0
+                    for b_ in since_final:
+                        since_final[b_] += 4       # an MFMA issue is at least 4 wait states
+                    i, j = blk // NB, blk % NB
+                    assert frag.get(areg) == (step, kk, "a", i), f"MFMA {mfma}: A operand {frag.get(areg)}"
+                    assert frag.get(breg) == (step, kk, "b", j), f"MFMA {mfma}: B operand {frag.get(breg)}"
+                    if step == 0 and kk == 0:
+                        assert src_c == "0" and blk not in acc_started
+                        acc_started.add(blk)
+                    else:
+                        assert src_c == acc and blk in acc_started
+                    mfma += 1
+                pc += 1
+            assert not lgkm, "LDS operations in flight at the end of the block"
+            assert not any(o[0] == "load" and o[1][0] == tile for o in vm), "this tile's loads in flight at its end"
+            assert all(n == 2 * kt for n in per_block.values()) and len(per_block) == NB * NB, "MFMAs per block"
+            assert acc_read == set(range(4 * NB * NB)), "accumulators not all written out"
+            assert sorted(stores) == [(i, q) for i in range(NB) for q in range(4)], "output rows not all stored once"
+            # between tiles: the workgroup barrier after the block
+            if has_next:
                 epoch += 1
                 reads_since_barrier = {0: 0, 1: 0}
                 for st in (0, 1):
-                    for n, (step, _) in landed[st].items():
-                        visible[st][n] = step
+                    for n, who in landed[st].items():
+                        visible[st][n] = who
                     landed[st] = {}
-            elif ln.startswith("ds_read_b128 ") and "%[er" in ln:
-                m = re.match(r"ds_read_b128 (v\[\d+:\d+\]), %\[er(\d)\] offset:(\d+)$", ln)
-                reg, q, buf = _regs(m.group(1)), int(m.group(2)), int(m.group(3)) // 4096
-                for v_ in range(reg, reg + 4):
-                    clobber(v_)
-                grp, js = staged.get(buf, (None, set()))
-                assert js == set(range(NB)), f"read-back of buffer {buf} before all its writes completed"
-                lgkm.append((reg, ("epi_r", grp, q)))
-            elif ln.startswith("ds_write_b64"):
-                m = re.match(r"ds_write_b64 %\[ew(\d)\], v\[(\d+):(\d+)\] offset:(\d+)$", ln)
-                j, r0, buf = int(m.group(1)), int(m.group(2)), int(m.group(4)) // 4096
-                lo, hi = vreg.get(r0), vreg.get(r0 + 1)
-                assert lo and hi and lo[0] == "pk" and hi[0] == "pk", "staging write of unconverted data"
-                b0 = lo[1] // 4
-                assert lo[1] == 4 * b0 and hi[1] == 4 * b0 + 2, "staging write of the wrong accumulator pairs"
-                grp, jj = b0 // NB, b0 % NB
-                assert jj == j and buf == grp % 2, f"block {b0} staged at column {j}, buffer {buf}"
-                if buf in staged and staged[buf][0] != grp:
-                    del staged[buf]
-                lgkm.append((-1, ("epi_w", buf, grp, j)))
-            elif ln.startswith("v_accvgpr_read_b32"):
-                m = re.match(r"v_accvgpr_read_b32 v(\d+), a(\d+)$", ln)
-                v, a = int(m.group(1)), int(m.group(2))
-                clobber(v)
-                blk = a // 4
-                assert blk in final_at and since_final[blk] >= 11, f"accumulator a{a} read too early"
-                assert a not in acc_read, f"a{a} read twice"
-                acc_read.add(a)
-                vreg[v] = ("acc", a)
-            elif ln.startswith("v_cvt_pk_f16_f32"):
-                m = re.match(r"v_cvt_pk_f16_f32 v(\d+), v(\d+), v(\d+)$", ln)
-                d_, x, y = int(m.group(1)), int(m.group(2)), int(m.group(3))
-                clobber(d_)
-                cx, cy = vreg.get(x), vreg.get(y)
-                assert cx and cy and cx[0] == "acc" and cy[0] == "acc" and cy[1] == cx[1] + 1, "conversion pair"
-                vreg[d_] = ("pk", cx[1])
-            elif ln == "s_mov_b32 %[sdo], 0":
-                sdo = 0
-            elif ln == "s_add_u32 %[sdo], %[sdo], %[gstr]":
-                sdo += 1
-            elif ln.startswith("buffer_store_dwordx4"):
-                m = re.match(r"buffer_store_dwordx4 (v\[\d+:\d+\]), %\[so(\d)\], %\[rsd\], %\[sdo\] offen( nt)?$", ln)
-                reg, q = _regs(m.group(1)), int(m.group(2))
-                assert vreg.get(reg) == (sdo, q), f"store of {vreg.get(reg)} at group {sdo}, rows {q}"
-                stores.append((sdo, q))
-            elif ln.startswith("ds_read_b128"):
-                m = re.match(r"ds_read_b128 (v\[\d+:\d+\]), %\[r([ab])(\d)(\d)\] offset:(\d+)", ln)
-                reg, op, st, kk, off = _regs(m.group(1)), m.group(2), int(m.group(3)), int(m.group(4)), int(m.group(5))
-                idx = off // 2048
-                assert not any(s == st for (_, s, _) in vm), "read of a stage with a load in flight"
-                steps = set(visible[st].values())
-                assert len(visible[st]) == 16 and len(steps) == 1, "read of an incompletely published stage"
-                step = steps.pop()
-                reads_since_barrier[st] += 1
-                frag.pop(reg, None)
-                lgkm.append((reg, (step, kk, op, idx)))
-            elif ln.startswith("v_mfma_f32_16x16x32_f16"):
-                m = re.match(r"v_mfma_f32_16x16x32_f16 (a\[(\d+):\d+\]), (v\[\d+:\d+\]), (v\[\d+:\d+\]), (\S+)$", ln)
-                acc, blk, breg, areg, src_c = m.group(1), int(m.group(2)) // 4, _regs(m.group(3)), _regs(m.group(4)), m.group(5)
-                # each block accumulates k steps in order, sub-step 0 before
-                # sub-step 1 (whatever the order across blocks)
-                step, kk = divmod(per_block.get(blk, 0), 2)
-                per_block[blk] = per_block.get(blk, 0) + 1
-                assert not any(4 * blk + r in acc_read for r in range(4)), "MFMA on an accumulator already written out"
-                if step == kt - 1 and kk == 1:
-                    final_at[blk] = pc
-                    since_final[blk] = 0
-                for b_ in since_final:
-                    since_final[b_] += 4       # an MFMA issue is at least 4 wait states
-                i, j = blk // NB, blk % NB
-                assert frag.get(areg) == (step, kk, "a", i), f"MFMA {mfma}: A operand {frag.get(areg)}"
-                assert frag.get(breg) == (step, kk, "b", j), f"MFMA {mfma}: B operand {frag.get(breg)}"
-                if step == 0 and kk == 0:
-                    assert src_c == "0" and blk not in acc_started
-                    acc_started.add(blk)
-                else:
-                    assert src_c == acc and blk in acc_started
-                mfma += 1
-            pc += 1
-        assert not vm and not lgkm, "operations in flight at the end of the block"
-        assert all(n == 2 * kt for n in per_block.values()) and len(per_block) == NB * NB, "MFMAs per block"
-        assert acc_read == set(range(4 * NB * NB)), "accumulators not all written out"
-        assert sorted(stores) == [(i, q) for i in range(NB) for q in range(4)], "output rows not all stored once"
+                par = par_next
+                first = 0 if hasn else 1
+        if self.tiles == 1:
+            assert not any(o[0] == "load" for o in vm), "loads in flight at the end"
         return {"mfma": mfma, "epoch": epoch, "acc": acc_started, "loaded": loaded_steps}
 
 
@@ -433,15 +485,54 @@ def test_simulator_catches_a_swapped_head_offset():
 
 
 def test_head_step_loads_are_step_zeros_only():
-    """The fourth form reads every step-0 row group through its head
-    offset (and no later step does)."""
+    """The fourth form reads every step-0 row group through a masked
+    offset: its own prologue's (first tile) into v64..v79, and the next
+    tile's from the last step (both copies) through %[ht]; no later step
+    does."""
     lines = GEN.generate4(GEN.DEFAULT4).split("\n")
-    ors = [ln for ln in lines if ln.startswith("v_or_b32")]
-    assert len(ors) == GEN.NLOAD
-    head_loads = [ln for ln in lines if re.match(r"buffer_load_dwordx4 v\d+,", ln)]
-    assert len(head_loads) == GEN.NLOAD
-    first_other = next(i for i, ln in enumerate(lines) if ln.startswith("buffer_load_dwordx4 %["))
-    assert all(lines.index(ln) < first_other for ln in head_loads)
+    own = [ln for ln in lines if re.match(r"v_or_b32 v\d+,", ln)]
+    nxt = [ln for ln in lines if ln.startswith("v_or_b32 %[ht]")]
+    assert len(own) == GEN.NLOAD and len(nxt) == 2 * GEN.NLOAD
+    head_loads = [n for n, ln in enumerate(lines) if re.match(r"buffer_load_dwordx4 v\d+,", ln)]
+    next_loads = [n for n, ln in enumerate(lines) if ln.startswith("buffer_load_dwordx4 %[ht]")]
+    assert len(head_loads) == GEN.NLOAD and len(next_loads) == 2 * GEN.NLOAD
+    first_other = next(n for n, ln in enumerate(lines) if ln.startswith("buffer_load_dwordx4 %["))
+    assert max(head_loads) < first_other < min(next_loads)
+    last_steps = [lines.index("2:"), lines.index("3:")]
+    assert all(n > min(last_steps) for n in next_loads)
+
+
+@pytest.mark.parametrize("kt", [2, 3, 4, 5, 8, 9])
+@pytest.mark.parametrize("tiles", [2, 3, 4])
+def test_fourth_form_carries_the_ring_across_tiles(kt, tiles):
+    """Consecutive tiles of a workgroup: each later tile's step 0 is loaded
+    during the last step of the tile before, into the stage that step does
+    not read (the logical stages swap when KT is odd), and waited for with
+    that tile's late stores still in flight; every tile reads only its own
+    data."""
+    for carry in (True, False):
+        res = Sim(GEN.generate4(GEN.DEFAULT4), kt, tiles, carry).run()
+        assert res["mfma"] == 2 * NB * NB * kt * tiles
+        assert sorted(res["loaded"]) == list(range(kt))
+
+
+def test_simulator_catches_a_short_next_tile_wait():
+    """Waiting for fewer operations than were issued after the next tile's
+    step-0 loads reads a stage before those loads have landed."""
+    text = GEN.generate4(GEN.DEFAULT4)
+    m = re.search(r"12:\ns_waitcnt vmcnt\((\d+)\)", text)
+    planted = text.replace(m.group(0), f"12:\ns_waitcnt vmcnt({int(m.group(1)) + 1})", 1)
+    with pytest.raises(AssertionError):
+        Sim(planted, 3, 2).run()
+
+
+def test_simulator_catches_next_tile_loads_into_the_busy_stage():
+    """The next tile's step 0 into the stage the last step still reads."""
+    text = GEN.generate4(GEN.DEFAULT4)
+    last = text.index("\n2:\n")
+    body = text[last:].replace("s_add_u32 m0, %[lb0], 0\n", "s_add_u32 m0, %[lb1], 0\n", 1)
+    with pytest.raises(AssertionError):
+        Sim(text[:last] + body, 4, 2).run()
 
 
 def _chunk(w: int, lane: int, q: int) -> int:
