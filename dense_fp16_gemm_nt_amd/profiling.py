@@ -24,6 +24,7 @@ import glob
 import hashlib
 import json
 import os
+import re
 import statistics
 import sys
 
@@ -32,11 +33,21 @@ KERNEL_SOURCES = ["common.hpp", "sched.hpp", "ladder.hpp", "ring.hpp", "ring4.hp
                   "persistent_ws.hpp", "gemm_f16_nt.hip"]
 
 
+def _code_only(text: str) -> str:
+    """Source text without comments and blank lines (the kernels' sources
+    hold no comment markers inside string literals)."""
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", "", text)
+    return "\n".join(ln.rstrip() for ln in text.split("\n") if ln.strip())
+
+
 def kernel_source_hash() -> str:
+    """Hash of the code (comments aside) of the sources the kernels are
+    built from: a profile summary is current when it carries this hash."""
     h = hashlib.sha256()
     for name in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, "dense_fp16_gemm_nt_amd", "csrc", name), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, "dense_fp16_gemm_nt_amd", "csrc", name), encoding="utf-8") as f:
+            h.update(_code_only(f.read()).encode())
     return h.hexdigest()[:16]
 
 
