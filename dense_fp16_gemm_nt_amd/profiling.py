@@ -8,6 +8,9 @@
       HBM bytes per dispatch of the kernel from FETCH_SIZE / WRITE_SIZE
       passes (KiB per dispatch), each scaled by what the same counter reads
       for a device copy of known size
+  python -m dense_fp16_gemm_nt_amd.profiling power --steps N --workload NAME --command CMD --out FILE
+      socket power and per-XCD shader clocks (amd-smi) sampled while
+      bench.py runs N back-to-back launches in a child process
   python -m dense_fp16_gemm_nt_amd.profiling counters --dir D --trace T --traffic F --flop X --kernel SUBSTR
       --workload NAME --rung NAME --cus N --command CMD --out FILE
       matrix-core and LDS figures per dispatch from one counter pass
@@ -26,7 +29,9 @@ import json
 import os
 import re
 import statistics
+import subprocess
 import sys
+import time
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 KERNEL_SOURCES = ["common.hpp", "sched.hpp", "ladder.hpp", "ring.hpp", "ring4.hpp", "ring4_sched.inc",
@@ -154,6 +159,56 @@ def cmd_counters(a):
     print(json.dumps(rec, indent=1))
 
 
+def _smi_sample():
+    """Socket power (W) and the per-XCD shader clocks (MHz) of GPU 0 from
+    one `amd-smi metric -p -c --json` call."""
+    out = subprocess.run(["amd-smi", "metric", "-p", "-c", "--json"], capture_output=True, text=True,
+                         timeout=30).stdout
+    d = json.loads(out)
+    g = d["gpu_data"][0] if isinstance(d, dict) else d[0]
+    clocks = g["clock"]
+    gfx = [clocks[f"gfx_{i}"]["clk"]["value"] for i in range(XCDS) if isinstance(clocks.get(f"gfx_{i}", {}).get("clk"), dict)]
+    return g["power"]["socket_power"]["value"], gfx
+
+
+def cmd_power(a):
+    """Run the bench (a child process: this one never touches the GPU) and
+    sample the board's socket power and per-XCD clocks while it runs."""
+    cmd = [sys.executable, os.path.join(ROOT, "bench.py"), "--steps", str(a.steps), "--warmup", "100",
+           "--no-cpu-baseline", "--workload", a.workload]
+    child = subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.PIPE, text=True)
+    samples = []
+    t0 = time.time()
+    while child.poll() is None and len(samples) < a.samples + 64:
+        try:
+            samples.append((round(time.time() - t0, 2),) + _smi_sample())
+        except (subprocess.SubprocessError, ValueError, KeyError, IndexError, TypeError):
+            pass
+        time.sleep(a.interval)
+    out, err = child.communicate()
+    if child.returncode != 0:
+        raise SystemExit(f"bench failed ({child.returncode}): {err[-2000:]}")
+    bench = json.loads(out.strip().splitlines()[-1])
+    # samples taken under load: power within 25% of the highest sample
+    top = max(p for _, p, _ in samples)
+    busy = [x for x in samples if x[1] >= 0.75 * top]
+    clocks = [statistics.mean(c[i] for _, _, c in busy) for i in range(len(busy[0][2]))] if busy else []
+    rec = {
+        "workload": a.workload, "bench_value_tflops": bench["value"], "bench_ms_per_step": bench["ms_per_step"],
+        "bench_steps": a.steps,
+        "samples_under_load": len(busy), "samples_total": len(samples),
+        "socket_power_w_mean": round(statistics.mean(p for _, p, _ in busy), 1),
+        "socket_power_w_min": min(p for _, p, _ in busy), "socket_power_w_max": max(p for _, p, _ in busy),
+        "xcd_clock_mhz_mean": [round(c) for c in clocks],
+        "clock_mhz_mean_all_xcds": round(statistics.mean(clocks), 1) if clocks else None,
+        "samples": samples,
+        "kernel_src_sha": kernel_source_hash(),
+        "command": a.command,
+    }
+    open(a.out, "w").write(json.dumps(rec, indent=1) + "\n")
+    print(json.dumps({k: v for k, v in rec.items() if k != "samples"}, indent=1))
+
+
 def main(argv=None):
     p = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     sub = p.add_subparsers(dest="cmd", required=True)
@@ -183,8 +238,15 @@ def main(argv=None):
     c.add_argument("--rung", required=True)
     c.add_argument("--command", required=True)
     c.add_argument("--out", required=True)
+    w = sub.add_parser("power")
+    w.add_argument("--steps", type=int, default=100000)
+    w.add_argument("--workload", default="square_4096")
+    w.add_argument("--samples", type=int, default=16)
+    w.add_argument("--interval", type=float, default=0.4)
+    w.add_argument("--command", required=True)
+    w.add_argument("--out", required=True)
     a = p.parse_args(argv)
-    {"stats": cmd_stats, "traffic": cmd_traffic, "counters": cmd_counters}[a.cmd](a)
+    {"stats": cmd_stats, "traffic": cmd_traffic, "counters": cmd_counters, "power": cmd_power}[a.cmd](a)
 
 
 if __name__ == "__main__":
