@@ -194,6 +194,12 @@ def suite(args):
         if w.kind == "gemm":
             def step():
                 return L.gemm_f16_nt(w.M, w.N, w.K, a, b, d, s_ptr)
+        elif w.kind == "splitk":
+            ws_bytes = max(16, g.splitk_workspace_bytes(w.M, w.N, w.K, 0))
+            ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+
+            def step():
+                return L.gemm_f16_nt_splitk(w.M, w.N, w.K, a, b, d, 0, ws.data_ptr(), ws_bytes, s_ptr)
         else:
             def step():
                 return L.gemm_f16_nt_strided_batched(w.M, w.N, w.K, a, lda, sa, b, ldb, sb, d, w.N, w.M * w.N,
@@ -244,12 +250,29 @@ def suite(args):
                     "frac": round(tflops / PEAK_FP16_TFLOPS, 4)}
         roof["traffic"] = None
         roof["kernel_src_sha"] = kernel_source_hash()
+        extra = {}
+        if w.kind == "splitk":
+            # context: the same product on gemm_f16_nt (no split)
+            def plain():
+                return L.gemm_f16_nt(w.M, w.N, w.K, a, b, d, s_ptr)
+            for _ in range(max(3, steps // 10)):
+                bad |= plain()
+            e0.record(stream)
+            for _ in range(steps):
+                bad |= plain()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            if bad:
+                raise SystemExit(f"{name}: gemm_f16_nt returned an error")
+            m_top, sl = g.splitk_plan(w.M, w.N, w.K, torch.cuda.get_device_properties(dev).multi_processor_count)
+            extra = {"plain_us_per_launch": round(e0.elapsed_time(e1) * 1e3 / steps, 3), "rows_unsplit": m_top,
+                     "slices": sl}
         print(json.dumps({
             "suite": "extra", "workload": w.name, "kind": w.kind, "batch": w.batch, "M": w.M, "N": w.N, "K": w.K,
             "value": round(tflops, 2), "unit": "TFLOP/s", "us_per_launch": round(launch_s * 1e6, 3),
             "steps": steps, "compulsory_bytes": w.min_bytes, "compulsory_gbs": round(gbs, 1),
             "flop_per_byte": round(w.flop / w.min_bytes, 2), "roofline": roof, "dtype": "f16",
-            "data": "synthetic"}), flush=True)
+            "data": "synthetic", **extra}), flush=True)
         del A, B, D
         torch.cuda.empty_cache()
 

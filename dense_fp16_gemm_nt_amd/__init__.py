@@ -77,6 +77,8 @@ def lib() -> ctypes.CDLL:
             L.gemm_f16_nt_status_string.argtypes = [i32]
             L.gemm_f16_nt_schedule.restype = i64
             L.gemm_f16_nt_schedule.argtypes = [i64, i64, i64, i64p, i64p, i64p, i64]
+            L.gemm_f16_nt_splitk_plan.restype = i32
+            L.gemm_f16_nt_splitk_plan.argtypes = [i64, i64, i64, i32, i64p, i64p]
             L.gemm_f16_nt_ring_plan.restype = i32
             L.gemm_f16_nt_ring_plan.argtypes = [i32, i64, ctypes.POINTER(ctypes.c_int), i64p, i64p]
             _lib = L
@@ -222,6 +224,16 @@ def attention_scores(Q, Kt):
         sl = tuple(idx)
         gemm_f16_nt_strided_batched(Q[sl], Kt[sl], S[sl])
     return S
+
+
+def splitk_plan(M: int, N: int, K: int, cus: int):
+    """(m_top, splits) that gemm_f16_nt_splitk with splits = 0 chooses on a
+    device with `cus` compute units (host evaluation, no GPU needed)."""
+    m_top, splits = ctypes.c_int64(), ctypes.c_int64()
+    st = lib().gemm_f16_nt_splitk_plan(int(M), int(N), int(K), int(cus), ctypes.byref(m_top), ctypes.byref(splits))
+    if st != OK:
+        raise GemmError(st, "gemm_f16_nt_splitk_plan")
+    return m_top.value, splits.value
 
 
 def splitk_workspace_bytes(M: int, N: int, K: int, splits: int = 0) -> int:

@@ -334,6 +334,53 @@ void split_plan(int64_t K, int64_t splits, int64_t* k_chunk, int64_t* n_slices)
     *n_slices = (K + *k_chunk - 1) / *k_chunk;
 }
 
+// Shapes with at least one full round of 256 x 256 tiles and a small last
+// round: the top rows that fill whole rounds run whole on the four-wave
+// ring, and the remaining rows split K, so that the last round's work is
+// shared by every compute unit instead of a few.  A cost model in units of
+// one four-wave k step per tile picks the slice count; the split is taken
+// when it models at most kHybridGain of the unsplit time.  Measured on
+// MI355X: the rows split K on the 8-wave ring at ~0.78 of the four-wave
+// ring's rate, and its partial sums (written once, read once) move at ~8
+// TB/s from the last-level cache, ~10 MB per step time.
+constexpr double kHybridGain = 0.90;
+constexpr double kSplitSlowdown = 1.28;
+constexpr double kBytesPerStepTime = 10.3e6;
+constexpr double kSplitFixedSteps = 6.7;   // two more launches and a slice's prologue and epilogue
+
+bool hybrid_plan(int64_t M, int64_t N, int64_t K, int cus, int64_t* m_top, int64_t* splits)
+{
+    if (K % 8 != 0 || !ring4_paired_shape(ring4::C::BM, N, K, K, K)) return false;
+    const int64_t tm = (M + kFastTile - 1) / kFastTile, tn = (N + kFastTile - 1) / kFastTile;
+    const int64_t tiles = tm * tn, kt = (K + RingCfg::BK - 1) / RingCfg::BK;
+    const int64_t rounds = tiles / cus;
+    if (rounds < 1 || tiles % cus == 0) return false;
+    const int64_t r_top = rounds * cus / tn;   // whole tile rows that fit in whole rounds
+    if (r_top < 1 || r_top >= tm) return false;
+    const int64_t m_rest = M - r_top * kFastTile;
+    const int64_t t_rest = (m_rest + kFastTile - 1) / kFastTile * tn;
+    const double plain = (double)((tiles + cus - 1) / cus * kt);
+    const double top = (double)((r_top * tn + cus - 1) / cus * kt);
+    double best = kHybridGain * plain;
+    int64_t best_s = 0;
+    for (int64_t sl = 2; sl <= kMaxSplits && sl <= kt / kMinStepsPerSlice; ++sl) {
+        int64_t k_chunk = 0, n_slices = 0;
+        split_plan(K, sl, &k_chunk, &n_slices);
+        const double rounds_sk = (double)((t_rest * n_slices + cus - 1) / cus);
+        const double bytes = (2.0 * (double)n_slices + 0.5) * (double)m_rest * (double)N * 4.0;
+        const double t = top + rounds_sk * (double)(k_chunk / RingCfg::BK) * kSplitSlowdown +
+                         bytes / kBytesPerStepTime + kSplitFixedSteps;
+        if (t < best) {
+            best = t;
+            best_s = sl;
+        }
+    }
+    if (best_s == 0) return false;
+    *m_top = r_top * kFastTile;
+    *splits = best_s;
+    return true;
+}
+
 int launch_splitk(int64_t M, int64_t N, int64_t K, const void* A, const void* B, void* D, int64_t splits,
                   float* P, hipStream_t s)
 {
@@ -525,16 +572,17 @@ int gemm_f16_nt_strided_batched(int64_t M, int64_t N, int64_t K, const void* A, 
 int64_t gemm_f16_nt_splitk_workspace(int64_t M, int64_t N, int64_t K, int splits)
 {
     if (M < 0 || N < 0 || K < 0 || splits < 0 || splits > kMaxSplits) return GEMM_F16_NT_INVALID_ARG;
-    int64_t s = splits;
+    int64_t s = splits, m_top = 0;
     if (s == 0) {
         int cus = 0;
         if (device_info(&cus) != GEMM_F16_NT_OK) return GEMM_F16_NT_DEVICE;
         s = choose_splits(M, N, K, cus);
+        if (s <= 1 && !hybrid_plan(M, N, K, cus, &m_top, &s)) m_top = 0;
     }
     if (s <= 1 || K == 0 || K % 8 != 0) return 0;
     int64_t k_chunk = 0, n_slices = 0;
     split_plan(K, s, &k_chunk, &n_slices);
-    return n_slices > 1 ? n_slices * M * N * 4 : 0;
+    return n_slices > 1 ? n_slices * (M - m_top) * N * 4 : 0;
 }
 
 int gemm_f16_nt_splitk(int64_t M, int64_t N, int64_t K, const void* A, const void* B, void* D, int splits,
@@ -550,17 +598,25 @@ int gemm_f16_nt_splitk(int64_t M, int64_t N, int64_t K, const void* A, const voi
     hipStream_t s = (hipStream_t)stream;
     if (K == 0) return launch_fill_zero(D, M * N, s);
     if (!fast_operands(K, K, K, 0, 0, A, B, D)) return launch_any(contiguous_args(M, N, K, A, B, D), s);
-    const int64_t want = splits == 0 ? choose_splits(M, N, K, cus) : splits;
+    int64_t want = splits == 0 ? choose_splits(M, N, K, cus) : splits, m_top = 0;
+    if (splits == 0 && want <= 1 && !hybrid_plan(M, N, K, cus, &m_top, &want)) m_top = 0;
     int64_t k_chunk = 0, n_slices = 1;
     if (want > 1) split_plan(K, want, &k_chunk, &n_slices);
     if (n_slices <= 1) return launch_ring(contiguous_args(M, N, K, A, B, D), s, kDefaultRing4);
-    const int64_t need = n_slices * M * N * 4;
+    // rows [m_top, M) split K; rows [0, m_top) (whole rounds of tiles) do not
+    const int64_t m_rest = M - m_top;
+    const int64_t need = n_slices * m_rest * N * 4;
     if (workspace == nullptr || workspace_bytes < need) return GEMM_F16_NT_INVALID_ARG;
     if ((uintptr_t)workspace & 15) return GEMM_F16_NT_UNSUPPORTED;
     if (overlaps(workspace, need, A, M * K * 2) || overlaps(workspace, need, B, N * K * 2) ||
         overlaps(workspace, need, D, M * N * 2))
         return GEMM_F16_NT_INVALID_ARG;
-    return launch_splitk(M, N, K, A, B, D, want, (float*)workspace, s);
+    if (m_top > 0) {
+        st = launch_ring(contiguous_args(m_top, N, K, A, B, D), s, kDefaultRing4);
+        if (st != GEMM_F16_NT_OK) return st;
+    }
+    return launch_splitk(m_rest, N, K, (const f16*)A + m_top * K, B, (f16*)D + m_top * N, want, (float*)workspace,
+                         s);
 }
 
 int gemm_f16_nt_check_strided(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, int64_t stride_a,
@@ -609,6 +665,18 @@ int64_t gemm_f16_nt_schedule(int64_t M, int64_t N, int64_t num_workgroups, int64
             ++n;
         }
     return n;
+}
+
+int gemm_f16_nt_splitk_plan(int64_t M, int64_t N, int64_t K, int cus, int64_t* m_top, int64_t* splits)
+{
+    if (M < 0 || N < 0 || K < 0 || cus < 1 || m_top == nullptr || splits == nullptr) return GEMM_F16_NT_INVALID_ARG;
+    *m_top = 0;
+    *splits = choose_splits(M, N, K, cus);
+    if (*splits <= 1 && !hybrid_plan(M, N, K, cus, m_top, splits)) {
+        *m_top = 0;
+        *splits = 1;
+    }
+    return GEMM_F16_NT_OK;
 }
 
 int gemm_f16_nt_ring_plan(int depth, int64_t steps, int* stage, int64_t* lap, int64_t* refill)

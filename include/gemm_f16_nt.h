@@ -118,7 +118,10 @@ int gemm_f16_nt_strided_batched(int64_t M, int64_t N, int64_t K, const void* A, 
  * into `splits` slices of whole 64-wide steps (0 = the library's choice,
  * at most 64), each slice's fp32 partial sums go to `workspace`, and a
  * second kernel adds the slices in slice order and rounds once to fp16 --
- * the single rounding at writeback is kept.  The fp32 summation order
+ * the single rounding at writeback is kept.  With splits = 0 the library
+ * also splits products whose 256 x 256 tiles fill whole rounds of the
+ * compute units plus a small last round: the top rows that fill the whole
+ * rounds run unsplit and only the remaining rows split K.  The fp32 summation order
  * differs from gemm_f16_nt's (any order is within the contract).
  * `workspace` is caller-owned device memory of at least
  * gemm_f16_nt_splitk_workspace(M, N, K, splits) bytes, 16-byte aligned,
@@ -159,6 +162,11 @@ int64_t gemm_f16_nt_schedule(int64_t M, int64_t N, int64_t num_workgroups, int64
  * refill[k] = the step loaded into stage[k] once step k is consumed (-1 if
  * none).  Returns 0 or a negative status. */
 int gemm_f16_nt_ring_plan(int depth, int64_t steps, int* stage, int64_t* lap, int64_t* refill);
+/* Host evaluation of gemm_f16_nt_splitk's choice for `splits` = 0 on a
+ * device with `cus` compute units, no HIP call: *m_top rows (0 or a
+ * multiple of 256) run unsplit, the other M - *m_top rows split K into
+ * *splits slices (1: no split).  Returns 0 or a negative status. */
+int gemm_f16_nt_splitk_plan(int64_t M, int64_t N, int64_t K, int cus, int64_t* m_top, int64_t* splits);
 
 #ifdef __cplusplus
 }

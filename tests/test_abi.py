@@ -225,6 +225,33 @@ def test_splitk_workspace_sizes():
     assert L.gemm_f16_nt_splitk_workspace(-1, 256, 512, 2) == g.INVALID_ARG
 
 
+@pytest.mark.parametrize("shape,cus,want", [
+    ((6144, 6144, 6144), 256, (5376, 3)),     # 2.25 rounds: 21 tile rows whole, 768 rows split 3 ways
+    ((4352, 4352, 4096), 256, (3840, 6)),
+    ((4096, 4096, 4096), 256, (0, 1)),        # whole rounds: no split
+    ((8192, 8192, 8192), 256, (0, 1)),
+    ((6144, 6144, 2048), 256, (0, 1)),        # short K: the split costs more than the last round
+    ((256, 256, 65536), 256, (0, 64)),        # tile-starved: every row splits
+])
+def test_splitk_plan(shape, cus, want):
+    assert g.splitk_plan(*shape, cus) == want
+
+
+@pytest.mark.parametrize("M,N,K", [(6144, 6144, 6144), (4352, 4352, 4096), (4500, 4352, 4096), (7168, 7168, 4096),
+                                   (10000, 3000, 8192), (3000, 10000, 1024)])
+@pytest.mark.parametrize("cus", [80, 256, 304])
+def test_splitk_plan_invariants(M, N, K, cus):
+    """Unsplit rows are whole 256-row tile rows that fit in whole rounds of
+    the compute units; the split rows take at least two slices."""
+    m_top, splits = g.splitk_plan(M, N, K, cus)
+    tn = (N + 255) // 256
+    tiles = (M + 255) // 256 * tn
+    assert m_top % 256 == 0 and 0 <= m_top < M
+    if m_top:
+        assert m_top // 256 * tn <= tiles // cus * cus and splits >= 2
+        assert tiles % cus != 0
+
+
 def test_splitk_argument_errors_before_any_device_work():
     L = g.lib()
     assert L.gemm_f16_nt_splitk(256, 256, 512, A0, B0, D0, -1, None, 0, None) == g.INVALID_ARG

@@ -557,6 +557,33 @@ def test_splitk(case):
     assert np.array_equal(host_bits(D), first)        # fixed slice order: repeatable
 
 
+@pytest.mark.parametrize("shape", [(4352, 4352, 4096), (4500, 4352, 4096)], ids=lambda s: "x".join(map(str, s)))
+def test_splitk_whole_rounds_plus_split_rows(shape):
+    """The library's split for a small last round of tiles: the top rows
+    run unsplit, the rest split K (ragged M included).  Sampled outputs
+    (rows on both sides of the boundary among them) against the oracle;
+    every output written; repeatable."""
+    M, N, K = shape
+    m_top, splits = g.splitk_plan(M, N, K, torch.cuda.get_device_properties(0).multi_processor_count)
+    assert m_top > 0 and splits > 1, (m_top, splits)
+    A, B = rand_case(M, N, K, 600 + M)
+    dA, dB = dev(A), dev(B)
+    D = torch.full((M, N), float("nan"), dtype=torch.float16, device=DEV)
+    say(f"[gpu] split-K whole rounds {M}x{N}x{K}: {m_top} rows unsplit, {splits} slices")
+    g.gemm_f16_nt_splitk(dA, dB, D)
+    torch.cuda.synchronize()
+    assert not torch.isnan(D).any().item()
+    rows, cols = sample_positions(M, N, 2000, M + K)
+    rows = np.concatenate([rows, np.full(64, m_top - 1), np.full(64, m_top), np.full(64, M - 1)])
+    cols = np.concatenate([cols, np.random.default_rng(5).integers(0, N, 192)])
+    want, _ = oracle.gemm_nt_sampled(A, B, rows, cols)
+    got = host_bits(D)
+    assert_parity(got[rows, cols], want, K, f"split rows {shape}")
+    g.gemm_f16_nt_splitk(dA, dB, D)
+    torch.cuda.synchronize()
+    assert np.array_equal(host_bits(D), got)
+
+
 def test_splitk_exact_pins():
     """Small integers: every fp32 partial and their sum are exact, so the
     split result equals the oracle bit for bit; all-ones gives K."""
@@ -601,6 +628,8 @@ def test_extra_workloads_sampled(name):
     D = torch.full((w.batch, w.M, w.N), float("nan"), dtype=torch.float16, device=DEV)
     if w.kind == "gemm":
         g.gemm_f16_nt(dev(A3[0]), dev(B3[0]), D[0])
+    elif w.kind == "splitk":
+        g.gemm_f16_nt_splitk(dev(A3[0]), dev(B3[0]), D[0])
     elif w.kind == "heads_rows":
         # (S, H, d) storage read as H products: leading dimension H*d, batch stride d
         A = dev(A3.transpose(1, 0, 2)).transpose(0, 1)

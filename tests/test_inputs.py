@@ -75,7 +75,7 @@ def test_extra_workloads_are_well_formed():
     names = [w.name for w in workloads.EXTRA_WORKLOADS]
     assert len(set(names)) == len(names)
     for w in workloads.EXTRA_WORKLOADS:
-        assert w.kind in ("gemm", "strided", "heads_rows")
+        assert w.kind in ("gemm", "splitk", "strided", "heads_rows")
         assert w.batch >= 1 and min(w.M, w.N, w.K) >= 1
-        assert w.kind != "gemm" or w.batch == 1
+        assert w.kind not in ("gemm", "splitk") or w.batch == 1
         assert w.flop == 2 * w.batch * w.M * w.N * w.K
