@@ -77,6 +77,9 @@ def lib() -> ctypes.CDLL:
             L.gemm_f16_nt_status_string.argtypes = [i32]
             L.gemm_f16_nt_schedule.restype = i64
             L.gemm_f16_nt_schedule.argtypes = [i64, i64, i64, i64p, i64p, i64p, i64]
+            L.gemm_f16_nt_plan.restype = i32
+            L.gemm_f16_nt_plan.argtypes = [i64, i64, i64, i32, ctypes.POINTER(ctypes.c_int), i64p,
+                                           ctypes.POINTER(ctypes.c_int)]
             L.gemm_f16_nt_splitk_plan.restype = i32
             L.gemm_f16_nt_splitk_plan.argtypes = [i64, i64, i64, i32, i64p, i64p]
             L.gemm_f16_nt_ring_plan.restype = i32
@@ -224,6 +227,17 @@ def attention_scores(Q, Kt):
         sl = tuple(idx)
         gemm_f16_nt_strided_batched(Q[sl], Kt[sl], S[sl])
     return S
+
+
+def plan(M: int, N: int, K: int, cus: int):
+    """(rung_top, m_top, rung_rest) that gemm_f16_nt chooses for contiguous
+    aligned operands on a device with `cus` compute units (host evaluation):
+    rows [0, m_top) on rung_top, the rest on rung_rest (0: none)."""
+    rt, mt, rr = ctypes.c_int(), ctypes.c_int64(), ctypes.c_int()
+    st = lib().gemm_f16_nt_plan(int(M), int(N), int(K), int(cus), ctypes.byref(rt), ctypes.byref(mt), ctypes.byref(rr))
+    if st != OK:
+        raise GemmError(st, "gemm_f16_nt_plan")
+    return rt.value, mt.value, rr.value
 
 
 def splitk_plan(M: int, N: int, K: int, cus: int):

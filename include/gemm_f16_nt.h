@@ -76,7 +76,10 @@ extern "C" {
                                            shorter than 2^21 elements); the library's choice for those
                                            shapes */
 
-/* D = A * B^T with the library's choice of kernel for the shape. */
+/* D = A * B^T with the library's choice of kernel for the shape (see
+ * gemm_f16_nt_plan; when the 256 x 256 tiles leave a small last round,
+ * the rows past the whole rounds run as a second launch on 128 x 128
+ * tiles). */
 int gemm_f16_nt(int64_t M, int64_t N, int64_t K, const void* A, const void* B, void* D, void* stream);
 
 /* The same product on one named rung of the ladder (for tests and the
@@ -162,6 +165,12 @@ int64_t gemm_f16_nt_schedule(int64_t M, int64_t N, int64_t num_workgroups, int64
  * refill[k] = the step loaded into stage[k] once step k is consumed (-1 if
  * none).  Returns 0 or a negative status. */
 int gemm_f16_nt_ring_plan(int depth, int64_t steps, int* stage, int64_t* lap, int64_t* refill);
+/* Host evaluation of gemm_f16_nt's kernel choice for contiguous, 16-byte
+ * aligned operands on a device with `cus` compute units, no HIP call: rows
+ * [0, *m_top) run on rung *rung_top and rows [*m_top, M) on rung
+ * *rung_rest (0 and *m_top = M when one kernel takes every row; rung 3
+ * stands for the general kernel).  Returns 0 or a negative status. */
+int gemm_f16_nt_plan(int64_t M, int64_t N, int64_t K, int cus, int* rung_top, int64_t* m_top, int* rung_rest);
 /* Host evaluation of gemm_f16_nt_splitk's choice for `splits` = 0 on a
  * device with `cus` compute units, no HIP call: *m_top rows (0 or a
  * multiple of 256) run unsplit, the other M - *m_top rows split K into

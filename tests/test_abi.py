@@ -225,6 +225,27 @@ def test_splitk_workspace_sizes():
     assert L.gemm_f16_nt_splitk_workspace(-1, 256, 512, 2) == g.INVALID_ARG
 
 
+@pytest.mark.parametrize("shape,want", [
+    ((6144, 6144, 6144), (10, 5376, 9)),      # 2.25 rounds: 21 tile rows on R10, 768 rows on 128x128 tiles
+    ((6144, 6144, 1024), (10, 5376, 9)),
+    ((6144, 6144, 512), (10, 6144, 0)),       # short K: one launch
+    ((4352, 4352, 4096), (10, 3840, 9)),
+    ((7168, 7168, 4096), (10, 6912, 9)),
+    ((5120, 5120, 4096), (10, 5120, 0)),      # more than a third of a round left
+    ((4096, 4096, 4096), (10, 4096, 0)),      # whole rounds
+    ((8192, 8192, 8192), (10, 8192, 0)),
+    ((32768, 1024, 8192), (10, 32768, 0)),
+    ((256, 256, 512), (9, 256, 0)),           # tile-starved
+    ((2560, 2560, 4096), (9, 2560, 0)),
+    ((4000, 4000, 4000), (10, 4000, 0)),
+    ((200, 4096, 1024), (9, 200, 0)),
+    ((4096, 4092, 1024), (4, 4096, 0)),       # N % 8 != 0: not the four-wave ring
+    ((100, 100, 100), (3, 100, 0)),           # K % 8 != 0: the general kernel
+])
+def test_library_plan(shape, want):
+    assert g.plan(*shape, 256) == want
+
+
 @pytest.mark.parametrize("shape,cus,want", [
     ((6144, 6144, 6144), 256, (5376, 3)),     # 2.25 rounds: 21 tile rows whole, 768 rows split 3 ways
     ((4352, 4352, 4096), 256, (3840, 6)),

@@ -356,6 +356,32 @@ def test_ring4_consecutive_tiles_bitwise(shape):
     assert_parity(got[rows, cols], want, K, f"{M}x{N}x{K}")
 
 
+@pytest.mark.parametrize("shape", [(4352, 4352, 1024), (4500, 4352, 1024)], ids=lambda s: "x".join(map(str, s)))
+def test_library_small_last_round(shape):
+    """gemm_f16_nt with a small last round of 256x256 tiles: rows up to the
+    whole rounds come from R10 and the rest from 128x128 tiles.  Each part
+    is bitwise equal to that rung run on the whole product (a tile's result
+    depends only on its own rows, columns and K), and sampled outputs,
+    boundary rows among them, match the oracle."""
+    M, N, K = shape
+    rung_top, m_top, rung_rest = g.plan(M, N, K, torch.cuda.get_device_properties(0).multi_processor_count)
+    assert (rung_top, rung_rest) == (10, 9) and 0 < m_top < M, (rung_top, m_top, rung_rest)
+    A, B = rand_case(M, N, K, 700 + M)
+    dA, dB = dev(A), dev(B)
+    say(f"[gpu] small last round {M}x{N}x{K}: rows [0, {m_top}) on rung 10, the rest on rung 9")
+    D = torch.full((M, N), float("nan"), dtype=torch.float16, device=DEV)
+    got = host_bits(run(0, dA, dB, D))
+    top = host_bits(run(10, dA, dB))
+    rest = host_bits(run(9, dA, dB))
+    assert np.array_equal(got[:m_top], top[:m_top])
+    assert np.array_equal(got[m_top:], rest[m_top:])
+    rows, cols = sample_positions(M, N, 1500, M)
+    rows = np.concatenate([rows, np.full(64, m_top - 1), np.full(64, m_top), np.full(64, M - 1)])
+    cols = np.concatenate([cols, np.random.default_rng(6).integers(0, N, 192)])
+    want, _ = oracle.gemm_nt_sampled(A, B, rows, cols)
+    assert_parity(got[rows, cols], want, K, f"small last round {shape}")
+
+
 def test_non_default_stream_and_interleaving():
     M, N, K = 512, 512, 512
     A, B = rand_case(M, N, K, 79)
