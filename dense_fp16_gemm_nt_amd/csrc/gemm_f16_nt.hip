@@ -386,9 +386,21 @@ constexpr double kSplitSlowdown = 1.28;
 constexpr double kBytesPerStepTime = 10.3e6;
 constexpr double kSplitFixedSteps = 6.7;   // two more launches and a slice's prologue and epilogue
 
+GemmArgs contiguous_args(int64_t M, int64_t N, int64_t K, const void* A, const void* B, void* D);
+
 bool hybrid_plan(int64_t M, int64_t N, int64_t K, int cus, int64_t* m_top, int64_t* splits)
 {
     if (K % 8 != 0 || !ring4_paired_shape(ring4::C::BM, N, K, K, K)) return false;
+    // where the unsplit call already moves a small last round to 128 x 128
+    // tiles that fit in one round, that is as fast (measured: 4352^2 x 4096
+    // 120 us unsplit against 128 us split); it loses to the split when they
+    // need two rounds (6144^3: 353 against 330 us)
+    int64_t rs_top = 0;
+    if (round_split(contiguous_args(M, N, K, nullptr, nullptr, nullptr), cus, &rs_top)) {
+        const int64_t small = (M - rs_top + RingSmallCfg::BM - 1) / RingSmallCfg::BM *
+                              ((N + RingSmallCfg::BN - 1) / RingSmallCfg::BN);
+        if (small <= (int64_t)cus) return false;
+    }
     const int64_t tm = (M + kFastTile - 1) / kFastTile, tn = (N + kFastTile - 1) / kFastTile;
     const int64_t tiles = tm * tn, kt = (K + RingCfg::BK - 1) / RingCfg::BK;
     const int64_t rounds = tiles / cus;

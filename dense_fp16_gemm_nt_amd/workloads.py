@@ -96,10 +96,10 @@ EXTRA_WORKLOADS = [
     ExtraWorkload("ragged_mn_4000x4000x4096", "gemm", 1, 4000, 4000, 4096, 12, U11),
     # K % 8 != 0: operand rows are not 16-byte aligned, so the general kernel runs
     ExtraWorkload("unaligned_k_4096x4096x4095", "gemm", 1, 4096, 4096, 4095, 13, U11),
-    # a small last round of tiles (2.25 and 1.13 rounds on 256 compute units):
-    # whole rounds unsplit, the remaining rows split K
+    # a small last round of tiles (2.25 rounds on 256 compute units, and a
+    # ragged M): whole rounds unsplit, the remaining rows split K
     ExtraWorkload("splitk_rounds_6144x6144x6144", "splitk", 1, 6144, 6144, 6144, 18, U11),
-    ExtraWorkload("splitk_rounds_4352x4352x4096", "splitk", 1, 4352, 4352, 4096, 19, U11),
+    ExtraWorkload("splitk_rounds_6280x5888x4096", "splitk", 1, 6280, 5888, 4096, 19, U11),
     # a batch of mid-size products, one launch
     ExtraWorkload("batched_16x1024x1024x4096", "strided", 16, 1024, 1024, 4096, 14, U11),
     # attention scores S = Q K^T, 32 heads of 4096 x 4096, head dimension 128 and 64

@@ -248,7 +248,8 @@ def test_library_plan(shape, want):
 
 @pytest.mark.parametrize("shape,cus,want", [
     ((6144, 6144, 6144), 256, (5376, 3)),     # 2.25 rounds: 21 tile rows whole, 768 rows split 3 ways
-    ((4352, 4352, 4096), 256, (3840, 6)),
+    ((6280, 5888, 4096), 256, (5632, 3)),     # ragged M
+    ((4352, 4352, 4096), 256, (0, 1)),        # the unsplit call's 128x128 tiles fit in one round: no split
     ((4096, 4096, 4096), 256, (0, 1)),        # whole rounds: no split
     ((8192, 8192, 8192), 256, (0, 1)),
     ((6144, 6144, 2048), 256, (0, 1)),        # short K: the split costs more than the last round

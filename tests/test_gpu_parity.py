@@ -583,7 +583,7 @@ def test_splitk(case):
     assert np.array_equal(host_bits(D), first)        # fixed slice order: repeatable
 
 
-@pytest.mark.parametrize("shape", [(4352, 4352, 4096), (4500, 4352, 4096)], ids=lambda s: "x".join(map(str, s)))
+@pytest.mark.parametrize("shape", [(6144, 6144, 6144), (6280, 5888, 4096)], ids=lambda s: "x".join(map(str, s)))
 def test_splitk_whole_rounds_plus_split_rows(shape):
     """The library's split for a small last round of tiles: the top rows
     run unsplit, the rest split K (ragged M included).  Sampled outputs
