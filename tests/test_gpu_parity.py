@@ -328,13 +328,16 @@ def test_ring4_partial_first_step(shape):
     assert_parity(host_bits(Ds[0]), ref, K, f"strided {M}x{N}x{K}")
 
 
-@pytest.mark.parametrize("shape", [(8192, 8192, 512), (32768, 4096, 128), (16384, 4096, 192), (8192, 4096, 2040)],
+@pytest.mark.parametrize("shape", [(8192, 8192, 512), (32768, 4096, 128), (16384, 4096, 192), (8192, 4096, 2040),
+                                   (8192, 4096, 200), (8192, 4096, 136), (16384, 4096, 1000)],
                          ids=lambda s: "x".join(map(str, s)))
 def test_ring4_consecutive_tiles_bitwise(shape):
     """Many tiles per workgroup on the fourth form, whose last step loads
-    the next tile's first step (odd step counts swap the stages): every
-    output is bitwise equal to the third form's (rung 8, one tile at a
-    time, the same MFMA sequence per accumulator), on repeated runs."""
+    the next tile's first step when K has at most 16 steps (odd step counts
+    swap the stages; K not a multiple of 64 makes that first step the
+    masked partial one): every output is bitwise equal to the third form's
+    (rung 8, one tile at a time, the same MFMA sequence per accumulator), on
+    repeated runs."""
     M, N, K = shape
     rng = np.random.default_rng(M + N + K)
     A = torch.from_numpy(rng.uniform(-1, 1, (M, K)).astype(np.float16)).to(DEV)
