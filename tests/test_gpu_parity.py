@@ -385,6 +385,54 @@ def test_library_small_last_round(shape):
     assert_parity(got[rows, cols], want, K, f"small last round {shape}")
 
 
+@pytest.mark.parametrize("case", [
+    ("plain", 4096, 4096, 1024),     # one launch of the four-wave ring
+    ("plain", 4352, 4352, 1024),     # two launches: whole rounds, then 128x128 tiles
+    ("plain", 256, 256, 512),        # 128x128 tiles only
+    ("plain", 300, 264, 0),          # K = 0: the fill kernel
+    ("splitk", 256, 256, 8192),      # split K: partial sums, then the reduction
+], ids=lambda c: "{}_{}x{}x{}".format(*c))
+def test_graph_capture_replays(case):
+    """Every launch the library makes can be captured into a HIP graph (no
+    memset, no allocation, no host synchronisation): replays of the graph,
+    with eager work and synchronisation between them, reproduce the eager
+    result bit for bit."""
+    kind, M, N, K = case
+    rng = np.random.default_rng(M + N + K)
+    A = torch.from_numpy(rng.uniform(-1, 1, (M, K)).astype(np.float16)).to(DEV)
+    B = torch.from_numpy(rng.uniform(-1, 1, (N, K)).astype(np.float16)).to(DEV)
+    D = torch.empty((M, N), dtype=torch.float16, device=DEV)
+    ws = None
+    if kind == "splitk":
+        ws = torch.empty(max(16, g.splitk_workspace_bytes(M, N, K, 0)), dtype=torch.uint8, device=DEV)
+
+    def call():
+        if kind == "splitk":
+            g.gemm_f16_nt_splitk(A, B, D, workspace=ws)
+        else:
+            g.gemm_f16_nt(A, B, D)
+
+    say(f"[gpu] graph capture {case}")
+    call()
+    torch.cuda.synchronize()
+    ref = host_bits(D)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        call()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        call()
+    for rep in range(3):
+        D.fill_(float("nan"))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(host_bits(D), ref), f"replay {rep} differs from the eager result"
+
+
 def test_non_default_stream_and_interleaving():
     M, N, K = 512, 512, 512
     A, B = rand_case(M, N, K, 79)
