@@ -6,6 +6,8 @@ One step = one call of the library on one batch of synthetic operands
 the timed region starts).  Prints one JSON line:
 
   value       whole-run throughput, TFLOP/s = 2*M*N*K*steps / timed seconds
+              (K host launches; --launch graph captures the K steps once
+              into a HIP graph and times its replay)
   roofline    the GEMM kernel against the dense-fp16 MFMA peak: achieved =
               2*M*N*K / mean launch duration (HIP events bracketing the timed
               region on the launch stream, divided by the number of
@@ -78,6 +80,8 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="target oracle time for the CPU sample")
     p.add_argument("--copy-calib", action="store_true", help="run only a plain device copy (counter scaling)")
+    p.add_argument("--launch", choices=("graph", "host"), default="host",
+                   help="time the K steps as K host launches (default) or as one captured HIP graph")
     p.add_argument("--suite", action="store_true", help="time the extra products (general shapes, attention scores)")
     p.add_argument("--only", default="", help="comma-separated extra product names for --suite")
     p.add_argument("--seconds", type=float, default=0.3, help="timed seconds per extra product")
@@ -315,20 +319,39 @@ def main():
         ws_bytes = max(16, g.splitk_workspace_bytes(w.M, w.N, w.K, args.splitk))
         ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
 
-        def step():
-            return L.gemm_f16_nt_splitk(w.M, w.N, w.K, a_ptr, b_ptr, d_ptr, args.splitk, ws.data_ptr(), ws_bytes,
-                                        s_ptr)
+        def step(sp):
+            return L.gemm_f16_nt_splitk(w.M, w.N, w.K, a_ptr, b_ptr, d_ptr, args.splitk, ws.data_ptr(), ws_bytes, sp)
     elif args.rung == 0:
-        def step():
-            return L.gemm_f16_nt(w.M, w.N, w.K, a_ptr, b_ptr, d_ptr, s_ptr)
+        def step(sp):
+            return L.gemm_f16_nt(w.M, w.N, w.K, a_ptr, b_ptr, d_ptr, sp)
     else:
-        def step():
-            return L.gemm_f16_nt_rung(args.rung, w.M, w.N, w.K, a_ptr, b_ptr, d_ptr, s_ptr)
+        def step(sp):
+            return L.gemm_f16_nt_rung(args.rung, w.M, w.N, w.K, a_ptr, b_ptr, d_ptr, sp)
 
     for _ in range(args.warmup):
-        if step() != 0:
+        if step(s_ptr) != 0:
             raise SystemExit("gemm_f16_nt returned an error")
     torch.cuda.synchronize()
+
+    bad = 0
+    graph = None
+    if args.launch == "graph":
+        # the K timed steps, captured once into one HIP graph (the same
+        # launches, replayed without a host call per step)
+        side = torch.cuda.Stream(dev)
+        side.wait_stream(stream)
+        with torch.cuda.stream(side):
+            bad |= step(ctypes.c_void_p(side.cuda_stream))
+        stream.wait_stream(side)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            cap = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+            for _ in range(args.steps):
+                bad |= step(cap)
+        torch.cuda.synchronize()
+        if bad:
+            raise SystemExit("gemm_f16_nt returned an error while captured")
 
     # timed region: bracketed by events on the launch stream, with the
     # device synchronised on both sides
@@ -337,9 +360,11 @@ def main():
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     region0.record(stream)
-    bad = 0
-    for _ in range(args.steps):
-        bad |= step()
+    if graph is not None:
+        graph.replay()
+    else:
+        for _ in range(args.steps):
+            bad |= step(s_ptr)
     region1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
@@ -371,6 +396,7 @@ def main():
             "workload": w.name, "M": w.M, "N": w.N, "K": w.K, "seed": w.seed,
             "dist": w.dist, "layout": "A MxK row-major, B NxK row-major, D MxN row-major",
             "accumulate": "f32", "kernel": rung_name,
+            "launch": "one HIP graph of the K steps" if graph is not None else "K host launches",
         },
         "pct_of_peak": round(100.0 * value / PEAK_FP16_TFLOPS, 2),
         "roofline": {
