@@ -140,8 +140,10 @@ int validate(int rung, int64_t M, int64_t N, int64_t K, const void* A, const voi
     // index ranges the kernels are built for: per-lane 32-bit byte offsets
     // within a 256-row band, 2^31 tiles, 2D grid limits of the 128-tile rungs
     if (K > (int64_t(1) << 22) || M > (int64_t(1) << 31) || N > (int64_t(1) << 31)) return GEMM_F16_NT_UNSUPPORTED;
-    // rungs other than R3 (and the library's choice) need 16-byte rows
-    const bool general_ok = rung == 0 || rung == GEMM_F16_NT_R3_GRID;
+    // rungs other than R3, R4 and R9 (and the library's choice) need 16-byte
+    // rows; R4's and R9's register-staged forms need K >= 8
+    const bool general_ok = rung == 0 || rung == GEMM_F16_NT_R3_GRID ||
+                            ((rung == GEMM_F16_NT_R4_RING || rung == GEMM_F16_NT_R9_RING_SMALL) && K >= 8);
     if (K % 8 != 0 && !general_ok) return GEMM_F16_NT_UNSUPPORTED;
     if (rung == GEMM_F16_NT_R1_SINGLE_TILE && !(M == 128 && N == 128 && K == 64)) return GEMM_F16_NT_UNSUPPORTED;
     if (rung == GEMM_F16_NT_R2_KLOOP && !(M == 128 && N == 128)) return GEMM_F16_NT_UNSUPPORTED;
@@ -155,7 +157,8 @@ int validate(int rung, int64_t M, int64_t N, int64_t K, const void* A, const voi
     if ((K > 0 && (((uintptr_t)A & 1) || ((uintptr_t)B & 1))) || ((uintptr_t)D & 1)) return GEMM_F16_NT_UNSUPPORTED;
     if (!fast_operands(K, K, K, 0, 0, A, B, D)) {
         if (!general_ok) return GEMM_F16_NT_UNSUPPORTED;
-        if ((N + 127) / 128 > 65535) return GEMM_F16_NT_UNSUPPORTED;   // grid y of the general kernel
+        // grid y of R3's general form (rung 3, and the library's choice for K < 8)
+        if ((rung == GEMM_F16_NT_R3_GRID || K < 8) && (N + 127) / 128 > 65535) return GEMM_F16_NT_UNSUPPORTED;
     }
     const int64_t dbytes = M * N * 2;
     if (K > 0 && (overlaps(A, M * K * 2, D, dbytes) || overlaps(B, N * K * 2, D, dbytes)))
@@ -184,8 +187,9 @@ int validate_strided(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda
         N > (int64_t(1) << 31) || batch > (int64_t(1) << 31))
         return GEMM_F16_NT_UNSUPPORTED;
     if ((K > 0 && (((uintptr_t)A & 1) || ((uintptr_t)B & 1))) || ((uintptr_t)D & 1)) return GEMM_F16_NT_UNSUPPORTED;
-    // the general kernel's grid: (tiles_m, tiles_n <= 65535, batch <= 65535)
-    if (!fast_operands(K, lda, ldb, sa, sb, A, B, D) && ((N + 127) / 128 > 65535 || batch > 65535))
+    // R3's general form (K < 8 on operands without 16-byte rows) has the
+    // grid (tiles_m, tiles_n <= 65535, batch <= 65535)
+    if (!fast_operands(K, lda, ldb, sa, sb, A, B, D) && K < 8 && ((N + 127) / 128 > 65535 || batch > 65535))
         return GEMM_F16_NT_UNSUPPORTED;
     const int64_t dbytes = span_elems(M, N, ldd, sd, batch) * 2;
     if (K > 0 && (overlaps(A, span_elems(M, K, lda, sa, batch) * 2, D, dbytes) ||
@@ -477,11 +481,40 @@ int launch_splitk(int64_t M, int64_t N, int64_t K, const void* A, const void* B,
 
 // General operands (any K, strides, 2-byte alignment): R3's structure with
 // element-wise operand copies.
-int launch_any(const GemmArgs& g, hipStream_t s)
+int launch_r3_any(const GemmArgs& g, hipStream_t s)
 {
     const dim3 grid((unsigned)((g.M + 127) / 128), (unsigned)((g.N + 127) / 128), (unsigned)g.batch);
     hipLaunchKernelGGL(ladder::r3_any, grid, dim3(ladder::THREADS), 0, s, g);
     return launched();
+}
+
+// R4 (256 x 256 tiles) or R9 (128 x 128, `small`) on general operands: the
+// pipelined ring with its loads staged through registers, which take rows
+// on any 2-byte boundary.  Needs K >= 8.
+int launch_staged(const GemmArgs& g0, hipStream_t s, bool small)
+{
+    GemmArgs g = g0;
+    const int64_t tile = small ? RingSmallCfg::BM : kFastTile;
+    g.tiles_m = (g.M + tile - 1) / tile;
+    g.tiles_n = (g.N + tile - 1) / tile;
+    const int64_t blocks = g.tiles_m * g.tiles_n * g.batch;
+    if (blocks > 0x7fffffff) return GEMM_F16_NT_UNSUPPORTED;
+    if (small)
+        hipLaunchKernelGGL((ring::ring_kernel<RingSmallCfg, true, kRingPre, kRingLsplit, true, false, false, true>),
+                           dim3((unsigned)blocks), dim3(RingSmallCfg::THREADS), 0, s, g);
+    else
+        hipLaunchKernelGGL((ring::ring_kernel<RingCfg, true, kRingPre, kRingLsplit, true, false, false, true>),
+                           dim3((unsigned)blocks), dim3(RingCfg::THREADS), 0, s, g);
+    return launched();
+}
+
+// The library's kernel for general operands: the staged ring, on 128 x 128
+// tiles when 256 x 256 ones would leave most compute units idle.  K < 8 (a
+// row shorter than one 16-byte load) runs on R3's general form.
+int launch_any(const GemmArgs& g, hipStream_t s)
+{
+    if (g.K < 8) return launch_r3_any(g, s);
+    return launch_staged(g, s, tile_starved(g));
 }
 
 GemmArgs contiguous_args(int64_t M, int64_t N, int64_t K, const void* A, const void* B, void* D)
@@ -536,12 +569,13 @@ int run(int rung, int64_t M, int64_t N, int64_t K, const void* A, const void* B,
         return launched();
     case GEMM_F16_NT_R2_KLOOP:
     case GEMM_F16_NT_R3_GRID: {
-        if (!fast_operands(K, K, K, 0, 0, A, B, D)) return launch_any(contiguous_args(M, N, K, A, B, D), s);
+        if (!fast_operands(K, K, K, 0, 0, A, B, D)) return launch_r3_any(contiguous_args(M, N, K, A, B, D), s);
         const dim3 grid((unsigned)((M + 127) / 128), (unsigned)((N + 127) / 128));
         hipLaunchKernelGGL(ladder::r23_kloop_grid, grid, dim3(ladder::THREADS), 0, s, a, b, d, M, N, K);
         return launched();
     }
     case GEMM_F16_NT_R4_RING:
+        if (!fast_operands(K, K, K, 0, 0, A, B, D)) return launch_staged(contiguous_args(M, N, K, A, B, D), s, false);
         return launch_ring(contiguous_args(M, N, K, A, B, D), s);
     case GEMM_F16_NT_R5_PERSISTENT_WS:
         return launch_ws(M, N, K, a, b, d, grid_override > 0 ? grid_override : cus, s);
@@ -552,6 +586,7 @@ int run(int rung, int64_t M, int64_t N, int64_t K, const void* A, const void* B,
     case GEMM_F16_NT_R8_RING4_GAP:
         return launch_ring4(contiguous_args(M, N, K, A, B, D), s, 3);
     case GEMM_F16_NT_R9_RING_SMALL:
+        if (!fast_operands(K, K, K, 0, 0, A, B, D)) return launch_staged(contiguous_args(M, N, K, A, B, D), s, true);
         return launch_ring_small(contiguous_args(M, N, K, A, B, D), s);
     case GEMM_F16_NT_R10_RING4_PAIRED:
         return launch_ring4(contiguous_args(M, N, K, A, B, D), s, 4);
@@ -724,11 +759,13 @@ int gemm_f16_nt_plan(int64_t M, int64_t N, int64_t K, int cus, int* rung_top, in
     GemmArgs g = contiguous_args(M, N, K, nullptr, nullptr, nullptr);
     *m_top = M;
     *rung_rest = 0;
-    if (K % 8 != 0) {
-        *rung_top = GEMM_F16_NT_R3_GRID;   // the general kernel
+    const int64_t tiles = ((M + kFastTile - 1) / kFastTile) * ((N + kFastTile - 1) / kFastTile);
+    if (K % 8 != 0) {   // R3's general form, or R9's / R4's register-staged form
+        *rung_top = K < 8 ? GEMM_F16_NT_R3_GRID
+                          : (tiles * 10 <= (int64_t)cus * kSmallTilesPer10Cus ? GEMM_F16_NT_R9_RING_SMALL
+                                                                               : GEMM_F16_NT_R4_RING);
         return GEMM_F16_NT_OK;
     }
-    const int64_t tiles = ((M + kFastTile - 1) / kFastTile) * ((N + kFastTile - 1) / kFastTile);
     if (tiles * 10 <= (int64_t)cus * kSmallTilesPer10Cus) {
         *rung_top = GEMM_F16_NT_R9_RING_SMALL;
     } else if (ring4_fits(g)) {

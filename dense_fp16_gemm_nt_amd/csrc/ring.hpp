@@ -36,6 +36,35 @@ namespace g16 {
 // 16 zero bytes: the source of every out-of-range lane of an edge tile.
 __device__ __attribute__((aligned(64))) uint32_t g_zero_line[16] = {0};
 
+// 16 bytes (8 fp16) of an operand row from element kk on, for rows that
+// start on any 2-byte boundary (K, leading dimensions or bases not
+// multiples of 8 elements).  The load goes through registers: gfx950's
+// global loads take unaligned addresses, its direct-to-LDS loads are only
+// used here on 16-byte aligned rows.  Nothing past the row's K-th element
+// is touched: a chunk that crosses K is read as the row's last 8 elements,
+// which chunk_shift then moves into place; a chunk at or beyond K, or of a
+// row past the operand, reads the zero line.  Needs K >= 8.
+__device__ __forceinline__ u32x4 load_row_chunk(const char* row_ptr, int kk, int K, bool row_ok)
+{
+    typedef uint32_t u32x4_a2 __attribute__((ext_vector_type(4), aligned(2)));
+    const int avail = K - kk;
+    const char* p = !(row_ok && avail > 0) ? (const char*)g_zero_line
+                                           : row_ptr + 2 * (uint32_t)(avail >= 8 ? kk : K - 8);
+    return *(const G16_GLOBAL u32x4_a2*)p;
+}
+
+// The chunk load_row_chunk returned for element kk, with elements at or
+// beyond K set to zero: a chunk that crosses K holds the row's last 8
+// elements, of which the last K - kk are this chunk's first ones.
+__device__ __forceinline__ u32x4 chunk_shift(u32x4 v, int kk, int K)
+{
+    const int avail = K - kk;
+    const int sh = (avail > 0 && avail < 8) ? (int)(8 - avail) : 0;
+    unsigned __int128 x = __builtin_bit_cast(unsigned __int128, v);
+    x >>= 16 * sh;
+    return __builtin_bit_cast(u32x4, x);
+}
+
 namespace ring {
 
 template <int BM_, int BN_, int BK_, int STAGES_, int SWZ_, int WM_ = 2, int WN_ = 2>
@@ -156,9 +185,13 @@ __device__ __forceinline__ void interleave_hint(int nr, int nl)
 // lines (the registers hold 4 consecutive columns per lane, which would
 // otherwise mean partial-line 8-byte stores).  Row r of the staged tile is FN*64 bytes;
 // 16-byte chunk c of row r sits at chunk c ^ (r mod CPR).
-template <class C>
+// EDGE: rows >= M and columns >= N are not written; a 16-byte chunk off a
+// 16-byte boundary of D is stored unaligned (gfx950's global stores take
+// any address), and the chunk that crosses N element by element.
+template <class C, bool EDGE = false>
 __device__ __forceinline__ void epilogue_lds(char* lds, f16* __restrict__ D, int64_t ldd, int64_t row0,
-                                             int64_t col0, const f32x16 (&acc)[C::FM][C::FN], int lane)
+                                             int64_t col0, const f32x16 (&acc)[C::FM][C::FN], int lane,
+                                             int64_t M = 0, int64_t N = 0)
 {
     constexpr int ROWB = C::FN * 64;      // bytes per staged row
     constexpr int CPR = ROWB / 16;        // chunks per row
@@ -181,8 +214,25 @@ __device__ __forceinline__ void epilogue_lds(char* lds, f16* __restrict__ D, int
         const int r = q * ROWS_PER_STORE + lane / CPR;
         const int c = lane % CPR;
         const u32x4 v = *reinterpret_cast<const u32x4*>(lds + r * ROWB + ((c ^ (r % CPR)) << 4));
+        f16* dst = D + (row0 + r) * ldd + col0 + 8 * c;
+        if (EDGE) {
+            typedef uint32_t u32x4_a2 __attribute__((ext_vector_type(4), aligned(2)));
+            const int64_t col = col0 + 8 * c;
+            if (row0 + r >= M || col >= N) continue;
+            if (col + 8 > N) {
+                const f16x8 h = __builtin_bit_cast(f16x8, v);
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    if (col + e < N) dst[e] = h[e];
+                continue;
+            }
+            if ((uintptr_t)dst & 15) {
+                *reinterpret_cast<u32x4_a2*>(dst) = v;
+                continue;
+            }
+        }
         // non-temporal: D is not read again by the kernel
-        __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(D + (row0 + r) * ldd + col0 + 8 * c));
+        __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(dst));
     }
 }
 
@@ -207,10 +257,18 @@ __device__ __forceinline__ void store_block_f32(float* __restrict__ P, int64_t l
     }
 }
 
-template <class C, bool EDGE, int PRE, int LSPLIT, bool EPI_LDS, bool READS_FIRST = false, bool SPLITK = false>
+// VSTAGE: operands on any 2-byte boundary (EDGE form only, K >= 8).  Each
+// wave's loads of step j + STAGES - 1 go to registers during step j
+// (load_row_chunk) and are written to their LDS slots just before the
+// barrier that ends step j; the slots are the ones the direct-to-LDS form
+// fills, so the fragment reads are the same.
+template <class C, bool EDGE, int PRE, int LSPLIT, bool EPI_LDS, bool READS_FIRST = false, bool SPLITK = false,
+          bool VSTAGE = false>
 __global__ __launch_bounds__(C::THREADS, 1) void ring_kernel(const GemmArgs g)
 {
     static_assert(LSPLIT >= 1 && LSPLIT < C::KSUB && C::LPW % LSPLIT == 0, "load split");
+    static_assert(!VSTAGE || (EDGE && !SPLITK), "register staging is an edge form");
+    static_assert(!EPI_LDS || C::WAVES * C::FM * 32 * C::FN * 64 <= C::LDS_BYTES, "epilogue staging");
     __shared__ __attribute__((aligned(1024))) char smem[C::LDS_BYTES];
     const int t = threadIdx.x, lane = t & 63;
     const int w = __builtin_amdgcn_readfirstlane(t >> 6);
@@ -239,10 +297,22 @@ __global__ __launch_bounds__(C::THREADS, 1) void ring_kernel(const GemmArgs g)
     const __amdgpu_buffer_rsrc_t a_rsrc = make_rsrc(a_base, (uint32_t)(C::BM * lda_b));
     const __amdgpu_buffer_rsrc_t b_rsrc = make_rsrc(b_base, (uint32_t)(C::BN * ldb_b));
 
+    // VSTAGE: one step's loads of this wave, held until written to LDS
+    u32x4 stg[C::LPW];
+
     // load q (0 .. LPW-1) of this wave for k step `step`
     auto load_one = [&](int64_t step, int q) {
         char* st = smem + (int)(step % C::STAGES) * C::STAGE_BYTES;
         const int64_t k0 = step * C::BK;
+        if (VSTAGE) {
+            const int qb = q - C::A_LOADS;
+            // (K <= 2^22: the element indices fit 32 bits)
+            stg[q] = q < C::A_LOADS ? load_row_chunk(a_base + (a_off[q] - 2 * a_kc[q]), (int)k0 + a_kc[q], (int)K,
+                                                     a_row[q] < a_rows)
+                                    : load_row_chunk(b_base + (b_off[qb] - 2 * b_kc[qb]), (int)k0 + b_kc[qb], (int)K,
+                                                     b_row[qb] < b_rows);
+            return;
+        }
         if (q < C::A_LOADS) {
             char* d = st + (w * C::A_LOADS + q) * 1024;
             if (EDGE) {
@@ -263,6 +333,35 @@ __global__ __launch_bounds__(C::THREADS, 1) void ring_kernel(const GemmArgs g)
         }
     };
 
+    // VSTAGE: the staged loads of step `step` into the slots the
+    // direct-to-LDS loads would fill (lane i of a load at 16*i)
+    // (the shift of a chunk that crosses K happens here, after the loads
+    // have landed, so that no wait for them falls inside the step; only the
+    // last step, a wave-uniform test, can hold such a chunk)
+    auto stage_write = [&](int64_t step) {
+        char* st = smem + (int)(step % C::STAGES) * C::STAGE_BYTES;
+        const int k0 = (int)(step * C::BK);
+        __builtin_amdgcn_sched_barrier(0);
+        if (k0 + C::BK > K) {
+#pragma unroll
+            for (int q = 0; q < C::LPW; ++q)
+                stg[q] = chunk_shift(stg[q], k0 + (q < C::A_LOADS ? a_kc[q] : b_kc[q - C::A_LOADS]), K);
+        }
+#pragma unroll
+        for (int q = 0; q < C::LPW; ++q) {
+            const int qb = q - C::A_LOADS;
+            char* d = q < C::A_LOADS ? st + (w * C::A_LOADS + q) * 1024 : st + C::A_BYTES + (w * C::B_LOADS + qb) * 1024;
+            *reinterpret_cast<u32x4*>(d + 16 * lane) = stg[q];
+        }
+    };
+    // VSTAGE: the barrier also orders the LDS writes before it against
+    // every wave's reads after it
+    auto staged_barrier = [&]() {
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+        wg_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+    };
+
     f32x16 acc[C::FM][C::FN];
 #pragma unroll
     for (int i = 0; i < C::FM; ++i)
@@ -273,14 +372,20 @@ __global__ __launch_bounds__(C::THREADS, 1) void ring_kernel(const GemmArgs g)
     // prologue: steps 0 .. STAGES-2
 #pragma unroll
     for (int s = 0; s < C::STAGES - 1; ++s)
-        if (s < KT)
+        if (s < KT) {
 #pragma unroll
             for (int q = 0; q < C::LPW; ++q) load_one(s, q);
-    if (KT >= C::STAGES - 1)
-        wait_vmcnt<(C::STAGES - 2) * C::LPW>();
-    else
-        wait_vmcnt<0>();
-    wg_barrier();
+            if (VSTAGE) stage_write(s);
+        }
+    if (VSTAGE)
+        staged_barrier();
+    else {
+        if (KT >= C::STAGES - 1)
+            wait_vmcnt<(C::STAGES - 2) * C::LPW>();
+        else
+            wait_vmcnt<0>();
+        wg_barrier();
+    }
 
     const int wm = (w / C::WAVES_N) * C::WTM, wn = (w % C::WAVES_N) * C::WTN;
     constexpr int NQ = C::FM * C::FN;
@@ -310,11 +415,18 @@ __global__ __launch_bounds__(C::THREADS, 1) void ring_kernel(const GemmArgs g)
         constexpr bool EXACT = decltype(exact_tag)::value;
         wait_lgkmcnt0();
         mfma_range<C, 0, PRE>(fa[LB], fb[LB], acc);
-        if (EXACT)
-            wait_vmcnt<(C::STAGES - 2) * C::LPW>();
-        else
-            wait_vmcnt<0>();
-        wg_barrier();
+        if (VSTAGE) {
+            // EXACT steps loaded step j + STAGES - 1; its slot held step
+            // j - 1, which every wave finished reading before the last barrier
+            if (EXACT) stage_write(j + C::STAGES - 1);
+            staged_barrier();
+        } else {
+            if (EXACT)
+                wait_vmcnt<(C::STAGES - 2) * C::LPW>();
+            else
+                wait_vmcnt<0>();
+            wg_barrier();
+        }
         read_frags<C>(smem + (int)((j + 1) % C::STAGES) * C::STAGE_BYTES, wm, wn, lane, 0, fa[0], fb[0]);
         mfma_range<C, PRE, NQ>(fa[LB], fb[LB], acc);
         interleave_hint<NQ - PRE, READS_FIRST>(NR, 0);
@@ -342,12 +454,12 @@ __global__ __launch_bounds__(C::THREADS, 1) void ring_kernel(const GemmArgs g)
 #pragma unroll
             for (int jj = 0; jj < C::FN; ++jj)
                 store_block_f32(P, N, M, N, m0 + wm + 32 * i, n0 + wn + 32 * jj, acc[i][jj], lane, vec);
-    } else if (!EDGE && EPI_LDS) {
+    } else if (EPI_LDS) {
         wg_barrier();  // every wave is done reading the ring
-        epilogue_lds<C>(smem + w * (C::FM * 32 * C::FN * 64), D, ldd, m0 + wm, n0 + wn, acc, lane);
+        epilogue_lds<C, EDGE>(smem + w * (C::FM * 32 * C::FN * 64), D, ldd, m0 + wm, n0 + wn, acc, lane, M, N);
     } else {
         // 8-byte stores need every row start of this batch entry aligned
-        const bool vec = ldd % 4 == 0 && g.sd % 4 == 0;
+        const bool vec = ldd % 4 == 0 && g.sd % 4 == 0 && ((uintptr_t)g.D & 7) == 0;
         const bool full = !EDGE || (m0 + C::BM <= M && n0 + C::BN <= N && vec);
 #pragma unroll
         for (int i = 0; i < C::FM; ++i)

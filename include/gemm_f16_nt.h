@@ -29,10 +29,13 @@
  * at the caller's next synchronisation of the stream.
  *
  * Shapes: M, N, K >= 0.  M = 0 or N = 0 is a no-op; K = 0 writes +0.0 to
- * all of D.  The fast kernels need every operand row to start on a 16-byte
- * boundary (K % 8 == 0 and A, B, D 16-byte aligned); other operands run on
- * a general kernel that copies operands element by element (the library's
- * choice and rung 3 only; same result contract, several times slower).
+ * all of D.  The fastest kernels need every operand row to start on a
+ * 16-byte boundary (K % 8 == 0 and A, B, D 16-byte aligned).  Other
+ * operands (any 2-byte aligned A, B, D) run on the library's choice, rung 3,
+ * and rungs 4 and 9 for K >= 8: rungs 4 and 9 then stage their loads
+ * through registers (about two thirds of the aligned speed), rung 3 copies
+ * operands element by element (several times slower; the library's choice
+ * for K < 8).  The result contract is the same.
  *
  * Return value: GEMM_F16_NT_OK (0) or a negative status below.
  */
@@ -56,7 +59,9 @@ extern "C" {
 #define GEMM_F16_NT_R1_SINGLE_TILE 1 /* M = N = 128, K = 64 only, one workgroup */
 #define GEMM_F16_NT_R2_KLOOP 2       /* M = N = 128, any K: K-loop into one accumulator */
 #define GEMM_F16_NT_R3_GRID 3        /* any shape and alignment: 2D grid of 128 x 128 tiles */
-#define GEMM_F16_NT_R4_RING 4        /* any shape: 256 x 256 tiles, direct-to-LDS pipelined ring */
+#define GEMM_F16_NT_R4_RING 4        /* any shape: 256 x 256 tiles, direct-to-LDS pipelined ring
+                                        (loads staged through registers on rows off 16-byte
+                                        boundaries, K >= 8) */
 #define GEMM_F16_NT_R5_PERSISTENT_WS 5 /* any shape: persistent, producer/consumer waves */
 #define GEMM_F16_NT_R6_RING4 6 /* rung 4's ring with 4 waves of 128 x 128 and a fixed instruction
                                   schedule: M, N >= 256, N a multiple of 8, K a multiple of 64,
@@ -67,8 +72,9 @@ extern "C" {
 #define GEMM_F16_NT_R8_RING4_GAP 8 /* rung 7's barriers with at most one instruction between two MFMAs
                                       (offset loads, 4 M0 writes per step); same shapes as rung 6 */
 #define GEMM_F16_NT_R9_RING_SMALL 9 /* any shape: rung 4's ring with 128 x 128 tiles, 8 waves of 64 x 32 and
-                                       4 stages; the library's choice when 256 x 256 tiles would number
-                                       at most 0.4 per compute unit */
+                                       4 stages (the same register staging on general rows); the
+                                       library's choice when 256 x 256 tiles would number at most 0.4
+                                       per compute unit */
 #define GEMM_F16_NT_R10_RING4_PAIRED 10 /* rung 8 with each 16 x 16 block's two 32-wide sub-steps issued
                                            back to back into its accumulator; the shapes of rung 6, and
                                            also K a multiple of 8 above 64 that is not a multiple of 64
@@ -107,10 +113,10 @@ int gemm_f16_nt_persistent(int64_t M, int64_t N, int64_t K, const void* A, const
  * stride_a, stride_b >= 0 (0 repeats one operand for every batch entry);
  * ldd >= N; stride_d >= 0, and for batch > 1 at least (M-1)*ldd + N so the
  * outputs do not overlap.  With K, lda, ldb, stride_a, stride_b multiples
- * of 8 and 16-byte aligned A, B and D the fast kernels run (rows of D that
- * are not 8-byte aligned are written element by element); otherwise the
- * general kernel, which also limits batch to 65535.  Same precision,
- * rounding, ownership and error behaviour as gemm_f16_nt. */
+ * of 8 and 16-byte aligned A, B and D the fastest kernels run; otherwise
+ * the register-staged ring (K >= 8) or R3's general form (K < 8, which also
+ * limits batch to 65535).  Same precision, rounding, ownership and error
+ * behaviour as gemm_f16_nt. */
 int gemm_f16_nt_strided_batched(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, int64_t stride_a,
                                 const void* B, int64_t ldb, int64_t stride_b, void* D, int64_t ldd,
                                 int64_t stride_d, int64_t batch, void* stream);
@@ -129,8 +135,8 @@ int gemm_f16_nt_strided_batched(int64_t M, int64_t N, int64_t K, const void* A, 
  * `workspace` is caller-owned device memory of at least
  * gemm_f16_nt_splitk_workspace(M, N, K, splits) bytes, 16-byte aligned,
  * not overlapping A, B or D; its contents are scratch.  When one slice
- * suffices, or the operands need the general kernel (see above), the call
- * is gemm_f16_nt and the workspace is not touched. */
+ * suffices, or the operand rows are off 16-byte boundaries (see above), the
+ * call is gemm_f16_nt and the workspace is not touched. */
 int gemm_f16_nt_splitk(int64_t M, int64_t N, int64_t K, const void* A, const void* B, void* D, int splits,
                        void* workspace, int64_t workspace_bytes, void* stream);
 
@@ -168,8 +174,9 @@ int gemm_f16_nt_ring_plan(int depth, int64_t steps, int* stage, int64_t* lap, in
 /* Host evaluation of gemm_f16_nt's kernel choice for contiguous, 16-byte
  * aligned operands on a device with `cus` compute units, no HIP call: rows
  * [0, *m_top) run on rung *rung_top and rows [*m_top, M) on rung
- * *rung_rest (0 and *m_top = M when one kernel takes every row; rung 3
- * stands for the general kernel).  Returns 0 or a negative status. */
+ * *rung_rest (0 and *m_top = M when one kernel takes every row).  For
+ * K % 8 != 0 rungs 4 and 9 stand for their register-staged forms and
+ * rung 3 for its general form.  Returns 0 or a negative status. */
 int gemm_f16_nt_plan(int64_t M, int64_t N, int64_t K, int cus, int* rung_top, int64_t* m_top, int* rung_rest);
 /* Host evaluation of gemm_f16_nt_splitk's choice for `splits` = 0 on a
  * device with `cus` compute units, no HIP call: *m_top rows (0 or a

@@ -56,18 +56,24 @@ A0, B0, D0 = 0x10000, 0x20000000, 0x40000000   # fake, 16-byte aligned, disjoint
     ((0, 64, 64, 64, 0, B0, D0), g.INVALID_ARG),
     ((0, 64, 64, 64, A0, 0, D0), g.INVALID_ARG),
     ((0, 64, 64, 64, A0, B0, 0), g.INVALID_ARG),
-    ((0, 64, 64, 12, A0, B0, D0), g.OK),                   # K % 8 != 0: the general kernel
-    ((0, 64, 64, 64, A0 + 2, B0, D0), g.OK),               # A rows not 16-byte aligned: general kernel
+    ((0, 64, 64, 12, A0, B0, D0), g.OK),                   # K % 8 != 0: register-staged loads
+    ((0, 64, 64, 64, A0 + 2, B0, D0), g.OK),               # A rows not 16-byte aligned: the same
     ((0, 64, 64, 64, A0, B0 + 8, D0), g.OK),
     ((0, 64, 64, 64, A0, B0, D0 + 4), g.OK),
     ((3, 64, 64, 13, A0, B0, D0), g.OK),                   # R3 takes general operands too
-    ((4, 64, 64, 12, A0, B0, D0), g.UNSUPPORTED),          # the other rungs need 16-byte rows
-    ((4, 64, 64, 64, A0 + 2, B0, D0), g.UNSUPPORTED),
+    ((4, 64, 64, 12, A0, B0, D0), g.OK),                   # R4 and R9 stage general rows through registers
+    ((9, 64, 64, 64, A0 + 2, B0, D0), g.OK),
+    ((4, 64, 64, 4, A0, B0, D0), g.UNSUPPORTED),           # ... for K >= 8
+    ((9, 64, 64, 6, A0, B0, D0), g.UNSUPPORTED),
+    ((5, 64, 64, 12, A0, B0, D0), g.UNSUPPORTED),          # the other rungs need 16-byte rows
+    ((5, 64, 64, 64, A0 + 2, B0, D0), g.UNSUPPORTED),
     ((6, 256, 256, 128, A0, B0, D0 + 8), g.UNSUPPORTED),
     ((1, 128, 128, 64, A0, B0 + 2, D0), g.UNSUPPORTED),
     ((0, 64, 64, 64, A0 + 1, B0, D0), g.UNSUPPORTED),      # odd address: not an fp16 array
     ((0, 64, 64, 64, A0, B0, D0 + 1), g.UNSUPPORTED),
-    ((0, 64, 10_000_000, 12, A0, B0, D0), g.UNSUPPORTED),  # general kernel grid: N/128 > 65535
+    ((0, 64, 10_000_000, 4, A0, B0, D0), g.UNSUPPORTED),   # K < 8 runs on R3's grid: N/128 > 65535
+    ((3, 64, 10_000_000, 12, A0, B0, D0), g.UNSUPPORTED),  # so does rung 3
+    ((0, 64, 10_000_000, 12, A0, B0, D0), g.OK),           # the staged ring's grid is one-dimensional
     ((0, 64, 64, 64, A0, B0, A0 + 4096), g.INVALID_ARG),   # D overlaps A
     ((0, 64, 64, 64, A0, B0, B0), g.INVALID_ARG),          # D overlaps B
     ((11, 64, 64, 64, A0, B0, D0), g.INVALID_ARG),         # unknown rung
@@ -192,11 +198,12 @@ def test_schedule_xcd_locality():
     ((64, 64, 64, A0, 72, 0, B0, 64, 0, D0, 64, 4096, 3), g.OK),           # broadcast A and B
     ((64, 64, 64, A0, 56, 0, B0, 64, 0, D0, 64, 4096, 1), g.INVALID_ARG),  # lda < K
     ((64, 64, 64, A0, 64, 0, B0, 64, 0, D0, 60, 4096, 1), g.INVALID_ARG),  # ldd < N
-    ((64, 64, 64, A0, 68, 0, B0, 64, 0, D0, 64, 4096, 1), g.OK),           # lda % 8 != 0: general kernel
-    ((64, 64, 64, A0, 64, 4, B0, 64, 0, D0, 64, 4096, 2), g.OK),           # stride_a % 8 != 0: general kernel
+    ((64, 64, 64, A0, 68, 0, B0, 64, 0, D0, 64, 4096, 1), g.OK),           # lda % 8 != 0: register-staged loads
+    ((64, 64, 64, A0, 64, 4, B0, 64, 0, D0, 64, 4096, 2), g.OK),           # stride_a % 8 != 0: the same
     ((64, 64, 13, A0, 13, 832, B0, 13, 0, D0, 64, 4096, 2), g.OK),         # K % 8 != 0
     ((64, 64, 64, A0 + 1, 64, 0, B0, 64, 0, D0, 64, 4096, 1), g.UNSUPPORTED),  # odd address
-    ((64, 64, 64, A0, 68, 0, B0, 64, 0, D0, 64, 4096, 70000), g.UNSUPPORTED),  # general kernel: batch > 65535
+    ((64, 64, 4, A0, 68, 0, B0, 64, 0, D0, 64, 4096, 70000), g.UNSUPPORTED),   # K < 8 on R3's grid: batch > 65535
+    ((64, 64, 64, A0, 68, 0, B0, 64, 0, D0, 64, 4096, 70000), g.OK),           # the staged ring takes it
     ((64, 64, 64, A0, 64, 0, B0, 64, 0, D0, 66, 8192, 2), g.OK),           # odd row pitch of D
     ((64, 64, 64, A0, 64, 0, B0, 64, 0, D0, 64, 4097, 2), g.OK),           # odd batch stride of D
     ((64, 64, 64, A0, 64, 0, B0, 64, 0, D0, 64, 4000, 2), g.INVALID_ARG),  # outputs overlap
@@ -217,7 +224,7 @@ def test_splitk_workspace_sizes():
     assert L.gemm_f16_nt_splitk_workspace(256, 256, 512, 3) == 3 * 256 * 256 * 4
     # more slices than steps: one step per slice
     assert L.gemm_f16_nt_splitk_workspace(100, 60, 136, 16) == 3 * 100 * 60 * 4
-    # K % 8 != 0 runs on the general kernel, never split
+    # K % 8 != 0 runs unsplit (register-staged loads)
     assert L.gemm_f16_nt_splitk_workspace(100, 60, 130, 16) == 0
     assert L.gemm_f16_nt_splitk_workspace(256, 256, 512, 1) == 0
     assert L.gemm_f16_nt_splitk_workspace(256, 256, 0, 4) == 0
@@ -240,7 +247,9 @@ def test_splitk_workspace_sizes():
     ((4000, 4000, 4000), (10, 4000, 0)),
     ((200, 4096, 1024), (9, 200, 0)),
     ((4096, 4092, 1024), (4, 4096, 0)),       # N % 8 != 0: not the four-wave ring
-    ((100, 100, 100), (3, 100, 0)),           # K % 8 != 0: the general kernel
+    ((100, 100, 5), (3, 100, 0)),             # K < 8 off 16-byte rows: R3's general form
+    ((100, 100, 100), (9, 100, 0)),           # K % 8 != 0: R9's register-staged form
+    ((4096, 4096, 4095), (4, 4096, 0)),       # ... R4's when 256 x 256 tiles fill the device
 ])
 def test_library_plan(shape, want):
     assert g.plan(*shape, 256) == want

@@ -195,8 +195,10 @@ def test_error_paths_launch_nothing():
         g.gemm_f16_nt_rung(1, A[:, :56].contiguous(), B[:, :56].contiguous(), D)   # R1 needs K = 64
     assert e.value.status == g.UNSUPPORTED
     L = g.lib()
-    st = L.gemm_f16_nt_rung(4, 128, 128, 60, A.data_ptr(), B.data_ptr(), D.data_ptr(), None)
-    assert st == g.UNSUPPORTED          # the fast rungs need K % 8 == 0
+    st = L.gemm_f16_nt_rung(5, 128, 128, 60, A.data_ptr(), B.data_ptr(), D.data_ptr(), None)
+    assert st == g.UNSUPPORTED          # rungs other than 3, 4 and 9 need K % 8 == 0
+    st = L.gemm_f16_nt_rung(4, 128, 128, 4, A.data_ptr(), B.data_ptr(), D.data_ptr(), None)
+    assert st == g.UNSUPPORTED          # rungs 4 and 9 stage such rows for K >= 8 only
     st = L.gemm_f16_nt(128, 128, 64, A.data_ptr() + 1, B.data_ptr(), D.data_ptr(), None)
     assert st == g.UNSUPPORTED          # odd address: not an fp16 array
     st = L.gemm_f16_nt(128, 128, 64, A.data_ptr(), B.data_ptr(), A.data_ptr() + 64, None)
@@ -485,12 +487,19 @@ def test_full_size_workloads_sampled(name):
 GENERAL = [(1, 1, 1), (5, 3, 7), (64, 64, 13), (130, 70, 100), (257, 129, 1001), (300, 260, 9), (128, 128, 66)]
 
 
-@pytest.mark.parametrize("rung", [0, 3])
+@pytest.mark.parametrize("rung", [0, 3, 4, 9])
 @pytest.mark.parametrize("shape", GENERAL, ids=lambda s: "x".join(map(str, s)))
 def test_general_k(rung, shape):
-    """K % 8 != 0: rows are not 16-byte aligned, so the general kernel runs."""
+    """K % 8 != 0: rows are not 16-byte aligned.  The library runs the ring
+    with register-staged loads (K >= 8) or R3's general form (K < 8); rung 3
+    always runs the latter, rungs 4 and 9 the former (K >= 8 only)."""
     M, N, K = shape
     A, B = rand_case(M, N, K, 200 + M + N + K)
+    if rung in (4, 9) and K < 8:
+        with pytest.raises(g.GemmError) as e:
+            g.gemm_f16_nt_rung(rung, dev(A), dev(B))
+        assert e.value.status == g.UNSUPPORTED
+        return
     ref, _ = oracle.gemm_nt(A, B)
     say(f"[gpu] general K rung={rung} M={M} N={N} K={K}")
     D = run(rung, dev(A), dev(B))
@@ -513,12 +522,85 @@ def test_misaligned_operands(offs):
     ref, _ = oracle.gemm_nt(A, B)
     dA, dB = _offset_view(A, offs[0]), _offset_view(B, offs[1])
     D = _offset_view(np.zeros((M, N), np.float16), offs[2])
-    say(f"[gpu] misaligned offsets {offs}")
-    run(0, dA, dB, D)
-    assert_parity(host_bits(D), ref, K, f"misaligned {offs}")
+    for rung in (0, 3, 4, 9):
+        say(f"[gpu] misaligned offsets {offs} rung={rung}")
+        D.fill_(float("nan"))
+        run(rung, dA, dB, D)
+        assert_parity(host_bits(D), ref, K, f"misaligned {offs} rung {rung}")
     with pytest.raises(g.GemmError) as e:     # the other rungs refuse them
-        g.gemm_f16_nt_rung(4, dA, dB, D)
+        g.gemm_f16_nt_rung(5, dA, dB, D)
     assert e.value.status == g.UNSUPPORTED
+
+
+# ------------------------ general operands on the pipelined ring (K >= 8)
+
+# (M, N, K, element offsets of A, B and D).  Operands whose rows are off
+# 16-byte boundaries run the ring with register-staged loads: on 128 x 128
+# tiles when 256 x 256 ones would leave most compute units idle (up to 102
+# tiles on 256 CUs), on 256 x 256 tiles otherwise.
+STAGED = [
+    (200, 136, 8, (0, 0, 0)),
+    (300, 260, 63, (0, 0, 0)),
+    (257, 385, 65, (1, 0, 0)),
+    (1000, 1000, 1001, (0, 0, 0)),
+    (2816, 2816, 9, (0, 0, 0)),
+    (3072, 2816, 133, (0, 0, 0)),
+    (2600, 2900, 517, (1, 3, 5)),
+    (2816, 3072, 1000, (0, 1, 0)),
+    (2944, 2816, 255, (7, 0, 2)),
+]
+
+
+def _staged_operands(A, B, M, N, offs):
+    dA, dB = _offset_view(A, offs[0]), _offset_view(B, offs[1])
+    D = _offset_view(np.full((M, N), np.nan, np.float16), offs[2])
+    return dA, dB, D
+
+
+@pytest.mark.parametrize("shape", STAGED, ids=lambda s: "{}x{}x{}_a{}b{}d{}".format(*s[:3], *s[3]))
+def test_staged_ring_general_operands(shape):
+    M, N, K, offs = shape
+    A, B = rand_case(M, N, K, 700 + K)
+    ref, _ = oracle.gemm_nt(A, B)
+    dA, dB, D = _staged_operands(A, B, M, N, offs)
+    say(f"[gpu] staged ring M={M} N={N} K={K} offsets={offs}")
+    run(0, dA, dB, D)
+    assert_parity(host_bits(D), ref, K, f"staged {M}x{N}x{K} {offs}")
+
+
+@pytest.mark.parametrize("shape", [(384, 320, 75, (3, 1, 0)), (2816, 2816, 203, (1, 0, 3))],
+                         ids=lambda s: "{}x{}x{}".format(*s[:3]))
+def test_staged_ring_selection_bitwise(shape):
+    """A selects one element of each B row per output: D = B[:, pick]^T
+    exactly.  Picks at both ends of K land in the chunk that crosses K and
+    in the first one."""
+    M, N, K, offs = shape
+    rng = np.random.default_rng(K)
+    pick = rng.integers(0, K, M)
+    pick[:10] = [K - 1, K - 2, K - 3, K - 7, K - 8, K - 9, 0, 1, 7, 8]
+    A = np.zeros((M, K), np.float16)
+    A[np.arange(M), pick] = 1
+    B = rng.uniform(-60000, 60000, (N, K)).astype(np.float16)
+    dA, dB, D = _staged_operands(A, B, M, N, offs)
+    say(f"[gpu] staged selection M={M} N={N} K={K} offsets={offs}")
+    run(0, dA, dB, D)
+    assert np.array_equal(host_bits(D), B[:, pick].T.view(np.uint16))
+
+
+@pytest.mark.parametrize("shape", [(264, 256, 1001, (0, 0, 0)), (2816, 2816, 777, (5, 2, 1))],
+                         ids=lambda s: "{}x{}x{}".format(*s[:3]))
+def test_staged_ring_small_integers_bitwise(shape):
+    """Integer sums below 2^24 are exact in any fp32 order: bitwise parity."""
+    M, N, K, offs = shape
+    rng = np.random.default_rng(M + K)
+    A = rng.integers(-4, 5, (M, K)).astype(np.float16)
+    B = rng.integers(-4, 5, (N, K)).astype(np.float16)
+    ref, _ = oracle.gemm_nt(A, B)
+    dA, dB, D = _staged_operands(A, B, M, N, offs)
+    say(f"[gpu] staged small-int M={M} N={N} K={K} offsets={offs}")
+    run(0, dA, dB, D)
+    got = host_bits(D)
+    assert np.array_equal(got, ref), f"{np.sum(got != ref)} mismatches"
 
 
 # ------------------------------------------------- strided / batched form
@@ -548,8 +630,9 @@ def _padded(X: np.ndarray, ld: int):
     (2, 256, 256, 64, 64, 0, 0, False),      # whole tiles with padded A rows
     (4, 130, 70, 40, 16, 8, 12, True),       # B shared by every batch entry
     (1, 1, 1, 8, 0, 0, 0, False),
-    (3, 97, 45, 21, 3, 5, 1, False),         # K % 8 != 0, odd pitches: the general kernel
-    (2, 256, 256, 128, 4, 0, 0, True),       # whole tiles but lda % 8 != 0: the general kernel
+    (3, 97, 45, 21, 3, 5, 1, False),         # K % 8 != 0, odd pitches: register-staged loads
+    (2, 256, 256, 128, 4, 0, 0, True),       # whole tiles but lda % 8 != 0: register-staged loads
+    (4, 1536, 1536, 200, 3, 0, 2, False),    # odd pitches on 256 x 256 tiles (144 of them)
 ], ids=lambda c: "b{}_{}x{}x{}".format(*c[:4]))
 def test_strided_batched(case):
     batch, M, N, K, pa, pb, pd, bcast = case
