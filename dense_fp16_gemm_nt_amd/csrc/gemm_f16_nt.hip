@@ -110,12 +110,13 @@ bool ring4_shape(int64_t M, int64_t N, int64_t K)
 // a multiple of 64, as long as it is a multiple of 8 above 64: its first
 // step is the partial one, whose chunks before a row's first element are
 // moved out of range by a mask that needs every operand band of 256 rows
-// under 2^30 bytes (lda, ldb < 2^21).
+// under 2^30 bytes (lda, ldb < 2^21).  It also takes any N >= 256: its
+// 16-byte output stores go to any 2-byte boundary (gfx950's buffer stores
+// take unaligned addresses), where the other forms keep N % 8 == 0.
 bool ring4_paired_shape(int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb)
 {
-    if (K % ring4::C::BK == 0) return ring4_shape(M, N, K);
-    return M >= ring4::C::BM && N >= ring4::C::BN && N % 8 == 0 && K % 8 == 0 && K > ring4::C::BK &&
-           lda < (int64_t(1) << 21) && ldb < (int64_t(1) << 21);
+    if (M < ring4::C::BM || N < ring4::C::BN || K % 8 != 0 || K <= ring4::C::BK) return false;
+    return K % ring4::C::BK == 0 || (lda < (int64_t(1) << 21) && ldb < (int64_t(1) << 21));
 }
 
 // Operands the 16-byte-load kernels take: every row of A and B starts on a
@@ -223,10 +224,10 @@ int launch_fill_zero(void* D, int64_t n, hipStream_t s)
 }
 
 // Whether the four-wave scheduled ring (its fourth form) covers this
-// problem: its shapes and 16-byte aligned output rows in every batch entry.
+// problem: its shapes and an output row pitch under 2^24 elements.
 bool ring4_fits(const GemmArgs& g)
 {
-    return ring4_paired_shape(g.M, g.N, g.K, g.lda, g.ldb) && g.ldd % 8 == 0 && g.sd % 8 == 0 &&
+    return ring4_paired_shape(g.M, g.N, g.K, g.lda, g.ldb) &&
            g.ldd < (int64_t(1) << 24);
 }
 

@@ -90,12 +90,16 @@ class ExtraWorkload:
 
 
 EXTRA_WORKLOADS = [
-    # ragged M, N and K (K % 64 != 0): the edge variant of the 8-wave ring
+    # ragged M, N and K (K % 64 != 0): the four-wave ring, partial first k step
     ExtraWorkload("ragged_4000", "gemm", 1, 4000, 4000, 4000, 11, U11),
     # ragged M and N, whole 64-wide k steps: the four-wave ring with clamped edge tiles
     ExtraWorkload("ragged_mn_4000x4000x4096", "gemm", 1, 4000, 4000, 4096, 12, U11),
-    # K % 8 != 0: operand rows are not 16-byte aligned, so the general kernel runs
+    # K % 8 != 0: operand rows are not 16-byte aligned, so the 8-wave ring
+    # stages its loads through registers
     ExtraWorkload("unaligned_k_4096x4096x4095", "gemm", 1, 4096, 4096, 4095, 13, U11),
+    # N % 8 != 0: rows of D are not 16-byte aligned, so the 8-wave ring with
+    # edge tiles runs (unaligned 16-byte stores, the last chunk of a row by element)
+    ExtraWorkload("ragged_n_4096x4092x4096", "gemm", 1, 4096, 4092, 4096, 20, U11),
     # a small last round of tiles (2.25 rounds on 256 compute units, and a
     # ragged M): whole rounds unsplit, the remaining rows split K
     ExtraWorkload("splitk_rounds_6144x6144x6144", "splitk", 1, 6144, 6144, 6144, 18, U11),

@@ -76,11 +76,11 @@ extern "C" {
                                        library's choice when 256 x 256 tiles would number at most 0.4
                                        per compute unit */
 #define GEMM_F16_NT_R10_RING4_PAIRED 10 /* rung 8 with each 16 x 16 block's two 32-wide sub-steps issued
-                                           back to back into its accumulator; the shapes of rung 6, and
-                                           also K a multiple of 8 above 64 that is not a multiple of 64
-                                           (the partial k step goes first; rows of A and B then
-                                           shorter than 2^21 elements); the library's choice for those
-                                           shapes */
+                                           back to back into its accumulator; the shapes of rung 6 with
+                                           any N >= 256 (rows of D on any 2-byte boundary), and also K a
+                                           multiple of 8 above 64 that is not a multiple of 64 (the
+                                           partial k step goes first; rows of A and B then shorter than
+                                           2^21 elements); the library's choice for those shapes */
 
 /* D = A * B^T with the library's choice of kernel for the shape (see
  * gemm_f16_nt_plan; when the 256 x 256 tiles leave a small last round,

@@ -79,6 +79,8 @@ A0, B0, D0 = 0x10000, 0x20000000, 0x40000000   # fake, 16-byte aligned, disjoint
     ((11, 64, 64, 64, A0, B0, D0), g.INVALID_ARG),         # unknown rung
     ((10, 64, 64, 64, A0, B0, D0), g.UNSUPPORTED),         # rung 10: M, N >= 256
     ((10, 512, 256, 192, A0, B0, D0), g.OK),
+    ((10, 256, 260, 128, A0, B0, D0), g.OK),              # rung 10 takes any N >= 256
+    ((6, 256, 260, 128, A0, B0, D0), g.UNSUPPORTED),      # rungs 6-8 keep N % 8 == 0
     ((10, 256, 256, 136, A0, B0, D0), g.OK),               # rung 10: K % 64 != 0, partial first step
     ((10, 256, 264, 72, A0, B0, D0), g.OK),
     ((10, 256, 256, 64, A0, B0, D0), g.UNSUPPORTED),       # ... but at least two k steps
@@ -246,7 +248,7 @@ def test_splitk_workspace_sizes():
     ((2560, 2560, 4096), (9, 2560, 0)),
     ((4000, 4000, 4000), (10, 4000, 0)),
     ((200, 4096, 1024), (9, 200, 0)),
-    ((4096, 4092, 1024), (4, 4096, 0)),       # N % 8 != 0: not the four-wave ring
+    ((4096, 4092, 1024), (10, 4096, 0)),      # N % 8 != 0: the fourth form stores unaligned rows
     ((100, 100, 5), (3, 100, 0)),             # K < 8 off 16-byte rows: R3's general form
     ((100, 100, 100), (9, 100, 0)),           # K % 8 != 0: R9's register-staged form
     ((4096, 4096, 4095), (4, 4096, 0)),       # ... R4's when 256 x 256 tiles fill the device

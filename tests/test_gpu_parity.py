@@ -50,8 +50,8 @@ def supported(rung, M, N, K):
         return (M, N, K) == (128, 128, 64)
     if rung == 2:
         return (M, N) == (128, 128)
-    if rung == 10:   # also a partial first step when K is not a multiple of 64
-        return M >= 256 and N >= 256 and N % 8 == 0 and K % 8 == 0 and K > 64
+    if rung == 10:   # also a partial first step when K is not a multiple of 64, and any N
+        return M >= 256 and N >= 256 and K % 8 == 0 and K > 64
     if rung in RING4_RUNGS:
         return M >= 256 and N >= 256 and N % 8 == 0 and K % 64 == 0 and K >= 128
     return True
@@ -263,7 +263,8 @@ def test_ring4_persistent_rounds(rung, shape):
     assert_parity(host_bits(D), ref, K, f"rung {rung} {M}x{N}x{K}")
 
 
-@pytest.mark.parametrize("shape", [(300, 264, 128), (520, 776, 256), (1000, 1032, 192), (4000, 4000, 1024)],
+@pytest.mark.parametrize("shape", [(300, 264, 128), (520, 776, 256), (1000, 1032, 192), (4000, 4000, 1024),
+                                   (300, 261, 128), (520, 777, 200), (1000, 1030, 1024)],
                          ids=lambda s: "x".join(map(str, s)))
 def test_ring4_ragged_tiles(shape):
     """M, N not multiples of 256 on the four-wave ring: the last tile row and
@@ -276,7 +277,9 @@ def test_ring4_ragged_tiles(shape):
     ref, _ = oracle.gemm_nt(A, B)
     dA, dB = dev(A), dev(B)
     for rung in (0,) + RING4_RUNGS:
-        assert supported(rung, M, N, K)
+        if not supported(rung, M, N, K):
+            assert N % 8 or K % 64, "only N % 8 != 0 or K % 64 != 0 leave out rungs 6-8"
+            continue
         D = torch.full((M, N), float("nan"), dtype=torch.float16, device=DEV)
         say(f"[gpu] ring4 ragged rung={rung} {M}x{N}x{K}")
         run(rung, dA, dB, D)
@@ -677,9 +680,11 @@ def test_attention_scores(layout):
             assert_parity(host_bits(S[b, h].contiguous()), ref, d, f"b{b} h{h}")
 
 
-def test_strided_unaligned_output_rows():
-    """Row pitch and batch stride of D that leave rows 2-byte aligned only."""
-    batch, M, N, K = 2, 260, 257, 64
+@pytest.mark.parametrize("K", [64, 128, 200])
+def test_strided_unaligned_output_rows(K):
+    """Row pitch and batch stride of D that leave rows 2-byte aligned only
+    (K = 64 on R4's edge tiles, longer K on the four-wave ring)."""
+    batch, M, N = 2, 260, 257
     rng = np.random.default_rng(31)
     As = [rng.uniform(-1, 1, (M, K)).astype(np.float16) for _ in range(batch)]
     Bs = [rng.uniform(-1, 1, (N, K)).astype(np.float16) for _ in range(batch)]
