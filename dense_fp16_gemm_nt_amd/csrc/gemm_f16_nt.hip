@@ -467,16 +467,22 @@ int launch_splitk(int64_t M, int64_t N, int64_t K, const void* A, const void* B,
                            dim3((unsigned)blocks), dim3(RingCfg::THREADS), 0, s, g);
     int st = launched();
     if (st != GEMM_F16_NT_OK) return st;
+    // one wave per workgroup when 4-wave ones would not reach every compute
+    // unit (a 256 x 256 output is 16384 items)
+    int cus = 0;
+    st = device_info(&cus);
+    if (st != GEMM_F16_NT_OK) return st;
     const bool vec = N % 4 == 0;
     const int64_t items = vec ? M * N / 4 : M * N;
-    const int64_t rblocks = (items + 255) / 256;
-    const unsigned rgrid = (unsigned)(rblocks < 8192 ? rblocks : 8192);
+    const int threads = items < 256 * (int64_t)cus ? 64 : 256;
+    const int64_t rblocks = (items + threads - 1) / threads;
+    const unsigned rgrid = (unsigned)(rblocks < 16384 ? rblocks : 16384);
     if (vec)
-        hipLaunchKernelGGL(ring::splitk_reduce_kernel<true>, dim3(rgrid), dim3(256), 0, s, P, (f16*)D, M, N, N,
+        hipLaunchKernelGGL(ring::splitk_reduce_kernel<true>, dim3(rgrid), dim3(threads), 0, s, P, (f16*)D, M, N, N,
                            n_slices);
     else
-        hipLaunchKernelGGL(ring::splitk_reduce_kernel<false>, dim3(rgrid), dim3(256), 0, s, P, (f16*)D, M, N, N,
-                           n_slices);
+        hipLaunchKernelGGL(ring::splitk_reduce_kernel<false>, dim3(rgrid), dim3(threads), 0, s, P, (f16*)D, M, N,
+                           N, n_slices);
     return launched();
 }
 

@@ -476,26 +476,41 @@ __global__ __launch_bounds__(C::THREADS, 1) void ring_kernel(const GemmArgs g)
 
 // Split-K reduction: D = fp16(sum over slices s = 0, 1, ... of P[s]), in
 // slice order, rounded once (round-to-nearest-even).  Four outputs per
-// thread when N % 4 == 0, else one.
+// thread when N % 4 == 0, else one.  The partial sums were written by other
+// XCDs, so each read waits on the fabric: with more than 2 * kReduceAhead
+// slices a thread loads kReduceAhead of them before adding them (in order);
+// measured on MI355X, that cut 256 x 256 x 65536 (64 slices) from 45.9 to
+// 35.6 us but cost 3% with 16 slices.
+constexpr int kReduceAhead = 8;
+
 template <bool VEC>
-__global__ void splitk_reduce_kernel(const float* __restrict__ P, f16* __restrict__ D, int64_t M, int64_t N,
-                                     int64_t ldd, int64_t splits)
+__global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restrict__ P, f16* __restrict__ D,
+                                                           int64_t M, int64_t N, int64_t ldd, int64_t splits)
 {
+    typedef typename std::conditional<VEC, f32x4, float>::type T;
+    constexpr int U = kReduceAhead;
     const int64_t MN = M * N;
     const int64_t per = VEC ? 4 : 1;
     const int64_t n_items = MN / per;
     const int64_t stride = (int64_t)gridDim.x * blockDim.x;
     for (int64_t it = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; it < n_items; it += stride) {
         const int64_t e = it * per, row = e / N, col = e - row * N;
-        if (VEC) {
-            f32x4 s = *reinterpret_cast<const f32x4*>(P + e);
-            for (int64_t k = 1; k < splits; ++k) s += *reinterpret_cast<const f32x4*>(P + k * MN + e);
-            *reinterpret_cast<f16x4*>(D + row * ldd + col) = cvt4(s[0], s[1], s[2], s[3]);
-        } else {
-            float s = P[e];
-            for (int64_t k = 1; k < splits; ++k) s += P[k * MN + e];
-            D[row * ldd + col] = (f16)s;
+        const T* p = reinterpret_cast<const T*>(P + e);
+        const int64_t step = MN / per;   // one slice, in units of T
+        T s = p[0];
+        int64_t k = 1;
+        for (; splits > 2 * U && k + U <= splits; k += U) {
+            T v[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) v[u] = p[(k + u) * step];
+#pragma unroll
+            for (int u = 0; u < U; ++u) s += v[u];
         }
+        for (; k < splits; ++k) s += p[k * step];
+        if constexpr (VEC)
+            *reinterpret_cast<f16x4*>(D + row * ldd + col) = cvt4(s[0], s[1], s[2], s[3]);
+        else
+            D[row * ldd + col] = (f16)s;
     }
 }
 
