@@ -281,6 +281,24 @@ int launch_ring_small(const GemmArgs& g0, hipStream_t s)
     return launched();
 }
 
+// Whether 128 x 128 tiles (R9) beat 256 x 256 ones (R4) on a shape the
+// four-wave ring does not take, counted in rounds of tiles over the compute
+// units: a 128-wide tile is a quarter of the work at about 0.75 of R4's
+// rate (measured on MI355X at 4096^3: 929 against 1232 TFLOP/s).  When M or
+// N is small, most of a 256-wide tile is padding and its tiles may not fill
+// the device (128 x 32768 x 4096: 128 tiles of 256^2, 91 us on R4 against
+// 48 us on R9's 256 tiles).
+constexpr double kSmallTileRate = 0.75;
+
+bool small_tiles_pay(int64_t M, int64_t N, int64_t batch, int cus)
+{
+    auto rounds = [&](int64_t t) {
+        const int64_t tiles = ((M + t - 1) / t) * ((N + t - 1) / t) * batch;
+        return (double)((tiles + cus - 1) / cus);
+    };
+    return rounds(RingSmallCfg::BM) * 0.25 / kSmallTileRate < rounds(kFastTile);
+}
+
 // Whether 256 x 256 tiles would leave most compute units idle.
 bool tile_starved(const GemmArgs& g)
 {
@@ -331,6 +349,11 @@ int launch_ring(const GemmArgs& g0, hipStream_t s, bool allow_ring4 = false)
         rest.D = g0.D + m_top * g0.ldd;
         st = launch_ring4(top, s);
         return st != GEMM_F16_NT_OK ? st : launch_ring_small(rest, s);
+    }
+    if (allow_ring4) {
+        int cus = 0, st = device_info(&cus);
+        if (st != GEMM_F16_NT_OK) return st;
+        if (small_tiles_pay(g0.M, g0.N, g0.batch, cus)) return launch_ring_small(g0, s);
     }
     GemmArgs g = g0;
     g.tiles_m = (g.M + kFastTile - 1) / kFastTile;
@@ -521,7 +544,9 @@ int launch_staged(const GemmArgs& g0, hipStream_t s, bool small)
 int launch_any(const GemmArgs& g, hipStream_t s)
 {
     if (g.K < 8) return launch_r3_any(g, s);
-    return launch_staged(g, s, tile_starved(g));
+    int cus = 0, st = device_info(&cus);
+    if (st != GEMM_F16_NT_OK) return st;
+    return launch_staged(g, s, tile_starved(g) || small_tiles_pay(g.M, g.N, g.batch, cus));
 }
 
 GemmArgs contiguous_args(int64_t M, int64_t N, int64_t K, const void* A, const void* B, void* D)
@@ -768,9 +793,8 @@ int gemm_f16_nt_plan(int64_t M, int64_t N, int64_t K, int cus, int* rung_top, in
     *rung_rest = 0;
     const int64_t tiles = ((M + kFastTile - 1) / kFastTile) * ((N + kFastTile - 1) / kFastTile);
     if (K % 8 != 0) {   // R3's general form, or R9's / R4's register-staged form
-        *rung_top = K < 8 ? GEMM_F16_NT_R3_GRID
-                          : (tiles * 10 <= (int64_t)cus * kSmallTilesPer10Cus ? GEMM_F16_NT_R9_RING_SMALL
-                                                                               : GEMM_F16_NT_R4_RING);
+        const bool small = tiles * 10 <= (int64_t)cus * kSmallTilesPer10Cus || small_tiles_pay(M, N, 1, cus);
+        *rung_top = K < 8 ? GEMM_F16_NT_R3_GRID : (small ? GEMM_F16_NT_R9_RING_SMALL : GEMM_F16_NT_R4_RING);
         return GEMM_F16_NT_OK;
     }
     if (tiles * 10 <= (int64_t)cus * kSmallTilesPer10Cus) {
@@ -782,7 +806,7 @@ int gemm_f16_nt_plan(int64_t M, int64_t N, int64_t K, int cus, int* rung_top, in
         else
             *m_top = M;
     } else {
-        *rung_top = GEMM_F16_NT_R4_RING;
+        *rung_top = small_tiles_pay(M, N, 1, cus) ? GEMM_F16_NT_R9_RING_SMALL : GEMM_F16_NT_R4_RING;
     }
     return GEMM_F16_NT_OK;
 }

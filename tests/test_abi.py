@@ -249,6 +249,11 @@ def test_splitk_workspace_sizes():
     ((4000, 4000, 4000), (10, 4000, 0)),
     ((200, 4096, 1024), (9, 200, 0)),
     ((4096, 4092, 1024), (10, 4096, 0)),      # N % 8 != 0: the fourth form stores unaligned rows
+    ((4096, 4096, 64), (4, 4096, 0)),         # one k step: not the four-wave ring
+    ((128, 32768, 4096), (9, 128, 0)),        # M = 128: half of every 256-row tile would be padding
+    ((200, 32768, 4096), (9, 200, 0)),        # M = 200: 128 tiles of 256^2 fill half the device
+    ((384, 65536, 64), (4, 384, 0)),          # 512 tiles of 256^2 against 1536 of 128^2
+    ((128, 32768, 4095), (9, 128, 0)),        # ... also for register-staged rows
     ((100, 100, 5), (3, 100, 0)),             # K < 8 off 16-byte rows: R3's general form
     ((100, 100, 100), (9, 100, 0)),           # K % 8 != 0: R9's register-staged form
     ((4096, 4096, 4095), (4, 4096, 0)),       # ... R4's when 256 x 256 tiles fill the device

@@ -535,6 +535,21 @@ def test_misaligned_operands(offs):
     assert e.value.status == g.UNSUPPORTED
 
 
+@pytest.mark.parametrize("shape", [(128, 30000, 320), (100, 28000, 203)], ids=lambda s: "x".join(map(str, s)))
+def test_library_thin_shapes(shape):
+    """M well under 256 with enough tiles not to be tile-starved: the library
+    takes 128 x 128 tiles (aligned rows, and register-staged ones for
+    K % 8 != 0), which it checks against the oracle on every output."""
+    M, N, K = shape
+    A, B = rand_case(M, N, K, 40 + M)
+    ref, _ = oracle.gemm_nt(A, B)
+    assert g.plan(M, N, K, 256)[0] == 9
+    say(f"[gpu] thin shape {M}x{N}x{K}")
+    D = torch.full((M, N), float("nan"), dtype=torch.float16, device=DEV)
+    run(0, dev(A), dev(B), D)
+    assert_parity(host_bits(D), ref, K, f"thin {M}x{N}x{K}")
+
+
 # ------------------------ general operands on the pipelined ring (K >= 8)
 
 # (M, N, K, element offsets of A, B and D).  Operands whose rows are off
