@@ -74,7 +74,8 @@ extern "C" {
 #define GEMM_F16_NT_R9_RING_SMALL 9 /* any shape: rung 4's ring with 128 x 128 tiles, 8 waves of 64 x 32 and
                                        4 stages (the same register staging on general rows); the
                                        library's choice when 256 x 256 tiles would number at most 0.4
-                                       per compute unit */
+                                       per compute unit, and, off the four-wave ring, where its tiles
+                                       take fewer rounds of the compute units than rung 4's */
 #define GEMM_F16_NT_R10_RING4_PAIRED 10 /* rung 8 with each 16 x 16 block's two 32-wide sub-steps issued
                                            back to back into its accumulator; the shapes of rung 6 with
                                            any N >= 256 (rows of D on any 2-byte boundary), and also K a
