@@ -100,6 +100,9 @@ EXTRA_WORKLOADS = [
     # N % 8 != 0: rows of D are not 16-byte aligned, so the 8-wave ring with
     # edge tiles runs (unaligned 16-byte stores, the last chunk of a row by element)
     ExtraWorkload("ragged_n_4096x4092x4096", "gemm", 1, 4096, 4092, 4096, 20, U11),
+    # M = 128: 256 x 256 tiles would be half padding and fill half the device,
+    # so the library takes 128 x 128 tiles
+    ExtraWorkload("thin_m_128x32768x4096", "gemm", 1, 128, 32768, 4096, 21, U11),
     # a small last round of tiles (2.25 rounds on 256 compute units, and a
     # ragged M): whole rounds unsplit, the remaining rows split K
     ExtraWorkload("splitk_rounds_6144x6144x6144", "splitk", 1, 6144, 6144, 6144, 18, U11),
