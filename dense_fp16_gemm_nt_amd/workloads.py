@@ -97,8 +97,8 @@ EXTRA_WORKLOADS = [
     # K % 8 != 0: operand rows are not 16-byte aligned, so the 8-wave ring
     # stages its loads through registers
     ExtraWorkload("unaligned_k_4096x4096x4095", "gemm", 1, 4096, 4096, 4095, 13, U11),
-    # N % 8 != 0: rows of D are not 16-byte aligned, so the 8-wave ring with
-    # edge tiles runs (unaligned 16-byte stores, the last chunk of a row by element)
+    # N % 8 != 0: rows of D are not 16-byte aligned, so the four-wave ring
+    # stores its 16-byte chunks of D unaligned
     ExtraWorkload("ragged_n_4096x4092x4096", "gemm", 1, 4096, 4092, 4096, 20, U11),
     # M = 128: 256 x 256 tiles would be half padding and fill half the device,
     # so the library takes 128 x 128 tiles
