@@ -77,6 +77,8 @@ def lib() -> ctypes.CDLL:
             L.gemm_f16_nt_status_string.argtypes = [i32]
             L.gemm_f16_nt_schedule.restype = i64
             L.gemm_f16_nt_schedule.argtypes = [i64, i64, i64, i64p, i64p, i64p, i64]
+            L.gemm_f16_nt_tile_walk.restype = i64
+            L.gemm_f16_nt_tile_walk.argtypes = [i32, i64, i64, i32, i64p, i64p, i64p, i64]
             L.gemm_f16_nt_plan.restype = i32
             L.gemm_f16_nt_plan.argtypes = [i64, i64, i64, i32, ctypes.POINTER(ctypes.c_int), i64p,
                                            ctypes.POINTER(ctypes.c_int)]
@@ -298,6 +300,24 @@ def schedule(M: int, N: int, num_workgroups: int):
     p = lambda a: a.ctypes.data_as(ctypes.POINTER(ctypes.c_int64))  # noqa: E731
     L.gemm_f16_nt_schedule(M, N, num_workgroups, p(wg), p(tm), p(tn), n)
     return wg, tm, tn
+
+
+def tile_walk(rung: int, M: int, N: int, cus: int):
+    """Host evaluation of a rung's tile walk on `cus` compute units:
+    (wg, row0, col0) arrays, one entry per tile visit in workgroup-major
+    visit order (the first output row and column of each tile)."""
+    import numpy as np
+
+    L = lib()
+    n = L.gemm_f16_nt_tile_walk(rung, M, N, cus, None, None, None, 0)
+    if n < 0:
+        raise GemmError(int(n), "gemm_f16_nt_tile_walk")
+    wg = np.empty(n, np.int64)
+    r0 = np.empty(n, np.int64)
+    c0 = np.empty(n, np.int64)
+    p = lambda a: a.ctypes.data_as(ctypes.POINTER(ctypes.c_int64))  # noqa: E731
+    L.gemm_f16_nt_tile_walk(rung, M, N, cus, p(wg), p(r0), p(c0), n)
+    return wg, r0, c0
 
 
 def ring_plan(depth: int, steps: int):

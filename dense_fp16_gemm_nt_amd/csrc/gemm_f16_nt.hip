@@ -119,6 +119,12 @@ bool ring4_paired_shape(int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ld
     return K % ring4::C::BK == 0 || (lda < (int64_t(1) << 21) && ldb < (int64_t(1) << 21));
 }
 
+// The four-wave ring's output buffer resource spans the 128 rows of a
+// wave's block, 256 * ldd bytes in a 32-bit size: the output row pitch
+// must stay under 2^24 elements (above, the size would wrap and the
+// hardware's range check would drop stores).
+bool ring4_pitch_ok(int64_t ldd) { return ldd < (int64_t(1) << 24); }
+
 // Operands the 16-byte-load kernels take: every row of A and B starts on a
 // 16-byte boundary (K, leading dimensions and batch strides multiples of 8
 // elements, 16-byte aligned bases) and D's base is 16-byte aligned.  Other
@@ -150,9 +156,10 @@ int validate(int rung, int64_t M, int64_t N, int64_t K, const void* A, const voi
     if (rung == GEMM_F16_NT_R2_KLOOP && !(M == 128 && N == 128)) return GEMM_F16_NT_UNSUPPORTED;
     if (rung == GEMM_F16_NT_R3_GRID && (N + 127) / 128 > 65535) return GEMM_F16_NT_UNSUPPORTED;
     if ((rung == GEMM_F16_NT_R6_RING4 || rung == GEMM_F16_NT_R7_RING4_2B || rung == GEMM_F16_NT_R8_RING4_GAP) &&
-        !ring4_shape(M, N, K))
+        !(ring4_shape(M, N, K) && ring4_pitch_ok(N)))
         return GEMM_F16_NT_UNSUPPORTED;
-    if (rung == GEMM_F16_NT_R10_RING4_PAIRED && !ring4_paired_shape(M, N, K, K, K)) return GEMM_F16_NT_UNSUPPORTED;
+    if (rung == GEMM_F16_NT_R10_RING4_PAIRED && !(ring4_paired_shape(M, N, K, K, K) && ring4_pitch_ok(N)))
+        return GEMM_F16_NT_UNSUPPORTED;
     if (!any_out) return GEMM_F16_NT_OK;
     // fp16 elements are 2-byte aligned; the fast kernels need 16 bytes
     if ((K > 0 && (((uintptr_t)A & 1) || ((uintptr_t)B & 1))) || ((uintptr_t)D & 1)) return GEMM_F16_NT_UNSUPPORTED;
@@ -227,8 +234,7 @@ int launch_fill_zero(void* D, int64_t n, hipStream_t s)
 // problem: its shapes and an output row pitch under 2^24 elements.
 bool ring4_fits(const GemmArgs& g)
 {
-    return ring4_paired_shape(g.M, g.N, g.K, g.lda, g.ldb) &&
-           g.ldd < (int64_t(1) << 24);
+    return ring4_paired_shape(g.M, g.N, g.K, g.lda, g.ldb) && ring4_pitch_ok(g.ldd);
 }
 
 // Persistent launch: one workgroup per compute unit (fewer when there are
@@ -418,7 +424,7 @@ GemmArgs contiguous_args(int64_t M, int64_t N, int64_t K, const void* A, const v
 
 bool hybrid_plan(int64_t M, int64_t N, int64_t K, int cus, int64_t* m_top, int64_t* splits)
 {
-    if (K % 8 != 0 || !ring4_paired_shape(ring4::C::BM, N, K, K, K)) return false;
+    if (K % 8 != 0 || !ring4_paired_shape(ring4::C::BM, N, K, K, K) || !ring4_pitch_ok(N)) return false;
     // where the unsplit call already moves a small last round to 128 x 128
     // tiles that fit in one round, that is as fast (measured: 4352^2 x 4096
     // 120 us unsplit against 128 us split); it loses to the split when they
@@ -778,6 +784,51 @@ int64_t gemm_f16_nt_schedule(int64_t M, int64_t N, int64_t num_workgroups, int64
                 wg[n] = w;
                 tile_m[n] = c.m_idx;
                 tile_n[n] = c.n_idx;
+            }
+            ++n;
+        }
+    return n;
+}
+
+int64_t gemm_f16_nt_tile_walk(int rung, int64_t M, int64_t N, int cus, int64_t* wg, int64_t* row0, int64_t* col0,
+                              int64_t capacity)
+{
+    if (M < 0 || N < 0 || cus < 1 || capacity < 0) return GEMM_F16_NT_INVALID_ARG;
+    if (capacity > 0 && (wg == nullptr || row0 == nullptr || col0 == nullptr)) return GEMM_F16_NT_INVALID_ARG;
+    const bool four_wave = rung == GEMM_F16_NT_R6_RING4 || rung == GEMM_F16_NT_R7_RING4_2B ||
+                           rung == GEMM_F16_NT_R8_RING4_GAP || rung == GEMM_F16_NT_R10_RING4_PAIRED;
+    if (!four_wave && rung != GEMM_F16_NT_R4_RING && rung != GEMM_F16_NT_R5_PERSISTENT_WS &&
+        rung != GEMM_F16_NT_R9_RING_SMALL)
+        return GEMM_F16_NT_INVALID_ARG;
+    if (M == 0 || N == 0) return 0;
+    if (four_wave && (M < ring4::C::BM || N < ring4::C::BN)) return GEMM_F16_NT_UNSUPPORTED;
+    const int64_t tile = rung == GEMM_F16_NT_R9_RING_SMALL ? RingSmallCfg::BM : kFastTile;
+    const int64_t tm = (M + tile - 1) / tile, tn = (N + tile - 1) / tile, total = tm * tn;
+    if (total > 0x7fffffff) return GEMM_F16_NT_UNSUPPORTED;
+    // the grids the launches use: one workgroup per tile (rungs 4 and 9),
+    // one per compute unit or fewer (the persistent rungs)
+    const int64_t grid = (rung == GEMM_F16_NT_R4_RING || rung == GEMM_F16_NT_R9_RING_SMALL) ? total
+                         : (total < cus ? total : cus);
+    int64_t n = 0;
+    for (int64_t w = 0; w < grid; ++w)
+        for (int64_t i = 0;; ++i) {
+            const int64_t t = persistent_tile(w, i, grid);
+            if (t >= total) break;
+            int64_t r, c;
+            if (four_wave) {
+                uint32_t mi, ni;
+                grouped_tile_in<uint32_t>((uint32_t)t, (uint32_t)tm, (uint32_t)tn, ring4::kRing4GroupM, &mi, &ni);
+                r = clamped_origin(mi, ring4::C::BM, M);
+                c = clamped_origin(ni, ring4::C::BN, N);
+            } else {
+                const TileCoord tc = grouped_tile(t, tm, tn);
+                r = tc.m_idx * tile;
+                c = tc.n_idx * tile;
+            }
+            if (n < capacity) {
+                wg[n] = w;
+                row0[n] = r;
+                col0[n] = c;
             }
             ++n;
         }

@@ -35,19 +35,42 @@ struct TileCoord {
     int64_t m_idx, n_idx;
 };
 
-// Linear tile id t (grouped order) -> tile coordinates.
+// Grouped order with groups of `group_m` tile rows, in the integer type I:
+// linear tile id t -> tile row *m_idx and tile column *n_idx.  Group g
+// holds tile rows [g*group_m, g*group_m + gm), gm = group_m except for a
+// shorter last group, walked column by column.  The four-wave ring runs it
+// in 32-bit arithmetic with groups of 4 (kRing4GroupM in ring4.hpp), the
+// other persistent and grouped rungs with kGroupM in 64-bit.
+template <typename I>
+__host__ __device__ __forceinline__ void grouped_tile_in(I t, I tiles_m, I tiles_n, I group_m, I* m_idx, I* n_idx)
+{
+    const I per_group = group_m * tiles_n;
+    const I g = t / per_group;
+    const I first_m = g * group_m;
+    const I rem = tiles_m - first_m;
+    const I gm = rem < group_m ? rem : group_m;
+    const I r = t - g * per_group;
+    *m_idx = first_m + r % gm;
+    *n_idx = r / gm;
+}
+
+// Linear tile id t (grouped order, groups of kGroupM) -> tile coordinates.
 __host__ __device__ __forceinline__ TileCoord grouped_tile(int64_t t, int64_t tiles_m, int64_t tiles_n)
 {
-    const int64_t per_group = (int64_t)kGroupM * tiles_n;
-    const int64_t g = t / per_group;
-    const int64_t first_m = g * kGroupM;
-    const int64_t rem = tiles_m - first_m;
-    const int64_t gm = rem < kGroupM ? rem : kGroupM;
-    const int64_t r = t - g * per_group;
     TileCoord c;
-    c.m_idx = first_m + r % gm;
-    c.n_idx = r / gm;
+    grouped_tile_in<int64_t>(t, tiles_m, tiles_n, (int64_t)kGroupM, &c.m_idx, &c.n_idx);
     return c;
+}
+
+// First output row (or column) of tile `idx` along an extent of `extent`
+// elements cut in tiles of `tile` (extent >= tile): the last tile is moved
+// back to end at the extent, so every tile is whole and in range (it
+// overlaps its neighbour, which computes the same values for the shared
+// rows).  The four-wave ring's tiles; the other rungs mask their edges.
+__host__ __device__ __forceinline__ int64_t clamped_origin(int64_t idx, int64_t tile, int64_t extent)
+{
+    const int64_t o = idx * tile;
+    return o < extent - tile ? o : extent - tile;
 }
 
 // Workgroup id -> slot in [0, grid) such that the workgroups dispatched to

@@ -65,8 +65,8 @@ extern "C" {
 #define GEMM_F16_NT_R5_PERSISTENT_WS 5 /* any shape: persistent, producer/consumer waves */
 #define GEMM_F16_NT_R6_RING4 6 /* rung 4's ring with 4 waves of 128 x 128 and a fixed instruction
                                   schedule: M, N >= 256, N a multiple of 8, K a multiple of 64,
-                                  K >= 128 (when M or N is not a multiple of 256 the last tile row
-                                  or column ends at M or N and overlaps its neighbour) */
+                                  K >= 128, N < 2^24 (when M or N is not a multiple of 256 the last
+                                  tile row or column ends at M or N and overlaps its neighbour) */
 #define GEMM_F16_NT_R7_RING4_2B 7 /* rung 6 with a release and a publish barrier per k step (loads start
                                      earlier and spread evenly); same shapes as rung 6 */
 #define GEMM_F16_NT_R8_RING4_GAP 8 /* rung 7's barriers with at most one instruction between two MFMAs
@@ -166,6 +166,21 @@ const char* gemm_f16_nt_status_string(int status);
  * count) or a negative status; writes at most `capacity` entries. */
 int64_t gemm_f16_nt_schedule(int64_t M, int64_t N, int64_t num_workgroups, int64_t* wg, int64_t* tile_m,
                              int64_t* tile_n, int64_t capacity);
+
+/* Host evaluation of the tile walk a rung's launch runs on a device with
+ * `cus` compute units, no HIP call ("TIRx GEMM detailed technical notes",
+ * V3 "Spatial Tiling with Multiple CTAs" for the tile origins, V6 "Better
+ * L2 Locality" for the grouped order).  rung: 4 and 9 (one workgroup per
+ * 256 x 256 or 128 x 128 tile, grouped order with groups of 8 tile rows),
+ * 5 (persistent, one workgroup per compute unit, the same order) or 6, 7,
+ * 8, 10 (the four-wave ring: persistent, groups of 4 tile rows, the last
+ * tile row and column moved back to end at M and N; M, N >= 256, else
+ * GEMM_F16_NT_UNSUPPORTED).  Writes one entry per tile visit in
+ * workgroup-major visit order: workgroup wg[i] computes the output block
+ * whose first row is row0[i] and first column col0[i].  Returns the number
+ * of entries or a negative status; writes at most `capacity` entries. */
+int64_t gemm_f16_nt_tile_walk(int rung, int64_t M, int64_t N, int cus, int64_t* wg, int64_t* row0, int64_t* col0,
+                              int64_t capacity);
 
 /* Host evaluation of the operand ring's bookkeeping for `depth` stages and
  * `steps` k steps: stage[k], lap[k] (the pages' phase is lap & 1) and

@@ -110,6 +110,13 @@ A0, B0, D0 = 0x10000, 0x20000000, 0x40000000   # fake, 16-byte aligned, disjoint
     ((0, 0, 64, 64, 0, 0, 0), g.OK),                       # empty output: nothing needed
     ((0, 64, 64, 0, 0, 0, D0), g.OK),                      # K = 0: D only
     ((0, 64, 64, 1 << 23, A0, B0, D0), g.UNSUPPORTED),     # beyond the kernels' index range
+    # the four-wave ring's output blocks span 256 * N bytes in a 32-bit size: N < 2^24
+    ((6, 256, 1 << 24, 128, A0, 1 << 34, 1 << 36), g.UNSUPPORTED),
+    ((10, 256, 1 << 24, 128, A0, 1 << 34, 1 << 36), g.UNSUPPORTED),
+    ((8, 256, (1 << 24) + 8, 128, A0, 1 << 34, 1 << 36), g.UNSUPPORTED),
+    ((10, 256, (1 << 24) - 8, 128, A0, 1 << 34, 1 << 36), g.OK),
+    ((6, 256, (1 << 24) - 8, 128, A0, 1 << 34, 1 << 36), g.OK),
+    ((0, 256, 1 << 24, 128, A0, 1 << 34, 1 << 36), g.OK),   # the library's choice takes another kernel
 ])
 def test_validation(args, want):
     assert g.check(*args) == want
@@ -192,6 +199,78 @@ def test_schedule_xcd_locality():
         sel = (wg % 8) == x
         assert sel.sum() == 32
         assert len(np.unique(tm[sel])) == 8 and len(np.unique(tn[sel])) == 4
+
+
+@pytest.mark.parametrize("rung,M,N,cus", [
+    (10, 4096, 4096, 256), (10, 8192, 8192, 256), (10, 32768, 1024, 256), (10, 4000, 4000, 256),
+    (10, 300, 264, 256), (10, 256, 256, 256), (10, 6144, 6144, 256), (10, 1000, 3000, 37), (8, 4608, 4608, 304),
+    (5, 4096, 4096, 256), (5, 1000, 3000, 37), (4, 4096, 4096, 256), (4, 1000, 3000, 256), (9, 4096, 4096, 256),
+    (9, 200, 32768, 256),
+])
+def test_tile_walk_covers_every_output_once(rung, M, N, cus):
+    """Every rung's tile walk covers every output element: exactly once
+    where the tiles divide M and N; the four-wave ring's moved-back last
+    row and column of tiles overlap only their neighbours, and every other
+    rung masks its edge tiles (its origins are whole multiples of the tile).
+    Every workgroup of a persistent walk gets its share to within one tile."""
+    wg, r0, c0 = g.tile_walk(rung, M, N, cus)
+    tile = 128 if rung == 9 else 256
+    tm, tn = -(-M // tile), -(-N // tile)
+    assert len(wg) == tm * tn
+    cover = np.zeros((M, N), np.int16)
+    for r, c in zip(r0.tolist(), c0.tolist()):
+        cover[r: r + tile, c: c + tile] += 1
+    assert cover.min() >= 1
+    if rung in (6, 7, 8, 10):
+        assert np.all((r0 >= 0) & (r0 + tile <= M) & (c0 >= 0) & (c0 + tile <= N))   # whole tiles, in range
+        # outputs computed twice: exactly the band where the moved-back last
+        # tile row (column) overlaps its neighbour
+        band_r = np.zeros(M, bool)
+        band_c = np.zeros(N, bool)
+        if M % tile:
+            band_r[M - tile: (M // tile) * tile] = True
+        if N % tile:
+            band_c[N - tile: (N // tile) * tile] = True
+        twice = band_r[:, None] | band_c[None, :]
+        assert np.array_equal(cover > 1, twice)
+        assert cover.max() <= 4
+    else:
+        assert np.all(r0 % tile == 0) and np.all(c0 % tile == 0)
+        assert cover.max() == 1
+    counts = np.bincount(wg)
+    assert counts.max() - counts.min() <= 1
+
+
+@pytest.mark.parametrize("M,N,rounds", [(4096, 4096, 1), (8192, 8192, 4), (32768, 1024, 2)])
+def test_tile_walk_four_wave_xcd_blocks(M, N, rounds):
+    """The library's kernel at the three large workloads: in every round of
+    tiles, the 32 workgroups of one XCD (w mod 8 equal) work on one block of
+    4 tile rows x 8 tile columns (24 MiB of operand bands at 4096^3, the
+    least for 32 tiles), so the bands they share stay in that XCD's L2
+    ("TIRx GEMM detailed technical notes", V6 "Better L2 Locality")."""
+    wg, r0, c0 = g.tile_walk(10, M, N, 256)
+    visit = np.zeros_like(wg)
+    for w in range(256):
+        sel = np.nonzero(wg == w)[0]
+        visit[sel] = np.arange(len(sel))
+    assert visit.max() + 1 == rounds
+    for i in range(rounds):
+        for x in range(8):
+            sel = (wg % 8 == x) & (visit == i)
+            assert sel.sum() == 32
+            rows, cols = np.unique(r0[sel]), np.unique(c0[sel])
+            assert (len(rows), len(cols)) == ((4, 8) if N >= 2048 else (8, 4))
+            assert rows.max() - rows.min() == 256 * (len(rows) - 1)
+            assert cols.max() - cols.min() == 256 * (len(cols) - 1)
+
+
+def test_tile_walk_argument_errors():
+    L = g.lib()
+    assert L.gemm_f16_nt_tile_walk(3, 256, 256, 256, None, None, None, 0) == g.INVALID_ARG   # no tile walk
+    assert L.gemm_f16_nt_tile_walk(10, 200, 4096, 256, None, None, None, 0) == g.UNSUPPORTED
+    assert L.gemm_f16_nt_tile_walk(10, 256, 256, 0, None, None, None, 0) == g.INVALID_ARG
+    assert L.gemm_f16_nt_tile_walk(10, 256, 256, 256, None, None, None, 1) == g.INVALID_ARG
+    assert L.gemm_f16_nt_tile_walk(10, 0, 256, 256, None, None, None, 0) == 0
 
 
 @pytest.mark.parametrize("args,want", [
