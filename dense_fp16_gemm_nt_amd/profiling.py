@@ -1,16 +1,21 @@
 """Summaries of rocprofv3 output for the GEMM kernels (short text files).
 
   python -m dense_fp16_gemm_nt_amd.profiling stats  --dir D --kernel SUBSTR --command CMD --out FILE
-      per-kernel dispatch count and mean/min/max duration from a
-      `rocprofv3 --kernel-trace --stats --output-format csv` run
+      per-kernel dispatch count and mean/median/min/max duration (one block
+      per kernel name) from a `rocprofv3 --kernel-trace --stats
+      --output-format csv` run
   python -m dense_fp16_gemm_nt_amd.profiling traffic --fetch D1 --write D2 --copy-fetch D3 --copy-write D4
       --copy-bytes N --kernel SUBSTR --workload NAME --rung NAME --command CMD --out FILE
       HBM bytes per dispatch of the kernel from FETCH_SIZE / WRITE_SIZE
       passes (KiB per dispatch), each scaled by what the same counter reads
       for a device copy of known size
-  python -m dense_fp16_gemm_nt_amd.profiling power --steps N --workload NAME --command CMD --out FILE
+  python -m dense_fp16_gemm_nt_amd.profiling power --steps N --workload NAME --command CMD --out FILE [--raw F]
       socket power and per-XCD shader clocks (amd-smi) sampled while
-      bench.py runs N back-to-back launches in a child process
+      bench.py runs N back-to-back launches in a child process (summary in
+      FILE, the raw samples in F)
+  python -m dense_fp16_gemm_nt_amd.profiling timeline --dir D --kernel SUBSTR --timed K --command CMD --out FILE
+      per-dispatch durations and gaps of one kernel over a traced bench run
+      whose last K dispatches are the timed region
   python -m dense_fp16_gemm_nt_amd.profiling counters --dir D --trace T --traffic F --flop X --kernel SUBSTR
       --workload NAME --rung NAME --cus N --command CMD --out FILE
       matrix-core and LDS figures per dispatch from one counter pass
@@ -82,17 +87,35 @@ def counter_per_dispatch(d: str, counter: str, substr: str) -> float:
     return statistics.mean(per.values())
 
 
+def per_kernel(d: str, substr: str):
+    """{kernel name: [durations in us, dispatch order]} for the kernels whose
+    name contains substr."""
+    rows = list(csv.DictReader(open(_find(d, "*kernel_trace.csv"))))
+    rows.sort(key=lambda r: int(r["Start_Timestamp"]))
+    out = {}
+    for r in rows:
+        if substr in r["Kernel_Name"]:
+            out.setdefault(r["Kernel_Name"], []).append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    return out
+
+
 def cmd_stats(a):
-    names, durs = kernel_stats(a.dir, a.kernel)
-    lines = [f"# rocprofv3 kernel trace summary: {a.kernel}",
+    """One block of figures per kernel name (never one mean over different
+    kernels)."""
+    groups = per_kernel(a.dir, a.kernel)
+    if not groups:
+        raise SystemExit(f"no dispatch of a kernel matching {a.kernel!r} in {a.dir}")
+    lines = [f"# rocprofv3 kernel trace summary: kernels matching {a.kernel!r}",
              f"command: {a.command}",
-             f"kernels: {', '.join(names)}",
-             f"dispatches: {len(durs)}",
-             f"mean_us: {statistics.mean(durs):.3f}",
-             f"median_us: {statistics.median(durs):.3f}",
-             f"min_us: {min(durs):.3f}",
-             f"max_us: {max(durs):.3f}",
              f"kernel_src_sha: {kernel_source_hash()}"]
+    for name, durs in sorted(groups.items(), key=lambda kv: -sum(kv[1])):
+        lines += ["",
+                  f"kernel: {name}",
+                  f"dispatches: {len(durs)}",
+                  f"mean_us: {statistics.mean(durs):.3f}",
+                  f"median_us: {statistics.median(durs):.3f}",
+                  f"min_us: {min(durs):.3f}",
+                  f"max_us: {max(durs):.3f}"]
     stats_csv = glob.glob(os.path.join(a.dir, "**", "*kernel_stats.csv"), recursive=True)
     if stats_csv:
         lines.append("")
@@ -100,7 +123,48 @@ def cmd_stats(a):
         for r in csv.DictReader(open(stats_csv[0])):
             lines.append(", ".join(f"{k}={v}" for k, v in r.items()))
     open(a.out, "w").write("\n".join(lines) + "\n")
-    print("\n".join(lines[:9]))
+    print("\n".join(lines[:12]))
+
+
+def cmd_timeline(a):
+    """Per-dispatch durations and the gaps between dispatches of one kernel
+    over a traced bench run: the last `timed` dispatches are the timed
+    region, the ones before them the warm-up launches."""
+    rows = list(csv.DictReader(open(_find(a.dir, "*kernel_trace.csv"))))
+    rows = [r for r in rows if a.kernel in r["Kernel_Name"]]
+    rows.sort(key=lambda r: int(r["Start_Timestamp"]))
+    if len(rows) < a.timed:
+        raise SystemExit(f"{len(rows)} dispatches, fewer than the {a.timed} timed ones")
+    t0 = int(rows[0]["Start_Timestamp"])
+    lines = [f"# rocprofv3 per-dispatch timeline: {a.kernel}",
+             f"command: {a.command}",
+             f"kernel_src_sha: {kernel_source_hash()}",
+             f"dispatches: {len(rows)} (the last {a.timed} are the timed region)",
+             "",
+             "index  start_us  duration_us  gap_before_us  region"]
+    prev_end = None
+    durs, gaps = [], []
+    for i, r in enumerate(rows):
+        st, en = int(r["Start_Timestamp"]), int(r["End_Timestamp"])
+        gap = (st - prev_end) / 1e3 if prev_end is not None else 0.0
+        timed = i >= len(rows) - a.timed
+        lines.append(f"{i:5d}  {(st - t0) / 1e3:8.1f}  {(en - st) / 1e3:11.3f}  {gap:13.3f}  "
+                     f"{'timed' if timed else 'warm-up'}")
+        if timed:
+            durs.append((en - st) / 1e3)
+            if i > len(rows) - a.timed:
+                gaps.append(gap)
+        prev_end = en
+    span = (int(rows[-1]["End_Timestamp"]) - int(rows[len(rows) - a.timed]["Start_Timestamp"])) / 1e3
+    lines += ["",
+              f"timed_mean_duration_us: {statistics.mean(durs):.3f}",
+              f"timed_first_half_mean_us: {statistics.mean(durs[:len(durs) // 2]):.3f}",
+              f"timed_second_half_mean_us: {statistics.mean(durs[len(durs) // 2:]):.3f}",
+              f"timed_gap_total_us: {sum(gaps):.3f}",
+              f"timed_span_first_start_to_last_end_us: {span:.3f}",
+              f"timed_span_per_dispatch_us: {span / a.timed:.3f}"]
+    open(a.out, "w").write("\n".join(lines) + "\n")
+    print("\n".join(lines[-7:]))
 
 
 def cmd_traffic(a):
@@ -201,12 +265,15 @@ def cmd_power(a):
         "socket_power_w_min": min(p for _, p, _ in busy), "socket_power_w_max": max(p for _, p, _ in busy),
         "xcd_clock_mhz_mean": [round(c) for c in clocks],
         "clock_mhz_mean_all_xcds": round(statistics.mean(clocks), 1) if clocks else None,
-        "samples": samples,
         "kernel_src_sha": kernel_source_hash(),
         "command": a.command,
     }
     open(a.out, "w").write(json.dumps(rec, indent=1) + "\n")
-    print(json.dumps({k: v for k, v in rec.items() if k != "samples"}, indent=1))
+    if a.raw:
+        # the raw samples (time s, socket power W, per-XCD clocks MHz) go
+        # to a file of their own, outside the summaries
+        open(a.raw, "w").write(json.dumps(samples) + "\n")
+    print(json.dumps(rec, indent=1))
 
 
 def main(argv=None):
@@ -245,8 +312,16 @@ def main(argv=None):
     w.add_argument("--interval", type=float, default=0.4)
     w.add_argument("--command", required=True)
     w.add_argument("--out", required=True)
+    w.add_argument("--raw", default="", help="file for the raw amd-smi samples")
+    tl = sub.add_parser("timeline")
+    tl.add_argument("--dir", required=True)
+    tl.add_argument("--kernel", required=True)
+    tl.add_argument("--timed", type=int, required=True)
+    tl.add_argument("--command", required=True)
+    tl.add_argument("--out", required=True)
     a = p.parse_args(argv)
-    {"stats": cmd_stats, "traffic": cmd_traffic, "counters": cmd_counters, "power": cmd_power}[a.cmd](a)
+    {"stats": cmd_stats, "traffic": cmd_traffic, "counters": cmd_counters, "power": cmd_power,
+     "timeline": cmd_timeline}[a.cmd](a)
 
 
 if __name__ == "__main__":
