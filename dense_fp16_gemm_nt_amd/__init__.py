@@ -21,6 +21,7 @@ INVALID_ARG = -1
 UNSUPPORTED = -2
 LAUNCH = -3
 DEVICE = -4
+SCRATCH = -5
 
 R1_SINGLE_TILE = 1
 R2_KLOOP = 2
@@ -69,6 +70,8 @@ def lib() -> ctypes.CDLL:
             L.gemm_f16_nt_check_strided.argtypes = [i64, i64, i64, vp, i64, i64, vp, i64, i64, vp, i64, i64, i64]
             L.gemm_f16_nt_splitk.restype = i32
             L.gemm_f16_nt_splitk.argtypes = [i64, i64, i64, vp, vp, vp, i32, vp, i64, vp]
+            L.gemm_f16_nt_splitk_noalloc.restype = i32
+            L.gemm_f16_nt_splitk_noalloc.argtypes = [i64, i64, i64, vp, vp, vp, i32, vp]
             L.gemm_f16_nt_splitk_workspace.restype = i64
             L.gemm_f16_nt_splitk_workspace.argtypes = [i64, i64, i64, i32]
             L.gemm_f16_nt_check.restype = i32
@@ -272,6 +275,18 @@ def gemm_f16_nt_splitk(A, B, D=None, splits: int = 0, workspace=None):
                                   workspace.data_ptr(), workspace.numel() * workspace.element_size(), _stream(A))
     if st != OK:
         raise GemmError(st, "gemm_f16_nt_splitk")
+    return D
+
+
+def gemm_f16_nt_splitk_noalloc(A, B, D, splits: int = 0):
+    """gemm_f16_nt_splitk with the library's own scratch array for the
+    partial sums: nothing is allocated, D must be given."""
+    if D is None:
+        raise ValueError("gemm_f16_nt_splitk_noalloc writes into a given D (it allocates nothing)")
+    M, N, K, D = _operands(A, B, D)
+    st = lib().gemm_f16_nt_splitk_noalloc(M, N, K, A.data_ptr(), B.data_ptr(), D.data_ptr(), int(splits), _stream(A))
+    if st != OK:
+        raise GemmError(st, "gemm_f16_nt_splitk_noalloc")
     return D
 
 

@@ -18,6 +18,11 @@
 
 using namespace g16;
 
+// Scratch memory of gemm_f16_nt_splitk_noalloc (see splitk_run below): 64
+// MiB of device memory per device, held until the process ends.
+constexpr int64_t kScratchBytes = int64_t(64) << 20;
+static __device__ __align__(256) char scratch[kScratchBytes];
+
 namespace {
 
 // Kernel configurations of the fast rungs (measured on MI355X; see the
@@ -634,6 +639,89 @@ int run(int rung, int64_t M, int64_t N, int64_t K, const void* A, const void* B,
     }
 }
 
+// ------------------------------------------------- no-allocation scratch
+// The split-K partial sums of gemm_f16_nt_splitk_noalloc live in this
+// file-scope device array, one copy per device the library runs on, held
+// until the process ends.  In host code `scratch` names a host-side
+// stand-in, not device memory: its device address comes from
+// hipGetSymbolAddress, taken once per device with that device current, and
+// only that address is passed to kernels.
+struct ScratchSlot {
+    std::atomic<int> state{0};  // 0 unknown, 1 ok, -1 unusable
+    void* ptr = nullptr;
+};
+ScratchSlot g_scratch[kMaxDevices];
+std::mutex g_scratch_lock;
+
+int scratch_address(void** out)
+{
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return GEMM_F16_NT_DEVICE;
+    ScratchSlot& sl = g_scratch[dev];
+    int st = sl.state.load(std::memory_order_acquire);
+    if (st == 0) {
+        std::lock_guard<std::mutex> lock(g_scratch_lock);
+        st = sl.state.load(std::memory_order_relaxed);
+        if (st == 0) {
+            void* p = nullptr;
+            const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+            st = (e == hipSuccess && p != nullptr) ? 1 : -1;
+            if (st == 1) sl.ptr = p;
+            sl.state.store(st, std::memory_order_release);
+        }
+    }
+    if (st != 1) return GEMM_F16_NT_DEVICE;
+    *out = sl.ptr;
+    return GEMM_F16_NT_OK;
+}
+
+// gemm_f16_nt_splitk's body: the partial sums go to the caller's workspace,
+// or (noalloc) to this device's scratch array.
+int splitk_run(int64_t M, int64_t N, int64_t K, const void* A, const void* B, void* D, int splits, void* workspace,
+               int64_t workspace_bytes, bool noalloc, hipStream_t s)
+{
+    int st = validate(0, M, N, K, A, B, D);
+    if (st != GEMM_F16_NT_OK) return st;
+    if (M == 0 || N == 0) return GEMM_F16_NT_OK;
+    // an explicit slice count fixes the scratch size before any HIP call
+    if (noalloc && splits > 0 && K > 0 && fast_operands(K, K, K, 0, 0, A, B, D)) {
+        int64_t k_chunk = 0, n_slices = 1;
+        if (splits > 1) split_plan(K, splits, &k_chunk, &n_slices);
+        if (n_slices > 1 && n_slices * M * N * 4 > kScratchBytes) return GEMM_F16_NT_SCRATCH;
+    }
+    int cus = 0;
+    st = device_info(&cus);
+    if (st != GEMM_F16_NT_OK) return st;
+    if (K == 0) return launch_fill_zero(D, M * N, s);
+    if (!fast_operands(K, K, K, 0, 0, A, B, D)) return launch_any(contiguous_args(M, N, K, A, B, D), s);
+    int64_t want = splits == 0 ? choose_splits(M, N, K, cus) : splits, m_top = 0;
+    if (splits == 0 && want <= 1 && !hybrid_plan(M, N, K, cus, &m_top, &want)) m_top = 0;
+    int64_t k_chunk = 0, n_slices = 1;
+    if (want > 1) split_plan(K, want, &k_chunk, &n_slices);
+    if (n_slices <= 1) return launch_ring(contiguous_args(M, N, K, A, B, D), s, kDefaultRing4);
+    // rows [m_top, M) split K; rows [0, m_top) (whole rounds of tiles) do not
+    const int64_t m_rest = M - m_top;
+    const int64_t need = n_slices * m_rest * N * 4;
+    if (noalloc) {
+        if (need > kScratchBytes) return GEMM_F16_NT_SCRATCH;
+        st = scratch_address(&workspace);
+        if (st != GEMM_F16_NT_OK) return st;
+        workspace_bytes = kScratchBytes;
+    } else {
+        if (workspace == nullptr || workspace_bytes < need) return GEMM_F16_NT_INVALID_ARG;
+        if ((uintptr_t)workspace & 15) return GEMM_F16_NT_UNSUPPORTED;
+        if (overlaps(workspace, need, A, M * K * 2) || overlaps(workspace, need, B, N * K * 2) ||
+            overlaps(workspace, need, D, M * N * 2))
+            return GEMM_F16_NT_INVALID_ARG;
+    }
+    if (m_top > 0) {
+        st = launch_ring(contiguous_args(m_top, N, K, A, B, D), s, kDefaultRing4);
+        if (st != GEMM_F16_NT_OK) return st;
+    }
+    return launch_splitk(m_rest, N, K, (const f16*)A + m_top * K, B, (f16*)D + m_top * N, want, (float*)workspace,
+                         s);
+}
+
 }  // namespace
 
 extern "C" {
@@ -712,34 +800,14 @@ int gemm_f16_nt_splitk(int64_t M, int64_t N, int64_t K, const void* A, const voi
                        void* workspace, int64_t workspace_bytes, void* stream)
 {
     if (splits < 0 || splits > kMaxSplits || workspace_bytes < 0) return GEMM_F16_NT_INVALID_ARG;
-    int st = validate(0, M, N, K, A, B, D);
-    if (st != GEMM_F16_NT_OK) return st;
-    if (M == 0 || N == 0) return GEMM_F16_NT_OK;
-    int cus = 0;
-    st = device_info(&cus);
-    if (st != GEMM_F16_NT_OK) return st;
-    hipStream_t s = (hipStream_t)stream;
-    if (K == 0) return launch_fill_zero(D, M * N, s);
-    if (!fast_operands(K, K, K, 0, 0, A, B, D)) return launch_any(contiguous_args(M, N, K, A, B, D), s);
-    int64_t want = splits == 0 ? choose_splits(M, N, K, cus) : splits, m_top = 0;
-    if (splits == 0 && want <= 1 && !hybrid_plan(M, N, K, cus, &m_top, &want)) m_top = 0;
-    int64_t k_chunk = 0, n_slices = 1;
-    if (want > 1) split_plan(K, want, &k_chunk, &n_slices);
-    if (n_slices <= 1) return launch_ring(contiguous_args(M, N, K, A, B, D), s, kDefaultRing4);
-    // rows [m_top, M) split K; rows [0, m_top) (whole rounds of tiles) do not
-    const int64_t m_rest = M - m_top;
-    const int64_t need = n_slices * m_rest * N * 4;
-    if (workspace == nullptr || workspace_bytes < need) return GEMM_F16_NT_INVALID_ARG;
-    if ((uintptr_t)workspace & 15) return GEMM_F16_NT_UNSUPPORTED;
-    if (overlaps(workspace, need, A, M * K * 2) || overlaps(workspace, need, B, N * K * 2) ||
-        overlaps(workspace, need, D, M * N * 2))
-        return GEMM_F16_NT_INVALID_ARG;
-    if (m_top > 0) {
-        st = launch_ring(contiguous_args(m_top, N, K, A, B, D), s, kDefaultRing4);
-        if (st != GEMM_F16_NT_OK) return st;
-    }
-    return launch_splitk(m_rest, N, K, (const f16*)A + m_top * K, B, (f16*)D + m_top * N, want, (float*)workspace,
-                         s);
+    return splitk_run(M, N, K, A, B, D, splits, workspace, workspace_bytes, false, (hipStream_t)stream);
+}
+
+int gemm_f16_nt_splitk_noalloc(int64_t M, int64_t N, int64_t K, const void* A, const void* B, void* D, int splits,
+                               void* stream)
+{
+    if (splits < 0 || splits > kMaxSplits) return GEMM_F16_NT_INVALID_ARG;
+    return splitk_run(M, N, K, A, B, D, splits, nullptr, 0, true, (hipStream_t)stream);
 }
 
 int gemm_f16_nt_check_strided(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, int64_t stride_a,
@@ -762,6 +830,7 @@ const char* gemm_f16_nt_status_string(int status)
     case GEMM_F16_NT_UNSUPPORTED: return "unsupported shape, alignment or rung";
     case GEMM_F16_NT_LAUNCH: return "kernel launch failed";
     case GEMM_F16_NT_DEVICE: return "no usable gfx950 device";
+    case GEMM_F16_NT_SCRATCH: return "the split-K partial sums exceed the library's 64 MiB scratch array";
     default: return "unknown status";
     }
 }

@@ -53,6 +53,7 @@ extern "C" {
 #define GEMM_F16_NT_UNSUPPORTED (-2) /* shape or alignment a rung does not implement, odd addresses */
 #define GEMM_F16_NT_LAUNCH (-3)      /* the HIP launch itself failed */
 #define GEMM_F16_NT_DEVICE (-4)      /* no usable device / device query failed / not gfx950 */
+#define GEMM_F16_NT_SCRATCH (-5)     /* gemm_f16_nt_splitk_noalloc: partial sums beyond its scratch array */
 
 /* The ladder of kernels ("GEMM I", Steps 1-3; "GEMM III", Step 7; "TIRx
  * GEMM detailed technical notes", V1-V7).  Every rung computes the same D. */
@@ -140,6 +141,25 @@ int gemm_f16_nt_strided_batched(int64_t M, int64_t N, int64_t K, const void* A, 
  * call is gemm_f16_nt and the workspace is not touched. */
 int gemm_f16_nt_splitk(int64_t M, int64_t N, int64_t K, const void* A, const void* B, void* D, int splits,
                        void* workspace, int64_t workspace_bytes, void* stream);
+
+/* gemm_f16_nt_splitk without a workspace argument and without any
+ * allocation, for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * The fp32 partial sums go to a scratch array of 64 MiB (67108864 bytes)
+ * that the library holds in device memory, one per device, for the life of
+ * the process (its address is taken on the first call on each device).
+ * Same arguments, kernel choice, slice plan and result bits as
+ * gemm_f16_nt_splitk with `splits`; where that call would need more than
+ * 64 MiB of workspace (gemm_f16_nt_splitk_workspace), this one returns
+ * GEMM_F16_NT_SCRATCH and launches nothing (with an explicit `splits` that
+ * is decided before any HIP call).  Every call on one device shares that
+ * device's array: calls that may overlap on one device (on different
+ * streams, or from different threads without ordering) race and may write
+ * wrong results; calls ordered on one stream do not.  Nothing in the array
+ * needs clearing between calls: every slice overwrites its partial sums
+ * before the reduction reads them. */
+int gemm_f16_nt_splitk_noalloc(int64_t M, int64_t N, int64_t K, const void* A, const void* B, void* D, int splits,
+                               void* stream);
 
 /* Bytes of workspace gemm_f16_nt_splitk needs (0 if it will not split), or
  * a negative status.  With splits = 0 this queries the current device's

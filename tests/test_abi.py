@@ -369,6 +369,25 @@ def test_splitk_plan_invariants(M, N, K, cus):
         assert tiles % cus != 0
 
 
+def test_splitk_noalloc_rejects_beyond_its_scratch():
+    """With an explicit slice count the no-allocation entry point sizes its
+    partial sums before any HIP call: beyond the 64 MiB scratch array it
+    returns GEMM_F16_NT_SCRATCH and launches nothing."""
+    L = g.lib()
+    A, B, D = 0x10000, 0x20000000, 0x40000000
+    # 64 slices of 1024 x 1024 fp32 partial sums: 256 MiB
+    assert L.gemm_f16_nt_splitk_noalloc(1024, 1024, 65536, A, B, D, 64, None) == g.SCRATCH
+    assert L.gemm_f16_nt_splitk_workspace(1024, 1024, 65536, 64) == 256 << 20
+    # 17 slices of 1024 x 1024 (68 MiB): over; 16 slices (64 MiB): fits, so
+    # the call goes on to the device query, which fails here without a GPU
+    assert L.gemm_f16_nt_splitk_noalloc(1024, 1024, 65536, A, B, D, 17, None) == g.SCRATCH
+    assert L.gemm_f16_nt_splitk_noalloc(1024, 1024, 65536, A, B, D, 16, None) == g.DEVICE
+    assert L.gemm_f16_nt_splitk_noalloc(1024, 1024, 65536, A, B, D, 65, None) == g.INVALID_ARG
+    assert L.gemm_f16_nt_splitk_noalloc(1024, 1024, 65536, A + 1, B, D, 64, None) == g.UNSUPPORTED
+    assert L.gemm_f16_nt_splitk_noalloc(0, 1024, 65536, A, B, D, 64, None) == g.OK
+    assert g.status_string(g.SCRATCH) != g.status_string(12345)
+
+
 def test_splitk_argument_errors_before_any_device_work():
     L = g.lib()
     assert L.gemm_f16_nt_splitk(256, 256, 512, A0, B0, D0, -1, None, 0, None) == g.INVALID_ARG
