@@ -87,6 +87,9 @@ def lib() -> ctypes.CDLL:
                                            ctypes.POINTER(ctypes.c_int)]
             L.gemm_f16_nt_splitk_plan.restype = i32
             L.gemm_f16_nt_splitk_plan.argtypes = [i64, i64, i64, i32, i64p, i64p]
+            L.gemm_f16_nt_handoff_plan.restype = i32
+            L.gemm_f16_nt_handoff_plan.argtypes = [i32, i32, i32, i64, ctypes.POINTER(ctypes.c_uint32),
+                                                   ctypes.POINTER(ctypes.c_uint32)]
             L.gemm_f16_nt_ring_plan.restype = i32
             L.gemm_f16_nt_ring_plan.argtypes = [i32, i64, ctypes.POINTER(ctypes.c_int), i64p, i64p]
             _lib = L
@@ -333,6 +336,20 @@ def tile_walk(rung: int, M: int, N: int, cus: int):
     p = lambda a: a.ctypes.data_as(ctypes.POINTER(ctypes.c_int64))  # noqa: E731
     L.gemm_f16_nt_tile_walk(rung, M, N, cus, p(wg), p(r0), p(c0), n)
     return wg, r0, c0
+
+
+def handoff_plan(depth: int, producers: int, consumers: int, steps: int):
+    """Host evaluation of rung 5's handoff counters: (ready_target,
+    free_target) per k step."""
+    import numpy as np
+
+    rt = np.empty(steps, np.uint32)
+    ft = np.empty(steps, np.uint32)
+    p = lambda a: a.ctypes.data_as(ctypes.POINTER(ctypes.c_uint32))  # noqa: E731
+    st = lib().gemm_f16_nt_handoff_plan(depth, producers, consumers, steps, p(rt), p(ft))
+    if st != OK:
+        raise GemmError(st, "gemm_f16_nt_handoff_plan")
+    return rt, ft
 
 
 def ring_plan(depth: int, steps: int):

@@ -943,6 +943,18 @@ int gemm_f16_nt_splitk_plan(int64_t M, int64_t N, int64_t K, int cus, int64_t* m
     return GEMM_F16_NT_OK;
 }
 
+int gemm_f16_nt_handoff_plan(int depth, int producers, int consumers, int64_t steps, uint32_t* ready_target,
+                             uint32_t* free_target)
+{
+    if (depth < 1 || producers < 1 || consumers < 1 || steps < 0) return GEMM_F16_NT_INVALID_ARG;
+    if (steps > 0 && (ready_target == nullptr || free_target == nullptr)) return GEMM_F16_NT_INVALID_ARG;
+    for (int64_t k = 0; k < steps; ++k) {
+        ready_target[k] = handoff_ready_target(k, depth, producers);
+        free_target[k] = handoff_free_target(k, depth, consumers);
+    }
+    return GEMM_F16_NT_OK;
+}
+
 int gemm_f16_nt_ring_plan(int depth, int64_t steps, int* stage, int64_t* lap, int64_t* refill)
 {
     if (depth < 1 || steps < 0) return GEMM_F16_NT_INVALID_ARG;

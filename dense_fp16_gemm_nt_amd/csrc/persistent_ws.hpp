@@ -12,15 +12,25 @@
 //    for the whole kernel (no per-role reallocation), so every wave gets
 //    512/3 registers; a consumer holds a 128 x 64 fp32 accumulator (128
 //    registers), the producers hold only addresses.
-//  * Producers issue direct-to-LDS loads (no data registers), wait on their
-//    own vmcnt, and arrive at the workgroup barrier; consumers only read LDS
-//    and issue MFMA.  One s_barrier per k step, reached by all 12 waves,
-//    carries both handoffs of the operand ring: "step k is in LDS"
-//    (producer -> consumer) and "stage of step k-1 is free" (consumer ->
-//    producer).  The producer starts with STAGES-1 free stages filled before
-//    the first barrier; the consumers start blocked at that barrier -- the
-//    pages' opposite initial phases.
-//  * The step counter runs across tiles and never resets, so a refill can
+//  * Producers issue direct-to-LDS loads (no data registers); consumers only
+//    read LDS and issue MFMA.  The two roles meet through two counters per
+//    ring stage in LDS instead of a workgroup barrier (the pages' full and
+//    empty mbarriers of each stage): a producer adds 1 to ready[s] once its
+//    own loads of the step in stage s have landed (its vmcnt), a consumer
+//    adds 1 to free[s] once its fragment reads of that step are done.  A
+//    consumer waits only for the stage it reads next, a producer only for
+//    the stage it refills next, so the producers run up to STAGES steps
+//    ahead of the consumers, and a consumer never waits for the other
+//    consumers.  The targets (handoff_ready_target, handoff_free_target in
+//    sched.hpp) start the producers with every stage free and the
+//    consumers blocked -- the pages' opposite initial phases -- and the
+//    counters never reset, so a wait names an absolute count that no
+//    earlier lap can meet.  Only the counters' initialisation takes a
+//    workgroup barrier.
+//  * Every wait is bounded (kSpinLimit polls); a wave whose wait runs out
+//    stops waiting and its tiles are written as NaN, so a protocol error
+//    shows as a failed result instead of a hung GPU.
+//  * The step counter runs across tiles and never resets, so the producers
 //    prefetch the next tile's first k steps while the consumers finish the
 //    current tile and write it back (the accumulator handoff of the pages'
 //    second ring is the consumers' own registers here).
@@ -52,8 +62,87 @@ struct Cfg {
     static constexpr int FM = WTM / 32, FN = WTN / 32;
     static constexpr int KSUB = BK / 16;
     static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
-    static_assert((STAGES - 2) * LPW < 64, "vmcnt range");
+    static_assert((STAGES - 1) * LPW < 64, "vmcnt range");
 };
+
+// Polls of one handoff wait before it gives up (a poll is an LDS read,
+// its wait and a short sleep, ~250 cycles: ~0.3 s in all, against a few
+// microseconds for the longest wait of a working ring).
+constexpr uint32_t kSpinLimit = 1u << 21;
+
+// The handoff counters are read and updated with inline LDS instructions
+// on their LDS byte addresses.  As ordinary loads and atomics the compiler
+// cannot tell them apart from the producers' direct-to-LDS loads and puts
+// a vmcnt(0) wait before each of them, which would leave a producer only
+// one k step of loads in flight; the kernel orders its own accesses with
+// explicit waits instead (vmcnt before a producer's arrival, lgkmcnt(0)
+// before a consumer's).
+// The counters of one kind (ready or free) sit in 16 contiguous bytes; a
+// poll reads all of them, and the wave keeps the values it saw.  The
+// counters only grow, so a kept value that already meets a target is
+// proof enough: a wave running behind the other role polls once per
+// several k steps instead of once per step.
+struct Seen {
+    uint32_t v[4];
+};
+
+__device__ __forceinline__ void lds_poll(uint32_t addr, Seen& seen)
+{
+    u32x4 x;
+    asm volatile("ds_read_b128 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(x) : "v"(addr) : "memory");
+#pragma unroll
+    for (int i = 0; i < 4; ++i) seen.v[i] = __builtin_amdgcn_readfirstlane(x[i]);
+}
+
+__device__ __forceinline__ uint32_t seen_at(const Seen& seen, int s)
+{
+    return s == 0 ? seen.v[0] : s == 1 ? seen.v[1] : s == 2 ? seen.v[2] : seen.v[3];
+}
+
+// Bounded wait until counter s of the block at `addr` reaches `target`.
+__device__ __forceinline__ bool wait_count(uint32_t addr, Seen& seen, int s, uint32_t target)
+{
+    if (handoff_reached(seen_at(seen, s), target)) return true;
+    for (uint32_t n = 0; n < kSpinLimit; ++n) {
+        lds_poll(addr, seen);
+        if (handoff_reached(seen_at(seen, s), target)) return true;
+        // a waiting wave sleeps between polls: it shares its SIMD's issue
+        // slots with two consumer waves' MFMA stream
+        __builtin_amdgcn_s_sleep(2);
+    }
+    return false;
+}
+
+// One arrival of this wave at the LDS handoff counter at `addr` (lane 0
+// adds 1).
+__device__ __forceinline__ void arrive(uint32_t addr, int lane)
+{
+    if (lane == 0) asm volatile("ds_add_u32 %0, %1" : : "v"(addr), "v"(1u) : "memory");
+}
+
+// Compiler fence: no memory operation moves across it (the handoff orders
+// LDS reads, LDS-DMA loads and counter updates by program order and waits).
+__device__ __forceinline__ void handoff_fence()
+{
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+}
+
+// vmcnt wait leaving the loads of `younger` later steps (LPW loads each) in flight.
+template <int LPW, int STAGES>
+__device__ __forceinline__ void wait_steps_in_flight(int64_t younger)
+{
+    static_assert(STAGES <= 4, "cases below");
+    if (younger >= 3 && STAGES > 3)
+        wait_vmcnt<3 * LPW>();
+    else if (younger == 2 && STAGES > 2)
+        wait_vmcnt<2 * LPW>();
+    else if (younger == 1)
+        wait_vmcnt<LPW>();
+    else
+        wait_vmcnt<0>();
+}
 
 template <class C>
 __device__ __forceinline__ void consume_stage(const char* As, const char* Bs, int wm, int wn, int lane,
@@ -84,6 +173,8 @@ __global__ __launch_bounds__(768, 1) void ws_kernel(const f16* __restrict__ A, c
                                                     int64_t tiles_m, int64_t tiles_n)
 {
     __shared__ __attribute__((aligned(1024))) char smem[C::LDS_BYTES];
+    static_assert(C::STAGES <= 4, "the counters of one kind fit one 16-byte LDS read");
+    __shared__ __attribute__((aligned(16))) uint32_t ready[4], freed[4];
     const int t = threadIdx.x, lane = t & 63;
     const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
     const int64_t total = tiles_m * tiles_n;
@@ -93,6 +184,15 @@ __global__ __launch_bounds__(768, 1) void ws_kernel(const f16* __restrict__ A, c
     const int64_t KT = (K + C::BK - 1) / C::BK;
     const int64_t S = my_tiles * KT;  // k steps this workgroup runs, over all its tiles
     const int64_t ldb = K * 2;
+    if (t < 4) {
+        ready[t] = 0;
+        freed[t] = 0;
+    }
+    __syncthreads();   // the one workgroup barrier: the counters start at 0
+    bool ok = true;    // false once a wait has run out
+    const uint32_t ready0 = (uint32_t)(uintptr_t)(G16_LDS uint32_t*)ready;
+    const uint32_t freed0 = (uint32_t)(uintptr_t)(G16_LDS uint32_t*)freed;
+    Seen seen{{0, 0, 0, 0}};   // the counters this wave waits on, as last read
 
     if (wave >= C::CONSUMERS) {
         // ------------------------------------------------------ producer
@@ -101,28 +201,38 @@ __global__ __launch_bounds__(768, 1) void ws_kernel(const f16* __restrict__ A, c
         int a_row[C::A_LOADS], b_row[C::B_LOADS], a_kc[C::A_LOADS], b_kc[C::B_LOADS];
         ring::lane_offsets<C, C::A_LOADS>(p, lane, ldb, a_off, a_row, a_kc);
         ring::lane_offsets<C, C::B_LOADS>(p, lane, ldb, b_off, b_row, b_kc);
+        // the tile and k step of the next refill, advanced step by step
+        int64_t ti = 0, tkt = 0;
+        TileCoord tc = grouped_tile(persistent_tile(wg, 0, grid), tiles_m, tiles_n);
         auto issue = [&](int64_t step) {
-            const int64_t i = step / KT, kt = step - i * KT;
-            const TileCoord tc = grouped_tile(persistent_tile(wg, i, grid), tiles_m, tiles_n);
             const int64_t m0 = tc.m_idx * C::BM, n0 = tc.n_idx * C::BN;
             char* st = smem + (int)(step % C::STAGES) * C::STAGE_BYTES;
-            const int64_t k0 = kt * C::BK;
+            const int64_t k0 = tkt * C::BK;
             ring::issue_loads<C, C::A_LOADS, EDGE>(reinterpret_cast<const char*>(A) + m0 * ldb, a_off, a_row,
                                                    a_kc, M - m0, K, k0, st, p);
             ring::issue_loads<C, C::B_LOADS, EDGE>(reinterpret_cast<const char*>(B) + n0 * ldb, b_off, b_row,
                                                    b_kc, N - n0, K, k0, st + C::A_BYTES, p);
+            if (++tkt == KT) {
+                tkt = 0;
+                if (++ti < my_tiles) tc = grouped_tile(persistent_tile(wg, ti, grid), tiles_m, tiles_n);
+            }
         };
-#pragma unroll
-        for (int s = 0; s < C::STAGES - 1; ++s)
-            if (s < S) issue(s);
-        for (int64_t g = 0; g < S; ++g) {
-            if (g + C::STAGES - 2 < S)
-                wait_vmcnt<(C::STAGES - 2) * C::LPW>();
-            else
-                wait_vmcnt<0>();
-            wg_barrier();
-            const int64_t nk = ring_refill_after(g - 1, C::STAGES, S);
-            if (nk >= 0) issue(nk);
+        // iteration g first publishes step g - (STAGES - 1) (once this
+        // wave's loads of it have landed; the loads of the steps after it
+        // stay in flight), then refills step g (once every consumer is done
+        // with step g - STAGES): a publish never waits for a release
+        for (int64_t g = 0; g < S + C::STAGES - 1; ++g) {
+            const int64_t j = g - (C::STAGES - 1);
+            if (j >= 0) {
+                wait_steps_in_flight<C::LPW, C::STAGES>((g - 1 < S - 1 ? g - 1 : S - 1) - j);
+                handoff_fence();
+                arrive(ready0 + 4u * (uint32_t)(j % C::STAGES), lane);
+            }
+            if (g < S) {
+                if (ok) ok = wait_count(freed0, seen, (int)(g % C::STAGES), handoff_free_target(g, C::STAGES, C::CONSUMERS));
+                handoff_fence();
+                issue(g);
+            }
         }
         return;
     }
@@ -140,9 +250,23 @@ __global__ __launch_bounds__(768, 1) void ws_kernel(const f16* __restrict__ A, c
 #pragma unroll
             for (int b = 0; b < C::FN; ++b) acc[a][b] = f32x16{};
         for (int64_t kt = 0; kt < KT; ++kt, ++g) {
-            wg_barrier();
-            const char* st = smem + (int)(g % C::STAGES) * C::STAGE_BYTES;
+            const int s = (int)(g % C::STAGES);
+            if (ok) ok = wait_count(ready0, seen, s, handoff_ready_target(g, C::STAGES, C::PRODUCERS));
+            handoff_fence();
+            const char* st = smem + s * C::STAGE_BYTES;
             consume_stage<C>(st, st + C::A_BYTES, wm, wn, lane, acc);
+            wait_lgkmcnt0();   // this wave's reads of the stage are done
+            handoff_fence();
+            arrive(freed0 + 4u * (uint32_t)s, lane);
+        }
+        if (!ok) {
+            // a wait ran out: the result is not trusted, and shows as NaN
+#pragma unroll
+            for (int a = 0; a < C::FM; ++a)
+#pragma unroll
+                for (int b = 0; b < C::FN; ++b)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) acc[a][b][r] = __builtin_nanf("");
         }
         const bool full = !EDGE || (m0 + C::BM <= M && n0 + C::BN <= N && N % 4 == 0);
 #pragma unroll

@@ -111,4 +111,32 @@ __host__ __device__ __forceinline__ int64_t ring_refill_after(int64_t k, int dep
     return p < total ? p : -1;
 }
 
+// Producer/consumer handoff of the wave-specialized ring (rung 5), the
+// pages' two mbarrier rings ("GEMM III", Step 7 "Four barriers = two
+// producer-consumer rings") as two monotonic counters per stage in LDS:
+// every producer wave adds 1 to ready[s] once its loads of a step in stage
+// s have landed, every consumer wave adds 1 to free[s] once it has read
+// the step.  The counters never reset (across tiles either), so each wait
+// names an absolute count and can never be satisfied by an earlier lap:
+//   a consumer reads step k once ready[k % depth] >= ready_target(k);
+//   a producer refills stage k % depth with step k once
+//   free[k % depth] >= free_target(k) (all consumers are done with step
+//   k - depth; 0 for the first lap, so the producers start with every
+//   stage free and the consumers start blocked -- the pages' opposite
+//   initial phases).
+__host__ __device__ __forceinline__ uint32_t handoff_ready_target(int64_t k, int depth, int producers)
+{
+    return (uint32_t)producers * (uint32_t)(k / depth + 1);
+}
+__host__ __device__ __forceinline__ uint32_t handoff_free_target(int64_t k, int depth, int consumers)
+{
+    return (uint32_t)consumers * (uint32_t)(k / depth);
+}
+// Whether a counter has reached a target (signed distance: the counters
+// may wrap around 2^32 in a very long persistent run).
+__host__ __device__ __forceinline__ bool handoff_reached(uint32_t counter, uint32_t target)
+{
+    return (int32_t)(counter - target) >= 0;
+}
+
 }  // namespace g16

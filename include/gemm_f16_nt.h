@@ -207,6 +207,17 @@ int64_t gemm_f16_nt_tile_walk(int rung, int64_t M, int64_t N, int cus, int64_t* 
  * refill[k] = the step loaded into stage[k] once step k is consumed (-1 if
  * none).  Returns 0 or a negative status. */
 int gemm_f16_nt_ring_plan(int depth, int64_t steps, int* stage, int64_t* lap, int64_t* refill);
+/* Host evaluation of rung 5's producer/consumer handoff ("GEMM III",
+ * Step 7 "Four barriers = two producer-consumer rings"), no HIP call: each
+ * ring stage has a ready and a free counter in LDS that never reset;
+ * every producer wave adds 1 to ready[k % depth] once its loads of step k
+ * have landed, every consumer wave adds 1 to free[k % depth] once it has
+ * read step k.  For each k step, writes the count a consumer waits for
+ * before reading it (ready_target[k]) and the count a producer waits for
+ * before refilling its stage with it (free_target[k]).  Returns 0 or a
+ * negative status. */
+int gemm_f16_nt_handoff_plan(int depth, int producers, int consumers, int64_t steps, uint32_t* ready_target,
+                             uint32_t* free_target);
 /* Host evaluation of gemm_f16_nt's kernel choice for contiguous, 16-byte
  * aligned operands on a device with `cus` compute units, no HIP call: rows
  * [0, *m_top) run on rung *rung_top and rows [*m_top, M) on rung
