@@ -43,8 +43,7 @@ PEAK_FP16_TFLOPS = 2516.6   # MI355X dense fp16 MFMA: 256 CU x 2.4 GHz x 4096 FL
 HBM_PEAK_GBS = 8000.0
 METRIC = "fp16 GEMM TFLOP/s at M=N=K=4096 (+ % of MI355X dense-fp16 peak)"
 RUNG_NAMES = {0: "auto", 1: "r1_single_tile", 2: "r2_kloop", 3: "r3_grid", 4: "r4_ring",
-              5: "r5_persistent_ws", 6: "r6_ring4", 7: "r7_ring4_2b", 8: "r8_ring4_gap",
-              9: "r9_ring_small", 10: "r10_ring4_paired"}
+              5: "r5_persistent_ws", 8: "r8_ring4_gap", 9: "r9_ring_small", 10: "r10_ring4_paired"}
 
 
 def kernel_source_hash() -> str:
@@ -74,7 +73,7 @@ def parse():
     p.add_argument("--steps", type=int, default=1000)
     p.add_argument("--warmup", type=int, default=100)
     p.add_argument("--workload", default="square_4096")
-    p.add_argument("--rung", type=int, default=0, help="0 = library choice, 1..7 = ladder rung")
+    p.add_argument("--rung", type=int, default=0, choices=sorted(RUNG_NAMES), help="0 = library choice, else a ladder rung")
     p.add_argument("--splitk", type=int, default=-1,
                    help="time gemm_f16_nt_splitk with this many K slices (0 = library choice)")
     p.add_argument("--no-cpu-baseline", action="store_true")

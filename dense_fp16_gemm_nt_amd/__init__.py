@@ -28,12 +28,10 @@ R2_KLOOP = 2
 R3_GRID = 3
 R4_RING = 4
 R5_PERSISTENT_WS = 5
-R6_RING4 = 6
-R7_RING4_2B = 7
 R8_RING4_GAP = 8
 R9_RING_SMALL = 9
 R10_RING4_PAIRED = 10
-RUNGS = (R1_SINGLE_TILE, R2_KLOOP, R3_GRID, R4_RING, R5_PERSISTENT_WS, R6_RING4, R7_RING4_2B, R8_RING4_GAP,
+RUNGS = (R1_SINGLE_TILE, R2_KLOOP, R3_GRID, R4_RING, R5_PERSISTENT_WS, R8_RING4_GAP,
          R9_RING_SMALL, R10_RING4_PAIRED)
 
 _lock = threading.Lock()

@@ -29,10 +29,10 @@ namespace {
 // bench): rung 4 = 256 x 256 tile, 64-wide k steps, 2-stage ring, 8 waves of
 // 128 x 64 (two per SIMD), loads issued in the first sub-step, 2 MFMAs ahead
 // of each barrier, LDS-staged epilogue; rung 5 = 32-wide k steps, 4 stages;
-// rung 6 = rung 4's ring with 4 waves of 128 x 128 on 16x16x32 MFMAs and a
-// generated instruction schedule, persistent (ring4.hpp), for whole tiles;
-// rung 7 = rung 6 with release and publish barriers per step; rung 8 =
-// rung 7's barriers with at most one instruction between two MFMAs; rung 9
+// rung 8 = rung 4's ring with 4 waves of 128 x 128 on 16x16x32 MFMAs and a
+// generated instruction schedule, persistent (ring4.hpp), release and
+// publish barriers per step, at most one instruction between two MFMAs
+// (rungs 6 and 7, earlier forms of it, were removed); rung 9
 // = rung 4's ring with 128 x 128 tiles, 8 waves of 64 x 32 and 4 stages (the
 // library's choice when 256 x 256 tiles would leave most compute units
 // idle); rung 10 = rung 8 with each block's two sub-steps back to back (the
@@ -142,9 +142,15 @@ bool fast_operands(int64_t K, int64_t lda, int64_t ldb, int64_t sa, int64_t sb, 
     return ((uintptr_t)D & 15) == 0;
 }
 
+// Rung numbers the library implements (6 and 7 are no longer used).
+bool known_rung(int rung)
+{
+    return rung >= 0 && rung <= GEMM_F16_NT_R10_RING4_PAIRED && rung != 6 && rung != 7;
+}
+
 int validate(int rung, int64_t M, int64_t N, int64_t K, const void* A, const void* B, const void* D)
 {
-    if (rung < 0 || rung > GEMM_F16_NT_R10_RING4_PAIRED) return GEMM_F16_NT_INVALID_ARG;
+    if (!known_rung(rung)) return GEMM_F16_NT_INVALID_ARG;
     if (M < 0 || N < 0 || K < 0) return GEMM_F16_NT_INVALID_ARG;
     const bool any_out = M > 0 && N > 0;
     if (any_out && K > 0 && (A == nullptr || B == nullptr)) return GEMM_F16_NT_INVALID_ARG;
@@ -160,8 +166,7 @@ int validate(int rung, int64_t M, int64_t N, int64_t K, const void* A, const voi
     if (rung == GEMM_F16_NT_R1_SINGLE_TILE && !(M == 128 && N == 128 && K == 64)) return GEMM_F16_NT_UNSUPPORTED;
     if (rung == GEMM_F16_NT_R2_KLOOP && !(M == 128 && N == 128)) return GEMM_F16_NT_UNSUPPORTED;
     if (rung == GEMM_F16_NT_R3_GRID && (N + 127) / 128 > 65535) return GEMM_F16_NT_UNSUPPORTED;
-    if ((rung == GEMM_F16_NT_R6_RING4 || rung == GEMM_F16_NT_R7_RING4_2B || rung == GEMM_F16_NT_R8_RING4_GAP) &&
-        !(ring4_shape(M, N, K) && ring4_pitch_ok(N)))
+    if (rung == GEMM_F16_NT_R8_RING4_GAP && !(ring4_shape(M, N, K) && ring4_pitch_ok(N)))
         return GEMM_F16_NT_UNSUPPORTED;
     if (rung == GEMM_F16_NT_R10_RING4_PAIRED && !(ring4_paired_shape(M, N, K, K, K) && ring4_pitch_ok(N)))
         return GEMM_F16_NT_UNSUPPORTED;
@@ -244,11 +249,10 @@ bool ring4_fits(const GemmArgs& g)
 
 // Persistent launch: one workgroup per compute unit (fewer when there are
 // fewer tiles); every workgroup walks its share of the tiles.  form: the
-// k loop (1 = one barrier per step, 2 = release and publish barriers, 3 =
-// the second form's barriers with one instruction per MFMA gap, 4 = each
-// block's two sub-steps back to back, 0 = the library's choice, 4: the
-// fastest at every size measured, whether the operands stay in the
-// last-level cache or stream from HBM).
+// k loop (3 = release and publish barriers with one instruction per MFMA
+// gap, 4 = each block's two sub-steps back to back, 0 = the library's
+// choice, 4: the fastest at every size measured, whether the operands
+// stay in the last-level cache or stream from HBM).
 int launch_ring4(const GemmArgs& g0, hipStream_t s, int form = 0)
 {
     GemmArgs g = g0;
@@ -264,12 +268,8 @@ int launch_ring4(const GemmArgs& g0, hipStream_t s, int form = 0)
     if (form != 4 && g.K % ring4::C::BK != 0) return GEMM_F16_NT_UNSUPPORTED;
     if (form == 4)
         hipLaunchKernelGGL(ring4::ring4_kernel<4>, dim3((unsigned)grid), dim3(ring4::C::THREADS), 0, s, g);
-    else if (form == 3)
-        hipLaunchKernelGGL(ring4::ring4_kernel<3>, dim3((unsigned)grid), dim3(ring4::C::THREADS), 0, s, g);
-    else if (form == 2)
-        hipLaunchKernelGGL(ring4::ring4_kernel<2>, dim3((unsigned)grid), dim3(ring4::C::THREADS), 0, s, g);
     else
-        hipLaunchKernelGGL(ring4::ring4_kernel<1>, dim3((unsigned)grid), dim3(ring4::C::THREADS), 0, s, g);
+        hipLaunchKernelGGL(ring4::ring4_kernel<3>, dim3((unsigned)grid), dim3(ring4::C::THREADS), 0, s, g);
     return launched();
 }
 
@@ -622,10 +622,6 @@ int run(int rung, int64_t M, int64_t N, int64_t K, const void* A, const void* B,
         return launch_ring(contiguous_args(M, N, K, A, B, D), s);
     case GEMM_F16_NT_R5_PERSISTENT_WS:
         return launch_ws(M, N, K, a, b, d, grid_override > 0 ? grid_override : cus, s);
-    case GEMM_F16_NT_R6_RING4:
-        return launch_ring4(contiguous_args(M, N, K, A, B, D), s, 1);
-    case GEMM_F16_NT_R7_RING4_2B:
-        return launch_ring4(contiguous_args(M, N, K, A, B, D), s, 2);
     case GEMM_F16_NT_R8_RING4_GAP:
         return launch_ring4(contiguous_args(M, N, K, A, B, D), s, 3);
     case GEMM_F16_NT_R9_RING_SMALL:
@@ -864,8 +860,7 @@ int64_t gemm_f16_nt_tile_walk(int rung, int64_t M, int64_t N, int cus, int64_t* 
 {
     if (M < 0 || N < 0 || cus < 1 || capacity < 0) return GEMM_F16_NT_INVALID_ARG;
     if (capacity > 0 && (wg == nullptr || row0 == nullptr || col0 == nullptr)) return GEMM_F16_NT_INVALID_ARG;
-    const bool four_wave = rung == GEMM_F16_NT_R6_RING4 || rung == GEMM_F16_NT_R7_RING4_2B ||
-                           rung == GEMM_F16_NT_R8_RING4_GAP || rung == GEMM_F16_NT_R10_RING4_PAIRED;
+    const bool four_wave = rung == GEMM_F16_NT_R8_RING4_GAP || rung == GEMM_F16_NT_R10_RING4_PAIRED;
     if (!four_wave && rung != GEMM_F16_NT_R4_RING && rung != GEMM_F16_NT_R5_PERSISTENT_WS &&
         rung != GEMM_F16_NT_R9_RING_SMALL)
         return GEMM_F16_NT_INVALID_ARG;

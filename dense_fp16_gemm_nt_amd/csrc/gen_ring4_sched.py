@@ -20,46 +20,40 @@ Pipeline (the pages' software pipeline with a double-buffered operand ring,
     B = 8i + j (all 256 accumulation registers).  The 16x16x32 form is
     used because it holds a higher clock than 32x32x16 at the same work per
     cycle (it reads and writes half the accumulator bytes per FLOP);
-  * a k step is 2 sub-steps of 32 k; the 16 fragments (8 A blocks, 8 B
-    blocks, one 16-byte LDS read each) of sub-step 1 are read while sub-step
-    0 runs, into the second of two fragment buffers (F0 = v[128:191],
-    F1 = v[192:255]);
-  * a wave's 16 loads of a step (8 A, 8 B row groups of 1 KiB) are split:
-    the first n_hand of step j+2 go out right after step j's barrier (which
-    frees the stage step j+2 refills), the rest during step j+1, so every
-    load has more than a step to land and the loads do not come in bursts;
-  * sub-step 1 waits for its own loads (vmcnt) and LDS reads (lgkmcnt),
-    crosses the one barrier of the step (which publishes step j+1 and frees
-    step j's stage), then reads step j+1's sub-step-0 fragments into F0;
-  * the prologue loads steps 0 and 1 (both stages are free), so step 0
-    issues no body loads; the last two steps issue no handoff loads and the
-    last step has no barrier.
+  * a k step is 2 sub-steps of 32 k; a wave issues 16 loads per step (8 A,
+    8 B row groups of 1 KiB) and 32 fragment reads (one 16-byte LDS read
+    per block and sub-step);
+  * each step has a release barrier, after the last reads of its stage
+    (step j+2 may then refill it), and a publish barrier, after this wave's
+    loads of step j+1 have landed (its fragment reads follow);
+  * the prologue loads steps 0 and 1 (both stages are free); the last two
+    steps issue no loads of their own and the last step has no barrier.
 
-That is the first form (generate, macro G16_RING4_KLOOP).  A second form
-(generate2, macro G16_RING4_KLOOP2) splits the handoff in two
-barriers per step: a release barrier right after sub-step 0's fragment reads
-(the stage is dead from there on) and a publish barrier in sub-step 1.  The
-loads of step j+2 then start a whole sub-step earlier and go out evenly, one
-every few MFMAs, instead of in a burst after one barrier: when the operands
-stream from HBM, bursts from all CUs of an XCD queue at its L2 and triple the
-load latency.  The third form (generate3, macro G16_RING4_KLOOP3, the
-library's choice) keeps those two barriers and places at most one
-instruction between two MFMAs (see its section below).
+Two forms are generated.  The third form (generate3, macro
+G16_RING4_KLOOP3, rung 8) places at most one instruction between two
+MFMAs; the fourth (generate4, macro G16_RING4_KLOOP4, rung 10, the
+library's choice) also issues each block's two sub-steps back to back
+into its accumulator and takes a partial first step and a ring carried
+from tile to tile (see their sections below).  The first two forms of the
+ladder (one barrier per step, and the release/publish split with clumped
+instructions) were removed once the third superseded them.
 
 MFMA operand roles: the B block feeds srcA and the A block srcB, so lane l
 of block (i, j) holds output row 16i + l%16 and the four consecutive output
 columns 16j + 4*(l/16) + 0..3.
 
-Operands expected by the block (see ring4.hpp): load offsets %[aoQ],
-%[boQ] and, for the third form, %[axQ], %[bxQ] (the same less 1024*(Q mod
-4)) (VGPR); fragment-read addresses %[raSK], %[rbSK] for stage S and
-sub-step K (VGPR); buffer resources %[rsa], %[rsb]; the wave's LDS load base
-%[lb]; the byte offsets %[ko] and %[kh] of the next two steps to load and
-the count %[rem] of k steps (SGPR, all modified; %[kh] is scratch); and for
-the epilogue the staging and store addresses %[ewJ], %[erQ], %[soQ], the
+Operands expected by the block (see ring4.hpp): load offsets %[axQ],
+%[bxQ] (the row groups' lane offsets less 1024*(Q mod 4), the instruction
+offset the loads carry) (VGPR); fragment-read addresses %[raSK], %[rbSK]
+for stage S and sub-step K (VGPR); buffer resources %[rsa], %[rsb]; the
+wave's LDS load base %[lb] (the fourth form: %[lb0], %[lb1]); the byte
+offsets %[ko] and %[kh] of the next two steps to load and the count
+%[rem] of k steps (SGPR, all modified; %[kh] is scratch); and for the
+epilogue the staging and store addresses %[ewJ], %[erQ], %[soQ], the
 output resource %[rsd], the row-group stride %[gstr] and the scratch
-%[sdo]; the fourth form also takes the head masks %[hm0], %[hm1].  The accumulators a0..a255 and fragment buffers v128..v255 are
-fixed registers of the block.
+%[sdo]; the fourth form also takes the head masks %[hm0], %[hm1].  The
+accumulators a0..a255 and fragment buffers v128..v255 are fixed
+registers of the block.
 """
 from __future__ import annotations
 
@@ -160,25 +154,6 @@ class Emitter:
         self.op("s_waitcnt vmcnt(0) lgkmcnt(0)")
         self.lgkm.clear()
 
-    # --- direct-to-LDS loads -----------------------------------------------
-    def load(self, n: int, stage: int, ahead: bool = False) -> None:
-        """Load n (0..15) of this wave into `stage`: even n are A loads, odd
-        n are B loads (row group n // 2 of the wave's share).  The global
-        k offset is %[ko], or %[kh] (= %[ko] + 128, the step after) when
-        ahead.  No immediate offset: for a direct-to-LDS load it would be
-        added to the LDS destination as well."""
-        q = n // 2
-        if n % 2 == 0:
-            dst = stage * 65536 + q * 1024
-            voff, rsrc = f"%[ao{q}]", "%[rsa]"
-        else:
-            dst = stage * 65536 + 32768 + q * 1024
-            voff, rsrc = f"%[bo{q}]", "%[rsb]"
-        self.op(f"s_add_u32 m0, %[lb], {dst}")
-        self.op("s_nop 0")  # M0 write -> LDS-DMA read of M0
-        koff = "%[kh]" if ahead else "%[ko]"
-        self.op(f"buffer_load_dwordx4 {voff}, {rsrc}, {koff} offen lds")
-
     # --- epilogue interleaved with the last sub-step -------------------------
     def epi_start(self, order: str) -> None:
         # row groups finish in row order only when the MFMAs go row by row
@@ -245,308 +220,6 @@ def read_order(order: str) -> list[tuple[str, int]]:
             if f not in seen:
                 seen.append(f)
     return seen
-
-
-def spread(n: int, start: int, every: int) -> list[int]:
-    return [start + every * k for k in range(n)]
-
-
-def emit_step(e: Emitter, stage: int, first: bool, body_loads: bool, hand_loads: bool, last: bool,
-              p: dict, wave: int = 0) -> None:
-    """One 64-wide k step j reading `stage`.
-
-    The 16 loads of a step are split: loads 0 .. n_hand-1 of step j+2 go out
-    right after step j's barrier (the barrier frees `stage`, which step j+2
-    refills), loads n_hand .. 15 of step j+1 go out during step j's body
-    (into the other stage, freed by step j-1's barrier).  body_loads /
-    hand_loads say whether those steps exist.  first: the accumulators
-    start from 0.  last: no handoff (no barrier, no next-step reads).
-    wave: the wave's index; its load slots move by wave * p["hand_shift"]
-    and wave * p["body_shift"] MFMAs, so that the waves of a workgroup do
-    not issue their loads in the same slot."""
-    n_hand = len(p["hand_slots"])
-    hs, bs = wave * p.get("hand_shift", 0), wave * p.get("body_shift", 0)
-    body = [(n_hand + k, g + bs) for k, g in enumerate(p["body_slots"])] if body_loads else []
-    nb = 0
-    ro = read_order(p.get("order", "ij"))
-    nr = len(ro)
-    hand: list[tuple[int, int]] = []
-    nh = 0
-    for kk in range(KSUB):
-        cur = kk & 1
-        if kk == 0:
-            # sub-step 1's fragments, from this stage, into F1
-            reads = [(1, op, idx, stage, 1) for (op, idx) in ro]
-            slots = spread(nr, p["read_start"], p["read_every"])
-        else:
-            reads, slots = [], []
-        r_next = 0
-        for q in range(NQ):
-            i, j = mfma_block(q, p.get("order", "ij"))
-            g = kk * NQ + q
-            if kk == KSUB - 1 and not last and q == p["pre"]:
-                # handoff: this wave's reads of the stage and its loads of
-                # the next step are complete; the barrier publishes the
-                # next step and frees this stage for the step after it
-                e.wait_all()
-                e.op("s_barrier")
-                reads = [(0, op, idx, stage ^ 1, 0) for (op, idx) in ro]
-                slots = spread(nr, q + p["post_start"], p["post_every"])
-                r_next = 0
-                if hand_loads:
-                    hand = [(k, q + off + hs) for k, off in enumerate(p["hand_slots"])]
-            if last and kk == KSUB - 1 and q == 0:
-                e.epi_start(p.get("order", "ij"))
-            e.mfma(cur, i, j, first and kk == 0)
-            if last and kk == KSUB - 1:
-                e.epi_after_mfma(q, p["epi_slot"], p["epi_delay"])
-            while r_next < len(reads) and slots[r_next] <= q:
-                e.read(*reads[r_next])
-                r_next += 1
-            if kk == KSUB - 1:
-                while nh < len(hand) and hand[nh][1] <= q:
-                    e.load(hand[nh][0], stage, ahead=True)  # step j+2 -> this stage
-                    nh += 1
-            while nb < len(body) and body[nb][1] <= g:
-                e.load(body[nb][0], stage ^ 1)          # step j+1 -> other stage
-                nb += 1
-        # whatever did not fit the MFMA slots goes out at the end
-        while r_next < len(reads):
-            e.read(*reads[r_next])
-            r_next += 1
-    while nh < len(hand):
-        e.load(hand[nh][0], stage, ahead=True)
-        nh += 1
-    if last:
-        e.epi_finish()
-    assert nb == len(body), "body load slots beyond the step"
-    if not last:
-        e.op("s_add_u32 %[ko], %[ko], 128")   # %[ko] is the offset of step j+1 during step j
-        e.op("s_add_u32 %[kh], %[kh], 128")   # %[kh] that of step j+2
-
-
-def generate(p: dict, wave: int = 0) -> str:
-    """The k loop of wave `wave`.  During step j, %[ko] is the byte offset
-    of step j+1 (body loads) and %[kh] that of step j+2 (handoff loads)."""
-    assert len(p["hand_slots"]) + len(p["body_slots"]) == NLOAD
-    e = Emitter()
-    # prologue: steps 0 and 1 into stages 0 and 1
-    for n in range(NLOAD):
-        e.load(n, 0)
-    e.op("s_add_u32 %[ko], %[ko], 128")
-    for n in range(NLOAD):
-        e.load(n, 1)
-    # %[ko] = offset of step 1 while step 0 runs, %[kh] that of step 2
-    e.op("s_add_u32 %[kh], %[ko], 128")
-    e.op(f"s_waitcnt vmcnt({NLOAD})")
-    e.op("s_barrier")
-    for (op, idx) in read_order(p.get("order", "ij")):
-        e.read(0, op, idx, 0, 0)
-    after_handoff = None
-
-    def step(stage, first, body_loads, hand_loads, last):
-        nonlocal after_handoff
-        if after_handoff is not None:
-            e.lgkm = list(after_handoff)
-        emit_step(e, stage, first, body_loads, hand_loads, last, p, wave)
-        if not last:
-            if after_handoff is None:
-                after_handoff = list(e.lgkm)
-            assert e.lgkm == after_handoff, "step entry state differs between paths"
-
-    # step 0 (stage 0): KT == 2 has no step 2 to load
-    e.op("s_cmp_eq_u32 %[rem], 2")
-    e.op("s_cbranch_scc1 5f")
-    step(0, True, False, True, False)
-    e.op("s_sub_u32 %[rem], %[rem], 1")
-    e.op("s_branch 1f")
-    e.label("5")
-    step(0, True, False, False, False)
-    e.op("s_sub_u32 %[rem], %[rem], 1")
-    e.op("s_branch 2f")
-    # steps in stage 1 (rem >= 2 here)
-    e.label("1")
-    e.op("s_cmp_eq_u32 %[rem], 2")
-    e.op("s_cbranch_scc1 6f")
-    step(1, False, True, True, False)
-    e.op("s_sub_u32 %[rem], %[rem], 1")
-    e.op("s_branch 7f")
-    e.label("6")
-    step(1, False, True, False, False)
-    e.op("s_sub_u32 %[rem], %[rem], 1")
-    e.op("s_branch 3f")
-    # steps in stage 0 (rem >= 2 here)
-    e.label("7")
-    e.op("s_cmp_eq_u32 %[rem], 2")
-    e.op("s_cbranch_scc1 8f")
-    step(0, False, True, True, False)
-    e.op("s_sub_u32 %[rem], %[rem], 1")
-    e.op("s_branch 1b")
-    e.label("8")
-    step(0, False, True, False, False)
-    e.op("s_sub_u32 %[rem], %[rem], 1")
-    # last step in stage 1
-    e.label("2")
-    step(1, False, False, False, True)
-    e.op("s_branch 4f")
-    # last step in stage 0
-    e.label("3")
-    step(0, False, False, False, True)
-    e.label("4")
-    return "\n".join(e.lines)
-
-
-def emit_step2(e: Emitter, stage: int, first: bool, carried: bool, ahead: bool, last: bool, p: dict,
-               wave: int = 0) -> None:
-    """One 64-wide k step j in the two-barrier form.
-
-    A release barrier after sub-step 0's reads of this stage (MFMA p["rel"])
-    frees the stage as soon as every wave has its fragments, instead of at
-    the end of the step.  The 16 loads of step j+2 then go out one every
-    p["load_every"] MFMAs from that barrier on; those that fall beyond the
-    step ("carried") go out at the start of step j+1.  A publish barrier in
-    sub-step 1 (MFMA 64 + p["pre"]) waits for step j+1's loads (vmcnt
-    counts only the younger loads of step j+2) and is followed by step
-    j+1's sub-step-0 fragment reads.  carried: step j+1's last loads are
-    issued at the start of this step; ahead: step j+2 exists.  first: the
-    accumulators start from 0.  last: no barriers, no next-step reads.
-    wave: the wave's index; its load slots move by wave * p["wave_shift"]
-    MFMAs."""
-    order = p.get("order", "ij")
-    ro = read_order(order)
-    nr = len(ro)
-    rel, every = p["rel"], p["load_every"]
-    pub = NQ + p["pre"]                                  # MFMA index of the publish barrier
-    shift = wave * p.get("wave_shift", 0)
-    slots = [rel + shift + every * n for n in range(NLOAD)]   # step j+2's loads, in step-j MFMA indices
-    own = [(n, g) for n, g in enumerate(slots) if g < 2 * NQ] if (ahead and not last) else []
-    carry = [(n, g - 2 * NQ) for n, g in enumerate(slots) if g >= 2 * NQ] if carried else []
-    n_after_own = None                                   # own loads issued before the publish wait
-    ci = oi = 0
-    reads: list = []
-    rslots: list = []
-    r_next = 0
-    for kk in range(KSUB):
-        cur = kk & 1
-        if kk == 0:
-            reads = [(1, op, idx, stage, 1) for (op, idx) in ro]
-            rslots = spread(nr, p["read_start"], p["read_every"])
-            r_next = 0
-        for q in range(NQ):
-            i, j = mfma_block(q, order)
-            g = kk * NQ + q
-            if not last and g == rel:
-                # release: this wave's reads of the stage are complete
-                while r_next < len(reads):
-                    e.read(*reads[r_next])
-                    r_next += 1
-                e.op("s_waitcnt lgkmcnt(0)")
-                e.lgkm.clear()
-                e.op("s_barrier")
-            if not last and g == pub:
-                # publish: step j+1's loads (all older than the own loads
-                # issued so far) have landed in every wave
-                # (loads issue in slot order; a carried load and an own
-                # load in one slot go carried first)
-                last_c = max([gg for (_, gg) in carry], default=-1)
-                n_young = sum(1 for (_, gg) in own if last_c < gg < pub or (gg == last_c and gg < pub))
-                e.op(f"s_waitcnt vmcnt({n_young}) lgkmcnt(0)")
-                e.lgkm.clear()
-                e.op("s_barrier")
-                reads = [(0, op, idx, stage ^ 1, 0) for (op, idx) in ro]
-                rslots = spread(nr, q + p["post_start"], p["post_every"])
-                r_next = 0
-            if last and kk == KSUB - 1 and q == 0:
-                e.epi_start(p.get("order", "ij"))
-            e.mfma(cur, i, j, first and kk == 0)
-            if last and kk == KSUB - 1:
-                e.epi_after_mfma(q, p["epi_slot"], p["epi_delay"])
-            while r_next < len(reads) and rslots[r_next] <= q:
-                e.read(*reads[r_next])
-                r_next += 1
-            while ci < len(carry) and carry[ci][1] <= g:
-                e.load(carry[ci][0], stage ^ 1, ahead=False)   # step j+1 -> other stage
-                ci += 1
-            while oi < len(own) and own[oi][1] <= g:
-                e.load(own[oi][0], stage, ahead=True)          # step j+2 -> this stage
-                oi += 1
-        while r_next < len(reads):
-            e.read(*reads[r_next])
-            r_next += 1
-    if last:
-        e.epi_finish()
-    assert ci == len(carry) and oi == len(own)
-    if not last:
-        e.op("s_add_u32 %[ko], %[ko], 128")
-        e.op("s_add_u32 %[kh], %[kh], 128")
-
-
-def generate2(p: dict, wave: int = 0) -> str:
-    """The k loop of wave `wave` in the two-barrier form (same branch
-    structure and operands as generate())."""
-    assert p["rel"] >= len(read_order(p.get("order", "ij"))) * p["read_every"] - 1 + p["read_start"], \
-        "release barrier before the sub-step-1 reads are issued"
-    last_slot = p["rel"] + 3 * p.get("wave_shift", 0) + p["load_every"] * (NLOAD - 1)
-    assert last_slot < 2 * NQ + NQ + p["pre"], "loads too sparse"
-    e = Emitter()
-    for n in range(NLOAD):
-        e.load(n, 0)
-    e.op("s_add_u32 %[ko], %[ko], 128")
-    for n in range(NLOAD):
-        e.load(n, 1)
-    e.op("s_add_u32 %[kh], %[ko], 128")
-    e.op(f"s_waitcnt vmcnt({NLOAD})")
-    e.op("s_barrier")
-    for (op, idx) in read_order(p.get("order", "ij")):
-        e.read(0, op, idx, 0, 0)
-    after = None
-
-    def step(stage, first, carried, ahead, last):
-        nonlocal after
-        if after is not None:
-            e.lgkm = list(after)
-        emit_step2(e, stage, first, carried, ahead, last, p, wave)
-        if not last:
-            if after is None:
-                after = list(e.lgkm)
-            assert e.lgkm == after, "step entry state differs between paths"
-
-    # step 0: nothing carried (the prologue loaded step 1 whole)
-    e.op("s_cmp_eq_u32 %[rem], 2")
-    e.op("s_cbranch_scc1 5f")
-    step(0, True, False, True, False)
-    e.op("s_sub_u32 %[rem], %[rem], 1")
-    e.op("s_branch 1f")
-    e.label("5")
-    step(0, True, False, False, False)
-    e.op("s_sub_u32 %[rem], %[rem], 1")
-    e.op("s_branch 2f")
-    e.label("1")
-    e.op("s_cmp_eq_u32 %[rem], 2")
-    e.op("s_cbranch_scc1 6f")
-    step(1, False, True, True, False)
-    e.op("s_sub_u32 %[rem], %[rem], 1")
-    e.op("s_branch 7f")
-    e.label("6")
-    step(1, False, True, False, False)
-    e.op("s_sub_u32 %[rem], %[rem], 1")
-    e.op("s_branch 3f")
-    e.label("7")
-    e.op("s_cmp_eq_u32 %[rem], 2")
-    e.op("s_cbranch_scc1 8f")
-    step(0, False, True, True, False)
-    e.op("s_sub_u32 %[rem], %[rem], 1")
-    e.op("s_branch 1b")
-    e.label("8")
-    step(0, False, True, False, False)
-    e.op("s_sub_u32 %[rem], %[rem], 1")
-    e.label("2")
-    step(1, False, False, False, True)
-    e.op("s_branch 4f")
-    e.label("3")
-    step(0, False, False, False, True)
-    e.label("4")
-    return "\n".join(e.lines)
 
 
 # ------------------------------------------------------------ third form
@@ -1135,25 +808,6 @@ DEFAULT4 = {
 }
 
 
-DEFAULT = {
-    "order": "snake",     # MFMA order inside a sub-step (see mfma_block)
-    "pre": 32,            # MFMAs of sub-step 1 before the barrier
-    "read_start": 0,      # sub-step 0: first read after MFMA read_start ...
-    "read_every": 1,      # ... then one every read_every MFMAs
-    "post_start": 0,      # after the barrier: first read after MFMA pre + post_start ...
-    "post_every": 1,      # ... then one every post_every MFMAs
-    "hand_slots": spread(8, 0, 4),     # loads 0-7 of step j+2 after step j's barrier
-    "body_slots": spread(8, 2, 8),     # loads 8-15 of step j+1 during step j
-    "epi_slot": 8,        # epilogue instructions per MFMA slot of the last sub-step
-    "epi_delay": 2,       # MFMAs between a row group's last MFMA and its first read
-}
-
-# two-barrier form (generate2): release after sub-step 0's reads, loads of
-# step j+2 one every 8 MFMAs from there, publish barrier at MFMA 64 + pre
-DEFAULT2 = {k: v for k, v in DEFAULT.items() if k not in ("hand_slots", "body_slots")}
-DEFAULT2.update(rel=24, load_every=8, pre=32)
-
-
 def as_macro(name: str, text: str) -> str:
     body = [f'    "{ln}\\n"' for ln in text.split("\n")]
     return f"#define {name} \\\n" + " \\\n".join(body) + "\n"
@@ -1166,21 +820,15 @@ def params_line(p: dict) -> str:
 def main(argv: list[str]) -> int:
     here = os.path.dirname(os.path.abspath(__file__))
     out = os.path.join(here, "ring4_sched.inc")
-    text1 = generate(DEFAULT)
-    text2 = generate2(DEFAULT2)
     text3 = generate3(DEFAULT3)
     text4 = generate4(DEFAULT4)
     with open(out, "w") as f:
         f.write("// Generated by gen_ring4_sched.py.  Do not edit.\n")
-        f.write("// G16_RING4_KLOOP: one barrier per k step; " + params_line(DEFAULT) + ".\n")
-        f.write(as_macro("G16_RING4_KLOOP", text1))
-        f.write("// G16_RING4_KLOOP2: release and publish barriers per k step; " + params_line(DEFAULT2) + ".\n")
-        f.write(as_macro("G16_RING4_KLOOP2", text2))
         f.write("// G16_RING4_KLOOP3: release and publish barriers per k step, one instruction per MFMA gap; " + params_line(DEFAULT3) + ".\n")
         f.write(as_macro("G16_RING4_KLOOP3", text3))
         f.write("// G16_RING4_KLOOP4: each block's two sub-steps back to back, release and publish barriers; " + params_line(DEFAULT4) + ".\n")
         f.write(as_macro("G16_RING4_KLOOP4", text4))
-    print(out, sum(len(t.split("\n")) for t in (text1, text2, text3, text4)), "lines")
+    print(out, sum(len(t.split("\n")) for t in (text3, text4)), "lines")
     return 0
 
 

@@ -49,7 +49,7 @@ extern "C" {
 #endif
 
 #define GEMM_F16_NT_OK 0
-#define GEMM_F16_NT_INVALID_ARG (-1) /* negative size, null pointer with data, unknown rung, overlap */
+#define GEMM_F16_NT_INVALID_ARG (-1) /* negative size, null pointer with data, unknown or removed rung, overlap */
 #define GEMM_F16_NT_UNSUPPORTED (-2) /* shape or alignment a rung does not implement, odd addresses */
 #define GEMM_F16_NT_LAUNCH (-3)      /* the HIP launch itself failed */
 #define GEMM_F16_NT_DEVICE (-4)      /* no usable device / device query failed / not gfx950 */
@@ -64,21 +64,22 @@ extern "C" {
                                         (loads staged through registers on rows off 16-byte
                                         boundaries, K >= 8) */
 #define GEMM_F16_NT_R5_PERSISTENT_WS 5 /* any shape: persistent, producer/consumer waves */
-#define GEMM_F16_NT_R6_RING4 6 /* rung 4's ring with 4 waves of 128 x 128 and a fixed instruction
-                                  schedule: M, N >= 256, N a multiple of 8, K a multiple of 64,
-                                  K >= 128, N < 2^24 (when M or N is not a multiple of 256 the last
-                                  tile row or column ends at M or N and overlaps its neighbour) */
-#define GEMM_F16_NT_R7_RING4_2B 7 /* rung 6 with a release and a publish barrier per k step (loads start
-                                     earlier and spread evenly); same shapes as rung 6 */
-#define GEMM_F16_NT_R8_RING4_GAP 8 /* rung 7's barriers with at most one instruction between two MFMAs
-                                      (offset loads, 4 M0 writes per step); same shapes as rung 6 */
+/* Rungs 6 and 7 (earlier forms of rung 8: one barrier per k step, then a
+ * release and a publish barrier with clumped instructions) were removed;
+ * their numbers are not reused and return GEMM_F16_NT_INVALID_ARG. */
+#define GEMM_F16_NT_R8_RING4_GAP 8 /* rung 4's ring with 4 waves of 128 x 128 on 16x16x32 MFMAs, a generated
+                                      instruction schedule with a release and a publish barrier per k step
+                                      and at most one instruction between two MFMAs, persistent: M, N >=
+                                      256, N a multiple of 8 and under 2^24, K a multiple of 64, K >= 128
+                                      (when M or N is not a multiple of 256 the last tile row or column ends
+                                      at M or N and overlaps its neighbour) */
 #define GEMM_F16_NT_R9_RING_SMALL 9 /* any shape: rung 4's ring with 128 x 128 tiles, 8 waves of 64 x 32 and
                                        4 stages (the same register staging on general rows); the
                                        library's choice when 256 x 256 tiles would number at most 0.4
                                        per compute unit, and, off the four-wave ring, where its tiles
                                        take fewer rounds of the compute units than rung 4's */
 #define GEMM_F16_NT_R10_RING4_PAIRED 10 /* rung 8 with each 16 x 16 block's two 32-wide sub-steps issued
-                                           back to back into its accumulator; the shapes of rung 6 with
+                                           back to back into its accumulator; the shapes of rung 8 with
                                            any N >= 256 (rows of D on any 2-byte boundary), and also K a
                                            multiple of 8 above 64 that is not a multiple of 64 (the
                                            partial k step goes first; rows of A and B then shorter than
@@ -192,8 +193,8 @@ int64_t gemm_f16_nt_schedule(int64_t M, int64_t N, int64_t num_workgroups, int64
  * V3 "Spatial Tiling with Multiple CTAs" for the tile origins, V6 "Better
  * L2 Locality" for the grouped order).  rung: 4 and 9 (one workgroup per
  * 256 x 256 or 128 x 128 tile, grouped order with groups of 8 tile rows),
- * 5 (persistent, one workgroup per compute unit, the same order) or 6, 7,
- * 8, 10 (the four-wave ring: persistent, groups of 4 tile rows, the last
+ * 5 (persistent, one workgroup per compute unit, the same order) or 8
+ * and 10 (the four-wave ring: persistent, groups of 4 tile rows, the last
  * tile row and column moved back to end at M and N; M, N >= 256, else
  * GEMM_F16_NT_UNSUPPORTED).  Writes one entry per tile visit in
  * workgroup-major visit order: workgroup wg[i] computes the output block

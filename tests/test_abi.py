@@ -67,7 +67,7 @@ A0, B0, D0 = 0x10000, 0x20000000, 0x40000000   # fake, 16-byte aligned, disjoint
     ((9, 64, 64, 6, A0, B0, D0), g.UNSUPPORTED),
     ((5, 64, 64, 12, A0, B0, D0), g.UNSUPPORTED),          # the other rungs need 16-byte rows
     ((5, 64, 64, 64, A0 + 2, B0, D0), g.UNSUPPORTED),
-    ((6, 256, 256, 128, A0, B0, D0 + 8), g.UNSUPPORTED),
+    ((8, 256, 256, 128, A0, B0, D0 + 8), g.UNSUPPORTED),
     ((1, 128, 128, 64, A0, B0 + 2, D0), g.UNSUPPORTED),
     ((0, 64, 64, 64, A0 + 1, B0, D0), g.UNSUPPORTED),      # odd address: not an fp16 array
     ((0, 64, 64, 64, A0, B0, D0 + 1), g.UNSUPPORTED),
@@ -80,7 +80,7 @@ A0, B0, D0 = 0x10000, 0x20000000, 0x40000000   # fake, 16-byte aligned, disjoint
     ((10, 64, 64, 64, A0, B0, D0), g.UNSUPPORTED),         # rung 10: M, N >= 256
     ((10, 512, 256, 192, A0, B0, D0), g.OK),
     ((10, 256, 260, 128, A0, B0, D0), g.OK),              # rung 10 takes any N >= 256
-    ((6, 256, 260, 128, A0, B0, D0), g.UNSUPPORTED),      # rungs 6-8 keep N % 8 == 0
+    ((8, 256, 260, 128, A0, B0, D0), g.UNSUPPORTED),      # rung 8 keeps N % 8 == 0
     ((10, 256, 256, 136, A0, B0, D0), g.OK),               # rung 10: K % 64 != 0, partial first step
     ((10, 256, 264, 72, A0, B0, D0), g.OK),
     ((10, 256, 256, 64, A0, B0, D0), g.UNSUPPORTED),       # ... but at least two k steps
@@ -98,24 +98,24 @@ A0, B0, D0 = 0x10000, 0x20000000, 0x40000000   # fake, 16-byte aligned, disjoint
     ((3, 1000, 333, 72, A0, B0, D0), g.OK),
     ((4, 1, 1, 8, A0, B0, D0), g.OK),
     ((5, 5000, 7, 8, A0, B0, D0), g.OK),
-    ((6, 256, 512, 128, A0, B0, D0), g.OK),
-    ((6, 64, 64, 64, A0, B0, D0), g.UNSUPPORTED),          # R6 needs M, N >= 256
-    ((6, 256, 256, 64, A0, B0, D0), g.UNSUPPORTED),        # ... and at least two k steps
-    ((6, 256, 256, 136, A0, B0, D0), g.UNSUPPORTED),       # ... of 64
-    ((6, 256, 300, 128, A0, B0, D0), g.UNSUPPORTED),       # ... N a multiple of 8
-    ((6, 300, 264, 128, A0, B0, D0), g.OK),                # ragged M, N: the last tiles move back
+    ((8, 256, 512, 128, A0, B0, D0), g.OK),
+    ((8, 64, 64, 64, A0, B0, D0), g.UNSUPPORTED),          # R8 needs M, N >= 256
+    ((8, 256, 256, 64, A0, B0, D0), g.UNSUPPORTED),        # ... and at least two k steps
+    ((8, 256, 256, 200, A0, B0, D0), g.UNSUPPORTED),       # ... of 64
+    ((8, 256, 300, 128, A0, B0, D0), g.UNSUPPORTED),       # ... N a multiple of 8
+    ((8, 300, 264, 128, A0, B0, D0), g.OK),                # ragged M, N: the last tiles move back
     ((8, 255, 264, 128, A0, B0, D0), g.UNSUPPORTED),       # ... but not below one tile
-    ((7, 512, 256, 192, A0, B0, D0), g.OK),
-    ((7, 256, 256, 64, A0, B0, D0), g.UNSUPPORTED),
+    ((6, 512, 256, 192, A0, B0, D0), g.INVALID_ARG),       # rungs 6 and 7 were removed
+    ((7, 512, 256, 192, A0, B0, D0), g.INVALID_ARG),
     ((0, 0, 64, 64, 0, 0, 0), g.OK),                       # empty output: nothing needed
     ((0, 64, 64, 0, 0, 0, D0), g.OK),                      # K = 0: D only
     ((0, 64, 64, 1 << 23, A0, B0, D0), g.UNSUPPORTED),     # beyond the kernels' index range
     # the four-wave ring's output blocks span 256 * N bytes in a 32-bit size: N < 2^24
-    ((6, 256, 1 << 24, 128, A0, 1 << 34, 1 << 36), g.UNSUPPORTED),
+    ((8, 256, 1 << 24, 128, A0, 1 << 34, 1 << 36), g.UNSUPPORTED),
     ((10, 256, 1 << 24, 128, A0, 1 << 34, 1 << 36), g.UNSUPPORTED),
     ((8, 256, (1 << 24) + 8, 128, A0, 1 << 34, 1 << 36), g.UNSUPPORTED),
     ((10, 256, (1 << 24) - 8, 128, A0, 1 << 34, 1 << 36), g.OK),
-    ((6, 256, (1 << 24) - 8, 128, A0, 1 << 34, 1 << 36), g.OK),
+    ((8, 256, (1 << 24) - 8, 128, A0, 1 << 34, 1 << 36), g.OK),
     ((0, 256, 1 << 24, 128, A0, 1 << 34, 1 << 36), g.OK),   # the library's choice takes another kernel
 ])
 def test_validation(args, want):
@@ -221,7 +221,7 @@ def test_tile_walk_covers_every_output_once(rung, M, N, cus):
     for r, c in zip(r0.tolist(), c0.tolist()):
         cover[r: r + tile, c: c + tile] += 1
     assert cover.min() >= 1
-    if rung in (6, 7, 8, 10):
+    if rung in (8, 10):
         assert np.all((r0 >= 0) & (r0 + tile <= M) & (c0 >= 0) & (c0 + tile <= N))   # whole tiles, in range
         # outputs computed twice: exactly the band where the moved-back last
         # tile row (column) overlaps its neighbour

@@ -25,8 +25,9 @@ released it, and read only after its load has landed and been published):
   * all waves cross the same number of barriers, and the committed include
     is what the generator writes.
 
-Both forms are checked: one barrier per step (generate) and release and
-publish barriers per step (generate2).
+Both generated forms are checked: the third (generate3, rung 8) and the
+fourth (generate4, rung 10, the library's choice), including the fourth
+form's partial first step and its ring carried across tiles.
 
 All four waves run the same instruction stream, so one stream stands for
 all of them; the checks treat every barrier as the point where all waves'
@@ -341,50 +342,6 @@ class Sim:
         return {"mfma": mfma, "epoch": epoch, "acc": acc_started, "loaded": loaded_steps}
 
 
-@pytest.mark.parametrize("kt", [2, 3, 4, 5, 6, 7, 8, 9, 16, 33])
-def test_schedule_ring_protocol(kt):
-    res = Sim(GEN.generate(GEN.DEFAULT), kt).run()
-    assert res["mfma"] == 2 * NB * NB * kt          # 128 MFMAs per 64-wide k step
-    assert res["epoch"] == kt                        # prologue barrier + one per handoff
-    assert len(res["acc"]) == NB * NB                # every block accumulated
-    assert sorted(res["loaded"]) == list(range(kt))
-    assert all(v == set(range(16)) for v in res["loaded"].values())
-
-
-@pytest.mark.parametrize("params", [
-    {"pre": 16}, {"pre": 48, "post_every": 1}, {"read_every": 1}, {"read_every": 3},
-    {"hand_slots": [], "body_slots": list(range(0, 64, 4))},
-    {"hand_slots": list(range(0, 32, 2)), "body_slots": []},
-])
-def test_schedule_variants_keep_protocol(params):
-    p = dict(GEN.DEFAULT)
-    p.update(params)
-    for kt in (2, 3, 4, 7):
-        Sim(GEN.generate(p), kt).run()
-
-
-@pytest.mark.parametrize("kt", [2, 3, 4, 5, 6, 7, 8, 9, 16, 33])
-def test_two_barrier_schedule_ring_protocol(kt):
-    res = Sim(GEN.generate2(GEN.DEFAULT2), kt).run()
-    assert res["mfma"] == 2 * NB * NB * kt
-    assert res["epoch"] == 1 + 2 * (kt - 1)          # prologue + release and publish per handoff
-    assert len(res["acc"]) == NB * NB
-    assert sorted(res["loaded"]) == list(range(kt))
-    assert all(v == set(range(16)) for v in res["loaded"].values())
-
-
-@pytest.mark.parametrize("params", [
-    {"rel": 20, "load_every": 6, "pre": 40}, {"rel": 32, "load_every": 8, "pre": 16},
-    {"rel": 24, "load_every": 10, "pre": 48}, {"rel": 16, "load_every": 4, "pre": 32},
-    {"rel": 24, "load_every": 11, "pre": 56},   # look-ahead loads interleave with the next step's own
-])
-def test_two_barrier_variants_keep_protocol(params):
-    p = dict(GEN.DEFAULT2)
-    p.update(params)
-    for kt in (2, 3, 4, 7):
-        Sim(GEN.generate2(p), kt).run()
-
-
 @pytest.mark.parametrize("kt", [2, 3, 4, 5, 6, 7, 8, 9, 16, 33, 64])
 def test_third_form_ring_protocol(kt):
     res = Sim(GEN.generate3(GEN.DEFAULT3), kt).run()
@@ -563,19 +520,22 @@ def test_head_mask_depends_on_row_group_parity_only():
 
 
 def test_simulator_catches_a_planted_race():
-    """Moving one handoff load ahead of its barrier must be caught."""
-    text = GEN.generate(GEN.DEFAULT).split("\n")
-    bar = text.index("s_barrier", text.index("s_barrier") + 1)   # step 0's handoff barrier
-    ld = next(i for i in range(bar, len(text)) if "%[kh] offen lds" in text[i])
-    planted = text[:bar - 1] + text[ld - 2: ld + 1] + text[bar - 1: ld - 2] + text[ld + 1:]
+    """Moving one look-ahead load ahead of the release barrier that frees
+    its stage must be caught (the third form)."""
+    text = GEN.generate3(GEN.DEFAULT3).split("\n")
+    loop = text.index("1:")
+    bar = text.index("s_barrier", loop)                          # a release barrier
+    ld = next(i for i in range(bar, len(text)) if "%[kh] offen" in text[i])
+    planted = text[:bar - 2] + [text[ld]] + text[bar - 2: ld] + text[ld + 1:]
     with pytest.raises(AssertionError):
-        Sim("\n".join(planted), 4).run()
+        Sim("\n".join(planted), 5).run()
 
 
 def test_simulator_catches_an_immediate_offset():
-    """A direct-to-LDS load with an instruction offset lands off its row
-    group in LDS (the offset applies to both addresses)."""
-    text = GEN.generate(GEN.DEFAULT).replace("%[kh] offen lds", "%[ko] offen offset:128 lds", 1)
+    """A direct-to-LDS load with an instruction offset that its lane offset
+    does not compensate lands off its row group in LDS (the offset applies
+    to both addresses)."""
+    text = GEN.generate3(GEN.DEFAULT3).replace("%[kh] offen lds", "%[kh] offen offset:128 lds", 1)
     with pytest.raises(AssertionError):
         Sim(text, 4).run()
 
@@ -583,19 +543,20 @@ def test_simulator_catches_an_immediate_offset():
 def test_simulator_catches_an_early_epilogue():
     """Queuing each row group as soon as its MFMAs are issued (no delay)
     reads accumulators before the MFMA latency has passed."""
-    p = dict(GEN.DEFAULT)
+    p = dict(GEN.DEFAULT3)
     p["epi_delay"] = -1
     with pytest.raises(AssertionError):
-        Sim(GEN.generate(p), 3).run()
+        Sim(GEN.generate3(p), 3).run()
 
 
 def test_simulator_catches_a_short_wait():
-    """Weakening an lgkmcnt wait before an MFMA must be caught."""
-    text = GEN.generate(GEN.DEFAULT).split("\n")
-    k = next(i for i, ln in enumerate(text) if ln.startswith("s_waitcnt lgkmcnt(") and "vmcnt" not in ln
-             and int(ln[len("s_waitcnt lgkmcnt("):-1]) < 14)
-    n = int(text[k][len("s_waitcnt lgkmcnt("):-1])
-    text[k] = f"s_waitcnt lgkmcnt({n + 1})"
+    """Weakening a fragment wait of the third form so that the reads an MFMA
+    needs may still be in flight must be caught."""
+    text = GEN.generate3(GEN.DEFAULT3).split("\n")
+    loop = text.index("1:")
+    k = next(i for i in range(loop, len(text)) if text[i] == "s_waitcnt lgkmcnt(0)"
+             and "s_barrier" not in text[i + 1: i + 3])
+    text[k] = "s_waitcnt lgkmcnt(15)"
     with pytest.raises(AssertionError):
         Sim("\n".join(text), 4).run()
 
@@ -603,7 +564,5 @@ def test_simulator_catches_a_short_wait():
 def test_committed_include_matches_generator():
     with open(os.path.join(CSRC, "ring4_sched.inc")) as f:
         inc = f.read()
-    assert GEN.as_macro("G16_RING4_KLOOP", GEN.generate(GEN.DEFAULT)) in inc
-    assert GEN.as_macro("G16_RING4_KLOOP2", GEN.generate2(GEN.DEFAULT2)) in inc
     assert GEN.as_macro("G16_RING4_KLOOP3", GEN.generate3(GEN.DEFAULT3)) in inc
     assert GEN.as_macro("G16_RING4_KLOOP4", GEN.generate4(GEN.DEFAULT4)) in inc
