@@ -31,8 +31,9 @@ R5_PERSISTENT_WS = 5
 R8_RING4_GAP = 8
 R9_RING_SMALL = 9
 R10_RING4_PAIRED = 10
+R11_WIDE = 11
 RUNGS = (R1_SINGLE_TILE, R2_KLOOP, R3_GRID, R4_RING, R5_PERSISTENT_WS, R8_RING4_GAP,
-         R9_RING_SMALL, R10_RING4_PAIRED)
+         R9_RING_SMALL, R10_RING4_PAIRED, R11_WIDE)
 
 _lock = threading.Lock()
 _lib = None

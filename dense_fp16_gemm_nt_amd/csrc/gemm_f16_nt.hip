@@ -14,6 +14,7 @@
 #include "persistent_ws.hpp"
 #include "ring.hpp"
 #include "ring4.hpp"
+#include "ring_wide.hpp"
 #include "sched.hpp"
 
 using namespace g16;
@@ -145,7 +146,17 @@ bool fast_operands(int64_t K, int64_t lda, int64_t ldb, int64_t sa, int64_t sb, 
 // Rung numbers the library implements (6 and 7 are no longer used).
 bool known_rung(int rung)
 {
-    return rung >= 0 && rung <= GEMM_F16_NT_R10_RING4_PAIRED && rung != 6 && rung != 7;
+    return rung >= 0 && rung <= GEMM_F16_NT_R11_WIDE && rung != 6 && rung != 7;
+}
+
+// Shapes of the 384 x 256 ring (rung 11): one tile row and column at least
+// (the last ones move back to end at M and N), whole 64-wide k steps, at
+// least two, and an output pitch under 2^23 (its output blocks span 384 *
+// ldd bytes in a 32-bit buffer size).
+bool wide_shape(int64_t M, int64_t N, int64_t K, int64_t ldd)
+{
+    return M >= wide::C::BM && N >= wide::C::BN && K % wide::C::BK == 0 && K >= 2 * wide::C::BK &&
+           ldd < (int64_t(1) << 23);
 }
 
 int validate(int rung, int64_t M, int64_t N, int64_t K, const void* A, const void* B, const void* D)
@@ -170,6 +181,7 @@ int validate(int rung, int64_t M, int64_t N, int64_t K, const void* A, const voi
         return GEMM_F16_NT_UNSUPPORTED;
     if (rung == GEMM_F16_NT_R10_RING4_PAIRED && !(ring4_paired_shape(M, N, K, K, K) && ring4_pitch_ok(N)))
         return GEMM_F16_NT_UNSUPPORTED;
+    if (rung == GEMM_F16_NT_R11_WIDE && !wide_shape(M, N, K, N)) return GEMM_F16_NT_UNSUPPORTED;
     if (!any_out) return GEMM_F16_NT_OK;
     // fp16 elements are 2-byte aligned; the fast kernels need 16 bytes
     if ((K > 0 && (((uintptr_t)A & 1) || ((uintptr_t)B & 1))) || ((uintptr_t)D & 1)) return GEMM_F16_NT_UNSUPPORTED;
@@ -273,6 +285,22 @@ int launch_ring4(const GemmArgs& g0, hipStream_t s, int form = 0)
     return launched();
 }
 
+// Rung 11: the four-wave ring on 384 x 256 tiles, persistent like rung 10.
+int launch_wide(const GemmArgs& g0, hipStream_t s)
+{
+    GemmArgs g = g0;
+    g.tiles_m = (g.M + wide::C::BM - 1) / wide::C::BM;
+    g.tiles_n = (g.N + wide::C::BN - 1) / wide::C::BN;
+    const int64_t tiles = g.tiles_m * g.tiles_n;
+    if (tiles > 0x7fffffff) return GEMM_F16_NT_UNSUPPORTED;
+    int cus = 0;
+    const int st = device_info(&cus);
+    if (st != GEMM_F16_NT_OK) return st;
+    const int64_t grid = tiles < cus ? tiles : cus;
+    hipLaunchKernelGGL(wide::wide_kernel, dim3((unsigned)grid), dim3(wide::C::THREADS), 0, s, g);
+    return launched();
+}
+
 // Rung 4's ring with 128 x 128 tiles (4 stages), one workgroup per tile.
 int launch_ring_small(const GemmArgs& g0, hipStream_t s)
 {
@@ -345,12 +373,40 @@ bool round_split(const GemmArgs& g, int cus, int64_t* m_top)
     return true;
 }
 
+// Whether rung 11's 384 x 256 tiles beat the four-wave ring's 256 x 256
+// ones on this shape, counted in rounds of tiles over the compute units.
+// Per FLOP the wider tile moves a sixth fewer operand bytes; measured on
+// MI355X at 12288 x 4096 x 4096, where both tile sizes fill whole rounds,
+// it runs 2.5% faster (1583 against 1545 TFLOP/s), so one 384-row tile
+// costs 1.5 / 1.025 of a 256-row one.  It pays where its tiles fill the
+// rounds better (6144 x 4096 x 4096: one round of 384-row tiles against
+// 1.5 of 256-row ones, 132 against 174 us) or equally well; where the
+// 256 x 256 tiles leave a small last round, the split of round_split is
+// kept, and so is the four-wave ring for short K (at most kCarryMaxSteps
+// steps), where it carries its ring from tile to tile and rung 11 does
+// not.
+constexpr double kWideTileCost = 1.5 / 1.025;
+
+bool wide_pays(const GemmArgs& g, int cus)
+{
+    if (g.batch != 1 || !wide_shape(g.M, g.N, g.K, g.ldd) || g.K / wide::C::BK <= ring4::kCarryMaxSteps)
+        return false;
+    int64_t m_top = 0;
+    if (round_split(g, cus, &m_top)) return false;
+    const int64_t tn = (g.N + kFastTile - 1) / kFastTile;
+    const int64_t t256 = (g.M + kFastTile - 1) / kFastTile * tn;
+    const int64_t t384 = (g.M + wide::C::BM - 1) / wide::C::BM * tn;
+    const double r256 = (double)((t256 + cus - 1) / cus), r384 = (double)((t384 + cus - 1) / cus);
+    return r384 * kWideTileCost < r256;
+}
+
 int launch_ring(const GemmArgs& g0, hipStream_t s, bool allow_ring4 = false)
 {
     if (allow_ring4 && tile_starved(g0)) return launch_ring_small(g0, s);
     if (allow_ring4 && ring4_fits(g0)) {
         int cus = 0, st = device_info(&cus);
         if (st != GEMM_F16_NT_OK) return st;
+        if (wide_pays(g0, cus)) return launch_wide(g0, s);
         int64_t m_top = 0;
         if (!round_split(g0, cus, &m_top)) return launch_ring4(g0, s);
         GemmArgs top = g0, rest = g0;
@@ -629,6 +685,8 @@ int run(int rung, int64_t M, int64_t N, int64_t K, const void* A, const void* B,
         return launch_ring_small(contiguous_args(M, N, K, A, B, D), s);
     case GEMM_F16_NT_R10_RING4_PAIRED:
         return launch_ring4(contiguous_args(M, N, K, A, B, D), s, 4);
+    case GEMM_F16_NT_R11_WIDE:
+        return launch_wide(contiguous_args(M, N, K, A, B, D), s);
     default:  // 0: the library's choice
         if (!fast_operands(K, K, K, 0, 0, A, B, D)) return launch_any(contiguous_args(M, N, K, A, B, D), s);
         return launch_ring(contiguous_args(M, N, K, A, B, D), s, kDefaultRing4);
@@ -860,14 +918,16 @@ int64_t gemm_f16_nt_tile_walk(int rung, int64_t M, int64_t N, int cus, int64_t* 
 {
     if (M < 0 || N < 0 || cus < 1 || capacity < 0) return GEMM_F16_NT_INVALID_ARG;
     if (capacity > 0 && (wg == nullptr || row0 == nullptr || col0 == nullptr)) return GEMM_F16_NT_INVALID_ARG;
-    const bool four_wave = rung == GEMM_F16_NT_R8_RING4_GAP || rung == GEMM_F16_NT_R10_RING4_PAIRED;
+    const bool wide_r = rung == GEMM_F16_NT_R11_WIDE;
+    const bool four_wave = rung == GEMM_F16_NT_R8_RING4_GAP || rung == GEMM_F16_NT_R10_RING4_PAIRED || wide_r;
     if (!four_wave && rung != GEMM_F16_NT_R4_RING && rung != GEMM_F16_NT_R5_PERSISTENT_WS &&
         rung != GEMM_F16_NT_R9_RING_SMALL)
         return GEMM_F16_NT_INVALID_ARG;
     if (M == 0 || N == 0) return 0;
-    if (four_wave && (M < ring4::C::BM || N < ring4::C::BN)) return GEMM_F16_NT_UNSUPPORTED;
     const int64_t tile = rung == GEMM_F16_NT_R9_RING_SMALL ? RingSmallCfg::BM : kFastTile;
-    const int64_t tm = (M + tile - 1) / tile, tn = (N + tile - 1) / tile, total = tm * tn;
+    const int64_t tile_m = wide_r ? wide::C::BM : tile;   // tile rows (M) and columns (N)
+    if (four_wave && (M < tile_m || N < tile)) return GEMM_F16_NT_UNSUPPORTED;
+    const int64_t tm = (M + tile_m - 1) / tile_m, tn = (N + tile - 1) / tile, total = tm * tn;
     if (total > 0x7fffffff) return GEMM_F16_NT_UNSUPPORTED;
     // the grids the launches use: one workgroup per tile (rungs 4 and 9),
     // one per compute unit or fewer (the persistent rungs)
@@ -881,9 +941,10 @@ int64_t gemm_f16_nt_tile_walk(int rung, int64_t M, int64_t N, int cus, int64_t* 
             int64_t r, c;
             if (four_wave) {
                 uint32_t mi, ni;
-                grouped_tile_in<uint32_t>((uint32_t)t, (uint32_t)tm, (uint32_t)tn, ring4::kRing4GroupM, &mi, &ni);
-                r = clamped_origin(mi, ring4::C::BM, M);
-                c = clamped_origin(ni, ring4::C::BN, N);
+                grouped_tile_in<uint32_t>((uint32_t)t, (uint32_t)tm, (uint32_t)tn,
+                                          wide_r ? wide::kGroupM : ring4::kRing4GroupM, &mi, &ni);
+                r = clamped_origin(mi, tile_m, M);
+                c = clamped_origin(ni, tile, N);
             } else {
                 const TileCoord tc = grouped_tile(t, tm, tn);
                 r = tc.m_idx * tile;
@@ -914,6 +975,8 @@ int gemm_f16_nt_plan(int64_t M, int64_t N, int64_t K, int cus, int* rung_top, in
     }
     if (tiles * 10 <= (int64_t)cus * kSmallTilesPer10Cus) {
         *rung_top = GEMM_F16_NT_R9_RING_SMALL;
+    } else if (ring4_fits(g) && wide_pays(g, cus)) {
+        *rung_top = GEMM_F16_NT_R11_WIDE;
     } else if (ring4_fits(g)) {
         *rung_top = GEMM_F16_NT_R10_RING4_PAIRED;
         if (round_split(g, cus, m_top))

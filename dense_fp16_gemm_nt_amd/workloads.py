@@ -107,6 +107,11 @@ EXTRA_WORKLOADS = [
     # ragged M): whole rounds unsplit, the remaining rows split K
     ExtraWorkload("splitk_rounds_6144x6144x6144", "splitk", 1, 6144, 6144, 6144, 18, U11),
     ExtraWorkload("splitk_rounds_6280x5888x4096", "splitk", 1, 6280, 5888, 4096, 19, U11),
+    # 384 x 256 tiles (each staged B band feeds two waves of 192 A rows):
+    # one round of them against 1.5 rounds of 256 x 256 tiles, and a shape
+    # both tile sizes fill in whole rounds
+    ExtraWorkload("wide_6144x4096x4096", "gemm", 1, 6144, 4096, 4096, 22, U11),
+    ExtraWorkload("wide_12288x4096x4096", "gemm", 1, 12288, 4096, 4096, 23, U11),
     # a batch of mid-size products, one launch
     ExtraWorkload("batched_16x1024x1024x4096", "strided", 16, 1024, 1024, 4096, 14, U11),
     # attention scores S = Q K^T, 32 heads of 4096 x 4096, head dimension 128 and 64

@@ -85,6 +85,12 @@ extern "C" {
                                            partial k step goes first; rows of A and B then shorter than
                                            2^21 elements); the library's choice for those shapes */
 
+#define GEMM_F16_NT_R11_WIDE 11 /* rung 10's four-wave ring on 384 x 256 tiles (each staged B band feeds
+                                   two waves of 192 A rows: a sixth fewer operand bytes per FLOP), one
+                                   barrier per k step: M >= 384, N >= 256, K a multiple of 64, K >= 128,
+                                   N < 2^23 (the last tile row or column ends at M or N and overlaps its
+                                   neighbour) */
+
 /* D = A * B^T with the library's choice of kernel for the shape (see
  * gemm_f16_nt_plan; when the 256 x 256 tiles leave a small last round,
  * the rows past the whole rounds run as a second launch on 128 x 128
@@ -193,9 +199,10 @@ int64_t gemm_f16_nt_schedule(int64_t M, int64_t N, int64_t num_workgroups, int64
  * V3 "Spatial Tiling with Multiple CTAs" for the tile origins, V6 "Better
  * L2 Locality" for the grouped order).  rung: 4 and 9 (one workgroup per
  * 256 x 256 or 128 x 128 tile, grouped order with groups of 8 tile rows),
- * 5 (persistent, one workgroup per compute unit, the same order) or 8
- * and 10 (the four-wave ring: persistent, groups of 4 tile rows, the last
- * tile row and column moved back to end at M and N; M, N >= 256, else
+ * 5 (persistent, one workgroup per compute unit, the same order) or 8,
+ * 10 and 11 (the four-wave ring: persistent, groups of 4 tile rows, the
+ * last tile row and column moved back to end at M and N; tiles of 256 x
+ * 256, 384 x 256 for rung 11; M, N at least one tile, else
  * GEMM_F16_NT_UNSUPPORTED).  Writes one entry per tile visit in
  * workgroup-major visit order: workgroup wg[i] computes the output block
  * whose first row is row0[i] and first column col0[i].  Returns the number

@@ -76,7 +76,15 @@ A0, B0, D0 = 0x10000, 0x20000000, 0x40000000   # fake, 16-byte aligned, disjoint
     ((0, 64, 10_000_000, 12, A0, B0, D0), g.OK),           # the staged ring's grid is one-dimensional
     ((0, 64, 64, 64, A0, B0, A0 + 4096), g.INVALID_ARG),   # D overlaps A
     ((0, 64, 64, 64, A0, B0, B0), g.INVALID_ARG),          # D overlaps B
-    ((11, 64, 64, 64, A0, B0, D0), g.INVALID_ARG),         # unknown rung
+    ((12, 64, 64, 64, A0, B0, D0), g.INVALID_ARG),         # unknown rung
+    ((11, 384, 256, 128, A0, B0, D0), g.OK),                # rung 11: 384 x 256 tiles
+    ((11, 383, 256, 128, A0, B0, D0), g.UNSUPPORTED),       # ... at least one tile row
+    ((11, 384, 255, 128, A0, B0, D0), g.UNSUPPORTED),       # ... and column
+    ((11, 384, 256, 136, A0, B0, D0), g.UNSUPPORTED),       # ... whole 64-wide k steps
+    ((11, 384, 256, 64, A0, B0, D0), g.UNSUPPORTED),        # ... at least two
+    ((11, 400, 300, 192, A0, B0, D0), g.OK),                # ragged M, N
+    ((11, 384, 1 << 23, 128, A0, 1 << 34, 1 << 36), g.UNSUPPORTED),   # output blocks span 384 * N bytes
+    ((11, 384, (1 << 23) - 8, 128, A0, 1 << 34, 1 << 36), g.OK),
     ((10, 64, 64, 64, A0, B0, D0), g.UNSUPPORTED),         # rung 10: M, N >= 256
     ((10, 512, 256, 192, A0, B0, D0), g.OK),
     ((10, 256, 260, 128, A0, B0, D0), g.OK),              # rung 10 takes any N >= 256
@@ -205,7 +213,7 @@ def test_schedule_xcd_locality():
     (10, 4096, 4096, 256), (10, 8192, 8192, 256), (10, 32768, 1024, 256), (10, 4000, 4000, 256),
     (10, 300, 264, 256), (10, 256, 256, 256), (10, 6144, 6144, 256), (10, 1000, 3000, 37), (8, 4608, 4608, 304),
     (5, 4096, 4096, 256), (5, 1000, 3000, 37), (4, 4096, 4096, 256), (4, 1000, 3000, 256), (9, 4096, 4096, 256),
-    (9, 200, 32768, 256),
+    (9, 200, 32768, 256), (11, 6144, 4096, 256), (11, 8192, 8192, 256), (11, 400, 300, 256), (11, 4000, 1000, 37),
 ])
 def test_tile_walk_covers_every_output_once(rung, M, N, cus):
     """Every rung's tile walk covers every output element: exactly once
@@ -215,27 +223,28 @@ def test_tile_walk_covers_every_output_once(rung, M, N, cus):
     Every workgroup of a persistent walk gets its share to within one tile."""
     wg, r0, c0 = g.tile_walk(rung, M, N, cus)
     tile = 128 if rung == 9 else 256
-    tm, tn = -(-M // tile), -(-N // tile)
+    tile_m = 384 if rung == 11 else tile
+    tm, tn = -(-M // tile_m), -(-N // tile)
     assert len(wg) == tm * tn
     cover = np.zeros((M, N), np.int16)
     for r, c in zip(r0.tolist(), c0.tolist()):
-        cover[r: r + tile, c: c + tile] += 1
+        cover[r: r + tile_m, c: c + tile] += 1
     assert cover.min() >= 1
-    if rung in (8, 10):
-        assert np.all((r0 >= 0) & (r0 + tile <= M) & (c0 >= 0) & (c0 + tile <= N))   # whole tiles, in range
+    if rung in (8, 10, 11):
+        assert np.all((r0 >= 0) & (r0 + tile_m <= M) & (c0 >= 0) & (c0 + tile <= N))   # whole tiles, in range
         # outputs computed twice: exactly the band where the moved-back last
         # tile row (column) overlaps its neighbour
         band_r = np.zeros(M, bool)
         band_c = np.zeros(N, bool)
-        if M % tile:
-            band_r[M - tile: (M // tile) * tile] = True
+        if M % tile_m:
+            band_r[M - tile_m: (M // tile_m) * tile_m] = True
         if N % tile:
             band_c[N - tile: (N // tile) * tile] = True
         twice = band_r[:, None] | band_c[None, :]
         assert np.array_equal(cover > 1, twice)
         assert cover.max() <= 4
     else:
-        assert np.all(r0 % tile == 0) and np.all(c0 % tile == 0)
+        assert np.all(r0 % tile_m == 0) and np.all(c0 % tile == 0)
         assert cover.max() == 1
     counts = np.bincount(wg)
     assert counts.max() - counts.min() <= 1
@@ -336,6 +345,11 @@ def test_splitk_workspace_sizes():
     ((100, 100, 5), (3, 100, 0)),             # K < 8 off 16-byte rows: R3's general form
     ((100, 100, 100), (9, 100, 0)),           # K % 8 != 0: R9's register-staged form
     ((4096, 4096, 4095), (4, 4096, 0)),       # ... R4's when 256 x 256 tiles fill the device
+    ((6144, 4096, 4096), (11, 6144, 0)),      # one round of 384 x 256 tiles against 1.5 of 256 x 256
+    ((12288, 4096, 4096), (11, 12288, 0)),    # both fill whole rounds: the wider tile's fewer bytes per FLOP
+    ((12288, 2048, 2048), (11, 12288, 0)),
+    ((6144, 4096, 4000), (10, 6144, 0)),      # K not whole 64-wide steps: the four-wave ring
+    ((6144, 4096, 1024), (10, 6144, 0)),      # short K: the four-wave ring carries its ring across tiles
 ])
 def test_library_plan(shape, want):
     assert g.plan(*shape, 256) == want

@@ -493,12 +493,96 @@ def test_full_size_workloads(name):
     np.testing.assert_array_equal(ref_s, ref[rows, cols])
     assert torch.isfinite(D).all().item()
     if name == "square_4096":
-        for rung in (4, 5, 8, 9, 10):
+        for rung in (4, 5, 8, 9, 10, 11):
             say(f"[gpu] full size square_4096 on rung {rung} (every output)")
             Dr = poisoned(w.M, w.N)
             run(rung, dA, dB, Dr)
             assert_parity(host_bits(Dr), ref, w.K, f"{name} rung {rung}")
             del Dr
+
+
+# ------------------------------------------- rung 11: 384 x 256 tiles
+
+WIDE = 11
+WIDE_SHAPES = [(384, 256, 128), (768, 512, 192), (400, 300, 256), (1000, 1032, 512), (1536, 2048, 1024),
+               (3456, 2560, 2048)]
+
+
+@pytest.mark.parametrize("shape", WIDE_SHAPES, ids=lambda s: "x".join(map(str, s)))
+def test_wide_parity(shape):
+    """Rung 11 (each staged B band feeds two waves of 192 A rows) against the
+    oracle on every output: whole and ragged tiles (the last tile row and
+    column move back and overlap), one and several tiles per workgroup,
+    into a NaN-poisoned D."""
+    M, N, K = shape
+    A, B = rand_case(M, N, K, 1100 + M + N + K)
+    ref, _ = oracle.gemm_nt(A, B)
+    say(f"[gpu] rung 11 M={M} N={N} K={K}")
+    D = poisoned(M, N)
+    run(WIDE, dev(A), dev(B), D)
+    assert_parity(host_bits(D), ref, K, f"rung 11 {M}x{N}x{K}")
+    # repeatable bit for bit
+    D2 = poisoned(M, N)
+    run(WIDE, dev(A), dev(B), D2)
+    assert torch.equal(D.view(torch.int16), D2.view(torch.int16))
+
+
+def test_wide_exact_pins():
+    """All-ones (D = K exactly), small integers (every fp32 partial sum
+    exact, so the result is bitwise the oracle's) and designed rows
+    (round-to-nearest-even ties, overflow to inf, subnormals) on rung 11."""
+    M, N = 768, 512
+    for K in (128, 4096):
+        say(f"[gpu] rung 11 all-ones K={K}")
+        D = run(WIDE, dev(np.ones((M, K), np.float16)), dev(np.ones((N, K), np.float16)))
+        assert torch.all(D == float(K)).item()
+    rng = np.random.default_rng(11)
+    K = 2048
+    A = rng.integers(-4, 5, (M, K)).astype(np.float16)
+    B = rng.integers(-4, 5, (N, K)).astype(np.float16)
+    ref, _ = oracle.gemm_nt(A, B)
+    say("[gpu] rung 11 small integers")
+    assert np.array_equal(host_bits(run(WIDE, dev(A), dev(B))), ref)
+    K = 128
+    A = np.zeros((M, K), np.float16)
+    B = np.zeros((N, K), np.float16)
+    A[5, :2] = [1, 1]
+    B[7, :2] = [2048, 1]
+    B[8, :2] = [2048, 3]
+    B[9, :2] = [65504, 16]
+    A[400, 0] = 2.0 ** -12
+    B[300, 0] = 2.0 ** -12
+    B[301, 0] = 2.0 ** -13
+    ref, _ = oracle.gemm_nt(A, B)
+    say("[gpu] rung 11 designed rows")
+    got = host_bits(run(WIDE, dev(A), dev(B)))
+    assert np.array_equal(got, ref)
+    d = as_f64(got)
+    assert d[5, 7] == 2048 and d[5, 8] == 2052 and np.isinf(d[5, 9]) and d[400, 300] == 2.0 ** -24 and d[400, 301] == 0
+
+
+def test_library_picks_wide_tiles():
+    """Where 384 x 256 tiles fill the rounds of compute units better
+    (6144 x 4096 x 4096: one round against 1.5), the library runs rung 11:
+    bitwise equal to that rung, and every output against the oracle."""
+    M, N, K = 6144, 4096, 4096
+    A, B = rand_case(M, N, K, 1201)
+    dA, dB = dev(A), dev(B)
+    say(f"[gpu] library choice M={M} N={N} K={K} (rung 11)")
+    D = poisoned(M, N)
+    run(0, dA, dB, D)
+    Dr = poisoned(M, N)
+    run(WIDE, dA, dB, Dr)
+    assert torch.equal(D.view(torch.int16), Dr.view(torch.int16))
+    ref, _ = oracle.gemm_nt(A, B)
+    assert_parity(host_bits(D), ref, K, "library 6144x4096x4096")
+
+
+def test_wide_rejects_shapes_it_does_not_take():
+    A, B = dev(np.ones((256, 128), np.float16)), dev(np.ones((256, 128), np.float16))
+    with pytest.raises(g.GemmError) as e:
+        g.gemm_f16_nt_rung(WIDE, A, B)           # M < 384
+    assert e.value.status == g.UNSUPPORTED
 
 
 # ------------------------------------------- general operands (any K, alignment)
