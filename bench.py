@@ -19,7 +19,7 @@ the timed region starts).  Prints one JSON line:
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
                        [--workload NAME] [--rung R] [--no-cpu-baseline]
-       python bench.py --suite [--only NAME,...] [--seconds S]
+       python bench.py --suite [--only NAME,...] [--seconds S] [--rung R]
                                       (one JSON line per product beyond the
                                        five fixed workloads: ragged and
                                        unaligned shapes, batches, attention
@@ -195,7 +195,12 @@ def suite(args):
             lda, sa, ldb, sb = w.K, w.M * w.K, w.K, w.N * w.K
         D = torch.empty((w.batch, w.M, w.N), dtype=torch.float16, device=dev)
         a, b, d = A.data_ptr(), B.data_ptr(), D.data_ptr()
-        if w.kind == "gemm":
+        if w.kind == "gemm" and args.rung:
+            def step():
+                return L.gemm_f16_nt_rung(args.rung, w.M, w.N, w.K, a, b, d, s_ptr)
+        elif args.rung:
+            raise SystemExit(f"{name}: --rung applies to the single products (kind gemm), not to {w.kind}")
+        elif w.kind == "gemm":
             def step():
                 return L.gemm_f16_nt(w.M, w.N, w.K, a, b, d, s_ptr)
         elif w.kind == "splitk":
@@ -220,7 +225,7 @@ def suite(args):
         e1.record(stream)
         torch.cuda.synchronize()
         est = e0.elapsed_time(e1) / 10 * 1e-3
-        steps = int(min(5000, max(20, args.seconds / max(est, 1e-6))))
+        steps = int(min(1_000_000, max(20, args.seconds / max(est, 1e-6))))
         for _ in range(steps // 4):
             bad |= step()
         torch.cuda.synchronize()
@@ -273,6 +278,7 @@ def suite(args):
                      "slices": sl}
         print(json.dumps({
             "suite": "extra", "workload": w.name, "kind": w.kind, "batch": w.batch, "M": w.M, "N": w.N, "K": w.K,
+            "kernel": RUNG_NAMES[args.rung],
             "value": round(tflops, 2), "unit": "TFLOP/s", "us_per_launch": round(launch_s * 1e6, 3),
             "steps": steps, "compulsory_bytes": w.min_bytes, "compulsory_gbs": round(gbs, 1),
             "flop_per_byte": round(w.flop / w.min_bytes, 2), "roofline": roof, "dtype": "f16",

@@ -99,10 +99,35 @@ def per_kernel(d: str, substr: str):
     return out
 
 
+def split_products(d: str, substr: str, products: list):
+    """{(kernel name, product): durations} for a run that timed several
+    products one after another with the same kernel: each kernel's
+    dispatches, in time order, are cut at its len(products) - 1 longest
+    gaps (the host work between two products) and the runs are named in
+    order."""
+    rows = list(csv.DictReader(open(_find(d, "*kernel_trace.csv"))))
+    rows = sorted((r for r in rows if substr in r["Kernel_Name"]), key=lambda r: int(r["Start_Timestamp"]))
+    out = {}
+    for name in sorted({r["Kernel_Name"] for r in rows}):
+        rs = [r for r in rows if r["Kernel_Name"] == name]
+        gaps = sorted(range(1, len(rs)), key=lambda i: int(rs[i - 1]["End_Timestamp"]) - int(rs[i]["Start_Timestamp"]))
+        cuts = sorted(gaps[:len(products) - 1]) if len(rs) >= len(products) else []
+        bounds = [0] + cuts + [len(rs)]
+        for k, prod in enumerate(products[:len(bounds) - 1]):
+            out[(name, prod)] = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+                                 for r in rs[bounds[k]:bounds[k + 1]]]
+    return out
+
+
 def cmd_stats(a):
     """One block of figures per kernel name (never one mean over different
-    kernels)."""
-    groups = per_kernel(a.dir, a.kernel)
+    kernels), and per product when --products names the products a run
+    timed in turn."""
+    if a.products:
+        groups = {f"{name}\nproduct: {prod}": durs
+                  for (name, prod), durs in split_products(a.dir, a.kernel, a.products.split(",")).items()}
+    else:
+        groups = per_kernel(a.dir, a.kernel)
     if not groups:
         raise SystemExit(f"no dispatch of a kernel matching {a.kernel!r} in {a.dir}")
     lines = [f"# rocprofv3 kernel trace summary: kernels matching {a.kernel!r}",
@@ -119,7 +144,8 @@ def cmd_stats(a):
     stats_csv = glob.glob(os.path.join(a.dir, "**", "*kernel_stats.csv"), recursive=True)
     if stats_csv:
         lines.append("")
-        lines.append("## rocprofv3 --stats (kernel_stats.csv rows)")
+        lines.append("## rocprofv3 --stats (kernel_stats.csv rows" +
+                     (", rocprofv3's own per-kernel totals over every product above)" if a.products else ")"))
         for r in csv.DictReader(open(stats_csv[0])):
             lines.append(", ".join(f"{k}={v}" for k, v in r.items()))
     open(a.out, "w").write("\n".join(lines) + "\n")
@@ -213,6 +239,13 @@ def cmd_counters(a):
         "mfma_flop_counted": c["SQ_INSTS_VALU_MFMA_MOPS_F16"] * 512,
         "mfma_cycles_per_instruction": c["SQ_VALU_MFMA_BUSY_CYCLES"] / max(c["SQ_INSTS_VALU_MFMA_MOPS_F16"] * 512 / 16384, 1.0),
         "lds_bank_conflict_pct": 100.0 * c["SQ_LDS_BANK_CONFLICT"] / max(c["SQ_LDS_IDX_ACTIVE"], 1.0),
+        # matrix-core cycles per SIMD over the traced kernel duration: the
+        # shader clock at which the MFMAs alone would fill the kernel.  The
+        # kernel's own busy fraction is this over the clock it ran at (the
+        # counter is exactly 16 cycles per 16x16x32 MFMA, so the clock is the
+        # only measured quantity in it)
+        "mfma_cycles_per_simd": c["SQ_VALU_MFMA_BUSY_CYCLES"] / simds,
+        "mfma_floor_clock_ghz": c["SQ_VALU_MFMA_BUSY_CYCLES"] / simds / (mean_s * 1e9),
         "kernel_mean_us_trace": mean_s * 1e6,
         "hbm_bytes_per_launch": traffic["hbm_bytes_per_launch"],
         "hbm_gbs": traffic["hbm_bytes_per_launch"] / mean_s / 1e9,
@@ -238,8 +271,13 @@ def _smi_sample():
 def cmd_power(a):
     """Run the bench (a child process: this one never touches the GPU) and
     sample the board's socket power and per-XCD clocks while it runs."""
-    cmd = [sys.executable, os.path.join(ROOT, "bench.py"), "--steps", str(a.steps), "--warmup", "100",
-           "--no-cpu-baseline", "--workload", a.workload]
+    if a.product:
+        # one extra product, timed by the suite for about `seconds`
+        cmd = [sys.executable, os.path.join(ROOT, "bench.py"), "--suite", "--only", a.product, "--rung", str(a.rung),
+               "--seconds", str(a.seconds)]
+    else:
+        cmd = [sys.executable, os.path.join(ROOT, "bench.py"), "--steps", str(a.steps), "--warmup", "100",
+               "--no-cpu-baseline", "--workload", a.workload, "--rung", str(a.rung)]
     child = subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.PIPE, text=True)
     samples = []
     t0 = time.time()
@@ -257,9 +295,10 @@ def cmd_power(a):
     top = max(p for _, p, _ in samples)
     busy = [x for x in samples if x[1] >= 0.75 * top]
     clocks = [statistics.mean(c[i] for _, _, c in busy) for i in range(len(busy[0][2]))] if busy else []
+    ms = bench["ms_per_step"] if "ms_per_step" in bench else bench["us_per_launch"] / 1e3
     rec = {
-        "workload": a.workload, "bench_value_tflops": bench["value"], "bench_ms_per_step": bench["ms_per_step"],
-        "bench_steps": a.steps,
+        "workload": a.product or a.workload, "rung": a.rung, "bench_value_tflops": bench["value"],
+        "bench_ms_per_step": ms, "bench_steps": bench["steps"],
         "samples_under_load": len(busy), "samples_total": len(samples),
         "socket_power_w_mean": round(statistics.mean(p for _, p, _ in busy), 1),
         "socket_power_w_min": min(p for _, p, _ in busy), "socket_power_w_max": max(p for _, p, _ in busy),
@@ -284,6 +323,7 @@ def main(argv=None):
     s.add_argument("--kernel", required=True)
     s.add_argument("--command", required=True)
     s.add_argument("--out", required=True)
+    s.add_argument("--products", default="", help="comma-separated names of the products the run timed in turn")
     t = sub.add_parser("traffic")
     for k in ("fetch", "write", "copy_fetch", "copy_write"):
         t.add_argument("--" + k.replace("_", "-"), dest=k, required=True)
@@ -308,6 +348,9 @@ def main(argv=None):
     w = sub.add_parser("power")
     w.add_argument("--steps", type=int, default=100000)
     w.add_argument("--workload", default="square_4096")
+    w.add_argument("--rung", type=int, default=0, help="0 = the library's choice")
+    w.add_argument("--product", default="", help="an extra product of bench.py --suite instead of a workload")
+    w.add_argument("--seconds", type=float, default=12.0, help="suite seconds for --product")
     w.add_argument("--samples", type=int, default=16)
     w.add_argument("--interval", type=float, default=0.4)
     w.add_argument("--command", required=True)
