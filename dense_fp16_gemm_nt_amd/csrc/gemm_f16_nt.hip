@@ -373,31 +373,51 @@ bool round_split(const GemmArgs& g, int cus, int64_t* m_top)
     return true;
 }
 
-// Whether rung 11's 384 x 256 tiles beat the four-wave ring's 256 x 256
-// ones on this shape, counted in rounds of tiles over the compute units.
-// Per FLOP the wider tile moves a sixth fewer operand bytes; measured on
-// MI355X at 12288 x 4096 x 4096, where both tile sizes fill whole rounds,
-// it runs 2.5% faster (1583 against 1545 TFLOP/s), so one 384-row tile
-// costs 1.5 / 1.025 of a 256-row one.  It pays where its tiles fill the
-// rounds better (6144 x 4096 x 4096: one round of 384-row tiles against
-// 1.5 of 256-row ones, 132 against 174 us) or equally well; where the
-// 256 x 256 tiles leave a small last round, the split of round_split is
-// kept, and so is the four-wave ring for short K (at most kCarryMaxSteps
-// steps), where it carries its ring from tile to tile and rung 11 does
-// not.
+// Rows of the product that run on rung 11's 384 x 256 tiles: 0 (none), M
+// (all of it), or the top rows, with the rest on the four-wave ring's 256 x
+// 256 tiles as a second launch.  The choice counts rounds of tiles over the
+// compute units.  Per FLOP the wider tile moves a sixth fewer operand bytes;
+// measured on MI355X at 12288 x 4096 x 4096, where both tile sizes fill
+// whole rounds, it runs 2.5% faster, so one 384-row tile costs 1.5 / 1.025
+// of a 256-row one.  It pays where its tiles fill the rounds better (6144 x
+// 4096 x 4096: one round against 1.5, 128 against 174 us) or equally well,
+// and as the top rows of products whose 256-row tiles fill whole rounds but
+// whose 384-row tiles do not (8192^3: two rounds of 384-row tiles over the
+// top 6144 rows plus one round of 256-row tiles, 707 against 722 us; the
+// output is bitwise that of the four-wave ring alone, both accumulating
+// each block's k steps in the same order).  A second launch is counted as
+// kWideSplitCost of a round.  Where the 256 x 256 tiles leave a small last
+// round, the split of round_split is kept, and so is the four-wave ring for
+// short K (at most kCarryMaxSteps steps), where it carries its ring from
+// tile to tile and rung 11 does not.
 constexpr double kWideTileCost = 1.5 / 1.025;
+constexpr double kWideSplitCost = 0.02;
 
-bool wide_pays(const GemmArgs& g, int cus)
+int64_t wide_rows(const GemmArgs& g, int cus)
 {
-    if (g.batch != 1 || !wide_shape(g.M, g.N, g.K, g.ldd) || g.K / wide::C::BK <= ring4::kCarryMaxSteps)
-        return false;
+    if (g.batch != 1 || !wide_shape(g.M, g.N, g.K, g.ldd) || g.K / wide::C::BK <= ring4::kCarryMaxSteps) return 0;
     int64_t m_top = 0;
-    if (round_split(g, cus, &m_top)) return false;
+    if (round_split(g, cus, &m_top)) return 0;
     const int64_t tn = (g.N + kFastTile - 1) / kFastTile;
-    const int64_t t256 = (g.M + kFastTile - 1) / kFastTile * tn;
-    const int64_t t384 = (g.M + wide::C::BM - 1) / wide::C::BM * tn;
-    const double r256 = (double)((t256 + cus - 1) / cus), r384 = (double)((t384 + cus - 1) / cus);
-    return r384 * kWideTileCost < r256;
+    const auto rounds = [&](int64_t rows, int64_t tile) {
+        return (double)(((rows + tile - 1) / tile * tn + cus - 1) / cus);
+    };
+    double best = rounds(g.M, kFastTile);   // the four-wave ring alone
+    int64_t best_rows = 0;
+    if (rounds(g.M, wide::C::BM) * kWideTileCost < best) {
+        best = rounds(g.M, wide::C::BM) * kWideTileCost;
+        best_rows = g.M;
+    }
+    // top rows in whole 384-row tiles; the rest (at least one 256-row tile
+    // row, as the four-wave ring needs) on 256 x 256 tiles
+    for (int64_t m = wide::C::BM; m + kFastTile <= g.M; m += wide::C::BM) {
+        const double c = rounds(m, wide::C::BM) * kWideTileCost + rounds(g.M - m, kFastTile) + kWideSplitCost;
+        if (c < best) {
+            best = c;
+            best_rows = m;
+        }
+    }
+    return best_rows;
 }
 
 int launch_ring(const GemmArgs& g0, hipStream_t s, bool allow_ring4 = false)
@@ -406,7 +426,17 @@ int launch_ring(const GemmArgs& g0, hipStream_t s, bool allow_ring4 = false)
     if (allow_ring4 && ring4_fits(g0)) {
         int cus = 0, st = device_info(&cus);
         if (st != GEMM_F16_NT_OK) return st;
-        if (wide_pays(g0, cus)) return launch_wide(g0, s);
+        const int64_t m_wide = wide_rows(g0, cus);
+        if (m_wide == g0.M) return launch_wide(g0, s);
+        if (m_wide > 0) {
+            GemmArgs top = g0, rest = g0;
+            top.M = m_wide;
+            rest.M = g0.M - m_wide;
+            rest.A = g0.A + m_wide * g0.lda;
+            rest.D = g0.D + m_wide * g0.ldd;
+            st = launch_wide(top, s);
+            return st != GEMM_F16_NT_OK ? st : launch_ring4(rest, s);
+        }
         int64_t m_top = 0;
         if (!round_split(g0, cus, &m_top)) return launch_ring4(g0, s);
         GemmArgs top = g0, rest = g0;
@@ -975,8 +1005,10 @@ int gemm_f16_nt_plan(int64_t M, int64_t N, int64_t K, int cus, int* rung_top, in
     }
     if (tiles * 10 <= (int64_t)cus * kSmallTilesPer10Cus) {
         *rung_top = GEMM_F16_NT_R9_RING_SMALL;
-    } else if (ring4_fits(g) && wide_pays(g, cus)) {
+    } else if (ring4_fits(g) && wide_rows(g, cus) > 0) {
         *rung_top = GEMM_F16_NT_R11_WIDE;
+        *m_top = wide_rows(g, cus);
+        if (*m_top < M) *rung_rest = GEMM_F16_NT_R10_RING4_PAIRED;
     } else if (ring4_fits(g)) {
         *rung_top = GEMM_F16_NT_R10_RING4_PAIRED;
         if (round_split(g, cus, m_top))

@@ -35,7 +35,10 @@ Schedule of one k step (192 MFMAs; gap g follows MFMA g):
     them (the block the last row finishes last is read by the next step at
     its own start) and its first A row into the free ring slot; the loads
     of step j+2 go into the released stage, one every `load_every` gaps,
-    the later ones carried into the first gaps of the next step.
+    the later ones carried into the next step.  Loads closer together
+    than ~6 gaps queue at the XCD's L2 (every 2, 3, 4 gaps: 6.6%, 3.6%,
+    1% slower than every 6 on 12288 x 4096 x 4096); further apart than ~8
+    the last ones land after the barrier's wait (every 9: 3.8% slower).
 """
 from __future__ import annotations
 
@@ -425,7 +428,7 @@ def generate(p: dict) -> str:
 
 DEFAULT = {
     "a_delay": 1,          # gaps between a position's first MFMA and the reads of the next row's A
-    "load_every": 4,       # step j+2's loads, one every this many gaps from the barrier
+    "load_every": 6,       # step j+2's loads, one every this many gaps from the barrier
     "epi_slot": 8,         # epilogue instructions per MFMA gap of the last step
     "epi_delay": 5,        # MFMAs between a row's last MFMA and its epilogue (VGPR results: >= 19 wait states)
 }

@@ -330,7 +330,7 @@ def test_splitk_workspace_sizes():
     ((7168, 7168, 4096), (10, 6912, 9)),
     ((5120, 5120, 4096), (10, 5120, 0)),      # more than a third of a round left
     ((4096, 4096, 4096), (10, 4096, 0)),      # whole rounds
-    ((8192, 8192, 8192), (10, 8192, 0)),
+    ((8192, 8192, 8192), (11, 6144, 10)),     # 2 rounds of 384-row tiles on the top rows + 1 of 256-row ones, against 4
     ((32768, 1024, 8192), (10, 32768, 0)),
     ((256, 256, 512), (9, 256, 0)),           # tile-starved
     ((2560, 2560, 4096), (9, 2560, 0)),
@@ -348,11 +348,39 @@ def test_splitk_workspace_sizes():
     ((6144, 4096, 4096), (11, 6144, 0)),      # one round of 384 x 256 tiles against 1.5 of 256 x 256
     ((12288, 4096, 4096), (11, 12288, 0)),    # both fill whole rounds: the wider tile's fewer bytes per FLOP
     ((12288, 2048, 2048), (11, 12288, 0)),
+    ((16384, 4096, 1088), (11, 12288, 10)),   # the top rows that fill whole rounds of 384-row tiles
+    ((12288, 12288, 4096), (11, 12288, 0)),
+    ((8192, 4096, 4096), (10, 8192, 0)),      # 2 rounds of 256-row tiles: no split beats it
     ((6144, 4096, 4000), (10, 6144, 0)),      # K not whole 64-wide steps: the four-wave ring
     ((6144, 4096, 1024), (10, 6144, 0)),      # short K: the four-wave ring carries its ring across tiles
 ])
 def test_library_plan(shape, want):
     assert g.plan(*shape, 256) == want
+
+
+@pytest.mark.parametrize("M,N,K", [(8192, 8192, 8192), (16384, 4096, 1088), (20480, 4096, 4096), (16384, 16384, 4096),
+                                   (10240, 8192, 4096), (12288, 4096, 4096), (6144, 4096, 4096)])
+@pytest.mark.parametrize("cus", [80, 256, 304])
+def test_wide_top_rows_plan_invariants(M, N, K, cus):
+    """When rung 11 takes only the top rows, they are whole 384-row tile
+    rows and the rest is at least one 256-row tile row on rung 10; the plan
+    never costs more rounds of tiles than rung 10 alone (a 384-row tile
+    counted as 1.5/1.025 of a 256-row one, a second launch as 0.02 of a
+    round)."""
+    rung_top, m_top, rung_rest = g.plan(M, N, K, cus)
+    tn = (N + 255) // 256
+
+    def rounds(rows, tile):
+        return -(-(-(-rows // tile) * tn) // cus)
+
+    base = rounds(M, 256)
+    if rung_top != 11:
+        return
+    if m_top == M:
+        assert rung_rest == 0 and rounds(M, 384) * 1.5 / 1.025 < base
+    else:
+        assert rung_rest == 10 and m_top % 384 == 0 and M - m_top >= 256
+        assert rounds(m_top, 384) * 1.5 / 1.025 + rounds(M - m_top, 256) + 0.02 < base
 
 
 @pytest.mark.parametrize("shape,cus,want", [

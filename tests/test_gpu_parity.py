@@ -578,6 +578,34 @@ def test_library_picks_wide_tiles():
     assert_parity(host_bits(D), ref, K, "library 6144x4096x4096")
 
 
+@pytest.mark.parametrize("shape", [(16384, 4096, 1088), (8192, 8192, 1088)], ids=lambda s: "x".join(map(str, s)))
+def test_library_wide_top_rows(shape):
+    """Where 256 x 256 tiles fill whole rounds but 384 x 256 tiles do not,
+    the library runs rung 11 on the top rows that fill whole rounds of
+    384-row tiles and rung 10 on the rest (16384 x 4096: two rounds of
+    384-row tiles and one of 256-row tiles against four).  Each part is
+    bitwise equal to its rung on the whole product, so the whole equals
+    rung 10's output bitwise (both accumulate each block's k steps in the
+    same order); sampled outputs, the boundary rows among them, match the
+    oracle."""
+    M, N, K = shape
+    rung_top, m_top, rung_rest = g.plan(M, N, K, torch.cuda.get_device_properties(0).multi_processor_count)
+    assert (rung_top, rung_rest) == (WIDE, 10) and 0 < m_top < M and m_top % 384 == 0, (rung_top, m_top, rung_rest)
+    A, B = rand_case(M, N, K, 1300 + M)
+    dA, dB = dev(A), dev(B)
+    say(f"[gpu] wide top rows {M}x{N}x{K}: rows [0, {m_top}) on rung 11, the rest on rung 10")
+    got = host_bits(run(0, dA, dB, poisoned(M, N)))
+    top = host_bits(run(WIDE, dA, dB, poisoned(M, N)))
+    whole = host_bits(run(10, dA, dB, poisoned(M, N)))
+    assert np.array_equal(got[:m_top], top[:m_top])
+    assert np.array_equal(got, whole)
+    rows, cols = sample_positions(M, N, 1500, M + 1)
+    rows = np.concatenate([rows, np.full(64, m_top - 1), np.full(64, m_top), np.full(64, M - 1)])
+    cols = np.concatenate([cols, np.random.default_rng(7).integers(0, N, 192)])
+    want, _ = oracle.gemm_nt_sampled(A, B, rows, cols)
+    assert_parity(got[rows, cols], want, K, f"wide top rows {shape}")
+
+
 def test_wide_rejects_shapes_it_does_not_take():
     A, B = dev(np.ones((256, 128), np.float16)), dev(np.ones((256, 128), np.float16))
     with pytest.raises(g.GemmError) as e:

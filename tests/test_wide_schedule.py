@@ -299,7 +299,7 @@ def test_wide_ring_protocol(kt):
     assert all(v == set(GEN.LOADS) for v in res["loaded"].values())
 
 
-@pytest.mark.parametrize("params", [{"load_every": 3}, {"load_every": 5}, {"load_every": 6}, {"epi_slot": 4}])
+@pytest.mark.parametrize("params", [{"load_every": 3}, {"load_every": 4}, {"load_every": 8}, {"epi_slot": 4}])
 def test_wide_variants_keep_protocol(params):
     p = dict(GEN.DEFAULT)
     p.update(params)
