@@ -396,6 +396,8 @@ def test_library_small_last_round(shape):
     ("plain", 256, 256, 512),        # 128x128 tiles only
     ("plain", 300, 264, 0),          # K = 0: the fill kernel
     ("splitk", 256, 256, 8192),      # split K: partial sums, then the reduction
+    ("plain", 6144, 4096, 1088),     # 384 x 256 tiles on every row
+    ("plain", 16384, 4096, 1088),    # two launches: 384 x 256 tiles on the top rows, then 256 x 256
 ], ids=lambda c: "{}_{}x{}x{}".format(*c))
 def test_graph_capture_replays(case):
     """Every launch the library makes can be captured into a HIP graph (no
