@@ -193,9 +193,16 @@ def cmd_timeline(a):
     print("\n".join(lines[-7:]))
 
 
+def counter_per_launch(d: str, counter: str, kernels: str) -> float:
+    """A counter per library call whose launches are the kernels named by
+    the comma-separated substrings (one dispatch of each per call): the
+    sum of each kernel's mean per dispatch."""
+    return sum(counter_per_dispatch(d, counter, k) for k in kernels.split(","))
+
+
 def cmd_traffic(a):
-    fetch_k = counter_per_dispatch(a.fetch, "FETCH_SIZE", a.kernel)
-    write_k = counter_per_dispatch(a.write, "WRITE_SIZE", a.kernel)
+    fetch_k = counter_per_launch(a.fetch, "FETCH_SIZE", a.kernel)
+    write_k = counter_per_launch(a.write, "WRITE_SIZE", a.kernel)
     copy_fetch_k = counter_per_dispatch(a.copy_fetch, "FETCH_SIZE", a.copy_kernel)
     copy_write_k = counter_per_dispatch(a.copy_write, "WRITE_SIZE", a.copy_kernel)
     f_scale = a.copy_bytes / (copy_fetch_k * 1024.0)
@@ -220,9 +227,9 @@ SIMDS_PER_CU = 4
 
 
 def cmd_counters(a):
-    c = {name: counter_per_dispatch(a.dir, name, a.kernel) for name in COUNTERS}
-    _, durs = kernel_stats(a.trace, a.kernel)
-    mean_s = statistics.mean(durs) * 1e-6
+    c = {name: counter_per_launch(a.dir, name, a.kernel) for name in COUNTERS}
+    # one library call: the sum of its kernels' mean durations
+    mean_s = sum(statistics.mean(kernel_stats(a.trace, k)[1]) for k in a.kernel.split(",")) * 1e-6
     gui = c["GRBM_GUI_ACTIVE"] / XCDS                 # shader-clock cycles of the dispatch
     simds = a.cus * SIMDS_PER_CU
     traffic = json.load(open(a.traffic))
@@ -329,7 +336,7 @@ def main(argv=None):
         t.add_argument("--" + k.replace("_", "-"), dest=k, required=True)
     t.add_argument("--copy-bytes", type=float, required=True)
     t.add_argument("--copy-kernel", default="copy")
-    t.add_argument("--kernel", required=True)
+    t.add_argument("--kernel", required=True, help="comma-separated name substrings: the kernels one call launches")
     t.add_argument("--workload", required=True)
     t.add_argument("--rung", required=True)
     t.add_argument("--command", required=True)
@@ -340,7 +347,7 @@ def main(argv=None):
     c.add_argument("--traffic", required=True)
     c.add_argument("--flop", type=float, required=True)
     c.add_argument("--cus", type=int, required=True)
-    c.add_argument("--kernel", required=True)
+    c.add_argument("--kernel", required=True, help="comma-separated name substrings: the kernels one call launches")
     c.add_argument("--workload", required=True)
     c.add_argument("--rung", required=True)
     c.add_argument("--command", required=True)

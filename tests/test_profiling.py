@@ -10,3 +10,35 @@ def test_code_only_drops_comments_and_blank_lines():
 def test_source_hash_is_stable_and_short():
     h = profiling.kernel_source_hash()
     assert h == profiling.kernel_source_hash() and len(h) == 16 and int(h, 16) >= 0
+
+
+def _write_trace(d, rows):
+    d.mkdir(parents=True, exist_ok=True)
+    with open(d / "run_kernel_trace.csv", "w") as f:
+        f.write("Kernel_Name,Start_Timestamp,End_Timestamp\n")
+        for name, st, en in rows:
+            f.write(f'"{name}",{st},{en}\n')
+
+
+def test_split_products_cuts_at_the_longest_gaps(tmp_path):
+    """Two products timed in turn with the same kernel: the dispatches are
+    cut at the long host gap between them, not at the short launch gaps."""
+    rows = [("k<1>", 1000 * i, 1000 * i + 900) for i in range(5)]                       # 0.9 us each
+    rows += [("k<1>", 10_000_000 + 2000 * i, 10_000_000 + 2000 * i + 1800) for i in range(3)]  # 1.8 us each
+    rows += [("other", 50, 60)]
+    _write_trace(tmp_path / "t", rows)
+    out = profiling.split_products(str(tmp_path / "t"), "k<", ["small", "large"])
+    assert [round(x, 3) for x in out[("k<1>", "small")]] == [0.9] * 5
+    assert [round(x, 3) for x in out[("k<1>", "large")]] == [1.8] * 3
+
+
+def test_counter_per_launch_sums_the_kernels_of_one_call(tmp_path):
+    d = tmp_path / "c"
+    d.mkdir()
+    with open(d / "run_counter_collection.csv", "w") as f:
+        f.write("Dispatch_Id,Kernel_Name,Counter_Name,Counter_Value\n")
+        for i in range(4):   # each call: one "wide" and one "ring4" dispatch; values summed over XCDs
+            f.write(f'{2 * i},"wide_kernel",FETCH_SIZE,30\n{2 * i},"wide_kernel",FETCH_SIZE,70\n')
+            f.write(f'{2 * i + 1},"ring4_kernel",FETCH_SIZE,40\n')
+    assert profiling.counter_per_dispatch(str(d), "FETCH_SIZE", "wide") == 100
+    assert profiling.counter_per_launch(str(d), "FETCH_SIZE", "wide,ring4") == 140
