@@ -46,7 +46,11 @@ constexpr int kRingPre = 2, kRingLsplit = 1;
 // two tie at ~100 tiles of 256 x 256 on 256 CUs (2560^3), 128 x 128 is
 // 1.6-2.2x faster at 16-64 tiles and 256 x 256 is 1.4x faster at 144.
 constexpr int64_t kSmallTilesPer10Cus = 4;
-using WsCfg = ws::Cfg<32, 4, 2>;
+// Rung 5's ring: two stages of 64-wide k steps (measured on MI355X against
+// four stages of 32-wide steps: 188.6 against 215.0 us at 4096^3, 1221.5
+// against 1391.6 us at 8192^3, bitwise equal outputs; half as many handoffs
+// per FLOP, each consumer wait covering twice the MFMAs).
+using WsCfg = ws::Cfg<64, 2, 2>;
 constexpr int kFastTile = 256;
 // the library's choice takes the four-wave scheduled ring where it applies
 constexpr bool kDefaultRing4 = true;
