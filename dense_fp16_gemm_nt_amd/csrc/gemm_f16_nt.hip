@@ -8,6 +8,7 @@
 #include <atomic>
 #include <cstring>
 #include <mutex>
+#include <numeric>
 
 #include "common.hpp"
 #include "ladder.hpp"
@@ -412,9 +413,11 @@ int64_t wide_rows(const GemmArgs& g, int cus)
         best = rounds(g.M, wide::C::BM) * kWideTileCost;
         best_rows = g.M;
     }
-    // top rows in whole 384-row tiles; the rest (at least one 256-row tile
-    // row, as the four-wave ring needs) on 256 x 256 tiles
-    for (int64_t m = wide::C::BM; m + kFastTile <= g.M; m += wide::C::BM) {
+    // top rows in 384-row tile rows that fill whole rounds of the compute
+    // units; the rest (at least one 256-row tile row, as the four-wave ring
+    // needs) on 256 x 256 tiles
+    const int64_t step_rows = cus / std::gcd(tn, (int64_t)cus);   // tile rows per whole round
+    for (int64_t m = step_rows * wide::C::BM; m + kFastTile <= g.M; m += step_rows * wide::C::BM) {
         const double c = rounds(m, wide::C::BM) * kWideTileCost + rounds(g.M - m, kFastTile) + kWideSplitCost;
         if (c < best) {
             best = c;
