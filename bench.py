@@ -290,8 +290,8 @@ def suite(args):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py: this build runs on exactly one GPU (got --gpus {args.gpus}); "
-              "the GEMM is not sharded across GPUs here.", file=sys.stderr)
+        print(f"bench.py: the library runs on exactly one GPU (got --gpus {args.gpus}); "
+              "it does not shard a GEMM across GPUs.", file=sys.stderr)
         sys.exit(2)
     if args.copy_calib:
         copy_calib()

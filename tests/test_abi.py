@@ -190,7 +190,7 @@ def test_schedule_is_a_bijection(M, N, grid):
 
 def test_schedule_matches_printed_persistent_arithmetic():
     M, N, tile, tiles, grid, mean_x10 = _golden("persistent_grid_4096.txt")[0]
-    # same tile count with this build's 256 x 256 tiles at twice the size
+    # same tile count with the library's 256 x 256 tiles at twice the size
     scale = 256 // tile
     wg, _, _ = g.schedule(M * scale, N * scale, grid)
     assert len(wg) == tiles
