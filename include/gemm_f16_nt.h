@@ -86,15 +86,19 @@ extern "C" {
                                            2^21 elements); the library's choice for those shapes */
 
 #define GEMM_F16_NT_R11_WIDE 11 /* rung 10's four-wave ring on 384 x 256 tiles (each staged B band feeds
-                                   two waves of 192 A rows: a sixth fewer operand bytes per FLOP), one
-                                   barrier per k step: M >= 384, N >= 256, K a multiple of 64, K >= 128,
-                                   N < 2^23 (the last tile row or column ends at M or N and overlaps its
-                                   neighbour) */
+                                   two waves of 192 A rows: a sixth fewer operand bytes per FLOP; "GEMM
+                                   III", Step 9, and "TIRx GEMM detailed technical notes", V9 "Why Share
+                                   B?"), one barrier per k step: M >= 384, N >= 256, K a multiple of 64,
+                                   K >= 128, N < 2^23 (the last tile row or column ends at M or N and
+                                   overlaps its neighbour); the library's choice, on every row or on the
+                                   top rows, where its rounds of tiles cost less than rung 10's */
 
 /* D = A * B^T with the library's choice of kernel for the shape (see
- * gemm_f16_nt_plan; when the 256 x 256 tiles leave a small last round,
- * the rows past the whole rounds run as a second launch on 128 x 128
- * tiles). */
+ * gemm_f16_nt_plan).  Some shapes take two launches on the stream: when
+ * the 256 x 256 tiles leave a small last round, the rows past the whole
+ * rounds run on 128 x 128 tiles; when whole rounds of 384 x 256 tiles fit
+ * over the top rows but not over all of them, the top rows run on rung 11
+ * and the rest on rung 10. */
 int gemm_f16_nt(int64_t M, int64_t N, int64_t K, const void* A, const void* B, void* D, void* stream);
 
 /* The same product on one named rung of the ladder (for tests and the
