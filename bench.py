@@ -26,6 +26,9 @@ Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
                                        scores; each against its own roofline)
        python bench.py --copy-calib   (a plain device copy of known size, for
                                        scaling the HBM byte counters)
+       python bench.py --library-gemm [--workload NAME] [--steps K]
+                                      (context: the platform's GEMM on the
+                                       same inputs; one JSON line)
 """
 from __future__ import annotations
 
@@ -80,6 +83,9 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="target oracle time for the CPU sample")
     p.add_argument("--copy-calib", action="store_true", help="run only a plain device copy (counter scaling)")
+    p.add_argument("--library-gemm", action="store_true",
+                   help="context only: time torch.matmul (hipBLASLt) on the workload (a fixed workload or a "
+                        "single extra product) instead of this library")
     p.add_argument("--launch", choices=("graph", "host"), default="host",
                    help="time the K steps as K host launches (default) or as one captured HIP graph")
     p.add_argument("--suite", action="store_true", help="time the extra products (general shapes, attention scores)")
@@ -99,6 +105,51 @@ def copy_calib():
         dst.copy_(src)
     torch.cuda.synchronize()
     print(json.dumps({"copy_calib_bytes_read": n, "copy_calib_bytes_written": n, "launches": 5}), flush=True)
+
+
+def library_gemm(args):
+    """Context only: the platform's GEMM (torch.matmul -> hipBLASLt) on the
+    same workload, inputs and launch pattern (warm-up launches, then the
+    timed launches bracketed by events on the launch stream).  Its output is
+    compared with this library's, which is not timed here."""
+    import numpy as np
+    import torch
+
+    import dense_fp16_gemm_nt_amd as g
+    from dense_fp16_gemm_nt_amd import inputs, workloads
+
+    w = workloads.BY_NAME.get(args.workload) or workloads.EXTRA_BY_NAME[args.workload]
+    if getattr(w, "kind", "gemm") != "gemm":
+        raise SystemExit(f"{w.name}: --library-gemm takes a single product")
+    M, N, K, seed, dist = w.M, w.N, w.K, w.seed, w.dist
+    dev = torch.device("cuda:0")
+    A_np, B_np = inputs.operands(M, N, K, seed, dist)
+    A, B = torch.from_numpy(A_np).to(dev), torch.from_numpy(B_np).to(dev)
+    stream = torch.cuda.current_stream(dev)
+    Bt = B.t()
+    out = torch.empty((M, N), dtype=torch.float16, device=dev)
+    for _ in range(args.warmup):
+        torch.matmul(A, Bt, out=out)
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(args.steps):
+        torch.matmul(A, Bt, out=out)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    mine = g.gemm_f16_nt(A, B)
+    torch.cuda.synchronize()
+    diff = (mine.float() - out.float()).abs()
+    flop = 2.0 * M * N * K
+    print(json.dumps({
+        "context": "torch.matmul (hipBLASLt), not this library", "workload": args.workload, "M": M, "N": N, "K": K,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
+        "value": round(flop / (ms * 1e-3) / 1e12, 2), "unit": "TFLOP/s",
+        "outputs_bitwise_equal_to_this_library": bool(torch.equal(mine.view(torch.int16), out.view(torch.int16))),
+        "max_abs_diff": float(diff.max().item()), "outputs_differing": int((diff > 0).sum().item()),
+    }), flush=True)
 
 
 def cpu_baseline(A, B, D_gpu_bits, w, target_s):
@@ -298,6 +349,9 @@ def main():
         return
     if args.suite:
         suite(args)
+        return
+    if args.library_gemm:
+        library_gemm(args)
         return
 
     import numpy as np
