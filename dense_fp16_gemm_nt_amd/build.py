@@ -1,4 +1,5 @@
-"""Build the HIP library (gfx950) in-tree: dense_fp16_gemm_nt_amd/libgemm_f16_nt.so."""
+"""Build the HIP library (gfx950) in-tree: dense_fp16_gemm_nt_amd/libgemm_f16_nt.so, and the
+matrix-core calibration kernel the profiling tools use (libmfma_calib.so)."""
 from __future__ import annotations
 
 import os
@@ -27,14 +28,24 @@ def hipcc() -> str:
     return "hipcc"
 
 
-def build(verbose: bool = False) -> str:
-    """Compile the library (always recompiles) and return its path."""
-    tmp = LIB + ".tmp"
-    cmd = [hipcc(), *HIPCC_FLAGS, "-o", tmp, SRC]
+CALIB_SRC = os.path.join(PKG, "csrc", "mfma_calib.hip")
+CALIB_LIB = os.path.join(PKG, "libmfma_calib.so")
+
+
+def _compile(src: str, lib: str, verbose: bool) -> None:
+    tmp = lib + ".tmp"
+    cmd = [hipcc(), *HIPCC_FLAGS, "-o", tmp, src]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
+
+
+def build(verbose: bool = False) -> str:
+    """Compile the library and the matrix-core calibration kernel of the
+    profiling tools (always recompiles); return the library's path."""
+    _compile(SRC, LIB, verbose)
+    _compile(CALIB_SRC, CALIB_LIB, verbose)
     return LIB
 
 

@@ -23,6 +23,15 @@
       SQ_LDS_BANK_CONFLICT, SQ_LDS_IDX_ACTIVE, SQ_BUSY_CU_CYCLES,
       GRBM_GUI_ACTIVE), the kernel's mean duration from a kernel trace
       and its HBM bytes from a traffic record
+  python -m dense_fp16_gemm_nt_amd.profiling calib-run --out STAMPS.npy [--iters N] [--launches L]
+      (on the GPU, under rocprofv3 --pmc SQ_VALU_MFMA_BUSY_CYCLES
+      --kernel-trace) L launches of the MFMA-only calibration kernel
+      (csrc/mfma_calib.hip) on every SIMD, saving each wave's shader-cycle
+      and reference-clock counts
+  python -m dense_fp16_gemm_nt_amd.profiling calib --dir D --stamps STAMPS.npy --command CMD --out FILE
+      the busy fraction the GEMM summaries use (matrix-core cycles per SIMD
+      over shader clock x traced duration) evaluated on that kernel, whose
+      true busy fraction is ~1
 """
 from __future__ import annotations
 
@@ -322,6 +331,89 @@ def cmd_power(a):
     print(json.dumps(rec, indent=1))
 
 
+SIMDS = 1024            # 256 compute units x 4 SIMDs
+CALIB_WAVES_PER_BLOCK = 4
+CALIB_CYCLES_PER_TRIP = 128 * 16   # 128 v_mfma_f32_16x16x32_f16 of 16 cycles
+
+
+def calib_source_hash() -> str:
+    with open(os.path.join(ROOT, "dense_fp16_gemm_nt_amd", "csrc", "mfma_calib.hip")) as f:
+        return hashlib.sha256(_code_only(f.read()).encode()).hexdigest()[:16]
+
+
+def calib_lib():
+    import ctypes
+
+    path = os.path.join(ROOT, "dense_fp16_gemm_nt_amd", "libmfma_calib.so")
+    if not os.path.exists(path):
+        raise SystemExit(f"{path} is not built: python -c 'import __graft_entry__ as g; g.build()'")
+    L = ctypes.CDLL(path)
+    L.mfma_calib_launch.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p]
+    return L
+
+
+def cmd_calib_run(a):
+    """Launch the calibration kernel on one workgroup of 4 waves per compute
+    unit and save the per-wave stamps (launch, wave, [cycles, ticks, sum])."""
+    import numpy as np
+    import torch
+
+    L = calib_lib()
+    dev = torch.device("cuda:0")
+    blocks = torch.cuda.get_device_properties(dev).multi_processor_count
+    waves = blocks * CALIB_WAVES_PER_BLOCK
+    # random fp16 operands in [-1, 1): the matrix cores' power depends on the data
+    rnd = (torch.rand(waves * 8192, device=dev) * 2 - 1).half()
+    out = torch.zeros(a.launches * waves * 3, dtype=torch.int64, device=dev)
+    s = torch.cuda.current_stream(dev).cuda_stream
+    for i in range(a.launches):
+        st = L.mfma_calib_launch(blocks, rnd.data_ptr(), out.data_ptr() + i * waves * 3 * 8, a.iters, s)
+        if st != 0:
+            raise SystemExit(f"mfma_calib_launch returned {st}")
+    torch.cuda.synchronize()
+    np.save(a.out, out.cpu().numpy().reshape(a.launches, waves, 3))
+    print(f"[calib] {a.launches} launches of {blocks} x {CALIB_WAVES_PER_BLOCK} waves, {a.iters} trips", flush=True)
+
+
+def cmd_calib(a):
+    import numpy as np
+
+    stamps = np.load(a.stamps).astype(np.float64)            # (launches, waves, 3)
+    rows = list(csv.DictReader(open(_find(a.dir, "*counter_collection.csv"))))
+    per = {}
+    for r in rows:
+        if "mfma_calib" in r["Kernel_Name"] and r["Counter_Name"] == "SQ_VALU_MFMA_BUSY_CYCLES":
+            per.setdefault(int(r["Dispatch_Id"]), 0.0)
+            per[int(r["Dispatch_Id"])] += float(r["Counter_Value"])
+    trace = sorted((r for r in csv.DictReader(open(_find(a.dir, "*kernel_trace.csv")))
+                    if "mfma_calib" in r["Kernel_Name"]), key=lambda r: int(r["Start_Timestamp"]))
+    busy_cycles = [per[k] for k in sorted(per)]
+    durs = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-9 for r in trace]
+    n = min(len(busy_cycles), len(durs), stamps.shape[0])
+    if n == 0:
+        raise SystemExit(f"no calibration dispatch with counters in {a.dir}")
+    lines = ["# Matrix-core busy calibration: the MFMA-only kernel (csrc/mfma_calib.hip) on every SIMD",
+             f"command: {a.command}", f"calib_src_sha: {calib_source_hash()}", "",
+             "launch  duration_us  clock_ghz (waves' min-max)  busy_cycles_per_simd  busy_pct  loop_cycles_per_ideal"]
+    fr = []
+    for i in range(n):
+        cyc, ticks = stamps[i, :, 0], stamps[i, :, 1]
+        clock = float(np.median(cyc / (ticks * 10.0)))          # GHz: 100 MHz reference ticks
+        per_simd = busy_cycles[i] / SIMDS
+        busy = per_simd / (clock * 1e9 * durs[i])
+        trips = per_simd / CALIB_CYCLES_PER_TRIP
+        ideal = float(np.median(cyc)) / (trips * CALIB_CYCLES_PER_TRIP)
+        fr.append(busy)
+        ck = cyc / (ticks * 10.0)
+        lines.append(f"{i:6d}  {durs[i] * 1e6:11.1f}  {clock:9.3f} ({ck.min():.3f}-{ck.max():.3f})"
+                     f"  {per_simd:20.0f}  {100 * busy:8.2f}  {ideal:21.4f}")
+    lines += ["", f"busy_pct_mean: {100 * statistics.mean(fr):.2f}",
+              "(busy_pct = matrix-core cycles per SIMD / (the clock the waves measured x the traced duration);"
+              " loop_cycles_per_ideal = the waves' own loop cycles over the MFMA cycles they issued)"]
+    open(a.out, "w").write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 def main(argv=None):
     p = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     sub = p.add_subparsers(dest="cmd", required=True)
@@ -369,9 +461,18 @@ def main(argv=None):
     tl.add_argument("--timed", type=int, required=True)
     tl.add_argument("--command", required=True)
     tl.add_argument("--out", required=True)
+    cr = sub.add_parser("calib-run")
+    cr.add_argument("--out", required=True)
+    cr.add_argument("--iters", type=int, default=1000)
+    cr.add_argument("--launches", type=int, default=12)
+    cb = sub.add_parser("calib")
+    cb.add_argument("--dir", required=True)
+    cb.add_argument("--stamps", required=True)
+    cb.add_argument("--command", required=True)
+    cb.add_argument("--out", required=True)
     a = p.parse_args(argv)
     {"stats": cmd_stats, "traffic": cmd_traffic, "counters": cmd_counters, "power": cmd_power,
-     "timeline": cmd_timeline}[a.cmd](a)
+     "timeline": cmd_timeline, "calib-run": cmd_calib_run, "calib": cmd_calib}[a.cmd](a)
 
 
 if __name__ == "__main__":

@@ -42,3 +42,33 @@ def test_counter_per_launch_sums_the_kernels_of_one_call(tmp_path):
             f.write(f'{2 * i + 1},"ring4_kernel",FETCH_SIZE,40\n')
     assert profiling.counter_per_dispatch(str(d), "FETCH_SIZE", "wide") == 100
     assert profiling.counter_per_launch(str(d), "FETCH_SIZE", "wide,ring4") == 140
+
+
+def test_calibration_summary_reads_full_busy_for_a_saturated_kernel(tmp_path):
+    """Synthetic counters for a kernel whose matrix cores are busy for the
+    whole traced duration at the clock its waves measured: the summary
+    reports 100% and the loop at its ideal cycle count."""
+    import numpy as np
+
+    d = tmp_path / "pmc"
+    d.mkdir()
+    clock, dur_ns, waves = 2.0, 1_000_000, 1024     # 2 GHz, 1 ms: 2e6 cycles per SIMD
+    cycles = 2_000_000
+    with open(d / "run_counter_collection.csv", "w") as f:
+        f.write("Dispatch_Id,Kernel_Name,Counter_Name,Counter_Value\n")
+        for i in range(2):
+            for x in range(8):   # one value per XCD, summed per dispatch
+                f.write(f'{i},"mfma_calib_kernel",SQ_VALU_MFMA_BUSY_CYCLES,{cycles * profiling.SIMDS / 8}\n')
+    with open(d / "run_kernel_trace.csv", "w") as f:
+        f.write("Kernel_Name,Start_Timestamp,End_Timestamp\n")
+        for i in range(2):
+            f.write(f'"mfma_calib_kernel",{10 * i * dur_ns},{10 * i * dur_ns + dur_ns}\n')
+    stamps = np.zeros((2, waves, 3))
+    stamps[:, :, 0] = cycles                       # shader cycles of the loop
+    stamps[:, :, 1] = dur_ns / 10.0                # 100 MHz ticks
+    np.save(tmp_path / "s.npy", stamps)
+    out = tmp_path / "calib.txt"
+    profiling.main(["calib", "--dir", str(d), "--stamps", str(tmp_path / "s.npy"), "--command", "x", "--out", str(out)])
+    text = out.read_text()
+    assert "busy_pct_mean: 100.00" in text
+    assert " 1.0000" in text
