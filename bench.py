@@ -13,7 +13,11 @@ the timed region starts).  Prints one JSON line:
               region on the launch stream, divided by the number of
               back-to-back launches), traffic = HBM bytes per launch from the
               committed rocprofv3 counter summary when it matches the
-              current kernel sources, else null
+              current kernel sources, else null; counters = the committed
+              matrix-core, LDS and HBM figures under the same condition
+              (mfma_busy_pct: the kernel's own busy fraction, its MFMA
+              cycles over the traced duration at the shader clock of a long
+              run of the same box)
   cpu_baseline  the CPU oracle timed on the host cores on a bounded sample
               (a block of full output rows), scaled to TFLOP/s
 
@@ -207,8 +211,24 @@ def counter_record(workload: str, rung_name: str):
         rec = json.load(f)
     if rec.get("kernel_src_sha") != kernel_source_hash() or rec.get("rung") != rung_name:
         return None
-    keys = ("mfma_busy_pct", "mfma_flop_counted", "lds_bank_conflict_pct", "hbm_gbs")
-    return {k: round(rec[k], 3) for k in keys}
+    out = {"mfma_flop_counted": rec["mfma_flop_counted"], "lds_bank_conflict_pct": round(rec["lds_bank_conflict_pct"], 3),
+           "hbm_gbs": round(rec["hbm_gbs"], 1),
+           # the clock at which the counted MFMA cycles alone fill the traced
+           # kernel time; over the shader clock of a long run of the same
+           # box (profiles/power_clock_*), the kernel's own busy fraction
+           "mfma_floor_clock_ghz": round(rec["mfma_floor_clock_ghz"], 4),
+           # busy cycles over the graphics engine's active window, which is
+           # longer than the kernel: a lower bound
+           "mfma_busy_pct_lower_bound": round(rec["mfma_busy_pct"], 2)}
+    ppath = os.path.join(ROOT, "profiles", f"power_clock_{rung_name}_{workload}.txt")
+    if os.path.exists(ppath):
+        with open(ppath) as f:
+            pw = json.load(f)
+        if pw.get("kernel_src_sha") == kernel_source_hash() and pw.get("clock_mhz_mean_all_xcds"):
+            clk = pw["clock_mhz_mean_all_xcds"] / 1e3
+            out["long_run_clock_ghz"] = round(clk, 4)
+            out["mfma_busy_pct"] = round(100.0 * rec["mfma_floor_clock_ghz"] / clk, 2)
+    return out
 
 
 def suite(args):
