@@ -50,8 +50,13 @@ constexpr int64_t kSmallTilesPer10Cus = 4;
 // Rung 5's ring: two stages of 64-wide k steps (measured on MI355X against
 // four stages of 32-wide steps: 188.6 against 215.0 us at 4096^3, 1221.5
 // against 1391.6 us at 8192^3, bitwise equal outputs; half as many handoffs
-// per FLOP, each consumer wait covering twice the MFMAs).
-using WsCfg = ws::Cfg<64, 2, 2>;
+// per FLOP, each consumer wait covering twice the MFMAs), 8 consumer and 4
+// producer waves, consumers reading the next sub-step's fragments while
+// the current one's MFMAs run (1% faster at 4096^3 and 8192^3).  4 consumer
+// and 4 producer waves on 256 x 128 tiles (256 registers each, 3 stages)
+// were 15-18% slower: the smaller tile moves 1.5x the operand bytes per
+// FLOP and one consumer per SIMD leaves its MFMA pipe idle during waits.
+using WsCfg = ws::Cfg<64, 2, 2, 2, 4, 4, true>;
 constexpr int kFastTile = 256;
 // the library's choice takes the four-wave scheduled ring where it applies
 constexpr bool kDefaultRing4 = true;
@@ -673,8 +678,8 @@ GemmArgs contiguous_args(int64_t M, int64_t N, int64_t K, const void* A, const v
 int launch_ws(int64_t M, int64_t N, int64_t K, const f16* A, const f16* B, f16* D, int64_t grid,
               hipStream_t s)
 {
-    const int64_t tm = (M + kFastTile - 1) / kFastTile, tn = (N + kFastTile - 1) / kFastTile;
-    const bool edge = (M % kFastTile) || (N % kFastTile) || (K % WsCfg::BK) || (N % 4);
+    const int64_t tm = (M + WsCfg::BM - 1) / WsCfg::BM, tn = (N + WsCfg::BN - 1) / WsCfg::BN;
+    const bool edge = (M % WsCfg::BM) || (N % WsCfg::BN) || (K % WsCfg::BK) || (N % 4);
     if (grid > tm * tn) grid = tm * tn;
     if (edge)
         hipLaunchKernelGGL((ws::ws_kernel<WsCfg, true>), dim3((unsigned)grid), dim3(WsCfg::THREADS), 0, s, A, B, D,
@@ -961,8 +966,10 @@ int64_t gemm_f16_nt_tile_walk(int rung, int64_t M, int64_t N, int cus, int64_t* 
         rung != GEMM_F16_NT_R9_RING_SMALL)
         return GEMM_F16_NT_INVALID_ARG;
     if (M == 0 || N == 0) return 0;
-    const int64_t tile = rung == GEMM_F16_NT_R9_RING_SMALL ? RingSmallCfg::BM : kFastTile;
-    const int64_t tile_m = wide_r ? wide::C::BM : tile;   // tile rows (M) and columns (N)
+    const bool ws_r = rung == GEMM_F16_NT_R5_PERSISTENT_WS;
+    const int64_t tile = rung == GEMM_F16_NT_R9_RING_SMALL ? RingSmallCfg::BM : ws_r ? WsCfg::BN : kFastTile;
+    // tile rows (M) and columns (N)
+    const int64_t tile_m = wide_r ? wide::C::BM : ws_r ? WsCfg::BM : tile;
     if (four_wave && (M < tile_m || N < tile)) return GEMM_F16_NT_UNSUPPORTED;
     const int64_t tm = (M + tile_m - 1) / tile_m, tn = (N + tile - 1) / tile, total = tm * tn;
     if (total > 0x7fffffff) return GEMM_F16_NT_UNSUPPORTED;
@@ -984,7 +991,7 @@ int64_t gemm_f16_nt_tile_walk(int rung, int64_t M, int64_t N, int cus, int64_t* 
                 c = clamped_origin(ni, tile, N);
             } else {
                 const TileCoord tc = grouped_tile(t, tm, tn);
-                r = tc.m_idx * tile;
+                r = tc.m_idx * tile_m;
                 c = tc.n_idx * tile;
             }
             if (n < capacity) {

@@ -7,11 +7,13 @@
 // and Tile Scheduler" and V7 "Warp Specialization and Pipelining").
 //
 // gfx950 form:
-//  * 12 waves: waves 0-7 are consumers (two per SIMD), waves 8-11 are
-//    producers (one per SIMD).  A gfx950 wave's register allocation is fixed
-//    for the whole kernel (no per-role reallocation), so every wave gets
-//    512/3 registers; a consumer holds a 128 x 64 fp32 accumulator (128
-//    registers), the producers hold only addresses.
+//  * 12 waves (the library's configuration; Cfg takes others): waves 0-7
+//    are consumers (two per SIMD), waves 8-11 are producers (one per SIMD).
+//    A gfx950 wave's register allocation is fixed for the whole kernel (no
+//    per-role reallocation), so every wave gets 512/3 registers; a consumer
+//    holds a 128 x 64 fp32 accumulator (128 registers) and reads the next
+//    sub-step's fragments while the current one's MFMAs run, the producers
+//    hold only addresses.
 //  * Producers issue direct-to-LDS loads (no data registers); consumers only
 //    read LDS and issue MFMA.  The two roles meet through two counters per
 //    ring stage in LDS instead of a workgroup barrier (the pages' full and
@@ -45,10 +47,16 @@
 namespace g16 {
 namespace ws {
 
-template <int BK_, int STAGES_, int SWZ_>
+// CM x CN consumer waves of 128 x 64 outputs each (workgroup tile
+// 128*CM x 64*CN) and P producer waves; DBUF: consumers read the next
+// sub-step's fragments into a second register set while the MFMAs of the
+// current one run (needs the registers of 8 waves or fewer per CU).
+template <int BK_, int STAGES_, int SWZ_, int CM_ = 2, int CN_ = 4, int P_ = 4, bool DBUF_ = false>
 struct Cfg {
-    static constexpr int BM = 256, BN = 256, BK = BK_, STAGES = STAGES_, SWZ = SWZ_;
-    static constexpr int CONSUMERS = 8, PRODUCERS = 4, WAVES = 12, THREADS = 64 * WAVES;
+    static constexpr int CM = CM_, CN = CN_;
+    static constexpr int BM = 128 * CM_, BN = 64 * CN_, BK = BK_, STAGES = STAGES_, SWZ = SWZ_;
+    static constexpr int CONSUMERS = CM_ * CN_, PRODUCERS = P_, WAVES = CM_ * CN_ + P_, THREADS = 64 * WAVES;
+    static constexpr bool DBUF = DBUF_;
     static constexpr int CH = BK / 8;
     static constexpr int ROW_BYTES = BK * 2;
     static constexpr int ROWS_PER_LOAD = 1024 / ROW_BYTES;
@@ -58,7 +66,7 @@ struct Cfg {
     static constexpr int A_LOADS = A_BYTES / 1024 / PRODUCERS;
     static constexpr int B_LOADS = B_BYTES / 1024 / PRODUCERS;
     static constexpr int LPW = A_LOADS + B_LOADS;
-    static constexpr int WTM = 128, WTN = 64;  // consumer tile: 2 x 4 consumers
+    static constexpr int WTM = 128, WTN = 64;  // consumer tile
     static constexpr int FM = WTM / 32, FN = WTN / 32;
     static constexpr int KSUB = BK / 16;
     static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
@@ -145,30 +153,49 @@ __device__ __forceinline__ void wait_steps_in_flight(int64_t younger)
 }
 
 template <class C>
+__device__ __forceinline__ void read_substep(const char* As, const char* Bs, int wm, int wn, int lane, int kk,
+                                             f16x8 (&a)[C::FM], f16x8 (&b)[C::FN])
+{
+    const int chunk = 2 * kk + (lane >> 5);
+#pragma unroll
+    for (int i = 0; i < C::FM; ++i)
+        a[i] = *reinterpret_cast<const f16x8*>(As + lds_chunk_offset<C::CH, C::SWZ>(wm + 32 * i + (lane & 31), chunk));
+#pragma unroll
+    for (int j = 0; j < C::FN; ++j)
+        b[j] = *reinterpret_cast<const f16x8*>(Bs + lds_chunk_offset<C::CH, C::SWZ>(wn + 32 * j + (lane & 31), chunk));
+}
+
+template <class C>
 __device__ __forceinline__ void consume_stage(const char* As, const char* Bs, int wm, int wn, int lane,
                                               f32x16 (&acc)[C::FM][C::FN])
 {
+    if constexpr (C::DBUF) {
+        // two fragment sets: sub-step kk+1 is read while kk's MFMAs run
+        f16x8 a[2][C::FM], b[2][C::FN];
+        read_substep<C>(As, Bs, wm, wn, lane, 0, a[0], b[0]);
 #pragma unroll
-    for (int kk = 0; kk < C::KSUB; ++kk) {
-        const int chunk = 2 * kk + (lane >> 5);
-        f16x8 a[C::FM], b[C::FN];
+        for (int kk = 0; kk < C::KSUB; ++kk) {
+            if (kk + 1 < C::KSUB) read_substep<C>(As, Bs, wm, wn, lane, kk + 1, a[(kk + 1) & 1], b[(kk + 1) & 1]);
 #pragma unroll
-        for (int i = 0; i < C::FM; ++i)
-            a[i] = *reinterpret_cast<const f16x8*>(
-                As + lds_chunk_offset<C::CH, C::SWZ>(wm + 32 * i + (lane & 31), chunk));
+            for (int i = 0; i < C::FM; ++i)
 #pragma unroll
-        for (int j = 0; j < C::FN; ++j)
-            b[j] = *reinterpret_cast<const f16x8*>(
-                Bs + lds_chunk_offset<C::CH, C::SWZ>(wn + 32 * j + (lane & 31), chunk));
+                for (int j = 0; j < C::FN; ++j) acc[i][j] = mfma_32x32x16(b[kk & 1][j], a[kk & 1][i], acc[i][j]);
+        }
+    } else {
 #pragma unroll
-        for (int i = 0; i < C::FM; ++i)
+        for (int kk = 0; kk < C::KSUB; ++kk) {
+            f16x8 a[C::FM], b[C::FN];
+            read_substep<C>(As, Bs, wm, wn, lane, kk, a, b);
 #pragma unroll
-            for (int j = 0; j < C::FN; ++j) acc[i][j] = mfma_32x32x16(b[j], a[i], acc[i][j]);
+            for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+                for (int j = 0; j < C::FN; ++j) acc[i][j] = mfma_32x32x16(b[j], a[i], acc[i][j]);
+        }
     }
 }
 
 template <class C, bool EDGE>
-__global__ __launch_bounds__(768, 1) void ws_kernel(const f16* __restrict__ A, const f16* __restrict__ B,
+__global__ __launch_bounds__(C::THREADS, 1) void ws_kernel(const f16* __restrict__ A, const f16* __restrict__ B,
                                                     f16* __restrict__ D, int64_t M, int64_t N, int64_t K,
                                                     int64_t tiles_m, int64_t tiles_n)
 {
@@ -239,7 +266,7 @@ __global__ __launch_bounds__(768, 1) void ws_kernel(const f16* __restrict__ A, c
 
     // ---------------------------------------------------------- consumer
     const int c = wave;
-    const int wm = (c >> 2) * C::WTM, wn = (c & 3) * C::WTN;
+    const int wm = (c / C::CN) * C::WTM, wn = (c % C::CN) * C::WTN;
     int64_t g = 0;
     for (int64_t i = 0; i < my_tiles; ++i) {
         const TileCoord tc = grouped_tile(persistent_tile(wg, i, grid), tiles_m, tiles_n);
