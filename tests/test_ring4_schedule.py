@@ -566,3 +566,23 @@ def test_committed_include_matches_generator():
         inc = f.read()
     assert GEN.as_macro("G16_RING4_KLOOP3", GEN.generate3(GEN.DEFAULT3)) in inc
     assert GEN.as_macro("G16_RING4_KLOOP4", GEN.generate4(GEN.DEFAULT4)) in inc
+
+
+# ----------------------------------------------- random schedule parameters
+
+from hypothesis import HealthCheck, assume, given, settings, strategies as st
+
+
+@settings(max_examples=60, deadline=None, suppress_health_check=[HealthCheck.too_slow])
+@given(rel=st.integers(8, 20), pub=st.integers(48, 80), load_every=st.integers(5, 9), a_delay=st.integers(0, 3),
+       epi_slot=st.integers(4, 8), kt=st.sampled_from([2, 3, 5]), tiles=st.sampled_from([1, 2]))
+def test_fourth_form_random_parameters_keep_protocol(rel, pub, load_every, a_delay, epi_slot, kt, tiles):
+    """Any schedule the generator accepts (it refuses parameters that do not
+    fit a step) keeps the ring protocol, across consecutive tiles too."""
+    p = dict(GEN.DEFAULT4)
+    p.update(rel=rel, pub=pub, load_every=load_every, a_delay=a_delay, epi_slot=epi_slot)
+    try:
+        text = GEN.generate4(p)
+    except AssertionError:
+        assume(False)
+    Sim(text, kt, tiles, tiles > 1).run()

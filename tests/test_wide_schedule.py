@@ -344,3 +344,22 @@ def test_committed_wide_include_matches_generator():
     with open(os.path.join(CSRC, "wide_sched.inc")) as f:
         inc = f.read()
     assert GEN.as_macro("G16_WIDE_KLOOP", GEN.generate(GEN.DEFAULT)) in inc
+
+
+from hypothesis import HealthCheck, assume, given, settings, strategies as st
+
+
+@settings(max_examples=60, deadline=None, suppress_health_check=[HealthCheck.too_slow])
+@given(load_every=st.integers(2, 8), a_delay=st.integers(0, 2), epi_slot=st.integers(2, 10),
+       epi_delay=st.integers(5, 9), kt=st.sampled_from([2, 3, 4, 7]))
+def test_wide_random_parameters_keep_protocol(load_every, a_delay, epi_slot, epi_delay, kt):
+    """Any schedule the generator accepts (it refuses parameters that do not
+    fit a step) keeps the ring protocol and the epilogue's hazards."""
+    p = dict(GEN.DEFAULT)
+    p.update(load_every=load_every, a_delay=a_delay, epi_slot=epi_slot, epi_delay=epi_delay)
+    try:
+        text = GEN.generate(p)
+    except AssertionError:
+        assume(False)
+    res = Sim(text, kt).run()
+    assert res["mfma"] == NBM * NBN * 2 * kt
