@@ -436,3 +436,24 @@ def test_splitk_argument_errors_before_any_device_work():
     assert L.gemm_f16_nt_splitk(256, 256, 512, A0, B0, D0, 65, None, 0, None) == g.INVALID_ARG
     assert L.gemm_f16_nt_splitk(256, 256, 512, A0 + 1, B0, D0, 2, None, 0, None) == g.UNSUPPORTED
     assert L.gemm_f16_nt_splitk(0, 256, 512, A0, B0, D0, 2, None, 0, None) == g.OK
+
+
+from hypothesis import given, settings, strategies as st
+
+
+@settings(max_examples=300, deadline=None)
+@given(M=st.integers(1, 20000), N=st.integers(1, 20000), K8=st.integers(1, 2048),
+       cus=st.sampled_from([80, 256, 304]))
+def test_library_plan_picks_rungs_that_take_their_rows(M, N, K8, cus):
+    """Whatever the library chooses for a shape, each launch of the plan is
+    one its rung accepts: rows [0, m_top) on rung_top, the rest on rung_rest
+    at the row offset the library launches them with."""
+    K = 8 * K8
+    A, B, D = 1 << 36, 2 << 36, 3 << 36          # fake, aligned, far apart
+    rt, mt, rr = g.plan(M, N, K, cus)
+    assert 0 < mt <= M
+    assert g.check(rt, mt, N, K, A, B, D) == g.OK, (rt, mt)
+    if mt == M:
+        assert rr == 0
+    else:
+        assert rr != 0 and g.check(rr, M - mt, N, K, A + 2 * mt * K, B, D + 2 * mt * N) == g.OK, (rr, M - mt)
