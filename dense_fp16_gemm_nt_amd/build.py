@@ -41,11 +41,32 @@ def _compile(src: str, lib: str, verbose: bool) -> None:
     os.replace(tmp, lib)
 
 
+CLIENT_SRC = os.path.join(ROOT, "tests", "c_client", "gemm_client.c")
+CLIENT = os.path.join(ROOT, "tests", "c_client", "gemm_client")
+ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
+
+
+def build_client(verbose: bool = False) -> str:
+    """The plain C caller of the C-ABI that a GPU test runs: host code only,
+    built with the system C compiler against the HIP runtime's C API."""
+    cmd = ["gcc", "-O2", "-std=c11", "-Wall", "-D__HIP_PLATFORM_AMD__", "-I", os.path.join(ROCM, "include"),
+           "-I", os.path.join(ROOT, "include"), "-o", CLIENT + ".tmp", CLIENT_SRC, "-L", PKG, "-lgemm_f16_nt",
+           "-L", os.path.join(ROCM, "lib"), "-lamdhip64", "-Wl,-rpath,$ORIGIN/../../dense_fp16_gemm_nt_amd",
+           "-Wl,-rpath," + os.path.join(ROCM, "lib")]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    subprocess.run(cmd, check=True)
+    os.replace(CLIENT + ".tmp", CLIENT)
+    return CLIENT
+
+
 def build(verbose: bool = False) -> str:
-    """Compile the library and the matrix-core calibration kernel of the
-    profiling tools (always recompiles); return the library's path."""
+    """Compile the library, the matrix-core calibration kernel of the
+    profiling tools and the C client of the tests (always recompiles);
+    return the library's path."""
     _compile(SRC, LIB, verbose)
     _compile(CALIB_SRC, CALIB_LIB, verbose)
+    build_client(verbose)
     return LIB
 
 
