@@ -958,3 +958,55 @@ def test_extra_workloads_sampled(name):
         got = host_bits(D[b][torch.from_numpy(rows).to(DEV), torch.from_numpy(cols).to(DEV)])
         worst = max(worst, assert_parity(got, ref, w.K, f"{name} entry {b}"))
     say(f"      worst err/tol = {worst:.3f}")
+
+
+# ----------------------------------------- random shapes through every path
+
+def _random_shapes(count, seed):
+    """Shapes that reach every branch of the library's choice: tiny and
+    tile-starved (128 x 128 tiles), thin, ragged M and N on the four-wave
+    ring, K not a multiple of 64 (partial first step), K not a multiple of
+    8 (register-staged rows), K < 8 (element copies), one k step."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(count):
+        kind = i % 6
+        if kind == 0:
+            M, N, K = rng.integers(1, 300, 3)
+        elif kind == 1:
+            M, N = rng.integers(256, 2600, 2)
+            K = 8 * int(rng.integers(9, 200))
+        elif kind == 2:
+            M, N = rng.integers(256, 1800, 2)
+            K = 64 * int(rng.integers(2, 20))
+        elif kind == 3:
+            M, N = rng.integers(1, 1500, 2)
+            K = int(rng.integers(8, 700)) | 1          # odd K: rows off 16-byte boundaries
+        elif kind == 4:
+            M, N, K = rng.integers(1, 40, 3)
+            K = int(K) % 7 + 1                           # K < 8
+        else:
+            M = int(rng.integers(1, 200))
+            N = int(rng.integers(2000, 9000))
+            K = int(rng.choice([64, 8 * int(rng.integers(1, 64))]))
+        out.append((int(M), int(N), int(K)))
+    return out
+
+
+@pytest.mark.parametrize("shape", _random_shapes(36, 2024), ids=lambda s: "x".join(map(str, s)))
+def test_random_shapes_library_choice(shape):
+    """The library's choice on random shapes: every output written (D
+    starts as NaN) and sampled outputs, the last row and column among them,
+    within the tolerance of the oracle; the result repeats bitwise."""
+    M, N, K = shape
+    A, B = rand_case(M, N, K, 3000 + M * 7 + N * 3 + K)
+    dA, dB = dev(A), dev(B)
+    say(f"[gpu] random shape M={M} N={N} K={K} plan={g.plan(M, N, K, torch.cuda.get_device_properties(0).multi_processor_count)}")
+    D = run(0, dA, dB, poisoned(M, N))
+    got = host_bits(D)
+    assert not np.isnan(as_f64(got)).any(), "output elements left unwritten"
+    rows, cols = sample_positions(M, N, 600, M + N + K)
+    want, _ = oracle.gemm_nt_sampled(A, B, rows, cols)
+    assert_parity(got[rows, cols], want, K, f"random {shape}")
+    again = host_bits(run(0, dA, dB, poisoned(M, N)))
+    assert np.array_equal(got, again)
