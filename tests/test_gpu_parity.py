@@ -1010,3 +1010,48 @@ def test_random_shapes_library_choice(shape):
     assert_parity(got[rows, cols], want, K, f"random {shape}")
     again = host_bits(run(0, dA, dB, poisoned(M, N)))
     assert np.array_equal(got, again)
+
+
+def _random_strided(count, seed):
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(count):
+        batch = int(rng.integers(1, 5))
+        M, N = (int(x) for x in rng.integers(1, 700, 2))
+        K = int(rng.choice([int(rng.integers(1, 600)), 8 * int(rng.integers(1, 80))]))
+        pad_a, pad_b, pad_d = (int(x) for x in rng.integers(0, 24, 3))
+        bcast = int(rng.integers(0, 3))     # 0: none, 1: A shared by the batch, 2: B shared
+        out.append((batch, M, N, K, pad_a, pad_b, pad_d, bcast))
+    return out
+
+
+@pytest.mark.parametrize("case", _random_strided(24, 77), ids=lambda c: "b{}_{}x{}x{}_pad{}-{}-{}_bc{}".format(*c))
+def test_random_strided_batched(case):
+    """The strided-batched entry on random batches, shapes and padded row
+    pitches (any 2-byte alignment), with A or B broadcast over the batch:
+    every output written and every batch entry's sampled outputs within the
+    oracle's tolerance."""
+    batch, M, N, K, pad_a, pad_b, pad_d, bcast = case
+    rng = np.random.default_rng(M + N + K + batch)
+    ba = 1 if bcast == 1 else batch
+    bb = 1 if bcast == 2 else batch
+    A3 = rng.uniform(-1, 1, (ba, M, K)).astype(np.float16)
+    B3 = rng.uniform(-1, 1, (bb, N, K)).astype(np.float16)
+    Af = torch.zeros((ba, M, K + pad_a), dtype=torch.float16, device=DEV)
+    Bf = torch.zeros((bb, N, K + pad_b), dtype=torch.float16, device=DEV)
+    Af[:, :, :K] = dev(A3)
+    Bf[:, :, :K] = dev(B3)
+    A = Af[:, :, :K] if bcast != 1 else Af[0, :, :K]
+    B = Bf[:, :, :K] if bcast != 2 else Bf[0, :, :K]
+    Df = torch.full((batch, M, N + pad_d), float("nan"), dtype=torch.float16, device=DEV)
+    D = Df[:, :, :N]
+    say(f"[gpu] random strided {case}")
+    g.gemm_f16_nt_strided_batched(A, B, D)
+    torch.cuda.synchronize()
+    got = D.cpu().view(torch.int16).numpy().view(np.uint16)
+    assert not np.isnan(as_f64(got)).any(), "output elements left unwritten"
+    assert torch.isnan(Df[:, :, N:]).all().item(), "the row padding of D was written"
+    for b in range(batch):
+        rows, cols = sample_positions(M, N, 150, b + 1)
+        want, _ = oracle.gemm_nt_sampled(A3[0 if ba == 1 else b], B3[0 if bb == 1 else b], rows, cols)
+        assert_parity(got[b][rows, cols], want, K, f"strided {case} entry {b}")
