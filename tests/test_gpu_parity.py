@@ -1055,3 +1055,41 @@ def test_random_strided_batched(case):
         rows, cols = sample_positions(M, N, 150, b + 1)
         want, _ = oracle.gemm_nt_sampled(A3[0 if ba == 1 else b], B3[0 if bb == 1 else b], rows, cols)
         assert_parity(got[b][rows, cols], want, K, f"strided {case} entry {b}")
+
+
+def _random_splitk(count, seed):
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(count):
+        M, N = (int(x) for x in rng.integers(1, 700, 2))
+        form = i % 3        # whole 64-wide steps, a ragged last step, any K
+        K = [64 * int(rng.integers(2, 129)), 8 * int(rng.integers(9, 1025)), int(rng.integers(1, 3000))][form]
+        splits = 0 if rng.random() < 0.3 else int(rng.integers(2, 65))     # 0: the library's count
+        out.append((M, N, K, splits))
+    return out
+
+
+@pytest.mark.parametrize("case", _random_splitk(18, 91), ids=lambda c: "{}x{}x{}_s{}".format(*c))
+def test_random_splitk(case):
+    """The split-K entry on random shapes and slice counts (more slices than
+    64-wide steps among them, K with a ragged last step, K the fast path
+    does not take): every output written (D starts as NaN), sampled outputs
+    within the oracle's tolerance, and the fixed slice order repeats the
+    result bitwise."""
+    M, N, K, splits = case
+    A, B = rand_case(M, N, K, 4000 + M * 5 + N * 11 + K + splits)
+    dA, dB = dev(A), dev(B)
+    say(f"[gpu] random split-K M={M} N={N} K={K} splits={splits} "
+        f"workspace={g.splitk_workspace_bytes(M, N, K, splits)}")
+    D = poisoned(M, N)
+    g.gemm_f16_nt_splitk(dA, dB, D, splits=splits)
+    torch.cuda.synchronize()
+    got = host_bits(D)
+    assert not np.isnan(as_f64(got)).any(), "output elements left unwritten"
+    rows, cols = sample_positions(M, N, 600, M * 3 + N + K)
+    want, _ = oracle.gemm_nt_sampled(A, B, rows, cols)
+    assert_parity(got[rows, cols], want, K, f"random split-K {case}")
+    D = poisoned(M, N)
+    g.gemm_f16_nt_splitk(dA, dB, D, splits=splits)
+    torch.cuda.synchronize()
+    assert np.array_equal(host_bits(D), got)
