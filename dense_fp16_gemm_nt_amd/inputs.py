@@ -105,3 +105,12 @@ def batched_operands(batch: int, M: int, N: int, K: int, seed: int, dist: dict):
     batch entries in order."""
     A, B = operands(batch * M, batch * N, K, seed, dist)
     return A.reshape(batch, M, K), B.reshape(batch, N, K)
+
+
+def periodic_index(rows: int, period: int, shift: int = 0) -> np.ndarray:
+    """Row r of an operand built from a small seeded pattern matrix P of
+    `period` rows is P[(r + shift) % period]; this returns those pattern
+    indices (int64).  Operands of several GiB are built this way on the
+    device from a P that is cheap to draw, and the same indices give the
+    host-side rows of any sample."""
+    return (np.arange(rows, dtype=np.int64) + int(shift)) % int(period)

@@ -79,3 +79,10 @@ def test_extra_workloads_are_well_formed():
         assert w.batch >= 1 and min(w.M, w.N, w.K) >= 1
         assert w.kind not in ("gemm", "splitk") or w.batch == 1
         assert w.flop == 2 * w.batch * w.M * w.N * w.K
+
+
+def test_periodic_index():
+    assert inputs.periodic_index(7, 3, 1).tolist() == [1, 2, 0, 1, 2, 0, 1]
+    idx = inputs.periodic_index(10 ** 6 + 3, 997, 13)
+    assert idx.dtype == np.int64 and idx.min() == 0 and idx.max() == 996
+    assert idx[986895] == (986895 + 13) % 997
