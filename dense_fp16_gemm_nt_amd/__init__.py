@@ -32,8 +32,9 @@ R8_RING4_GAP = 8
 R9_RING_SMALL = 9
 R10_RING4_PAIRED = 10
 R11_WIDE = 11
+R12_SKINNY = 12
 RUNGS = (R1_SINGLE_TILE, R2_KLOOP, R3_GRID, R4_RING, R5_PERSISTENT_WS, R8_RING4_GAP,
-         R9_RING_SMALL, R10_RING4_PAIRED, R11_WIDE)
+         R9_RING_SMALL, R10_RING4_PAIRED, R11_WIDE, R12_SKINNY)
 
 _lock = threading.Lock()
 _lib = None
@@ -138,7 +139,7 @@ def gemm_f16_nt(A, B, D=None):
 
 
 def gemm_f16_nt_rung(rung: int, A, B, D=None):
-    """The same product on one rung of the kernel ladder (1..10)."""
+    """The same product on one rung of the kernel ladder (1-5, 8-12)."""
     M, N, K, D = _operands(A, B, D)
     st = lib().gemm_f16_nt_rung(int(rung), M, N, K, A.data_ptr(), B.data_ptr(), D.data_ptr(), _stream(A))
     if st != OK:

@@ -17,6 +17,7 @@
 #include "ring4.hpp"
 #include "ring_wide.hpp"
 #include "sched.hpp"
+#include "skinny.hpp"
 
 using namespace g16;
 
@@ -156,7 +157,28 @@ bool fast_operands(int64_t K, int64_t lda, int64_t ldb, int64_t sa, int64_t sb, 
 // Rung numbers the library implements (6 and 7 are no longer used).
 bool known_rung(int rung)
 {
-    return rung >= 0 && rung <= GEMM_F16_NT_R11_WIDE && rung != 6 && rung != 7;
+    return rung >= 0 && rung <= GEMM_F16_NT_R12_SKINNY && rung != 6 && rung != 7;
+}
+
+// Shapes of rung 12: one side of at most 64 rows, K >= 8 (the chunk that
+// crosses K is read as a row's last 8 elements), rows on any 2-byte boundary.
+bool skinny_shape(int64_t M, int64_t N, int64_t K)
+{
+    return (M <= skinny::kMaxSmall || N <= skinny::kMaxSmall) && K >= 8;
+}
+
+// Where the library's choice takes rung 12: a single product whose small
+// side has at most 32 rows, or at most 64 with a large side of at most
+// 16384 rows.  Measured on MI355X against the 128 x 128 tiles that ran
+// these shapes before (interleaved, best of two): 16 x 4096 x 14336 120.7 ->
+// 26.8 us, 64 x 8192 x 8192 70.8 -> 45.8 us, 32 x 8192 x 8192 70.1 -> 35.8
+// us, 4096 x 64 x 4096 36.3 -> 20.1 us; with 64 rows and a large side of
+// 28672 the small side's re-reads cost more (133.7 against 106.9 us).
+bool skinny_pays(int64_t M, int64_t N, int64_t K, int64_t batch)
+{
+    if (batch != 1 || !skinny_shape(M, N, K)) return false;
+    const int64_t small = M < N ? M : N, large = M < N ? N : M;
+    return small <= 32 || large <= 16384;
 }
 
 // Shapes of the 384 x 256 ring (rung 11): one tile row and column at least
@@ -182,7 +204,9 @@ int validate(int rung, int64_t M, int64_t N, int64_t K, const void* A, const voi
     // rungs other than R3, R4 and R9 (and the library's choice) need 16-byte
     // rows; R4's and R9's register-staged forms need K >= 8
     const bool general_ok = rung == 0 || rung == GEMM_F16_NT_R3_GRID ||
-                            ((rung == GEMM_F16_NT_R4_RING || rung == GEMM_F16_NT_R9_RING_SMALL) && K >= 8);
+                            ((rung == GEMM_F16_NT_R4_RING || rung == GEMM_F16_NT_R9_RING_SMALL ||
+                              rung == GEMM_F16_NT_R12_SKINNY) &&
+                             K >= 8);
     if (K % 8 != 0 && !general_ok) return GEMM_F16_NT_UNSUPPORTED;
     if (rung == GEMM_F16_NT_R1_SINGLE_TILE && !(M == 128 && N == 128 && K == 64)) return GEMM_F16_NT_UNSUPPORTED;
     if (rung == GEMM_F16_NT_R2_KLOOP && !(M == 128 && N == 128)) return GEMM_F16_NT_UNSUPPORTED;
@@ -192,6 +216,7 @@ int validate(int rung, int64_t M, int64_t N, int64_t K, const void* A, const voi
     if (rung == GEMM_F16_NT_R10_RING4_PAIRED && !(ring4_paired_shape(M, N, K, K, K) && ring4_pitch_ok(N)))
         return GEMM_F16_NT_UNSUPPORTED;
     if (rung == GEMM_F16_NT_R11_WIDE && !wide_shape(M, N, K, N)) return GEMM_F16_NT_UNSUPPORTED;
+    if (rung == GEMM_F16_NT_R12_SKINNY && !skinny_shape(M, N, K)) return GEMM_F16_NT_UNSUPPORTED;
     if (!any_out) return GEMM_F16_NT_OK;
     // fp16 elements are 2-byte aligned; the fast kernels need 16 bytes
     if ((K > 0 && (((uintptr_t)A & 1) || ((uintptr_t)B & 1))) || ((uintptr_t)D & 1)) return GEMM_F16_NT_UNSUPPORTED;
@@ -630,6 +655,59 @@ int launch_r3_any(const GemmArgs& g, hipStream_t s)
 // R4 (256 x 256 tiles) or R9 (128 x 128, `small`) on general operands: the
 // pipelined ring with its loads staged through registers, which take rows
 // on any 2-byte boundary.  Needs K >= 8.
+template <int MT, int NF, bool TRANS>
+void launch_skinny_t(const skinny::Args& a, int64_t grid, hipStream_t s)
+{
+    hipLaunchKernelGGL((skinny::skinny_kernel<MT, NF, NF == 1 ? 8 : 4, TRANS>), dim3((unsigned)grid),
+                       dim3(64 * skinny::kWaves), 0, s, a);
+}
+
+template <bool TRANS>
+int launch_skinny_nf(const skinny::Args& a, int mt, int nf, hipStream_t s)
+{
+    const int64_t grid = (a.l_rows + 16 * nf - 1) / (16 * nf);
+    switch (mt * 8 + nf) {
+    case 9: launch_skinny_t<1, 1, TRANS>(a, grid, s); break;
+    case 10: launch_skinny_t<1, 2, TRANS>(a, grid, s); break;
+    case 12: launch_skinny_t<1, 4, TRANS>(a, grid, s); break;
+    case 17: launch_skinny_t<2, 1, TRANS>(a, grid, s); break;
+    case 18: launch_skinny_t<2, 2, TRANS>(a, grid, s); break;
+    case 20: launch_skinny_t<2, 4, TRANS>(a, grid, s); break;
+    case 25: launch_skinny_t<3, 1, TRANS>(a, grid, s); break;
+    case 26: launch_skinny_t<3, 2, TRANS>(a, grid, s); break;
+    case 28: launch_skinny_t<3, 4, TRANS>(a, grid, s); break;
+    case 33: launch_skinny_t<4, 1, TRANS>(a, grid, s); break;
+    case 34: launch_skinny_t<4, 2, TRANS>(a, grid, s); break;
+    case 36: launch_skinny_t<4, 4, TRANS>(a, grid, s); break;
+    default: return GEMM_F16_NT_UNSUPPORTED;
+    }
+    return launched();
+}
+
+// Rung 12 on one product (batch 1): the side with at most 64 rows is the
+// small side (A when both qualify and M <= N), the other gets one
+// workgroup per 16 * NF rows.
+int launch_skinny(const GemmArgs& g, hipStream_t s)
+{
+    if (g.batch != 1 || !skinny_shape(g.M, g.N, g.K)) return GEMM_F16_NT_UNSUPPORTED;
+    int cus = 0;
+    const int st = device_info(&cus);
+    if (st != GEMM_F16_NT_OK) return st;
+    const bool trans = !(g.M <= skinny::kMaxSmall && (g.M <= g.N || g.N > skinny::kMaxSmall));
+    skinny::Args a;
+    a.S = trans ? g.B : g.A;
+    a.ld_s = trans ? g.ldb : g.lda;
+    a.s_rows = trans ? g.N : g.M;
+    a.L = trans ? g.A : g.B;
+    a.ld_l = trans ? g.lda : g.ldb;
+    a.l_rows = trans ? g.M : g.N;
+    a.K = g.K;
+    a.D = g.D;
+    a.ldd = g.ldd;
+    const int mt = (int)((a.s_rows + 15) / 16), nf = skinny::choose_nf(a.l_rows, cus);
+    return trans ? launch_skinny_nf<true>(a, mt, nf, s) : launch_skinny_nf<false>(a, mt, nf, s);
+}
+
 int launch_staged(const GemmArgs& g0, hipStream_t s, bool small)
 {
     GemmArgs g = g0;
@@ -729,7 +807,10 @@ int run(int rung, int64_t M, int64_t N, int64_t K, const void* A, const void* B,
         return launch_ring4(contiguous_args(M, N, K, A, B, D), s, 4);
     case GEMM_F16_NT_R11_WIDE:
         return launch_wide(contiguous_args(M, N, K, A, B, D), s);
+    case GEMM_F16_NT_R12_SKINNY:
+        return launch_skinny(contiguous_args(M, N, K, A, B, D), s);
     default:  // 0: the library's choice
+        if (skinny_pays(M, N, K, 1)) return launch_skinny(contiguous_args(M, N, K, A, B, D), s);
         if (!fast_operands(K, K, K, 0, 0, A, B, D)) return launch_any(contiguous_args(M, N, K, A, B, D), s);
         return launch_ring(contiguous_args(M, N, K, A, B, D), s, kDefaultRing4);
     }
@@ -789,12 +870,18 @@ int splitk_run(int64_t M, int64_t N, int64_t K, const void* A, const void* B, vo
     st = device_info(&cus);
     if (st != GEMM_F16_NT_OK) return st;
     if (K == 0) return launch_fill_zero(D, M * N, s);
-    if (!fast_operands(K, K, K, 0, 0, A, B, D)) return launch_any(contiguous_args(M, N, K, A, B, D), s);
+    // one slice, or rows off 16-byte boundaries: gemm_f16_nt's choice
+    const auto unsplit = [&]() {
+        const GemmArgs g = contiguous_args(M, N, K, A, B, D);
+        if (skinny_pays(M, N, K, 1)) return launch_skinny(g, s);
+        return fast_operands(K, K, K, 0, 0, A, B, D) ? launch_ring(g, s, kDefaultRing4) : launch_any(g, s);
+    };
+    if (!fast_operands(K, K, K, 0, 0, A, B, D)) return unsplit();
     int64_t want = splits == 0 ? choose_splits(M, N, K, cus) : splits, m_top = 0;
     if (splits == 0 && want <= 1 && !hybrid_plan(M, N, K, cus, &m_top, &want)) m_top = 0;
     int64_t k_chunk = 0, n_slices = 1;
     if (want > 1) split_plan(K, want, &k_chunk, &n_slices);
-    if (n_slices <= 1) return launch_ring(contiguous_args(M, N, K, A, B, D), s, kDefaultRing4);
+    if (n_slices <= 1) return unsplit();
     // rows [m_top, M) split K; rows [0, m_top) (whole rounds of tiles) do not
     const int64_t m_rest = M - m_top;
     const int64_t need = n_slices * m_rest * N * 4;
@@ -872,6 +959,7 @@ int gemm_f16_nt_strided_batched(int64_t M, int64_t N, int64_t K, const void* A, 
     g.sb = stride_b;
     g.sd = stride_d;
     g.batch = batch;
+    if (skinny_pays(M, N, K, batch)) return launch_skinny(g, s);
     if (!fast_operands(K, lda, ldb, stride_a, stride_b, A, B, D)) return launch_any(g, s);
     return launch_ring(g, s, kDefaultRing4);
 }
@@ -1011,6 +1099,10 @@ int gemm_f16_nt_plan(int64_t M, int64_t N, int64_t K, int cus, int* rung_top, in
     GemmArgs g = contiguous_args(M, N, K, nullptr, nullptr, nullptr);
     *m_top = M;
     *rung_rest = 0;
+    if (skinny_pays(M, N, K, 1)) {
+        *rung_top = GEMM_F16_NT_R12_SKINNY;
+        return GEMM_F16_NT_OK;
+    }
     const int64_t tiles = ((M + kFastTile - 1) / kFastTile) * ((N + kFastTile - 1) / kFastTile);
     if (K % 8 != 0) {   // R3's general form, or R9's / R4's register-staged form
         const bool small = tiles * 10 <= (int64_t)cus * kSmallTilesPer10Cus || small_tiles_pay(M, N, 1, cus);

@@ -49,7 +49,7 @@ import time
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 KERNEL_SOURCES = ["common.hpp", "sched.hpp", "ladder.hpp", "ring.hpp", "ring4.hpp", "ring4_sched.inc",
-                  "ring_wide.hpp", "wide_sched.inc", "persistent_ws.hpp", "gemm_f16_nt.hip"]
+                  "ring_wide.hpp", "wide_sched.inc", "persistent_ws.hpp", "skinny.hpp", "gemm_f16_nt.hip"]
 
 
 def _code_only(text: str) -> str:

@@ -92,9 +92,17 @@ extern "C" {
                                    K >= 128, N < 2^23 (the last tile row or column ends at M or N and
                                    overlaps its neighbour); the library's choice, on every row or on the
                                    top rows, where its rounds of tiles cost less than rung 10's */
+#define GEMM_F16_NT_R12_SKINNY 12 /* one side of at most 64 rows (M <= 64 or N <= 64), K >= 8, rows on
+                                     any 2-byte boundary: each workgroup owns 16, 32 or 64 rows of the
+                                     large side and all of the small side, its 8 waves split K, and their
+                                     fp32 partial sums are added in LDS before the one rounding (no
+                                     workspace); the library's choice for single products whose small
+                                     side has at most 32 rows, or at most 64 with a large side of at
+                                     most 16384 rows */
 
 /* D = A * B^T with the library's choice of kernel for the shape (see
- * gemm_f16_nt_plan).  Some shapes take two launches on the stream: when
+ * gemm_f16_nt_plan; products with one small side run on rung 12).  Some
+ * shapes take two launches on the stream: when
  * the 256 x 256 tiles leave a small last round, the rows past the whole
  * rounds run on 128 x 128 tiles; when whole rounds of 384 x 256 tiles fit
  * over the top rows but not over all of them, the top rows run on rung 11
@@ -235,7 +243,8 @@ int gemm_f16_nt_handoff_plan(int depth, int producers, int consumers, int64_t st
  * [0, *m_top) run on rung *rung_top and rows [*m_top, M) on rung
  * *rung_rest (0 and *m_top = M when one kernel takes every row).  For
  * K % 8 != 0 rungs 4 and 9 stand for their register-staged forms and
- * rung 3 for its general form.  Returns 0 or a negative status. */
+ * rung 3 for its general form; rung 12 takes any K >= 8.  Returns 0 or a
+ * negative status. */
 int gemm_f16_nt_plan(int64_t M, int64_t N, int64_t K, int cus, int* rung_top, int64_t* m_top, int* rung_rest);
 /* Host evaluation of gemm_f16_nt_splitk's choice for `splits` = 0 on a
  * device with `cus` compute units, no HIP call: *m_top rows (0 or a

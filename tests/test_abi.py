@@ -76,7 +76,12 @@ A0, B0, D0 = 0x10000, 0x20000000, 0x40000000   # fake, 16-byte aligned, disjoint
     ((0, 64, 10_000_000, 12, A0, B0, D0), g.OK),           # the staged ring's grid is one-dimensional
     ((0, 64, 64, 64, A0, B0, A0 + 4096), g.INVALID_ARG),   # D overlaps A
     ((0, 64, 64, 64, A0, B0, B0), g.INVALID_ARG),          # D overlaps B
-    ((12, 64, 64, 64, A0, B0, D0), g.INVALID_ARG),         # unknown rung
+    ((13, 64, 64, 64, A0, B0, D0), g.INVALID_ARG),         # unknown rung
+    ((12, 64, 4096, 4096, A0, B0, D0), g.OK),               # rung 12: one side of at most 64 rows
+    ((12, 4096, 64, 4096, A0, B0, D0), g.OK),
+    ((12, 65, 65, 4096, A0, B0, D0), g.UNSUPPORTED),        # ... neither side small
+    ((12, 16, 4096, 7, A0, B0, D0), g.UNSUPPORTED),         # ... K >= 8
+    ((12, 16, 4096, 4095, A0 + 2, B0 + 6, D0 + 2), g.OK),   # ... rows on any 2-byte boundary
     ((11, 384, 256, 128, A0, B0, D0), g.OK),                # rung 11: 384 x 256 tiles
     ((11, 383, 256, 128, A0, B0, D0), g.UNSUPPORTED),       # ... at least one tile row
     ((11, 384, 255, 128, A0, B0, D0), g.UNSUPPORTED),       # ... and column
@@ -353,6 +358,14 @@ def test_splitk_workspace_sizes():
     ((8192, 4096, 4096), (10, 8192, 0)),      # 2 rounds of 256-row tiles: no split beats it
     ((6144, 4096, 4000), (10, 6144, 0)),      # K not whole 64-wide steps: the four-wave ring
     ((6144, 4096, 1024), (10, 6144, 0)),      # short K: the four-wave ring carries its ring across tiles
+    ((16, 4096, 14336), (12, 16, 0)),         # one small side: rung 12 splits K inside each workgroup
+    ((4096, 16, 14336), (12, 4096, 0)),       # ... either side
+    ((64, 8192, 8192), (12, 64, 0)),
+    ((32, 28672, 8192), (12, 32, 0)),         # at most 32 rows: any large side
+    ((64, 28672, 8192), (9, 64, 0)),          # 64 rows and a large side over 16384: 128 x 128 tiles
+    ((65, 4096, 4096), (9, 65, 0)),           # neither side small
+    ((16, 4096, 4095), (12, 16, 0)),          # any K >= 8 ...
+    ((16, 4096, 7), (3, 16, 0)),              # ... below that, R3's general form
 ])
 def test_library_plan(shape, want):
     assert g.plan(*shape, 256) == want

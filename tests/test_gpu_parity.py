@@ -1093,3 +1093,92 @@ def test_random_splitk(case):
     g.gemm_f16_nt_splitk(dA, dB, D, splits=splits)
     torch.cuda.synchronize()
     assert np.array_equal(host_bits(D), got)
+
+
+# ------------------------------------- rung 12: one side of at most 64 rows
+
+SKINNY = [(1, 1, 8), (5, 300, 100), (16, 4096, 4096), (64, 1000, 777), (33, 17, 1030), (300, 40, 515),
+          (50, 5000, 4095), (4000, 7, 333), (64, 64, 64), (16, 200, 14336), (64, 2048, 2047), (2, 70000, 64),
+          (48, 3000, 40), (64, 65, 9), (7, 9000, 2048)]
+
+
+@pytest.mark.parametrize("shape", SKINNY, ids=lambda s: "x".join(map(str, s)))
+def test_skinny_parity(shape):
+    """Rung 12 (and the library's choice where it picks rung 12) against the
+    full oracle, output by output, into a NaN-poisoned D: either side
+    small, ragged row counts, K with a crossing chunk (K % 32 != 0) and K
+    % 8 != 0 (rows on 2-byte boundaries), more waves than k chunks."""
+    M, N, K = shape
+    A, B = rand_case(M, N, K, 7000 + M + 3 * N + K)
+    ref, _ = oracle.gemm_nt(A, B)
+    dA, dB = dev(A), dev(B)
+    say(f"[gpu] rung 12 M={M} N={N} K={K} plan={g.plan(M, N, K, 256)}")
+    D = run(12, dA, dB, poisoned(M, N))
+    assert_parity(host_bits(D), ref, K, f"rung 12 {shape}")
+    if g.plan(M, N, K, 256)[0] == 12:
+        D0 = run(0, dA, dB, poisoned(M, N))
+        assert np.array_equal(host_bits(D0), host_bits(D))
+
+
+@pytest.mark.parametrize("shape", [(16, 4096, 8192), (4096, 40, 2040), (64, 512, 1000)], ids=lambda s: "x".join(map(str, s)))
+def test_skinny_exact_pins(shape):
+    """Small integers: every fp32 partial sum and the waves' total are
+    exact, so rung 12 equals the oracle bit for bit; all-ones gives K."""
+    M, N, K = shape
+    rng = np.random.default_rng(M + N + K)
+    A = rng.integers(-4, 5, (M, K)).astype(np.float16)
+    B = rng.integers(-4, 5, (N, K)).astype(np.float16)
+    ref, _ = oracle.gemm_nt(A, B)
+    say(f"[gpu] rung 12 small integers {shape}")
+    D = run(12, dev(A), dev(B), poisoned(M, N))
+    assert np.array_equal(host_bits(D), ref)
+    ones = torch.ones((M, K), dtype=torch.float16, device=DEV)
+    onesb = torch.ones((N, K), dtype=torch.float16, device=DEV)
+    D = run(12, ones, onesb, poisoned(M, N))
+    assert torch.all(D.float() == float(K)).item()
+
+
+@pytest.mark.parametrize("offs", [(1, 0, 0), (0, 3, 5), (7, 1, 3)], ids=lambda o: "a{}b{}d{}".format(*o))
+def test_skinny_misaligned_and_pitched(offs):
+    """Rung 12 on operands at 2-byte offsets (through the library's choice)
+    and on padded row pitches with batch 1 (through the strided entry),
+    against the full oracle; the padding of D stays unwritten."""
+    M, N, K = 24, 3000, 1001
+    A, B = rand_case(M, N, K, 7100 + sum(offs))
+    ref, _ = oracle.gemm_nt(A, B)
+    assert g.plan(M, N, K, 256)[0] == 12
+    say(f"[gpu] rung 12 offsets {offs}")
+    dA, dB = _offset_view(A, offs[0]), _offset_view(B, offs[1])
+    D = _offset_view(np.full((M, N), np.nan, np.float16), offs[2])
+    g.gemm_f16_nt(dA, dB, D)
+    torch.cuda.synchronize()
+    assert_parity(host_bits(D), ref, K, f"rung 12 offsets {offs}")
+    pa, pb, pd = 3 + offs[0], 5 + offs[1], 7 + offs[2]
+    Af = torch.zeros((1, M, K + pa), dtype=torch.float16, device=DEV)
+    Bf = torch.zeros((1, N, K + pb), dtype=torch.float16, device=DEV)
+    Af[0, :, :K] = dev(A)
+    Bf[0, :, :K] = dev(B)
+    Df = torch.full((1, M, N + pd), float("nan"), dtype=torch.float16, device=DEV)
+    g.gemm_f16_nt_strided_batched(Af[:, :, :K], Bf[:, :, :K], Df[:, :, :N])
+    torch.cuda.synchronize()
+    assert_parity(host_bits(Df[0, :, :N]), ref, K, f"rung 12 pitched {offs}")
+    assert torch.isnan(Df[:, :, N:]).all().item()
+
+
+def test_skinny_repeatable_and_split_k_entry():
+    """Rung 12's fixed summation order repeats bitwise; the split-K entry
+    with one slice runs the library's choice (rung 12 here) and equals it."""
+    M, N, K = 32, 8192, 8192
+    A, B = rand_case(M, N, K, 7200)
+    dA, dB = dev(A), dev(B)
+    say("[gpu] rung 12 repeatable")
+    first = host_bits(run(0, dA, dB, poisoned(M, N)))
+    for _ in range(3):
+        assert np.array_equal(host_bits(run(0, dA, dB, poisoned(M, N))), first)
+    D = poisoned(M, N)
+    g.gemm_f16_nt_splitk(dA, dB, D, splits=1)
+    torch.cuda.synchronize()
+    assert np.array_equal(host_bits(D), first)
+    rows, cols = sample_positions(M, N, 800, 7)
+    want, _ = oracle.gemm_nt_sampled(A, B, rows, cols)
+    assert_parity(first[rows, cols], want, K, "rung 12 32x8192x8192")
