@@ -103,6 +103,9 @@ EXTRA_WORKLOADS = [
     # M = 128: 256 x 256 tiles would be half padding and fill half the device,
     # so the library takes 128 x 128 tiles
     ExtraWorkload("thin_m_128x32768x4096", "gemm", 1, 128, 32768, 4096, 21, U11),
+    # one side of 16 rows (a small batch against a large weight): rung 12
+    # splits K among each workgroup's waves
+    ExtraWorkload("skinny_16x4096x14336", "gemm", 1, 16, 4096, 14336, 24, U11),
     # a small last round of tiles (2.25 rounds on 256 compute units, and a
     # ragged M): whole rounds unsplit, the remaining rows split K
     ExtraWorkload("splitk_rounds_6144x6144x6144", "splitk", 1, 6144, 6144, 6144, 18, U11),
