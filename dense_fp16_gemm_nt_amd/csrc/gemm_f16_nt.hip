@@ -658,8 +658,8 @@ int launch_r3_any(const GemmArgs& g, hipStream_t s)
 template <int MT, int NF, bool TRANS>
 void launch_skinny_t(const skinny::Args& a, int64_t grid, hipStream_t s)
 {
-    hipLaunchKernelGGL((skinny::skinny_kernel<MT, NF, NF == 1 ? 8 : 4, TRANS>), dim3((unsigned)grid),
-                       dim3(64 * skinny::kWaves), 0, s, a);
+    hipLaunchKernelGGL((skinny::skinny_kernel<MT, NF, TRANS>), dim3((unsigned)grid), dim3(64 * skinny::kWaves), 0,
+                       s, a);
 }
 
 template <bool TRANS>
@@ -669,16 +669,12 @@ int launch_skinny_nf(const skinny::Args& a, int mt, int nf, hipStream_t s)
     switch (mt * 8 + nf) {
     case 9: launch_skinny_t<1, 1, TRANS>(a, grid, s); break;
     case 10: launch_skinny_t<1, 2, TRANS>(a, grid, s); break;
-    case 12: launch_skinny_t<1, 4, TRANS>(a, grid, s); break;
     case 17: launch_skinny_t<2, 1, TRANS>(a, grid, s); break;
     case 18: launch_skinny_t<2, 2, TRANS>(a, grid, s); break;
-    case 20: launch_skinny_t<2, 4, TRANS>(a, grid, s); break;
     case 25: launch_skinny_t<3, 1, TRANS>(a, grid, s); break;
     case 26: launch_skinny_t<3, 2, TRANS>(a, grid, s); break;
-    case 28: launch_skinny_t<3, 4, TRANS>(a, grid, s); break;
     case 33: launch_skinny_t<4, 1, TRANS>(a, grid, s); break;
     case 34: launch_skinny_t<4, 2, TRANS>(a, grid, s); break;
-    case 36: launch_skinny_t<4, 4, TRANS>(a, grid, s); break;
     default: return GEMM_F16_NT_UNSUPPORTED;
     }
     return launched();

@@ -13,20 +13,25 @@
 // the spirit of the persistent scheduler of "TIRx GEMM detailed technical
 // notes", V6, that keeps every compute unit on work).
 //
-// Operands go straight from global memory into MFMA operand registers, one
-// 16-byte load per lane per fragment (no LDS staging: the large side is
-// read once, so only the memory-level parallelism of the waves' loads
-// matters).  v_mfma_f32_16x16x32_f16 lane layout: lane l supplies row
-// l % 16 of a 16-row block at k elements 8 * (l / 16) .. + 7 of the chunk,
-// for both operands, and holds the outputs (row 4 * (l / 16) + r, column
-// l % 16), r = 0..3, of the 16 x 16 block (S rows by L rows).
-//
-// Any 2-byte alignment of rows (gfx950's global loads take unaligned
-// addresses) and any K >= 8: the chunk that crosses K is read as the
-// row's last 8 elements and shifted (load_row_chunk, chunk_shift).  Rows
-// past the operand are read as its last row and their outputs are not
-// stored.  Each output's sum runs in a fixed order (k chunks in order
-// within a wave, then waves 0..7), so results repeat bit for bit.
+// Loads: each 32-wide k chunk of a 16-row block is one MFMA fragment per
+// lane (lane l: row l % 16, k elements 8 * (l / 16) .. + 7 of the chunk:
+// the v_mfma_f32_16x16x32_f16 operand layout), but a load instruction in
+// that layout touches 16 rows x 64 bytes.  Measured on MI355X such loads
+// stream at ~35 GB/s per compute unit, so each wave instead loads four
+// chunks (128 k) of a block at a time as 4 instructions of 4 rows x 256
+// bytes (lane l: row 4u + l / 16, k elements 8 * (l % 16) .. + 7 of the
+// 128), writes them into its own 4 KiB of LDS (16-byte slots XOR-swizzled
+// by row, so neither the writes nor the reads conflict) and reads them back
+// as fragments.  No barrier: only the wave itself reads its buffer.  Rows
+// on any 2-byte boundary (gfx950's global loads take unaligned addresses).
+// The rest of a wave's range after its whole 4-chunk groups, including the
+// chunk that crosses K, is read as fragments directly: the crossing chunk
+// as the row's last 8 elements, shifted (load_row_chunk, chunk_shift);
+// this needs K >= 8.  Rows past the operand are read as its last row and
+// their outputs are not stored.  The output block layout: lane l holds
+// (small row 4 * (l / 16) + r, large row l % 16), r = 0..3.  Each output's
+// sum runs in a fixed order (k chunks in order within a wave, then waves
+// 0..7), so results repeat bit for bit.
 #pragma once
 
 #include "common.hpp"
@@ -46,67 +51,86 @@ struct Args {
 };
 
 // TRANS = false: S is A (D[s][l]); TRANS = true: S is B (D[l][s]).
-template <int MT, int NF, int U, bool TRANS>
+template <int MT, int NF, bool TRANS>
 __global__ __launch_bounds__(64 * kWaves) void skinny_kernel(const Args g)
 {
+    constexpr int NB = MT + NF;   // 16-row blocks: MT of S, then NF of L
     __shared__ f32x4 red[kWaves][MT * NF][64];
+    __shared__ __attribute__((aligned(16))) char tbuf[kWaves][4096];
     const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int r16 = lane & 15, kq = lane >> 4;
     const int64_t j0 = (int64_t)blockIdx.x * 16 * NF;
-    const char* lrow[NF];
-    const char* srow[MT];
+    auto row_ptr = [&](int b, int r) -> const char* {
+        if (b < MT) {
+            const int64_t rr = 16 * b + r;
+            return reinterpret_cast<const char*>(g.S + (rr < g.s_rows ? rr : g.s_rows - 1) * g.ld_s);
+        }
+        const int64_t rr = j0 + 16 * (b - MT) + r;
+        return reinterpret_cast<const char*>(g.L + (rr < g.l_rows ? rr : g.l_rows - 1) * g.ld_l);
+    };
+    const char* gptr[NB][4];   // group loads: row 4u + kq of block b
+    const char* fptr[NB];      // fragment loads: row r16 of block b
 #pragma unroll
-    for (int f = 0; f < NF; ++f) {
-        const int64_t r = j0 + 16 * f + r16;
-        lrow[f] = reinterpret_cast<const char*>(g.L + (r < g.l_rows ? r : g.l_rows - 1) * g.ld_l);
-    }
+    for (int b = 0; b < NB; ++b) {
 #pragma unroll
-    for (int t = 0; t < MT; ++t) {
-        const int64_t r = 16 * t + r16;
-        srow[t] = reinterpret_cast<const char*>(g.S + (r < g.s_rows ? r : g.s_rows - 1) * g.ld_s);
+        for (int u = 0; u < 4; ++u) gptr[b][u] = row_ptr(b, 4 * u + kq);
+        fptr[b] = row_ptr(b, r16);
     }
-    // this wave's chunks [c0, c1); [c0, cf) lie wholly inside K (at most
-    // one chunk, the last of K, crosses it)
-    const int64_t K = g.K, chunks = (K + 31) / 32, per = (chunks + kWaves - 1) / kWaves;
+    // this wave's chunks [c0, c1): whole groups of 4 chunks inside K, then the rest
+    const int64_t K = g.K, chunks = (K + 31) / 32;
+    const int64_t per = ((chunks + kWaves - 1) / kWaves + 3) / 4 * 4;
     const int64_t c0 = w * per, c1 = c0 + per < chunks ? c0 + per : chunks;
-    const int64_t whole = K / 32, cf = c1 < whole ? c1 : (whole > c0 ? whole : c0);
+    const int64_t cw = c1 < K / 32 ? c1 : K / 32;
+    const int64_t groups = cw > c0 ? (cw - c0) / 4 : 0;
     f32x4 acc[MT][NF];
 #pragma unroll
     for (int t = 0; t < MT; ++t)
 #pragma unroll
         for (int f = 0; f < NF; ++f) acc[t][f] = f32x4{0.f, 0.f, 0.f, 0.f};
-    auto mma = [&](const u32x4 (&sv)[MT], const u32x4 (&lv)[NF]) {
+    auto mma = [&](const u32x4 (&sv)[NB]) {
 #pragma unroll
         for (int t = 0; t < MT; ++t)
 #pragma unroll
             for (int f = 0; f < NF; ++f)
                 acc[t][f] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, sv[t]),
-                                                                   __builtin_bit_cast(f16x8, lv[f]), acc[t][f], 0, 0, 0);
+                                                                   __builtin_bit_cast(f16x8, sv[MT + f]), acc[t][f], 0, 0, 0);
     };
+    // LDS slots: the write of (row 4u + kq, 8-element group r16) and the
+    // read of (row r16, group 4u + kq), 16-byte slots XOR-swizzled by row
+    char* tb = tbuf[w];
+    uint32_t wo[4], ro[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        const int row = 4 * u + kq, kg = 4 * u + kq;
+        wo[u] = (uint32_t)(row * 256 + ((r16 ^ row) & 15) * 16);
+        ro[u] = (uint32_t)(r16 * 256 + ((kg ^ r16) & 15) * 16);
+    }
     typedef uint32_t u32x4_a2 __attribute__((ext_vector_type(4), aligned(2)));
     int64_t c = c0;
-    for (; c + U <= cf; c += U) {
-        // U chunks' loads first, then their MFMAs
-        u32x4 lv[U][NF], sv[U][MT];
+    for (int64_t gi = 0; gi < groups; ++gi, c += 4) {
+        const int64_t kb = (c * 32 + 8 * r16) * 2;
+        u32x4 v[NB][4];
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int64_t kb = ((c + u) * 32 + 8 * kq) * 2;
+        for (int b = 0; b < NB; ++b)
 #pragma unroll
-            for (int f = 0; f < NF; ++f) lv[u][f] = *(const G16_GLOBAL u32x4_a2*)(lrow[f] + kb);
+            for (int u = 0; u < 4; ++u) v[b][u] = *(const G16_GLOBAL u32x4_a2*)(gptr[b][u] + kb);
+        u32x4 fr[4][NB];
 #pragma unroll
-            for (int t = 0; t < MT; ++t) sv[u][t] = *(const G16_GLOBAL u32x4_a2*)(srow[t] + kb);
+        for (int b = 0; b < NB; ++b) {
+#pragma unroll
+            for (int u = 0; u < 4; ++u) *reinterpret_cast<u32x4*>(tb + wo[u]) = v[b][u];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) fr[u][b] = *reinterpret_cast<const u32x4*>(tb + ro[u]);
         }
 #pragma unroll
-        for (int u = 0; u < U; ++u) mma(sv[u], lv[u]);
+        for (int u = 0; u < 4; ++u) mma(fr[u]);
     }
     for (; c < c1; ++c) {
         const int kk = (int)(c * 32 + 8 * kq);
-        u32x4 lv[NF], sv[MT];
+        u32x4 fv[NB];
 #pragma unroll
-        for (int f = 0; f < NF; ++f) lv[f] = chunk_shift(load_row_chunk(lrow[f], kk, (int)K, true), kk, (int)K);
-#pragma unroll
-        for (int t = 0; t < MT; ++t) sv[t] = chunk_shift(load_row_chunk(srow[t], kk, (int)K, true), kk, (int)K);
-        mma(sv, lv);
+        for (int b = 0; b < NB; ++b) fv[b] = chunk_shift(load_row_chunk(fptr[b], kk, (int)K, true), kk, (int)K);
+        mma(fv);
     }
     // the waves' partial sums, added in wave order, rounded once
 #pragma unroll
@@ -132,15 +156,12 @@ __global__ __launch_bounds__(64 * kWaves) void skinny_kernel(const Args g)
     }
 }
 
-// Large-side rows per workgroup: the largest 16 * NF (NF in 4, 2, 1) that
-// still gives at least three workgroups per four compute units (more rows
-// per workgroup re-read the small side less often; measured on MI355X,
-// 16 x 28672 x 8192: 106.6 / 111.1 / 124.4 us for NF = 4 / 2 / 1).
+// Large-side rows per workgroup: 32 when that still gives every compute
+// unit a workgroup, else 16 (measured on MI355X: 64 x 8192 x 8192 28.5 us
+// with 32 rows against 35.4 with 16; 64 x 4096 x 4096 13.2 against 11.9).
 inline int choose_nf(int64_t l_rows, int cus)
 {
-    for (int nf = 4; nf > 1; nf /= 2)
-        if ((l_rows + 16 * nf - 1) / (16 * nf) * 4 >= (int64_t)cus * 3) return nf;
-    return 1;
+    return (l_rows + 31) / 32 >= (int64_t)cus ? 2 : 1;
 }
 
 }  // namespace skinny

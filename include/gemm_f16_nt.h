@@ -93,9 +93,9 @@ extern "C" {
                                    overlaps its neighbour); the library's choice, on every row or on the
                                    top rows, where its rounds of tiles cost less than rung 10's */
 #define GEMM_F16_NT_R12_SKINNY 12 /* one side of at most 64 rows (M <= 64 or N <= 64), K >= 8, rows on
-                                     any 2-byte boundary: each workgroup owns 16, 32 or 64 rows of the
-                                     large side and all of the small side, its 8 waves split K, and their
-                                     fp32 partial sums are added in LDS before the one rounding (no
+                                     any 2-byte boundary: each workgroup owns 16 or 32 rows of the large
+                                     side and all of the small side, its 8 waves split K, and their fp32
+                                     partial sums are added in LDS before the one rounding (no
                                      workspace); the library's choice for single products whose small
                                      side has at most 32 rows, or at most 64 with a large side of at
                                      most 16384 rows */
