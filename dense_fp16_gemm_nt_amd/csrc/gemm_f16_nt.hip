@@ -510,17 +510,28 @@ int launch_ring(const GemmArgs& g0, hipStream_t s, bool allow_ring4 = false)
 // workgroup, but at least kMinStepsPerSlice 64-wide steps per slice (a
 // slice pays a prologue, a partial-sum write and its share of the
 // reduction; measured on MI355X, K = 512 on one 256 x 256 tile is faster
-// unsplit) and at most kMaxSplits slices.
+// unsplit) and at most kMaxSplits slices.  With at most kFewTiles tiles
+// and K of at least 32 steps, half as many steps per slice pay (32 slices
+// against 16, interleaved:
+// 256 x 1024 x 8192 29.0 -> 25.4 us, 64 x 1024 x 8192 21.3 -> 17.8 us,
+// 128 x 1024 x 8192 25.0 -> 22.7 us).
 constexpr int64_t kMaxSplits = 64;
 constexpr int64_t kMinStepsPerSlice = 8;
+constexpr int64_t kFewTiles = 4;
 
 int64_t choose_splits(int64_t M, int64_t N, int64_t K, int cus)
 {
+    // one small side: rung 12 splits K inside its workgroups without a
+    // workspace, faster than slices (measured on MI355X: 64 x 8192 x 8192
+    // 28.3 us against 34.7 us in 8 slices, 64 x 1024 x 8192 15.3 against 17.7)
+    if (skinny_pays(M, N, K, 1)) return 1;
     const int64_t tiles = ((M + kFastTile - 1) / kFastTile) * ((N + kFastTile - 1) / kFastTile);
     const int64_t kt = (K + RingCfg::BK - 1) / RingCfg::BK;
     if (tiles * 2 >= cus) return 1;
+    const int64_t min_steps =
+        tiles <= kFewTiles && kt >= 4 * kMinStepsPerSlice ? kMinStepsPerSlice / 2 : kMinStepsPerSlice;
     int64_t s = cus / tiles;
-    s = s < kt / kMinStepsPerSlice ? s : kt / kMinStepsPerSlice;
+    s = s < kt / min_steps ? s : kt / min_steps;
     s = s < kMaxSplits ? s : kMaxSplits;
     return s > 1 ? s : 1;
 }

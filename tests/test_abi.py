@@ -404,6 +404,12 @@ def test_wide_top_rows_plan_invariants(M, N, K, cus):
     ((8192, 8192, 8192), 256, (0, 1)),
     ((6144, 6144, 2048), 256, (0, 1)),        # short K: the split costs more than the last round
     ((256, 256, 65536), 256, (0, 64)),        # tile-starved: every row splits
+    ((256, 1024, 8192), 256, (0, 32)),        # at most 4 tiles: slices of 4 steps
+    ((128, 1024, 8192), 256, (0, 32)),
+    ((64, 1024, 8192), 256, (0, 1)),          # one small side: rung 12, unsplit
+    ((16, 4096, 14336), 256, (0, 1)),
+    ((1024, 1024, 8192), 256, (0, 16)),       # 16 tiles: slices of at least 8 steps
+    ((256, 256, 512), 256, (0, 1)),           # 8 steps on one tile: unsplit
 ])
 def test_splitk_plan(shape, cus, want):
     assert g.splitk_plan(*shape, cus) == want
