@@ -160,7 +160,7 @@ bool known_rung(int rung)
     return rung >= 0 && rung <= GEMM_F16_NT_R12_SKINNY && rung != 6 && rung != 7;
 }
 
-// Shapes of rung 12: one side of at most 64 rows, K >= 8 (the chunk that
+// Shapes of rung 12: one side of at most 96 rows, K >= 8 (the chunk that
 // crosses K is read as a row's last 8 elements), rows on any 2-byte boundary.
 bool skinny_shape(int64_t M, int64_t N, int64_t K)
 {
@@ -168,17 +168,19 @@ bool skinny_shape(int64_t M, int64_t N, int64_t K)
 }
 
 // Where the library's choice takes rung 12: a single product whose small
-// side has at most 32 rows, or at most 64 with a large side of at most
-// 16384 rows.  Measured on MI355X against the 128 x 128 tiles that ran
-// these shapes before (interleaved, best of two): 16 x 4096 x 14336 120.7 ->
-// 26.8 us, 64 x 8192 x 8192 70.8 -> 45.8 us, 32 x 8192 x 8192 70.1 -> 35.8
-// us, 4096 x 64 x 4096 36.3 -> 20.1 us; with 64 rows and a large side of
-// 28672 the small side's re-reads cost more (133.7 against 106.9 us).
+// side has at most 32 rows, at most 64 with a large side of at most 16384
+// rows, or at most 96 with a large side of at most 12288.  Measured on
+// MI355X against the 128 x 128 tiles that ran these shapes before
+// (interleaved, best of two): 16 x 4096 x 14336 120.7 -> 24.3 us, 64 x 8192
+// x 8192 70.8 -> 28.1 us, 80 x 8192 x 8192 71.6 -> 29.8 us, 96 x 4096 x
+// 14336 121.3 -> 42.2 us; the workgroups' re-reads of the small side cost
+// more than those tiles from 64 rows with a large side of 28672 (119.6
+// against 108.6 us) and break even from 96 rows at 14336 to 16384.
 bool skinny_pays(int64_t M, int64_t N, int64_t K, int64_t batch)
 {
     if (batch != 1 || !skinny_shape(M, N, K)) return false;
     const int64_t small = M < N ? M : N, large = M < N ? N : M;
-    return small <= 32 || large <= 16384;
+    return small <= 32 || (small <= 64 && large <= 16384) || large <= 12288;
 }
 
 // Shapes of the 384 x 256 ring (rung 11): one tile row and column at least
@@ -686,12 +688,16 @@ int launch_skinny_nf(const skinny::Args& a, int mt, int nf, hipStream_t s)
     case 26: launch_skinny_t<3, 2, TRANS>(a, grid, s); break;
     case 33: launch_skinny_t<4, 1, TRANS>(a, grid, s); break;
     case 34: launch_skinny_t<4, 2, TRANS>(a, grid, s); break;
+    case 41: launch_skinny_t<5, 1, TRANS>(a, grid, s); break;
+    case 42: launch_skinny_t<5, 2, TRANS>(a, grid, s); break;
+    case 49: launch_skinny_t<6, 1, TRANS>(a, grid, s); break;
+    case 50: launch_skinny_t<6, 2, TRANS>(a, grid, s); break;
     default: return GEMM_F16_NT_UNSUPPORTED;
     }
     return launched();
 }
 
-// Rung 12 on one product (batch 1): the side with at most 64 rows is the
+// Rung 12 on one product (batch 1): the side with at most 96 rows is the
 // small side (A when both qualify and M <= N), the other gets one
 // workgroup per 16 * NF rows.
 int launch_skinny(const GemmArgs& g, hipStream_t s)

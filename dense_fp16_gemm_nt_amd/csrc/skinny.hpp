@@ -1,10 +1,10 @@
-// Rung 12: products with one side of at most 64 rows (M <= 64 or N <= 64),
+// Rung 12: products with one side of at most 96 rows (M <= 96 or N <= 96),
 // the tile-starved shapes of small-batch inference (e.g. 16 x 4096 x 14336).
 //
 // Tiles of 128 or 256 rows leave most of such a tile empty and, with few
 // tiles, most compute units idle, each of the few busy ones walking all of
 // K.  Here every workgroup owns 16 * NF rows of the large side ("L") and
-// all rows of the small side ("S", 16 * MT rows, MT <= 4), so the large
+// all rows of the small side ("S", 16 * MT rows, MT <= 6), so the large
 // side alone sets the workgroup count, and its 8 waves split K between
 // them: wave w contracts a contiguous range of 32-wide k chunks, and the
 // waves' fp32 partial sums are added through LDS in wave order before the
@@ -41,7 +41,7 @@ namespace g16 {
 namespace skinny {
 
 constexpr int kWaves = 8;
-constexpr int kMaxSmall = 64;   // rows of the small side: 16 * MT, MT <= 4
+constexpr int kMaxSmall = 96;   // rows of the small side: 16 * MT, MT <= 6 (more spills registers)
 
 struct Args {
     const f16* S;   // small side: s_rows x K, row pitch ld_s

@@ -92,13 +92,13 @@ extern "C" {
                                    K >= 128, N < 2^23 (the last tile row or column ends at M or N and
                                    overlaps its neighbour); the library's choice, on every row or on the
                                    top rows, where its rounds of tiles cost less than rung 10's */
-#define GEMM_F16_NT_R12_SKINNY 12 /* one side of at most 64 rows (M <= 64 or N <= 64), K >= 8, rows on
+#define GEMM_F16_NT_R12_SKINNY 12 /* one side of at most 96 rows (M <= 96 or N <= 96), K >= 8, rows on
                                      any 2-byte boundary: each workgroup owns 16 or 32 rows of the large
                                      side and all of the small side, its 8 waves split K, and their fp32
                                      partial sums are added in LDS before the one rounding (no
                                      workspace); the library's choice for single products whose small
-                                     side has at most 32 rows, or at most 64 with a large side of at
-                                     most 16384 rows */
+                                     side has at most 32 rows, at most 64 with a large side of at most
+                                     16384 rows, or at most 96 with a large side of at most 12288 */
 
 /* D = A * B^T with the library's choice of kernel for the shape (see
  * gemm_f16_nt_plan; products with one small side run on rung 12).  Some

@@ -79,7 +79,8 @@ A0, B0, D0 = 0x10000, 0x20000000, 0x40000000   # fake, 16-byte aligned, disjoint
     ((13, 64, 64, 64, A0, B0, D0), g.INVALID_ARG),         # unknown rung
     ((12, 64, 4096, 4096, A0, B0, D0), g.OK),               # rung 12: one side of at most 64 rows
     ((12, 4096, 64, 4096, A0, B0, D0), g.OK),
-    ((12, 65, 65, 4096, A0, B0, D0), g.UNSUPPORTED),        # ... neither side small
+    ((12, 96, 4096, 4096, A0, B0, D0), g.OK),               # ... up to 96 rows
+    ((12, 97, 97, 4096, A0, B0, D0), g.UNSUPPORTED),        # ... neither side small
     ((12, 16, 4096, 7, A0, B0, D0), g.UNSUPPORTED),         # ... K >= 8
     ((12, 16, 4096, 4095, A0 + 2, B0 + 6, D0 + 2), g.OK),   # ... rows on any 2-byte boundary
     ((11, 384, 256, 128, A0, B0, D0), g.OK),                # rung 11: 384 x 256 tiles
@@ -363,7 +364,9 @@ def test_splitk_workspace_sizes():
     ((64, 8192, 8192), (12, 64, 0)),
     ((32, 28672, 8192), (12, 32, 0)),         # at most 32 rows: any large side
     ((64, 28672, 8192), (9, 64, 0)),          # 64 rows and a large side over 16384: 128 x 128 tiles
-    ((65, 4096, 4096), (9, 65, 0)),           # neither side small
+    ((80, 8192, 8192), (12, 80, 0)),          # up to 96 rows with a large side up to 12288
+    ((96, 16384, 8192), (9, 96, 0)),          # ... beyond it, 128 x 128 tiles
+    ((97, 4096, 4096), (9, 97, 0)),           # neither side small
     ((16, 4096, 4095), (12, 16, 0)),          # any K >= 8 ...
     ((16, 4096, 7), (3, 16, 0)),              # ... below that, R3's general form
 ])

@@ -1095,11 +1095,12 @@ def test_random_splitk(case):
     assert np.array_equal(host_bits(D), got)
 
 
-# ------------------------------------- rung 12: one side of at most 64 rows
+# ------------------------------------- rung 12: one side of at most 96 rows
 
 SKINNY = [(1, 1, 8), (5, 300, 100), (16, 4096, 4096), (64, 1000, 777), (33, 17, 1030), (300, 40, 515),
           (50, 5000, 4095), (4000, 7, 333), (64, 64, 64), (16, 200, 14336), (64, 2048, 2047), (2, 70000, 64),
-          (48, 3000, 40), (64, 65, 9), (7, 9000, 2048)]
+          (48, 3000, 40), (64, 65, 9), (7, 9000, 2048), (80, 3000, 1000), (96, 5000, 4095), (4000, 90, 333),
+          (72, 2048, 64), (96, 96, 4096)]
 
 
 @pytest.mark.parametrize("shape", SKINNY, ids=lambda s: "x".join(map(str, s)))
