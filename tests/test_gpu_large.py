@@ -102,11 +102,12 @@ def test_output_past_4gib():
     free()
 
 
-@pytest.mark.parametrize("side", ["A", "B"])
-def test_operand_past_4gib(side):
+@pytest.mark.parametrize("side,small", [("A", 512), ("B", 512), ("A", 16), ("B", 16)])
+def test_operand_past_4gib(side, small):
     """A (or B) of 4.6 GB: 1048876 rows of K = 2176, so row bases pass the
-    2^31 and 2^32 byte offsets; the other operand has 512 rows."""
-    big, small, K = 1048876, 512, 2176
+    2^31 and 2^32 byte offsets; the other operand has 512 rows (the
+    four-wave ring) or 16 (rung 12, whose large side it is)."""
+    big, K = 1048876, 2176
     P = pattern(997, K, 72, 0)
     S = inputs.generate(small, K, 72, 1, workloads.U11)
     shift = 13
