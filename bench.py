@@ -51,7 +51,7 @@ HBM_PEAK_GBS = 8000.0
 METRIC = "fp16 GEMM TFLOP/s at M=N=K=4096 (+ % of MI355X dense-fp16 peak)"
 RUNG_NAMES = {0: "auto", 1: "r1_single_tile", 2: "r2_kloop", 3: "r3_grid", 4: "r4_ring",
               5: "r5_persistent_ws", 8: "r8_ring4_gap", 9: "r9_ring_small", 10: "r10_ring4_paired",
-              11: "r11_wide", 12: "r12_skinny"}
+              11: "r11_wide", 12: "r12_skinny", 13: "r13_ksplit"}
 
 
 def kernel_source_hash() -> str:

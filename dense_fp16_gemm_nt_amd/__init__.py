@@ -33,8 +33,9 @@ R9_RING_SMALL = 9
 R10_RING4_PAIRED = 10
 R11_WIDE = 11
 R12_SKINNY = 12
+R13_KSPLIT = 13
 RUNGS = (R1_SINGLE_TILE, R2_KLOOP, R3_GRID, R4_RING, R5_PERSISTENT_WS, R8_RING4_GAP,
-         R9_RING_SMALL, R10_RING4_PAIRED, R11_WIDE, R12_SKINNY)
+         R9_RING_SMALL, R10_RING4_PAIRED, R11_WIDE, R12_SKINNY, R13_KSPLIT)
 
 _lock = threading.Lock()
 _lib = None
@@ -87,6 +88,8 @@ def lib() -> ctypes.CDLL:
                                            ctypes.POINTER(ctypes.c_int)]
             L.gemm_f16_nt_splitk_plan.restype = i32
             L.gemm_f16_nt_splitk_plan.argtypes = [i64, i64, i64, i32, i64p, i64p]
+            L.gemm_f16_nt_ksplit_plan.restype = i32
+            L.gemm_f16_nt_ksplit_plan.argtypes = [i32, i64, i64, i64, i32] + [ctypes.POINTER(ctypes.c_int)] * 3
             L.gemm_f16_nt_handoff_plan.restype = i32
             L.gemm_f16_nt_handoff_plan.argtypes = [i32, i32, i32, i64, ctypes.POINTER(ctypes.c_uint32),
                                                    ctypes.POINTER(ctypes.c_uint32)]
@@ -139,7 +142,7 @@ def gemm_f16_nt(A, B, D=None):
 
 
 def gemm_f16_nt_rung(rung: int, A, B, D=None):
-    """The same product on one rung of the kernel ladder (1-5, 8-12)."""
+    """The same product on one rung of the kernel ladder (1-5, 8-13)."""
     M, N, K, D = _operands(A, B, D)
     st = lib().gemm_f16_nt_rung(int(rung), M, N, K, A.data_ptr(), B.data_ptr(), D.data_ptr(), _stream(A))
     if st != OK:
@@ -256,6 +259,19 @@ def splitk_plan(M: int, N: int, K: int, cus: int):
     if st != OK:
         raise GemmError(st, "gemm_f16_nt_splitk_plan")
     return m_top.value, splits.value
+
+
+def ksplit_plan(rung: int, M: int, N: int, K: int, cus: int):
+    """(mt, nf, db): the workgroup tile rung 12 or 13 launches for an
+    M x N x K product on a device with `cus` compute units (host
+    evaluation): 16*mt rows of the side with fewer rows, 16*nf of the
+    other, db load groups in flight per wave."""
+    mt, nf, db = ctypes.c_int(), ctypes.c_int(), ctypes.c_int()
+    st = lib().gemm_f16_nt_ksplit_plan(int(rung), int(M), int(N), int(K), int(cus), ctypes.byref(mt),
+                                       ctypes.byref(nf), ctypes.byref(db))
+    if st != OK:
+        raise GemmError(st, "gemm_f16_nt_ksplit_plan")
+    return mt.value, nf.value, db.value
 
 
 def splitk_workspace_bytes(M: int, N: int, K: int, splits: int = 0) -> int:

@@ -157,7 +157,7 @@ bool fast_operands(int64_t K, int64_t lda, int64_t ldb, int64_t sa, int64_t sb, 
 // Rung numbers the library implements (6 and 7 are no longer used).
 bool known_rung(int rung)
 {
-    return rung >= 0 && rung <= GEMM_F16_NT_R12_SKINNY && rung != 6 && rung != 7;
+    return rung >= 0 && rung <= GEMM_F16_NT_R13_KSPLIT && rung != 6 && rung != 7;
 }
 
 // Shapes of rung 12: one side of at most 96 rows, K >= 8 (the chunk that
@@ -181,6 +181,69 @@ bool skinny_pays(int64_t M, int64_t N, int64_t K, int64_t batch)
     if (batch != 1 || !skinny_shape(M, N, K)) return false;
     const int64_t small = M < N ? M : N, large = M < N ? N : M;
     return small <= 32 || (small <= 64 && large <= 16384) || large <= 12288;
+}
+
+// Shapes of rung 13: K >= 8 (as rung 12), and tile counts within a 1-D
+// grid for its smallest tile (16 x 16).
+bool ksplit_shape(int64_t M, int64_t N, int64_t K)
+{
+    return K >= 8 && ((M + 15) / 16) * ((N + 15) / 16) <= (int64_t(1) << 31) - 1;
+}
+
+// Models, in microseconds on MI355X, of the ring kernels and of rung 13 on
+// shapes whose 128- and 256-row tiles number fewer than the compute units
+// (the case rung 13 is for; elsewhere the ring's model is optimistic, which
+// keeps rung 13 away).  The ring: the better of 128 x 128 tiles (R9, ~0.40
+// us per 64-wide k step of a round of tiles when few compute units are
+// busy, 1.4x in its bounds-checked form for M, N not multiples of 128 or K
+// of 64: 200 x 1024 x 8192 70.4 us against 49.6 at 128 rows) and 256 x 256
+// ones (~1.1 us), plus ~2 us, 1.5x with register-staged loads (K % 8 !=
+// 0), and at least its compulsory bytes at ~6 TB/s.
+// Rung 13: skinny::ksplit_tile's model, and at least its bytes from HBM at
+// ~6 TB/s, where the larger side is read once per round of workgroups (the
+// tile rows of the smaller side that run together share its blocks in the
+// caches), at most once per tile row, unless it fits the last-level cache
+// (taken as 128 MiB).
+constexpr double kRingStepUs128 = 0.40, kRingEdge128 = 1.4, kRingStepUs256 = 1.1, kRingFixedUs = 2.0;
+constexpr double kHbmBytesPerUs = 6.0e6;
+constexpr int64_t kCachedSideBytes = int64_t(128) << 20;
+// rung 13 runs where its model is at most this fraction of the ring's
+// (measured on 75 shapes: every shape below it ran 1.2-4.9x faster on
+// rung 13; the one at 0.84 ran 1.2x slower)
+constexpr double kKsplitGain = 0.80;
+
+double ring_model_us(int64_t M, int64_t N, int64_t K, int cus)
+{
+    const int64_t kt = (K + 63) / 64;
+    auto rounds = [&](int64_t t) { return (((M + t - 1) / t) * ((N + t - 1) / t) + cus - 1) / cus; };
+    const bool edge = M % 128 || N % 128 || K % 64;
+    const double r128 = (double)rounds(128) * (double)kt * kRingStepUs128 * (edge ? kRingEdge128 : 1.0);
+    const double r256 = (double)rounds(256) * (double)kt * kRingStepUs256;
+    double t = (r128 < r256 ? r128 : r256) * (K % 8 != 0 ? 1.5 : 1.0) + kRingFixedUs;
+    const double hbm = (double)((M + N) * K * 2) / kHbmBytesPerUs;
+    return t > hbm ? t : hbm;
+}
+
+double ksplit_model_us(int64_t M, int64_t N, int64_t K, int cus, skinny::Tile* tile)
+{
+    const int64_t s_rows = M <= N ? M : N, l_rows = M <= N ? N : M;
+    double t = 0;
+    const skinny::Tile tl = skinny::ksplit_tile(s_rows, l_rows, K, cus, &t);
+    const int64_t s_tiles = (s_rows + 16 * tl.mt - 1) / (16 * tl.mt);
+    const int64_t rounds = (s_tiles * ((l_rows + 16 * tl.nf - 1) / (16 * tl.nf)) + cus - 1) / cus;
+    const int64_t l_bytes = l_rows * K * 2;
+    const int64_t l_reads = l_bytes <= kCachedSideBytes ? 1 : (rounds < s_tiles ? rounds : s_tiles);
+    const double hbm = (double)(l_bytes * l_reads + s_rows * K * 2) / kHbmBytesPerUs;
+    if (tile) *tile = tl;
+    return t > hbm ? t : hbm;
+}
+
+// Where the library's choice takes rung 13: single products not taken by
+// rung 12 whose model beats the ring's by kKsplitGain.
+bool ksplit_pays(int64_t M, int64_t N, int64_t K, int64_t batch, int cus)
+{
+    if (batch != 1 || !ksplit_shape(M, N, K) || skinny_pays(M, N, K, 1) || M == 0 || N == 0) return false;
+    return ksplit_model_us(M, N, K, cus, nullptr) <= kKsplitGain * ring_model_us(M, N, K, cus);
 }
 
 // Shapes of the 384 x 256 ring (rung 11): one tile row and column at least
@@ -207,7 +270,7 @@ int validate(int rung, int64_t M, int64_t N, int64_t K, const void* A, const voi
     // rows; R4's and R9's register-staged forms need K >= 8
     const bool general_ok = rung == 0 || rung == GEMM_F16_NT_R3_GRID ||
                             ((rung == GEMM_F16_NT_R4_RING || rung == GEMM_F16_NT_R9_RING_SMALL ||
-                              rung == GEMM_F16_NT_R12_SKINNY) &&
+                              rung == GEMM_F16_NT_R12_SKINNY || rung == GEMM_F16_NT_R13_KSPLIT) &&
                              K >= 8);
     if (K % 8 != 0 && !general_ok) return GEMM_F16_NT_UNSUPPORTED;
     if (rung == GEMM_F16_NT_R1_SINGLE_TILE && !(M == 128 && N == 128 && K == 64)) return GEMM_F16_NT_UNSUPPORTED;
@@ -219,6 +282,7 @@ int validate(int rung, int64_t M, int64_t N, int64_t K, const void* A, const voi
         return GEMM_F16_NT_UNSUPPORTED;
     if (rung == GEMM_F16_NT_R11_WIDE && !wide_shape(M, N, K, N)) return GEMM_F16_NT_UNSUPPORTED;
     if (rung == GEMM_F16_NT_R12_SKINNY && !skinny_shape(M, N, K)) return GEMM_F16_NT_UNSUPPORTED;
+    if (rung == GEMM_F16_NT_R13_KSPLIT && !ksplit_shape(M, N, K)) return GEMM_F16_NT_UNSUPPORTED;
     if (!any_out) return GEMM_F16_NT_OK;
     // fp16 elements are 2-byte aligned; the fast kernels need 16 bytes
     if ((K > 0 && (((uintptr_t)A & 1) || ((uintptr_t)B & 1))) || ((uintptr_t)D & 1)) return GEMM_F16_NT_UNSUPPORTED;
@@ -606,6 +670,35 @@ bool hybrid_plan(int64_t M, int64_t N, int64_t K, int cus, int64_t* m_top, int64
     return true;
 }
 
+// Modeled time (us) of a split-K call with `splits` slices, in the units of
+// hybrid_plan (one four-wave k step of a round of tiles, ~1.1 us when few
+// compute units are busy).
+double splitk_model_us(int64_t M, int64_t N, int64_t K, int64_t splits, int cus)
+{
+    int64_t k_chunk = 0, n_slices = 0;
+    split_plan(K, splits, &k_chunk, &n_slices);
+    const int64_t tiles = ((M + kFastTile - 1) / kFastTile) * ((N + kFastTile - 1) / kFastTile);
+    const double rounds = (double)((tiles * n_slices + cus - 1) / cus);
+    const double bytes = (2.0 * (double)n_slices + 0.5) * (double)M * (double)N * 4.0;
+    return (rounds * (double)(k_chunk / RingCfg::BK) * kSplitSlowdown + bytes / kBytesPerStepTime + kSplitFixedSteps) *
+           kRingStepUs256;
+}
+
+// The split-K entry's slice count for splits = 0: choose_splits, unless the
+// product is one the plain entry runs on rung 13 and rung 13's model beats
+// the slices' (measured on MI355X: 256 x 1024 x 8192 14.1 us on rung 13
+// against 25.2 in 32 slices, 128 x 1024 x 8192 10.2 against 22.7; with K
+// long against a small output, e.g. 256 x 256 x 65536, the slices' 256 x 256
+// tiles win).
+int64_t plan_splits(int64_t M, int64_t N, int64_t K, int cus)
+{
+    const int64_t s = choose_splits(M, N, K, cus);
+    if (s > 1 && ksplit_pays(M, N, K, 1, cus) &&
+        ksplit_model_us(M, N, K, cus, nullptr) <= splitk_model_us(M, N, K, s, cus))
+        return 1;
+    return s;
+}
+
 int launch_splitk(int64_t M, int64_t N, int64_t K, const void* A, const void* B, void* D, int64_t splits,
                   float* P, hipStream_t s)
 {
@@ -668,45 +761,60 @@ int launch_r3_any(const GemmArgs& g, hipStream_t s)
 // R4 (256 x 256 tiles) or R9 (128 x 128, `small`) on general operands: the
 // pipelined ring with its loads staged through registers, which take rows
 // on any 2-byte boundary.  Needs K >= 8.
-template <int MT, int NF, bool TRANS>
+template <int MT, int NF, int DB, bool TRANS>
 void launch_skinny_t(const skinny::Args& a, int64_t grid, hipStream_t s)
 {
-    hipLaunchKernelGGL((skinny::skinny_kernel<MT, NF, TRANS>), dim3((unsigned)grid), dim3(64 * skinny::kWaves), 0,
+    hipLaunchKernelGGL((skinny::skinny_kernel<MT, NF, DB, TRANS>), dim3((unsigned)grid), dim3(64 * skinny::kWaves), 0,
                        s, a);
 }
 
+// The instantiated tiles: rung 12's (skinny::skinny_tile: mt = 1..6 blocks
+// of S, 1 or 2 of L) and rung 13's (skinny::kTiles13).
 template <bool TRANS>
-int launch_skinny_nf(const skinny::Args& a, int mt, int nf, hipStream_t s)
+int launch_skinny_tile(const skinny::Args& a, const skinny::Tile& t, int64_t grid, hipStream_t s)
 {
-    const int64_t grid = (a.l_rows + 16 * nf - 1) / (16 * nf);
-    switch (mt * 8 + nf) {
-    case 9: launch_skinny_t<1, 1, TRANS>(a, grid, s); break;
-    case 10: launch_skinny_t<1, 2, TRANS>(a, grid, s); break;
-    case 17: launch_skinny_t<2, 1, TRANS>(a, grid, s); break;
-    case 18: launch_skinny_t<2, 2, TRANS>(a, grid, s); break;
-    case 25: launch_skinny_t<3, 1, TRANS>(a, grid, s); break;
-    case 26: launch_skinny_t<3, 2, TRANS>(a, grid, s); break;
-    case 33: launch_skinny_t<4, 1, TRANS>(a, grid, s); break;
-    case 34: launch_skinny_t<4, 2, TRANS>(a, grid, s); break;
-    case 41: launch_skinny_t<5, 1, TRANS>(a, grid, s); break;
-    case 42: launch_skinny_t<5, 2, TRANS>(a, grid, s); break;
-    case 49: launch_skinny_t<6, 1, TRANS>(a, grid, s); break;
-    case 50: launch_skinny_t<6, 2, TRANS>(a, grid, s); break;
+    switch (t.mt * 100 + t.nf * 10 + t.db) {
+    case 112: launch_skinny_t<1, 1, 2, TRANS>(a, grid, s); break;
+    case 121: launch_skinny_t<1, 2, 1, TRANS>(a, grid, s); break;
+    case 122: launch_skinny_t<1, 2, 2, TRANS>(a, grid, s); break;
+    case 211: launch_skinny_t<2, 1, 1, TRANS>(a, grid, s); break;
+    case 221: launch_skinny_t<2, 2, 1, TRANS>(a, grid, s); break;
+    case 241: launch_skinny_t<2, 4, 1, TRANS>(a, grid, s); break;
+    case 311: launch_skinny_t<3, 1, 1, TRANS>(a, grid, s); break;
+    case 321: launch_skinny_t<3, 2, 1, TRANS>(a, grid, s); break;
+    case 341: launch_skinny_t<3, 4, 1, TRANS>(a, grid, s); break;
+    case 411: launch_skinny_t<4, 1, 1, TRANS>(a, grid, s); break;
+    case 421: launch_skinny_t<4, 2, 1, TRANS>(a, grid, s); break;
+    case 511: launch_skinny_t<5, 1, 1, TRANS>(a, grid, s); break;
+    case 521: launch_skinny_t<5, 2, 1, TRANS>(a, grid, s); break;
+    case 611: launch_skinny_t<6, 1, 1, TRANS>(a, grid, s); break;
+    case 621: launch_skinny_t<6, 2, 1, TRANS>(a, grid, s); break;
     default: return GEMM_F16_NT_UNSUPPORTED;
     }
     return launched();
 }
 
-// Rung 12 on one product (batch 1): the side with at most 96 rows is the
-// small side (A when both qualify and M <= N), the other gets one
-// workgroup per 16 * NF rows.
-int launch_skinny(const GemmArgs& g, hipStream_t s)
+// The workgroup tile rung 12 or 13 takes for a product (S = the side with
+// fewer rows, A on a tie).
+skinny::Tile ksplit_tile_for(int rung, int64_t M, int64_t N, int64_t K, int cus)
 {
-    if (g.batch != 1 || !skinny_shape(g.M, g.N, g.K)) return GEMM_F16_NT_UNSUPPORTED;
+    const int64_t s_rows = M <= N ? M : N, l_rows = M <= N ? N : M;
+    if (rung == GEMM_F16_NT_R12_SKINNY) return skinny::skinny_tile(s_rows, l_rows, K, cus);
+    return skinny::ksplit_tile(s_rows, l_rows, K, cus, nullptr);
+}
+
+// Rungs 12 and 13 on one product (batch 1): the side with fewer rows is S
+// (A on a tie); rung 12 puts all of it in every workgroup (one row of
+// tiles), rung 13 tiles it too.
+int launch_skinny(const GemmArgs& g, hipStream_t s, int rung = GEMM_F16_NT_R12_SKINNY)
+{
+    if (g.batch != 1) return GEMM_F16_NT_UNSUPPORTED;
+    if (rung == GEMM_F16_NT_R12_SKINNY ? !skinny_shape(g.M, g.N, g.K) : !ksplit_shape(g.M, g.N, g.K))
+        return GEMM_F16_NT_UNSUPPORTED;
     int cus = 0;
     const int st = device_info(&cus);
     if (st != GEMM_F16_NT_OK) return st;
-    const bool trans = !(g.M <= skinny::kMaxSmall && (g.M <= g.N || g.N > skinny::kMaxSmall));
+    const bool trans = g.N < g.M;
     skinny::Args a;
     a.S = trans ? g.B : g.A;
     a.ld_s = trans ? g.ldb : g.lda;
@@ -717,8 +825,12 @@ int launch_skinny(const GemmArgs& g, hipStream_t s)
     a.K = g.K;
     a.D = g.D;
     a.ldd = g.ldd;
-    const int mt = (int)((a.s_rows + 15) / 16), nf = skinny::choose_nf(a.l_rows, cus);
-    return trans ? launch_skinny_nf<true>(a, mt, nf, s) : launch_skinny_nf<false>(a, mt, nf, s);
+    const skinny::Tile t = ksplit_tile_for(rung, g.M, g.N, g.K, cus);
+    const int64_t l_tiles = (a.l_rows + 16 * t.nf - 1) / (16 * t.nf);
+    const int64_t grid = l_tiles * ((a.s_rows + 16 * t.mt - 1) / (16 * t.mt));
+    if (grid > (int64_t(1) << 31) - 1) return GEMM_F16_NT_UNSUPPORTED;
+    a.l_tiles = (uint32_t)l_tiles;
+    return trans ? launch_skinny_tile<true>(a, t, grid, s) : launch_skinny_tile<false>(a, t, grid, s);
 }
 
 int launch_staged(const GemmArgs& g0, hipStream_t s, bool small)
@@ -822,8 +934,12 @@ int run(int rung, int64_t M, int64_t N, int64_t K, const void* A, const void* B,
         return launch_wide(contiguous_args(M, N, K, A, B, D), s);
     case GEMM_F16_NT_R12_SKINNY:
         return launch_skinny(contiguous_args(M, N, K, A, B, D), s);
+    case GEMM_F16_NT_R13_KSPLIT:
+        return launch_skinny(contiguous_args(M, N, K, A, B, D), s, GEMM_F16_NT_R13_KSPLIT);
     default:  // 0: the library's choice
         if (skinny_pays(M, N, K, 1)) return launch_skinny(contiguous_args(M, N, K, A, B, D), s);
+        if (ksplit_pays(M, N, K, 1, cus))
+            return launch_skinny(contiguous_args(M, N, K, A, B, D), s, GEMM_F16_NT_R13_KSPLIT);
         if (!fast_operands(K, K, K, 0, 0, A, B, D)) return launch_any(contiguous_args(M, N, K, A, B, D), s);
         return launch_ring(contiguous_args(M, N, K, A, B, D), s, kDefaultRing4);
     }
@@ -887,10 +1003,11 @@ int splitk_run(int64_t M, int64_t N, int64_t K, const void* A, const void* B, vo
     const auto unsplit = [&]() {
         const GemmArgs g = contiguous_args(M, N, K, A, B, D);
         if (skinny_pays(M, N, K, 1)) return launch_skinny(g, s);
+        if (ksplit_pays(M, N, K, 1, cus)) return launch_skinny(g, s, GEMM_F16_NT_R13_KSPLIT);
         return fast_operands(K, K, K, 0, 0, A, B, D) ? launch_ring(g, s, kDefaultRing4) : launch_any(g, s);
     };
     if (!fast_operands(K, K, K, 0, 0, A, B, D)) return unsplit();
-    int64_t want = splits == 0 ? choose_splits(M, N, K, cus) : splits, m_top = 0;
+    int64_t want = splits == 0 ? plan_splits(M, N, K, cus) : splits, m_top = 0;
     if (splits == 0 && want <= 1 && !hybrid_plan(M, N, K, cus, &m_top, &want)) m_top = 0;
     int64_t k_chunk = 0, n_slices = 1;
     if (want > 1) split_plan(K, want, &k_chunk, &n_slices);
@@ -973,6 +1090,7 @@ int gemm_f16_nt_strided_batched(int64_t M, int64_t N, int64_t K, const void* A, 
     g.sd = stride_d;
     g.batch = batch;
     if (skinny_pays(M, N, K, batch)) return launch_skinny(g, s);
+    if (ksplit_pays(M, N, K, batch, cus)) return launch_skinny(g, s, GEMM_F16_NT_R13_KSPLIT);
     if (!fast_operands(K, lda, ldb, stride_a, stride_b, A, B, D)) return launch_any(g, s);
     return launch_ring(g, s, kDefaultRing4);
 }
@@ -984,7 +1102,7 @@ int64_t gemm_f16_nt_splitk_workspace(int64_t M, int64_t N, int64_t K, int splits
     if (s == 0) {
         int cus = 0;
         if (device_info(&cus) != GEMM_F16_NT_OK) return GEMM_F16_NT_DEVICE;
-        s = choose_splits(M, N, K, cus);
+        s = plan_splits(M, N, K, cus);
         if (s <= 1 && !hybrid_plan(M, N, K, cus, &m_top, &s)) m_top = 0;
     }
     if (s <= 1 || K == 0 || K % 8 != 0) return 0;
@@ -1116,6 +1234,10 @@ int gemm_f16_nt_plan(int64_t M, int64_t N, int64_t K, int cus, int* rung_top, in
         *rung_top = GEMM_F16_NT_R12_SKINNY;
         return GEMM_F16_NT_OK;
     }
+    if (ksplit_pays(M, N, K, 1, cus)) {
+        *rung_top = GEMM_F16_NT_R13_KSPLIT;
+        return GEMM_F16_NT_OK;
+    }
     const int64_t tiles = ((M + kFastTile - 1) / kFastTile) * ((N + kFastTile - 1) / kFastTile);
     if (K % 8 != 0) {   // R3's general form, or R9's / R4's register-staged form
         const bool small = tiles * 10 <= (int64_t)cus * kSmallTilesPer10Cus || small_tiles_pay(M, N, 1, cus);
@@ -1144,11 +1266,25 @@ int gemm_f16_nt_splitk_plan(int64_t M, int64_t N, int64_t K, int cus, int64_t* m
 {
     if (M < 0 || N < 0 || K < 0 || cus < 1 || m_top == nullptr || splits == nullptr) return GEMM_F16_NT_INVALID_ARG;
     *m_top = 0;
-    *splits = choose_splits(M, N, K, cus);
+    *splits = plan_splits(M, N, K, cus);
     if (*splits <= 1 && !hybrid_plan(M, N, K, cus, m_top, splits)) {
         *m_top = 0;
         *splits = 1;
     }
+    return GEMM_F16_NT_OK;
+}
+
+int gemm_f16_nt_ksplit_plan(int rung, int64_t M, int64_t N, int64_t K, int cus, int* mt, int* nf, int* db)
+{
+    if ((rung != GEMM_F16_NT_R12_SKINNY && rung != GEMM_F16_NT_R13_KSPLIT) || M < 1 || N < 1 || K < 0 || cus < 1 ||
+        mt == nullptr || nf == nullptr || db == nullptr)
+        return GEMM_F16_NT_INVALID_ARG;
+    if (rung == GEMM_F16_NT_R12_SKINNY ? !skinny_shape(M, N, K) : !ksplit_shape(M, N, K))
+        return GEMM_F16_NT_UNSUPPORTED;
+    const skinny::Tile t = ksplit_tile_for(rung, M, N, K, cus);
+    *mt = t.mt;
+    *nf = t.nf;
+    *db = t.db;
     return GEMM_F16_NT_OK;
 }
 

@@ -1,17 +1,20 @@
-// Rung 12: products with one side of at most 96 rows (M <= 96 or N <= 96),
-// the tile-starved shapes of small-batch inference (e.g. 16 x 4096 x 14336).
+// Rungs 12 and 13: K split among a workgroup's waves on small output tiles.
 //
-// Tiles of 128 or 256 rows leave most of such a tile empty and, with few
+// Rung 12 takes products with one side of at most 96 rows (M <= 96 or
+// N <= 96), the tile-starved shapes of small-batch inference (e.g. 16 x
+// 4096 x 14336); rung 13 takes products whose 128- and 256-row tiles would
+// leave most compute units idle for a long K (e.g. 256 x 1024 x 8192).
+// Tiles of 128 or 256 rows leave most of such a tile empty or, with few
 // tiles, most compute units idle, each of the few busy ones walking all of
-// K.  Here every workgroup owns 16 * NF rows of the large side ("L") and
-// all rows of the small side ("S", 16 * MT rows, MT <= 6), so the large
-// side alone sets the workgroup count, and its 8 waves split K between
-// them: wave w contracts a contiguous range of 32-wide k chunks, and the
-// waves' fp32 partial sums are added through LDS in wave order before the
-// one fp16 rounding ("GEMM I - the tiled baseline", the problem statement;
-// K split inside one workgroup, so no workspace and no second launch, in
-// the spirit of the persistent scheduler of "TIRx GEMM detailed technical
-// notes", V6, that keeps every compute unit on work).
+// K.  Here every workgroup owns a small tile of the output: 16 * MT rows
+// of the smaller side ("S") and 16 * NF rows of the larger side ("L"), all
+// of S on rung 12 (MT <= 6), a 2-D grid of tiles on rung 13.  Its 8 waves
+// split K between them: wave w contracts a contiguous range of 32-wide k
+// chunks, and the waves' fp32 partial sums are added through LDS in wave
+// order before the one fp16 rounding ("GEMM I - the tiled baseline", the
+// problem statement; K split inside one workgroup, so no workspace and no
+// second launch, in the spirit of the persistent scheduler of "TIRx GEMM
+// detailed technical notes", V6, that keeps every compute unit on work).
 //
 // Loads: each 32-wide k chunk of a 16-row block is one MFMA fragment per
 // lane (lane l: row l % 16, k elements 8 * (l / 16) .. + 7 of the chunk:
@@ -22,16 +25,19 @@
 // bytes (lane l: row 4u + l / 16, k elements 8 * (l % 16) .. + 7 of the
 // 128), writes them into its own 4 KiB of LDS (16-byte slots XOR-swizzled
 // by row, so neither the writes nor the reads conflict) and reads them back
-// as fragments.  No barrier: only the wave itself reads its buffer.  Rows
-// on any 2-byte boundary (gfx950's global loads take unaligned addresses).
-// The rest of a wave's range after its whole 4-chunk groups, including the
-// chunk that crosses K, is read as fragments directly: the crossing chunk
-// as the row's last 8 elements, shifted (load_row_chunk, chunk_shift);
-// this needs K >= 8.  Rows past the operand are read as its last row and
-// their outputs are not stored.  The output block layout: lane l holds
-// (small row 4 * (l / 16) + r, large row l % 16), r = 0..3.  Each output's
-// sum runs in a fixed order (k chunks in order within a wave, then waves
-// 0..7), so results repeat bit for bit.
+// as fragments.  No barrier: only the wave itself reads its buffer.  The
+// loads are latency-bound (each wave waits for its group before using it),
+// so with DB = 2 a wave keeps two groups in flight: the next group's loads
+// go out before the current group is used (registers allow it for up to 4
+// blocks).  Rows on any 2-byte boundary (gfx950's global loads take
+// unaligned addresses).  The rest of a wave's range after its whole
+// 4-chunk groups, including the chunk that crosses K, is read as fragments
+// directly: the crossing chunk as the row's last 8 elements, shifted
+// (load_row_chunk, chunk_shift); this needs K >= 8.  Rows past the operand
+// are read as its last row and their outputs are not stored.  The output
+// block layout: lane l holds (S row 4 * (l / 16) + r, L row l % 16), r =
+// 0..3.  Each output's sum runs in a fixed order (k chunks in order within
+// a wave, then waves 0..7), so results repeat bit for bit, whatever DB.
 #pragma once
 
 #include "common.hpp"
@@ -41,28 +47,40 @@ namespace g16 {
 namespace skinny {
 
 constexpr int kWaves = 8;
-constexpr int kMaxSmall = 96;   // rows of the small side: 16 * MT, MT <= 6 (more spills registers)
+constexpr int kMaxSmall = 96;   // rung 12: all of S in one workgroup, 16 * MT rows, MT <= 6 (more spills registers)
 
 struct Args {
-    const f16* S;   // small side: s_rows x K, row pitch ld_s
-    const f16* L;   // large side: l_rows x K, row pitch ld_l
+    const f16* S;   // smaller side: s_rows x K, row pitch ld_s
+    const f16* L;   // larger side: l_rows x K, row pitch ld_l
     f16* D;
     int64_t ld_s, s_rows, ld_l, l_rows, K, ldd;
+    uint32_t l_tiles;   // workgroups along L; workgroup b takes L tile b % l_tiles, S tile b / l_tiles
 };
 
+// LDS of one workgroup: the waves' 4 KiB transposition buffers during the
+// k loop, then (after a barrier) the waves' partial sums.
+template <int MT, int NF>
+constexpr int lds_bytes()
+{
+    constexpr int red = kWaves * MT * NF * 64 * 16, tb = kWaves * 4096;
+    return red > tb ? red : tb;
+}
+
 // TRANS = false: S is A (D[s][l]); TRANS = true: S is B (D[l][s]).
-template <int MT, int NF, bool TRANS>
+// DB: 4-chunk groups in flight per wave (1 or 2).
+template <int MT, int NF, int DB, bool TRANS>
 __global__ __launch_bounds__(64 * kWaves) void skinny_kernel(const Args g)
 {
+    static_assert(DB == 1 || DB == 2, "one or two groups in flight");
     constexpr int NB = MT + NF;   // 16-row blocks: MT of S, then NF of L
-    __shared__ f32x4 red[kWaves][MT * NF][64];
-    __shared__ __attribute__((aligned(16))) char tbuf[kWaves][4096];
+    __shared__ __attribute__((aligned(16))) char smem[lds_bytes<MT, NF>()];
     const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int r16 = lane & 15, kq = lane >> 4;
-    const int64_t j0 = (int64_t)blockIdx.x * 16 * NF;
+    const uint32_t ty = blockIdx.x / g.l_tiles, tx = blockIdx.x - ty * g.l_tiles;
+    const int64_t i0 = (int64_t)ty * 16 * MT, j0 = (int64_t)tx * 16 * NF;
     auto row_ptr = [&](int b, int r) -> const char* {
         if (b < MT) {
-            const int64_t rr = 16 * b + r;
+            const int64_t rr = i0 + 16 * b + r;
             return reinterpret_cast<const char*>(g.S + (rr < g.s_rows ? rr : g.s_rows - 1) * g.ld_s);
         }
         const int64_t rr = j0 + 16 * (b - MT) + r;
@@ -97,7 +115,7 @@ __global__ __launch_bounds__(64 * kWaves) void skinny_kernel(const Args g)
     };
     // LDS slots: the write of (row 4u + kq, 8-element group r16) and the
     // read of (row r16, group 4u + kq), 16-byte slots XOR-swizzled by row
-    char* tb = tbuf[w];
+    char* tb = smem + w * 4096;
     uint32_t wo[4], ro[4];
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
@@ -106,14 +124,14 @@ __global__ __launch_bounds__(64 * kWaves) void skinny_kernel(const Args g)
         ro[u] = (uint32_t)(r16 * 256 + ((kg ^ r16) & 15) * 16);
     }
     typedef uint32_t u32x4_a2 __attribute__((ext_vector_type(4), aligned(2)));
-    int64_t c = c0;
-    for (int64_t gi = 0; gi < groups; ++gi, c += 4) {
+    auto load_group = [&](u32x4 (&v)[NB][4], int64_t c) {
         const int64_t kb = (c * 32 + 8 * r16) * 2;
-        u32x4 v[NB][4];
 #pragma unroll
         for (int b = 0; b < NB; ++b)
 #pragma unroll
             for (int u = 0; u < 4; ++u) v[b][u] = *(const G16_GLOBAL u32x4_a2*)(gptr[b][u] + kb);
+    };
+    auto use_group = [&](const u32x4 (&v)[NB][4]) {
         u32x4 fr[4][NB];
 #pragma unroll
         for (int b = 0; b < NB; ++b) {
@@ -124,6 +142,35 @@ __global__ __launch_bounds__(64 * kWaves) void skinny_kernel(const Args g)
         }
 #pragma unroll
         for (int u = 0; u < 4; ++u) mma(fr[u]);
+    };
+    int64_t c = c0;
+    if constexpr (DB == 1) {
+        for (int64_t gi = 0; gi < groups; ++gi, c += 4) {
+            u32x4 v[NB][4];
+            load_group(v, c);
+            use_group(v);
+        }
+    } else {
+        // two register sets; the steady loop has no branch inside, so the
+        // wait before each use covers only the group being used
+        u32x4 v0[NB][4], v1[NB][4];
+        int64_t gi = 0;
+        if (groups > 0) load_group(v0, c);
+        for (; gi + 2 < groups; gi += 2, c += 8) {
+            load_group(v1, c + 4);
+            use_group(v0);
+            load_group(v0, c + 8);
+            use_group(v1);
+        }
+        if (gi + 1 < groups) {
+            load_group(v1, c + 4);
+            use_group(v0);
+            use_group(v1);
+            c += 8;
+        } else if (gi < groups) {
+            use_group(v0);
+            c += 4;
+        }
     }
     for (; c < c1; ++c) {
         const int kk = (int)(c * 32 + 8 * kq);
@@ -132,20 +179,23 @@ __global__ __launch_bounds__(64 * kWaves) void skinny_kernel(const Args g)
         for (int b = 0; b < NB; ++b) fv[b] = chunk_shift(load_row_chunk(fptr[b], kk, (int)K, true), kk, (int)K);
         mma(fv);
     }
-    // the waves' partial sums, added in wave order, rounded once
+    // the waves' partial sums (in the LDS the buffers used, once every wave
+    // is done with its buffer), added in wave order, rounded once
+    f32x4* red = reinterpret_cast<f32x4*>(smem);
+    __syncthreads();
 #pragma unroll
     for (int t = 0; t < MT; ++t)
 #pragma unroll
-        for (int f = 0; f < NF; ++f) red[w][t * NF + f][lane] = acc[t][f];
+        for (int f = 0; f < NF; ++f) red[(w * MT * NF + t * NF + f) * 64 + lane] = acc[t][f];
     __syncthreads();
     for (int b = w; b < MT * NF; b += kWaves) {
-        f32x4 sum = red[0][b][lane];
+        f32x4 sum = red[b * 64 + lane];
 #pragma unroll
-        for (int v = 1; v < kWaves; ++v) sum += red[v][b][lane];
+        for (int v = 1; v < kWaves; ++v) sum += red[(v * MT * NF + b) * 64 + lane];
         const int t = b / NF, f = b % NF;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            const int64_t si = 16 * t + 4 * kq + r, lj = j0 + 16 * f + r16;
+            const int64_t si = i0 + 16 * t + 4 * kq + r, lj = j0 + 16 * f + r16;
             if (si < g.s_rows && lj < g.l_rows) {
                 if (TRANS)
                     g.D[lj * g.ldd + si] = (f16)sum[r];
@@ -156,12 +206,67 @@ __global__ __launch_bounds__(64 * kWaves) void skinny_kernel(const Args g)
     }
 }
 
-// Large-side rows per workgroup: 32 when that still gives every compute
-// unit a workgroup, else 16 (measured on MI355X: 64 x 8192 x 8192 28.5 us
-// with 32 rows against 35.4 with 16; 64 x 4096 x 4096 13.2 against 11.9).
-inline int choose_nf(int64_t l_rows, int cus)
+// A workgroup tile: 16 * mt rows of S and 16 * nf rows of L, db groups in flight.
+struct Tile {
+    int mt, nf, db;
+};
+
+// Rung 12's tile: all of S (mt = ceil(S / 16)) and 16 or 32 rows of L.
+// 32 L rows ("wide") need every compute unit to get a workgroup; measured
+// on MI355X (16 or 32 rows of S, L of 4096-28672 rows, K of 4096-28672)
+// they pay from K = 14336 for up to 32 rows of S (16 x 8192 x 28672: 79.9
+// us against 87.3 with 16 rows, 32 x 14336 x 14336: 87.7 against 103.3)
+// and lose below it (16 x 14336 x 8192: 38.1 against 34.9), and from 48
+// rows of S they pay at any K (64 x 8192 x 8192 28.5 against 35.4).  With
+// 16 rows of S and one L block a wave keeps two groups in flight (16 x
+// 4096 x 14336 24.3 -> 19.1 us, 16 x 14336 x 4096 22.9 -> 18.8); other
+// tiles gain nothing from it.
+constexpr int64_t kWideMinK = 12288;
+
+inline Tile skinny_tile(int64_t s_rows, int64_t l_rows, int64_t K, int cus)
 {
-    return (l_rows + 31) / 32 >= (int64_t)cus ? 2 : 1;
+    const int mt = (int)((s_rows + 15) / 16);
+    const bool wide = (l_rows + 31) / 32 >= (int64_t)cus;
+    if (mt <= 2) {
+        if (wide && K >= kWideMinK) return Tile{mt, 2, 1};
+        return Tile{mt, 1, mt == 1 ? 2 : 1};
+    }
+    return Tile{mt, wide ? 2 : 1, 1};
+}
+
+// Rung 13's tiles, and a model of their time in microseconds: a workgroup
+// streams (mt + nf) 16-row blocks of K elements at ~75 GB/s (one workgroup
+// per compute unit, latency-bound loads), rounds of workgroups over the
+// compute units, plus ~3 us of launch and reduction.  Fitted on MI355X over
+// 75 shapes of 128-2048 x 1024-14336 x 1024-14336 rows: on the 29 of them
+// where these tiles beat the ring kernels, the tile the model picks runs
+// within 2.3% of the best of 16 tiles on average (16% at worst).  (6 x 2
+// blocks, best on a few shapes, never has the smallest model: 3 x 4 has the
+// same workgroup count with fewer blocks.)
+constexpr Tile kTiles13[] = {{1, 1, 2}, {1, 2, 2}, {2, 2, 1}, {2, 4, 1}, {3, 4, 1}};
+constexpr double kBytesPerUsPerCu = 75e3;
+constexpr double kFixedUs = 3.0;
+
+inline double tile_model_us(int64_t s_rows, int64_t l_rows, int64_t K, int cus, const Tile& t)
+{
+    const int64_t wgs = ((l_rows + 16 * t.nf - 1) / (16 * t.nf)) * ((s_rows + 16 * t.mt - 1) / (16 * t.mt));
+    const int64_t rounds = (wgs + cus - 1) / cus;
+    return (double)rounds * (double)(t.mt + t.nf) * 32.0 * (double)K / kBytesPerUsPerCu + kFixedUs;
+}
+
+inline Tile ksplit_tile(int64_t s_rows, int64_t l_rows, int64_t K, int cus, double* model_us)
+{
+    Tile best = kTiles13[0];
+    double bt = tile_model_us(s_rows, l_rows, K, cus, best);
+    for (const Tile& t : kTiles13) {
+        const double v = tile_model_us(s_rows, l_rows, K, cus, t);
+        if (v < bt) {
+            bt = v;
+            best = t;
+        }
+    }
+    if (model_us) *model_us = bt;
+    return best;
 }
 
 }  // namespace skinny

@@ -106,6 +106,11 @@ EXTRA_WORKLOADS = [
     # one side of 16 rows (a small batch against a large weight): rung 12
     # splits K among each workgroup's waves
     ExtraWorkload("skinny_16x4096x14336", "gemm", 1, 16, 4096, 14336, 24, U11),
+    # few output tiles and a long K (128- and 256-row tiles would keep a
+    # sixteenth of the compute units busy): rung 13 splits K among the waves
+    # of many small tiles
+    ExtraWorkload("few_tiles_256x1024x8192", "gemm", 1, 256, 1024, 8192, 25, U11),
+    ExtraWorkload("few_tiles_128x4096x14336", "gemm", 1, 128, 4096, 14336, 26, U11),
     # a small last round of tiles (2.25 rounds on 256 compute units, and a
     # ragged M): whole rounds unsplit, the remaining rows split K
     ExtraWorkload("splitk_rounds_6144x6144x6144", "splitk", 1, 6144, 6144, 6144, 18, U11),

@@ -99,9 +99,17 @@ extern "C" {
                                      workspace); the library's choice for single products whose small
                                      side has at most 32 rows, at most 64 with a large side of at most
                                      16384 rows, or at most 96 with a large side of at most 12288 */
+#define GEMM_F16_NT_R13_KSPLIT 13 /* rung 12's kernel on a 2-D grid of small tiles (16-96 rows of the
+                                     side with fewer rows by 16-64 rows of the other, picked by a
+                                     model of the tile's load time), any M, N >= 1 and K >= 8, rows on
+                                     any 2-byte boundary, no workspace; the library's choice for single
+                                     products that rung 12 does not take and whose 128- and 256-row
+                                     tiles would leave most compute units idle over a long K, where
+                                     that model beats the ring's by a fifth (gemm_f16_nt_plan) */
 
 /* D = A * B^T with the library's choice of kernel for the shape (see
- * gemm_f16_nt_plan; products with one small side run on rung 12).  Some
+ * gemm_f16_nt_plan; products with one small side run on rung 12, and
+ * products with few tiles and a long K on rung 13).  Some
  * shapes take two launches on the stream: when
  * the 256 x 256 tiles leave a small last round, the rows past the whole
  * rounds run on 128 x 128 tiles; when whole rounds of 384 x 256 tiles fit
@@ -243,14 +251,21 @@ int gemm_f16_nt_handoff_plan(int depth, int producers, int consumers, int64_t st
  * [0, *m_top) run on rung *rung_top and rows [*m_top, M) on rung
  * *rung_rest (0 and *m_top = M when one kernel takes every row).  For
  * K % 8 != 0 rungs 4 and 9 stand for their register-staged forms and
- * rung 3 for its general form; rung 12 takes any K >= 8.  Returns 0 or a
- * negative status. */
+ * rung 3 for its general form; rungs 12 and 13 take any K >= 8.  Returns 0
+ * or a negative status. */
 int gemm_f16_nt_plan(int64_t M, int64_t N, int64_t K, int cus, int* rung_top, int64_t* m_top, int* rung_rest);
 /* Host evaluation of gemm_f16_nt_splitk's choice for `splits` = 0 on a
  * device with `cus` compute units, no HIP call: *m_top rows (0 or a
  * multiple of 256) run unsplit, the other M - *m_top rows split K into
  * *splits slices (1: no split).  Returns 0 or a negative status. */
 int gemm_f16_nt_splitk_plan(int64_t M, int64_t N, int64_t K, int cus, int64_t* m_top, int64_t* splits);
+/* Host evaluation of the workgroup tile rung 12 or 13 (`rung`) launches for
+ * an M x N x K product on a device with `cus` compute units, no HIP call:
+ * 16 * *mt rows of the side with fewer rows (A on a tie), 16 * *nf rows of
+ * the other, and *db groups of 128 k elements in flight per wave.  Returns
+ * 0, GEMM_F16_NT_INVALID_ARG (another rung, M or N < 1, null outputs) or
+ * GEMM_F16_NT_UNSUPPORTED (a shape the rung does not take). */
+int gemm_f16_nt_ksplit_plan(int rung, int64_t M, int64_t N, int64_t K, int cus, int* mt, int* nf, int* db);
 
 #ifdef __cplusplus
 }

@@ -76,7 +76,13 @@ A0, B0, D0 = 0x10000, 0x20000000, 0x40000000   # fake, 16-byte aligned, disjoint
     ((0, 64, 10_000_000, 12, A0, B0, D0), g.OK),           # the staged ring's grid is one-dimensional
     ((0, 64, 64, 64, A0, B0, A0 + 4096), g.INVALID_ARG),   # D overlaps A
     ((0, 64, 64, 64, A0, B0, B0), g.INVALID_ARG),          # D overlaps B
-    ((13, 64, 64, 64, A0, B0, D0), g.INVALID_ARG),         # unknown rung
+    ((14, 64, 64, 64, A0, B0, D0), g.INVALID_ARG),         # unknown rung
+    ((13, 64, 64, 64, A0, B0, D0), g.OK),                   # rung 13: any M, N >= 1 ...
+    ((13, 5000, 3000, 4096, A0, B0, D0), g.OK),
+    ((13, 1, 1, 8, A0, B0, D0), g.OK),
+    ((13, 16, 4096, 7, A0, B0, D0), g.UNSUPPORTED),         # ... and K >= 8
+    ((13, 300, 4096, 4095, A0 + 2, B0 + 6, D0 + 2), g.OK),  # ... rows on any 2-byte boundary
+    ((13, 1 << 31, 1 << 31, 64, A0, 1 << 40, 1 << 44), g.UNSUPPORTED),  # 2^46 tiles of 16 x 16
     ((12, 64, 4096, 4096, A0, B0, D0), g.OK),               # rung 12: one side of at most 64 rows
     ((12, 4096, 64, 4096, A0, B0, D0), g.OK),
     ((12, 96, 4096, 4096, A0, B0, D0), g.OK),               # ... up to 96 rows
@@ -338,10 +344,10 @@ def test_splitk_workspace_sizes():
     ((4096, 4096, 4096), (10, 4096, 0)),      # whole rounds
     ((8192, 8192, 8192), (11, 6144, 10)),     # 2 rounds of 384-row tiles on the top rows + 1 of 256-row ones, against 4
     ((32768, 1024, 8192), (10, 32768, 0)),
-    ((256, 256, 512), (9, 256, 0)),           # tile-starved
+    ((256, 256, 512), (13, 256, 0)),          # tile-starved: K split among the waves of 16 x 16 tiles
     ((2560, 2560, 4096), (9, 2560, 0)),
     ((4000, 4000, 4000), (10, 4000, 0)),
-    ((200, 4096, 1024), (9, 200, 0)),
+    ((200, 4096, 1024), (13, 200, 0)),        # 64 tiles of 128^2 in their bounds-checked form: rung 13
     ((4096, 4092, 1024), (10, 4096, 0)),      # N % 8 != 0: the fourth form stores unaligned rows
     ((4096, 4096, 64), (4, 4096, 0)),         # one k step: not the four-wave ring
     ((128, 32768, 4096), (9, 128, 0)),        # M = 128: half of every 256-row tile would be padding
@@ -366,7 +372,17 @@ def test_splitk_workspace_sizes():
     ((64, 28672, 8192), (9, 64, 0)),          # 64 rows and a large side over 16384: 128 x 128 tiles
     ((80, 8192, 8192), (12, 80, 0)),          # up to 96 rows with a large side up to 12288
     ((96, 16384, 8192), (9, 96, 0)),          # ... beyond it, 128 x 128 tiles
-    ((97, 4096, 4096), (9, 97, 0)),           # neither side small
+    ((97, 4096, 4096), (13, 97, 0)),          # neither side small: 32 x 64 tiles, K split among waves
+    ((128, 1024, 8192), (13, 128, 0)),        # 8 tiles of 128^2 for 128 steps: rung 13
+    ((4096, 128, 4096), (13, 4096, 0)),       # ... either side
+    ((300, 2000, 3000), (13, 300, 0)),
+    ((128, 8192, 8192), (9, 128, 0)),         # rung 13's model within a fifth of the ring's: the ring
+    ((256, 4096, 14336), (9, 256, 0)),
+    ((1024, 1024, 8192), (9, 1024, 0)),
+    ((384, 4096, 1024), (9, 384, 0)),
+    ((384, 4096, 4096), (9, 384, 0)),         # rung 13 would take 3 rounds of workgroups
+    ((64, 28672, 8192), (9, 64, 0)),          # ... and a large side re-read from HBM per round
+    ((256, 2048, 65536), (13, 256, 0)),       # one round: the tile rows share the large side's blocks
     ((16, 4096, 4095), (12, 16, 0)),          # any K >= 8 ...
     ((16, 4096, 7), (3, 16, 0)),              # ... below that, R3's general form
 ])
@@ -407,8 +423,10 @@ def test_wide_top_rows_plan_invariants(M, N, K, cus):
     ((8192, 8192, 8192), 256, (0, 1)),
     ((6144, 6144, 2048), 256, (0, 1)),        # short K: the split costs more than the last round
     ((256, 256, 65536), 256, (0, 64)),        # tile-starved: every row splits
-    ((256, 1024, 8192), 256, (0, 32)),        # at most 4 tiles: slices of 4 steps
-    ((128, 1024, 8192), 256, (0, 32)),
+    ((256, 1024, 8192), 256, (0, 1)),         # rung 13's model beats 32 slices: unsplit, rung 13
+    ((128, 1024, 8192), 256, (0, 1)),
+    ((256, 2048, 65536), 256, (0, 32)),       # at most 4 tiles and a long K: slices of 4 steps
+    ((256, 256, 65536), 256, (0, 64)),        # ... where rung 13's per-workgroup K costs more
     ((64, 1024, 8192), 256, (0, 1)),          # one small side: rung 12, unsplit
     ((16, 4096, 14336), 256, (0, 1)),
     ((1024, 1024, 8192), 256, (0, 16)),       # 16 tiles: slices of at least 8 steps
@@ -416,6 +434,57 @@ def test_wide_top_rows_plan_invariants(M, N, K, cus):
 ])
 def test_splitk_plan(shape, cus, want):
     assert g.splitk_plan(*shape, cus) == want
+
+
+@pytest.mark.parametrize("rung,shape,cus,want", [
+    (12, (16, 4096, 14336), 256, (1, 1, 2)),      # 16 rows of S: one L block, two groups in flight
+    (12, (16, 14336, 8192), 256, (1, 1, 2)),      # ... also with 32-row L tiles on every CU, below K = 12288
+    (12, (16, 8192, 28672), 256, (1, 2, 1)),      # 32 L rows for every compute unit and a long K
+    (12, (4096, 32, 4096), 256, (2, 1, 1)),
+    (12, (32, 14336, 14336), 256, (2, 2, 1)),
+    (12, (64, 8192, 8192), 256, (4, 2, 1)),       # from 48 rows of S, 32 L rows whenever every CU gets them
+    (12, (64, 4096, 4096), 256, (4, 1, 1)),       # ... here they would not
+    (12, (96, 16384, 8192), 80, (6, 2, 1)),
+    (13, (256, 1024, 8192), 256, (2, 2, 1)),      # 512 workgroups of 32 x 32: 2 rounds of 4 blocks
+    (13, (128, 1024, 8192), 256, (1, 2, 2)),      # 256 of 16 x 32: one round of 3 blocks
+    (13, (128, 4096, 4096), 256, (2, 4, 1)),      # 256 of 32 x 64
+    (13, (300, 2000, 3000), 256, (3, 4, 1)),      # 224 of 48 x 64
+    (13, (100, 100, 1001), 256, (1, 1, 2)),
+    (13, (4096, 128, 4096), 256, (2, 4, 1)),      # S is the side with fewer rows, here B
+    (13, (128, 4096, 4096), 64, (3, 4, 1)),       # fewer compute units: larger tiles
+])
+def test_ksplit_plan(rung, shape, cus, want):
+    """The workgroup tile of rungs 12 and 13, as the host evaluates it."""
+    assert g.ksplit_plan(rung, *shape, cus) == want
+
+
+def test_ksplit_plan_model_choice():
+    """Rung 13's tile is the one with the fewest rounds of workgroups times
+    blocks per workgroup (each round streams (mt + nf) 16-row blocks of K
+    per workgroup), the first of the list on ties."""
+    tiles = [(1, 1, 2), (1, 2, 2), (2, 2, 1), (2, 4, 1), (3, 4, 1)]
+    for (M, N, K) in [(256, 1024, 8192), (97, 4096, 4096), (1000, 1000, 1001), (300, 2000, 3000), (700, 130, 1001),
+                      (5000, 5000, 64), (129, 129, 129)]:
+        for cus in (64, 256, 304):
+            s, l = min(M, N), max(M, N)
+
+            def cost(t):
+                wgs = -(-l // (16 * t[1])) * -(-s // (16 * t[0]))
+                return -(-wgs // cus) * (t[0] + t[1])
+            want = min(tiles, key=cost)
+            assert g.ksplit_plan(13, M, N, K, cus) == want, (M, N, K, cus)
+
+
+def test_ksplit_plan_errors():
+    L = g.lib()
+    x = ctypes.c_int()
+    p = ctypes.byref(x)
+    assert L.gemm_f16_nt_ksplit_plan(11, 64, 64, 64, 256, p, p, p) == g.INVALID_ARG
+    assert L.gemm_f16_nt_ksplit_plan(13, 0, 64, 64, 256, p, p, p) == g.INVALID_ARG
+    assert L.gemm_f16_nt_ksplit_plan(13, 64, 64, 64, 0, p, p, p) == g.INVALID_ARG
+    assert L.gemm_f16_nt_ksplit_plan(13, 64, 64, 64, 256, None, p, p) == g.INVALID_ARG
+    assert L.gemm_f16_nt_ksplit_plan(12, 97, 97, 4096, 256, p, p, p) == g.UNSUPPORTED
+    assert L.gemm_f16_nt_ksplit_plan(13, 64, 64, 7, 256, p, p, p) == g.UNSUPPORTED
 
 
 @pytest.mark.parametrize("M,N,K", [(6144, 6144, 6144), (4352, 4352, 4096), (4500, 4352, 4096), (7168, 7168, 4096),

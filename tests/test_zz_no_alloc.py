@@ -52,10 +52,11 @@ def both(M, N, K, seed, splits=0):
 
 def test_noalloc_matches_workspace_entry_on_two_calls():
     # first: 64 slices of 512 x 512 fp32 partial sums, the whole 64 MiB
-    # array; second: a smaller product (16 slices of 256 x 256, 4 MiB) over
-    # the first call's leftovers
-    for (M, N, K, seed) in ((512, 512, 32768, 901), (256, 256, 8192, 902)):
-        d_ws, d_na, ref = both(M, N, K, seed)
+    # array; second: a smaller product (16 slices of 256 x 256, 4 MiB, asked
+    # for explicitly: the library's own choice runs it unsplit) over the
+    # first call's leftovers
+    for (M, N, K, seed, sp) in ((512, 512, 32768, 901, 0), (256, 256, 8192, 902, 16)):
+        d_ws, d_na, ref = both(M, N, K, seed, sp)
         np.testing.assert_array_equal(d_na, d_ws)
         assert_parity(d_na, ref, K, f"noalloc {M}x{N}x{K}")
 
