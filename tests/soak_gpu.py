@@ -90,7 +90,7 @@ def one_case(rng, n):
     A, B = dev(Ah), dev(Bh)
     D = torch.full((M, N), float("nan"), dtype=torch.float16, device=DEV)
     if kind == "rung":
-        rung = int(rng.choice([3, 4, 5, 8, 9, 10, 11]))
+        rung = int(rng.choice([3, 4, 5, 8, 9, 10, 11, 12, 13]))
         what += f" rung={rung}"
         if g.check(rung, M, N, K, A.data_ptr(), B.data_ptr(), D.data_ptr()) != g.OK:
             print(what + " (shape not taken)", flush=True)
