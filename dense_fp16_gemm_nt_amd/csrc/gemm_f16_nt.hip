@@ -684,19 +684,29 @@ double splitk_model_us(int64_t M, int64_t N, int64_t K, int64_t splits, int cus)
            kRingStepUs256;
 }
 
-// The split-K entry's slice count for splits = 0: choose_splits, unless the
-// product is one the plain entry runs on rung 13 and rung 13's model beats
-// the slices' (measured on MI355X: 256 x 1024 x 8192 14.1 us on rung 13
-// against 25.2 in 32 slices, 128 x 1024 x 8192 10.2 against 22.7; with K
-// long against a small output, e.g. 256 x 256 x 65536, the slices' 256 x 256
-// tiles win).
-int64_t plan_splits(int64_t M, int64_t N, int64_t K, int cus)
+// The split-K entry's choice for splits = 0 (before hybrid_plan's split of
+// whole rounds): choose_splits' slice count, or 1 for one launch when a
+// model of that beats the slices' -- rung 13 when *r13 is set (its model
+// the smallest), else gemm_f16_nt's choice.  Measured on MI355X (one box,
+// interleaved): 256 x 1024 x 8192 14.1 us on rung 13 against 25.2 in 32
+// slices; 256 x 4096 x 4096 25.3 on rung 13 against 28.1 in 8 slices;
+// 128 x 14336 x 4096 28.6 unsplit against 38.9 in 4 slices; with a long K
+// on a small output the slices' 256 x 256 tiles win (256 x 256 x 65536:
+// 35.6 against 50.1 on rung 13).
+int64_t plan_splits(int64_t M, int64_t N, int64_t K, int cus, bool* r13)
 {
+    *r13 = false;
     const int64_t s = choose_splits(M, N, K, cus);
-    if (s > 1 && ksplit_pays(M, N, K, 1, cus) &&
-        ksplit_model_us(M, N, K, cus, nullptr) <= splitk_model_us(M, N, K, s, cus))
+    if (s <= 1) return 1;
+    const double split = splitk_model_us(M, N, K, s, cus);
+    const double ring = ring_model_us(M, N, K, cus);
+    const bool k13 = ksplit_shape(M, N, K) && !skinny_pays(M, N, K, 1);
+    const double t13 = k13 ? ksplit_model_us(M, N, K, cus, nullptr) : 0.0;
+    if (k13 && t13 <= split && t13 <= ring) {
+        *r13 = true;
         return 1;
-    return s;
+    }
+    return ring <= split ? 1 : s;
 }
 
 int launch_splitk(int64_t M, int64_t N, int64_t K, const void* A, const void* B, void* D, int64_t splits,
@@ -1007,11 +1017,13 @@ int splitk_run(int64_t M, int64_t N, int64_t K, const void* A, const void* B, vo
         return fast_operands(K, K, K, 0, 0, A, B, D) ? launch_ring(g, s, kDefaultRing4) : launch_any(g, s);
     };
     if (!fast_operands(K, K, K, 0, 0, A, B, D)) return unsplit();
-    int64_t want = splits == 0 ? plan_splits(M, N, K, cus) : splits, m_top = 0;
+    bool r13 = false;
+    int64_t want = splits == 0 ? plan_splits(M, N, K, cus, &r13) : splits, m_top = 0;
     if (splits == 0 && want <= 1 && !hybrid_plan(M, N, K, cus, &m_top, &want)) m_top = 0;
     int64_t k_chunk = 0, n_slices = 1;
     if (want > 1) split_plan(K, want, &k_chunk, &n_slices);
-    if (n_slices <= 1) return unsplit();
+    if (n_slices <= 1)
+        return r13 ? launch_skinny(contiguous_args(M, N, K, A, B, D), s, GEMM_F16_NT_R13_KSPLIT) : unsplit();
     // rows [m_top, M) split K; rows [0, m_top) (whole rounds of tiles) do not
     const int64_t m_rest = M - m_top;
     const int64_t need = n_slices * m_rest * N * 4;
@@ -1102,7 +1114,8 @@ int64_t gemm_f16_nt_splitk_workspace(int64_t M, int64_t N, int64_t K, int splits
     if (s == 0) {
         int cus = 0;
         if (device_info(&cus) != GEMM_F16_NT_OK) return GEMM_F16_NT_DEVICE;
-        s = plan_splits(M, N, K, cus);
+        bool r13 = false;
+        s = plan_splits(M, N, K, cus, &r13);
         if (s <= 1 && !hybrid_plan(M, N, K, cus, &m_top, &s)) m_top = 0;
     }
     if (s <= 1 || K == 0 || K % 8 != 0) return 0;
@@ -1266,7 +1279,8 @@ int gemm_f16_nt_splitk_plan(int64_t M, int64_t N, int64_t K, int cus, int64_t* m
 {
     if (M < 0 || N < 0 || K < 0 || cus < 1 || m_top == nullptr || splits == nullptr) return GEMM_F16_NT_INVALID_ARG;
     *m_top = 0;
-    *splits = plan_splits(M, N, K, cus);
+    bool r13 = false;
+    *splits = plan_splits(M, N, K, cus, &r13);
     if (*splits <= 1 && !hybrid_plan(M, N, K, cus, m_top, splits)) {
         *m_top = 0;
         *splits = 1;

@@ -163,9 +163,11 @@ int gemm_f16_nt_strided_batched(int64_t M, int64_t N, int64_t K, const void* A, 
  * differs from gemm_f16_nt's (any order is within the contract).
  * `workspace` is caller-owned device memory of at least
  * gemm_f16_nt_splitk_workspace(M, N, K, splits) bytes, 16-byte aligned,
- * not overlapping A, B or D; its contents are scratch.  When one slice
- * suffices, or the operand rows are off 16-byte boundaries (see above), the
- * call is gemm_f16_nt and the workspace is not touched. */
+ * not overlapping A, B or D; its contents are scratch.  With splits = 0 the
+ * library compares models of the slices, of rung 13 and of the ring kernels
+ * and may run one launch instead: rung 13 where it is modeled fastest,
+ * otherwise gemm_f16_nt's choice; then, as for one slice or operand rows
+ * off 16-byte boundaries (see above), the workspace is not touched. */
 int gemm_f16_nt_splitk(int64_t M, int64_t N, int64_t K, const void* A, const void* B, void* D, int splits,
                        void* workspace, int64_t workspace_bytes, void* stream);
 

@@ -427,6 +427,9 @@ def test_wide_top_rows_plan_invariants(M, N, K, cus):
     ((128, 1024, 8192), 256, (0, 1)),
     ((256, 2048, 65536), 256, (0, 32)),       # at most 4 tiles and a long K: slices of 4 steps
     ((256, 256, 65536), 256, (0, 64)),        # ... where rung 13's per-workgroup K costs more
+    ((256, 4096, 4096), 256, (0, 1)),         # rung 13 modeled faster than 8 slices (the plain entry keeps R9)
+    ((128, 14336, 4096), 256, (0, 1)),        # R9's 112 tiles unsplit modeled faster than 4 slices
+    ((128, 8192, 8192), 256, (0, 8)),
     ((64, 1024, 8192), 256, (0, 1)),          # one small side: rung 12, unsplit
     ((16, 4096, 14336), 256, (0, 1)),
     ((1024, 1024, 8192), 256, (0, 16)),       # 16 tiles: slices of at least 8 steps

@@ -1266,6 +1266,28 @@ def test_ksplit_misaligned_and_pitched(offs):
     assert torch.isnan(Df[:, :, N:]).all().item()
 
 
+def test_splitk_entry_takes_rung13_or_one_launch_where_modeled_faster():
+    """The split-K entry with splits = 0 runs rung 13 unsplit where its model
+    beats the slices' and the ring's (256 x 4096 x 4096, where the plain
+    entry keeps 128 x 128 tiles): bitwise equal to rung 13, no workspace
+    needed; and one launch where the ring is modeled faster (128 x 14336 x
+    4096): bitwise equal to the plain entry."""
+    cus = _cus()
+    for (M, N, K, other) in [(256, 4096, 4096, 13), (128, 14336, 4096, 0)]:
+        assert g.splitk_plan(M, N, K, cus) == (0, 1) and g.splitk_workspace_bytes(M, N, K) == 0
+        A, B = rand_case(M, N, K, 7600 + M)
+        dA, dB = dev(A), dev(B)
+        say(f"[gpu] split-K entry one launch {M}x{N}x{K} (against rung {other})")
+        D = poisoned(M, N)
+        g.gemm_f16_nt_splitk(dA, dB, D)
+        torch.cuda.synchronize()
+        got = host_bits(D)
+        assert np.array_equal(got, host_bits(run(other, dA, dB, poisoned(M, N))))
+        rows, cols = sample_positions(M, N, 600, M + N + K)
+        want, _ = oracle.gemm_nt_sampled(A, B, rows, cols)
+        assert_parity(got[rows, cols], want, K, f"split-K entry {M}x{N}x{K}")
+
+
 @pytest.mark.parametrize("shape", [(128, 4096, 14336), (4096, 128, 4096), (256, 1024, 8192)], ids=lambda s: "x".join(map(str, s)))
 def test_ksplit_full_size_repeatable_and_split_k_entry(shape):
     """Full-size products the library runs on rung 13: sampled outputs
