@@ -551,3 +551,23 @@ def test_library_plan_picks_rungs_that_take_their_rows(M, N, K8, cus):
         assert rr == 0
     else:
         assert rr != 0 and g.check(rr, M - mt, N, K, A + 2 * mt * K, B, D + 2 * mt * N) == g.OK, (rr, M - mt)
+
+
+def test_rung13_only_where_tiles_are_few():
+    """The library takes rung 13 only for single products whose 256 x 256
+    tiles number fewer than the compute units (its model never beats the
+    ring's by a fifth once the tiles fill them), and never where rung 12
+    applies; its tile always keeps every workgroup's blocks within the
+    instantiated set.  (The split-K entry may still prefer slices there:
+    with a workspace, long K on a tiny output splits better.)"""
+    tiles13 = {(1, 1, 2), (1, 2, 2), (2, 2, 1), (2, 4, 1), (3, 4, 1)}
+    for cus in (80, 256, 304):
+        for M in (97, 128, 200, 256, 384, 512, 768, 1024, 1536, 2048, 4096, 8192):
+            for N in (128, 1024, 2048, 4096, 8192, 14336, 28672):
+                for K in (64, 1000, 2048, 4096, 8192, 14336, 28672):
+                    top = g.plan(M, N, K, cus)[0]
+                    if top != 13:
+                        continue
+                    tiles = -(-M // 256) * -(-N // 256)
+                    assert tiles < cus, (M, N, K, cus)
+                    assert g.ksplit_plan(13, M, N, K, cus) in tiles13
