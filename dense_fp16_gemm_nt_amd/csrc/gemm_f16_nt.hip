@@ -207,10 +207,12 @@ bool ksplit_shape(int64_t M, int64_t N, int64_t K)
 constexpr double kRingStepUs128 = 0.40, kRingEdge128 = 1.4, kRingStepUs256 = 1.1, kRingFixedUs = 2.0;
 constexpr double kHbmBytesPerUs = 6.0e6;
 constexpr int64_t kCachedSideBytes = int64_t(128) << 20;
-// rung 13 runs where its model is at most this fraction of the ring's
-// (measured on 75 shapes: every shape below it ran 1.2-4.9x faster on
-// rung 13; the one at 0.84 ran 1.2x slower)
-constexpr double kKsplitGain = 0.80;
+// rung 13 runs where its model is at most this fraction of the ring's.
+// Measured on MI355X: on 75 shapes every one below 0.8 ran 1.2-4.9x faster
+// on rung 13; on 71 shapes between 0.6 and 1.0, those from 0.83 to 0.87 ran
+// 1.06-1.37x faster on rung 13 except three with 128 rows against 6144-8192
+// (0.84-0.97x), those around 0.91 and above gained nothing on balance.
+constexpr double kKsplitGain = 0.87;
 
 double ring_model_us(int64_t M, int64_t N, int64_t K, int cus)
 {

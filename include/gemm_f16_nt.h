@@ -105,7 +105,7 @@ extern "C" {
                                      any 2-byte boundary, no workspace; the library's choice for single
                                      products that rung 12 does not take and whose 128- and 256-row
                                      tiles would leave most compute units idle over a long K, where
-                                     that model beats the ring's by a fifth (gemm_f16_nt_plan) */
+                                     that model is at most 0.87 of the ring's (gemm_f16_nt_plan) */
 
 /* D = A * B^T with the library's choice of kernel for the shape (see
  * gemm_f16_nt_plan; products with one small side run on rung 12, and

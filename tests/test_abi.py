@@ -355,7 +355,8 @@ def test_splitk_workspace_sizes():
     ((384, 65536, 64), (4, 384, 0)),          # 512 tiles of 256^2 against 1536 of 128^2
     ((128, 32768, 4095), (9, 128, 0)),        # ... also for register-staged rows
     ((100, 100, 5), (3, 100, 0)),             # K < 8 off 16-byte rows: R3's general form
-    ((100, 100, 100), (9, 100, 0)),           # K % 8 != 0: R9's register-staged form
+    ((100, 100, 100), (13, 100, 0)),          # K % 8 != 0 with one tile: rung 13 takes any 2-byte rows
+    ((3000, 1000, 999), (9, 3000, 0)),        # K % 8 != 0: R9's register-staged form
     ((4096, 4096, 4095), (4, 4096, 0)),       # ... R4's when 256 x 256 tiles fill the device
     ((6144, 4096, 4096), (11, 6144, 0)),      # one round of 384 x 256 tiles against 1.5 of 256 x 256
     ((12288, 4096, 4096), (11, 12288, 0)),    # both fill whole rounds: the wider tile's fewer bytes per FLOP
@@ -376,9 +377,10 @@ def test_splitk_workspace_sizes():
     ((128, 1024, 8192), (13, 128, 0)),        # 8 tiles of 128^2 for 128 steps: rung 13
     ((4096, 128, 4096), (13, 4096, 0)),       # ... either side
     ((300, 2000, 3000), (13, 300, 0)),
-    ((128, 8192, 8192), (9, 128, 0)),         # rung 13's model within a fifth of the ring's: the ring
-    ((256, 4096, 14336), (9, 256, 0)),
-    ((1024, 1024, 8192), (9, 1024, 0)),
+    ((128, 8192, 8192), (13, 128, 0)),        # rung 13's model at most 0.87 of the ring's
+    ((256, 4096, 14336), (13, 256, 0)),
+    ((1024, 1024, 8192), (13, 1024, 0)),
+    ((1024, 1024, 2048), (9, 1024, 0)),       # above 0.87: the ring
     ((384, 4096, 1024), (9, 384, 0)),
     ((384, 4096, 4096), (9, 384, 0)),         # rung 13 would take 3 rounds of workgroups
     ((64, 28672, 8192), (9, 64, 0)),          # ... and a large side re-read from HBM per round

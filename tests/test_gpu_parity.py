@@ -1268,10 +1268,9 @@ def test_ksplit_misaligned_and_pitched(offs):
 
 def test_splitk_entry_takes_rung13_or_one_launch_where_modeled_faster():
     """The split-K entry with splits = 0 runs rung 13 unsplit where its model
-    beats the slices' and the ring's (256 x 4096 x 4096, where the plain
-    entry keeps 128 x 128 tiles): bitwise equal to rung 13, no workspace
-    needed; and one launch where the ring is modeled faster (128 x 14336 x
-    4096): bitwise equal to the plain entry."""
+    beats the slices' and the ring's (256 x 4096 x 4096): bitwise equal to
+    rung 13, no workspace needed; and one launch where the ring is modeled
+    faster (128 x 14336 x 4096): bitwise equal to the plain entry."""
     cus = _cus()
     for (M, N, K, other) in [(256, 4096, 4096, 13), (128, 14336, 4096, 0)]:
         assert g.splitk_plan(M, N, K, cus) == (0, 1) and g.splitk_workspace_bytes(M, N, K) == 0
