@@ -200,10 +200,10 @@ bool ksplit_shape(int64_t M, int64_t N, int64_t K)
 // ones (~1.1 us), plus ~2 us, 1.5x with register-staged loads (K % 8 !=
 // 0), and at least its compulsory bytes at ~6 TB/s.
 // Rung 13: skinny::ksplit_tile's model, and at least its bytes from HBM at
-// ~6 TB/s, where the larger side is read once per round of workgroups (the
-// tile rows of the smaller side that run together share its blocks in the
-// caches), at most once per tile row, unless it fits the last-level cache
-// (taken as 128 MiB).
+// ~6 TB/s, where the larger side is read once when the S tiles of an L tile
+// run together (in one round, or in the S-major order of the 64-row L
+// tiles, skinny::kSMajorMinBytes) or when it fits the last-level cache
+// (taken as 128 MiB), else once per round, at most once per tile row.
 constexpr double kRingStepUs128 = 0.40, kRingEdge128 = 1.4, kRingStepUs256 = 1.1, kRingFixedUs = 2.0;
 constexpr double kHbmBytesPerUs = 6.0e6;
 constexpr int64_t kCachedSideBytes = int64_t(128) << 20;
@@ -232,9 +232,11 @@ double ksplit_model_us(int64_t M, int64_t N, int64_t K, int cus, skinny::Tile* t
     double t = 0;
     const skinny::Tile tl = skinny::ksplit_tile(s_rows, l_rows, K, cus, &t);
     const int64_t s_tiles = (s_rows + 16 * tl.mt - 1) / (16 * tl.mt);
-    const int64_t rounds = (s_tiles * ((l_rows + 16 * tl.nf - 1) / (16 * tl.nf)) + cus - 1) / cus;
+    const int64_t wgs = s_tiles * ((l_rows + 16 * tl.nf - 1) / (16 * tl.nf));
+    const int64_t rounds = (wgs + cus - 1) / cus;
     const int64_t l_bytes = l_rows * K * 2;
-    const int64_t l_reads = l_bytes <= kCachedSideBytes ? 1 : (rounds < s_tiles ? rounds : s_tiles);
+    const bool once = l_bytes <= kCachedSideBytes || rounds <= 1 || tl.nf == 4;
+    const int64_t l_reads = once ? 1 : (rounds < s_tiles ? rounds : s_tiles);
     const double hbm = (double)(l_bytes * l_reads + s_rows * K * 2) / kHbmBytesPerUs;
     if (tile) *tile = tl;
     return t > hbm ? t : hbm;
@@ -780,11 +782,27 @@ void launch_skinny_t(const skinny::Args& a, int64_t grid, hipStream_t s)
                        s, a);
 }
 
+// Rung 13's tiles with 64 L rows in the S-major order (skinny::kSMajorMinBytes).
+template <int MT, int NF, int DB, bool TRANS>
+void launch_skinny_smaj(const skinny::Args& a, int64_t grid, hipStream_t s)
+{
+    hipLaunchKernelGGL((skinny::skinny_kernel<MT, NF, DB, TRANS, true>), dim3((unsigned)grid),
+                       dim3(64 * skinny::kWaves), 0, s, a);
+}
+
 // The instantiated tiles: rung 12's (skinny::skinny_tile: mt = 1..6 blocks
 // of S, 1 or 2 of L) and rung 13's (skinny::kTiles13).
 template <bool TRANS>
-int launch_skinny_tile(const skinny::Args& a, const skinny::Tile& t, int64_t grid, hipStream_t s)
+int launch_skinny_tile(const skinny::Args& a, const skinny::Tile& t, int64_t grid, bool smaj, hipStream_t s)
 {
+    if (smaj) {
+        switch (t.mt * 100 + t.nf * 10 + t.db) {
+        case 241: launch_skinny_smaj<2, 4, 1, TRANS>(a, grid, s); break;
+        case 341: launch_skinny_smaj<3, 4, 1, TRANS>(a, grid, s); break;
+        default: return GEMM_F16_NT_UNSUPPORTED;
+        }
+        return launched();
+    }
     switch (t.mt * 100 + t.nf * 10 + t.db) {
     case 112: launch_skinny_t<1, 1, 2, TRANS>(a, grid, s); break;
     case 121: launch_skinny_t<1, 2, 1, TRANS>(a, grid, s); break;
@@ -839,10 +857,14 @@ int launch_skinny(const GemmArgs& g, hipStream_t s, int rung = GEMM_F16_NT_R12_S
     a.ldd = g.ldd;
     const skinny::Tile t = ksplit_tile_for(rung, g.M, g.N, g.K, cus);
     const int64_t l_tiles = (a.l_rows + 16 * t.nf - 1) / (16 * t.nf);
-    const int64_t grid = l_tiles * ((a.s_rows + 16 * t.mt - 1) / (16 * t.mt));
+    const int64_t s_tiles = (a.s_rows + 16 * t.mt - 1) / (16 * t.mt);
+    const int64_t grid = l_tiles * s_tiles;
     if (grid > (int64_t(1) << 31) - 1) return GEMM_F16_NT_UNSUPPORTED;
     a.l_tiles = (uint32_t)l_tiles;
-    return trans ? launch_skinny_tile<true>(a, t, grid, s) : launch_skinny_tile<false>(a, t, grid, s);
+    a.s_tiles = (uint32_t)s_tiles;
+    const bool smaj = rung == GEMM_F16_NT_R13_KSPLIT && t.nf == 4 && a.l_rows * a.K * 2 > skinny::kSMajorMinBytes &&
+                      grid > cus;
+    return trans ? launch_skinny_tile<true>(a, t, grid, smaj, s) : launch_skinny_tile<false>(a, t, grid, smaj, s);
 }
 
 int launch_staged(const GemmArgs& g0, hipStream_t s, bool small)

@@ -42,6 +42,7 @@
 
 #include "common.hpp"
 #include "ring.hpp"
+#include "sched.hpp"
 
 namespace g16 {
 namespace skinny {
@@ -54,8 +55,24 @@ struct Args {
     const f16* L;   // larger side: l_rows x K, row pitch ld_l
     f16* D;
     int64_t ld_s, s_rows, ld_l, l_rows, K, ldd;
-    uint32_t l_tiles;   // workgroups along L; workgroup b takes L tile b % l_tiles, S tile b / l_tiles
+    uint32_t l_tiles, s_tiles;   // workgroups along L and along S
 };
+
+// Tile order.  L-major: workgroup b takes L tile b % l_tiles and S tile
+// b / l_tiles, so the workgroups of a round (dealt to the XCDs in turn)
+// cover whole rows of L tiles.  When L is large and takes more than one
+// round, that reads it from HBM once per round; S-major instead gives each
+// XCD a contiguous run of workgroups (xcd_slot) over groups of kSGroup S
+// tiles by all L tiles, so the S tiles of one L tile run together on one
+// XCD and L is read once.  Measured on MI355X (interleaved, the same bits):
+// 128 x 8192 x 8192 59.5 -> 41.2 us, 4096 x 256 x 8192 44.8 -> 41.3,
+// 256 x 4096 x 14336 66.3 -> 63.3; with one round or a small L it lost
+// (512 x 2048 x 4096 22.4 -> 23.4), so it is taken only for L over
+// kSMajorMinBytes and more than one round, and only on the tiles of 64 L
+// rows (32 x 32 tiles ran 2x slower with the mapping's code in the kernel,
+// 256 x 1024 x 8192 14.2 -> 30.6, whatever the order).
+constexpr int64_t kSGroup = 8;
+constexpr int64_t kSMajorMinBytes = int64_t(32) << 20;
 
 // LDS of one workgroup: the waves' 4 KiB transposition buffers during the
 // k loop, then (after a barrier) the waves' partial sums.
@@ -67,8 +84,12 @@ constexpr int lds_bytes()
 }
 
 // TRANS = false: S is A (D[s][l]); TRANS = true: S is B (D[l][s]).
-// DB: 4-chunk groups in flight per wave (1 or 2).
-template <int MT, int NF, int DB, bool TRANS>
+// DB: 4-chunk groups in flight per wave (1 or 2).  SMAJ: the S-major tile
+// order (a template parameter: with the L-major order the kernel is the
+// same code as without the option; measured on MI355X, a run-time choice
+// made the 32 x 32 tile's loop twice as slow, 15.5 -> 30.8 us on 256 x
+// 1024 x 8192).
+template <int MT, int NF, int DB, bool TRANS, bool SMAJ = false>
 __global__ __launch_bounds__(64 * kWaves) void skinny_kernel(const Args g)
 {
     static_assert(DB == 1 || DB == 2, "one or two groups in flight");
@@ -76,8 +97,18 @@ __global__ __launch_bounds__(64 * kWaves) void skinny_kernel(const Args g)
     __shared__ __attribute__((aligned(16))) char smem[lds_bytes<MT, NF>()];
     const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int r16 = lane & 15, kq = lane >> 4;
-    const uint32_t ty = blockIdx.x / g.l_tiles, tx = blockIdx.x - ty * g.l_tiles;
-    const int64_t i0 = (int64_t)ty * 16 * MT, j0 = (int64_t)tx * 16 * NF;
+    int64_t i0, j0;
+    if constexpr (SMAJ) {
+        int64_t ty, tx;
+        grouped_tile_in<int64_t>(xcd_slot(blockIdx.x, (int64_t)g.l_tiles * g.s_tiles), g.s_tiles, g.l_tiles, kSGroup,
+                                 &ty, &tx);
+        i0 = ty * 16 * MT;
+        j0 = tx * 16 * NF;
+    } else {
+        const uint32_t ty = blockIdx.x / g.l_tiles, tx = blockIdx.x - ty * g.l_tiles;
+        i0 = (int64_t)ty * 16 * MT;
+        j0 = (int64_t)tx * 16 * NF;
+    }
     auto row_ptr = [&](int b, int r) -> const char* {
         if (b < MT) {
             const int64_t rr = i0 + 16 * b + r;

@@ -372,7 +372,7 @@ def test_splitk_workspace_sizes():
     ((32, 28672, 8192), (12, 32, 0)),         # at most 32 rows: any large side
     ((64, 28672, 8192), (9, 64, 0)),          # 64 rows and a large side over 16384: 128 x 128 tiles
     ((80, 8192, 8192), (12, 80, 0)),          # up to 96 rows with a large side up to 12288
-    ((96, 16384, 8192), (9, 96, 0)),          # ... beyond it, 128 x 128 tiles
+    ((96, 16384, 8192), (13, 96, 0)),         # ... beyond it, rung 13's 48 x 64 tiles in S-major order
     ((97, 4096, 4096), (13, 97, 0)),          # neither side small: 32 x 64 tiles, K split among waves
     ((128, 1024, 8192), (13, 128, 0)),        # 8 tiles of 128^2 for 128 steps: rung 13
     ((4096, 128, 4096), (13, 4096, 0)),       # ... either side

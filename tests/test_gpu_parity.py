@@ -1287,7 +1287,27 @@ def test_splitk_entry_takes_rung13_or_one_launch_where_modeled_faster():
         assert_parity(got[rows, cols], want, K, f"split-K entry {M}x{N}x{K}")
 
 
-@pytest.mark.parametrize("shape", [(128, 4096, 14336), (4096, 128, 4096), (256, 1024, 8192)], ids=lambda s: "x".join(map(str, s)))
+@pytest.mark.parametrize("shape", [(130, 17000, 1001), (17000, 130, 1001)], ids=lambda s: "x".join(map(str, s)))
+def test_ksplit_s_major_parity(shape):
+    """Rung 13 in its S-major tile order (64-row L tiles, an L side over 32
+    MiB, more than one round of workgroups): every output against the
+    oracle into NaN-poisoned D, either operand as S, bitwise repeatable."""
+    M, N, K = shape
+    mt, nf, db = g.ksplit_plan(13, M, N, K, _cus())
+    s_rows, l_rows = min(M, N), max(M, N)
+    wgs = -(-l_rows // (16 * nf)) * -(-s_rows // (16 * mt))
+    assert nf == 4 and l_rows * K * 2 > 32 << 20 and wgs > _cus() and g.plan(M, N, K, _cus())[0] == 13
+    A, B = rand_case(M, N, K, 7700 + M)
+    ref, _ = oracle.gemm_nt(A, B)
+    dA, dB = dev(A), dev(B)
+    say(f"[gpu] rung 13 S-major {M}x{N}x{K} tile={(mt, nf, db)} workgroups={wgs}")
+    got = host_bits(run(13, dA, dB, poisoned(M, N)))
+    assert_parity(got, ref, K, f"rung 13 S-major {shape}")
+    assert np.array_equal(host_bits(run(0, dA, dB, poisoned(M, N))), got)
+
+
+@pytest.mark.parametrize("shape", [(128, 4096, 14336), (4096, 128, 4096), (256, 1024, 8192), (96, 16384, 8192),
+                                   (128, 8192, 8192)], ids=lambda s: "x".join(map(str, s)))
 def test_ksplit_full_size_repeatable_and_split_k_entry(shape):
     """Full-size products the library runs on rung 13: sampled outputs
     against the oracle, no output left unwritten, bitwise repeats, and the
