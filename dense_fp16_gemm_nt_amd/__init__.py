@@ -89,7 +89,7 @@ def lib() -> ctypes.CDLL:
             L.gemm_f16_nt_splitk_plan.restype = i32
             L.gemm_f16_nt_splitk_plan.argtypes = [i64, i64, i64, i32, i64p, i64p]
             L.gemm_f16_nt_ksplit_plan.restype = i32
-            L.gemm_f16_nt_ksplit_plan.argtypes = [i32, i64, i64, i64, i32] + [ctypes.POINTER(ctypes.c_int)] * 3
+            L.gemm_f16_nt_ksplit_plan.argtypes = [i32, i64, i64, i64, i32] + [ctypes.POINTER(ctypes.c_int)] * 4
             L.gemm_f16_nt_handoff_plan.restype = i32
             L.gemm_f16_nt_handoff_plan.argtypes = [i32, i32, i32, i64, ctypes.POINTER(ctypes.c_uint32),
                                                    ctypes.POINTER(ctypes.c_uint32)]
@@ -262,16 +262,16 @@ def splitk_plan(M: int, N: int, K: int, cus: int):
 
 
 def ksplit_plan(rung: int, M: int, N: int, K: int, cus: int):
-    """(mt, nf, db): the workgroup tile rung 12 or 13 launches for an
-    M x N x K product on a device with `cus` compute units (host
+    """(mt, nf, db, waves): the workgroup tile rung 12 or 13 launches for
+    an M x N x K product on a device with `cus` compute units (host
     evaluation): 16*mt rows of the side with fewer rows, 16*nf of the
-    other, db load groups in flight per wave."""
-    mt, nf, db = ctypes.c_int(), ctypes.c_int(), ctypes.c_int()
+    other, db load groups in flight per wave, `waves` waves splitting K."""
+    mt, nf, db, nw = ctypes.c_int(), ctypes.c_int(), ctypes.c_int(), ctypes.c_int()
     st = lib().gemm_f16_nt_ksplit_plan(int(rung), int(M), int(N), int(K), int(cus), ctypes.byref(mt),
-                                       ctypes.byref(nf), ctypes.byref(db))
+                                       ctypes.byref(nf), ctypes.byref(db), ctypes.byref(nw))
     if st != OK:
         raise GemmError(st, "gemm_f16_nt_ksplit_plan")
-    return mt.value, nf.value, db.value
+    return mt.value, nf.value, db.value, nw.value
 
 
 def splitk_workspace_bytes(M: int, N: int, K: int, splits: int = 0) -> int:

@@ -235,7 +235,7 @@ double ksplit_model_us(int64_t M, int64_t N, int64_t K, int cus, skinny::Tile* t
     const int64_t wgs = s_tiles * ((l_rows + 16 * tl.nf - 1) / (16 * tl.nf));
     const int64_t rounds = (wgs + cus - 1) / cus;
     const int64_t l_bytes = l_rows * K * 2;
-    const bool once = l_bytes <= kCachedSideBytes || rounds <= 1 || tl.nf == 4;
+    const bool once = l_bytes <= kCachedSideBytes || rounds <= 1 || skinny::smajor_tile(tl);
     const int64_t l_reads = once ? 1 : (rounds < s_tiles ? rounds : s_tiles);
     const double hbm = (double)(l_bytes * l_reads + s_rows * K * 2) / kHbmBytesPerUs;
     if (tile) *tile = tl;
@@ -775,26 +775,44 @@ int launch_r3_any(const GemmArgs& g, hipStream_t s)
 // R4 (256 x 256 tiles) or R9 (128 x 128, `small`) on general operands: the
 // pipelined ring with its loads staged through registers, which take rows
 // on any 2-byte boundary.  Needs K >= 8.
-template <int MT, int NF, int DB, bool TRANS>
+template <int MT, int NF, int DB, bool TRANS, int NW = skinny::kWaves>
 void launch_skinny_t(const skinny::Args& a, int64_t grid, hipStream_t s)
 {
-    hipLaunchKernelGGL((skinny::skinny_kernel<MT, NF, DB, TRANS>), dim3((unsigned)grid), dim3(64 * skinny::kWaves), 0,
+    hipLaunchKernelGGL((skinny::skinny_kernel<MT, NF, DB, TRANS, false, NW>), dim3((unsigned)grid), dim3(64 * NW), 0,
                        s, a);
 }
 
 // Rung 13's tiles with 64 L rows in the S-major order (skinny::kSMajorMinBytes).
-template <int MT, int NF, int DB, bool TRANS>
+template <int MT, int NF, int DB, bool TRANS, int NW = skinny::kWaves>
 void launch_skinny_smaj(const skinny::Args& a, int64_t grid, hipStream_t s)
 {
-    hipLaunchKernelGGL((skinny::skinny_kernel<MT, NF, DB, TRANS, true>), dim3((unsigned)grid),
-                       dim3(64 * skinny::kWaves), 0, s, a);
+    hipLaunchKernelGGL((skinny::skinny_kernel<MT, NF, DB, TRANS, true, NW>), dim3((unsigned)grid), dim3(64 * NW), 0,
+                       s, a);
 }
 
 // The instantiated tiles: rung 12's (skinny::skinny_tile: mt = 1..6 blocks
-// of S, 1 or 2 of L) and rung 13's (skinny::kTiles13).
+// of S, 1 or 2 of L) and rung 13's (skinny::kTiles13, two of them with 4
+// waves).
 template <bool TRANS>
 int launch_skinny_tile(const skinny::Args& a, const skinny::Tile& t, int64_t grid, bool smaj, hipStream_t s)
 {
+    if (t.nw == 4) {
+        switch (t.mt * 100 + t.nf * 10 + t.db) {
+        case 241:
+            if (smaj)
+                launch_skinny_smaj<2, 4, 1, TRANS, 4>(a, grid, s);
+            else
+                launch_skinny_t<2, 4, 1, TRANS, 4>(a, grid, s);
+            break;
+        case 441:
+            if (smaj) return GEMM_F16_NT_UNSUPPORTED;
+            launch_skinny_t<4, 4, 1, TRANS, 4>(a, grid, s);
+            break;
+        default: return GEMM_F16_NT_UNSUPPORTED;
+        }
+        return launched();
+    }
+    if (t.nw != skinny::kWaves) return GEMM_F16_NT_UNSUPPORTED;
     if (smaj) {
         switch (t.mt * 100 + t.nf * 10 + t.db) {
         case 241: launch_skinny_smaj<2, 4, 1, TRANS>(a, grid, s); break;
@@ -862,8 +880,8 @@ int launch_skinny(const GemmArgs& g, hipStream_t s, int rung = GEMM_F16_NT_R12_S
     if (grid > (int64_t(1) << 31) - 1) return GEMM_F16_NT_UNSUPPORTED;
     a.l_tiles = (uint32_t)l_tiles;
     a.s_tiles = (uint32_t)s_tiles;
-    const bool smaj = rung == GEMM_F16_NT_R13_KSPLIT && t.nf == 4 && a.l_rows * a.K * 2 > skinny::kSMajorMinBytes &&
-                      grid > cus;
+    const bool smaj = rung == GEMM_F16_NT_R13_KSPLIT && skinny::smajor_tile(t) &&
+                      a.l_rows * a.K * 2 > skinny::kSMajorMinBytes && grid > cus;
     return trans ? launch_skinny_tile<true>(a, t, grid, smaj, s) : launch_skinny_tile<false>(a, t, grid, smaj, s);
 }
 
@@ -1312,10 +1330,11 @@ int gemm_f16_nt_splitk_plan(int64_t M, int64_t N, int64_t K, int cus, int64_t* m
     return GEMM_F16_NT_OK;
 }
 
-int gemm_f16_nt_ksplit_plan(int rung, int64_t M, int64_t N, int64_t K, int cus, int* mt, int* nf, int* db)
+int gemm_f16_nt_ksplit_plan(int rung, int64_t M, int64_t N, int64_t K, int cus, int* mt, int* nf, int* db,
+                            int* waves)
 {
     if ((rung != GEMM_F16_NT_R12_SKINNY && rung != GEMM_F16_NT_R13_KSPLIT) || M < 1 || N < 1 || K < 0 || cus < 1 ||
-        mt == nullptr || nf == nullptr || db == nullptr)
+        mt == nullptr || nf == nullptr || db == nullptr || waves == nullptr)
         return GEMM_F16_NT_INVALID_ARG;
     if (rung == GEMM_F16_NT_R12_SKINNY ? !skinny_shape(M, N, K) : !ksplit_shape(M, N, K))
         return GEMM_F16_NT_UNSUPPORTED;
@@ -1323,6 +1342,7 @@ int gemm_f16_nt_ksplit_plan(int rung, int64_t M, int64_t N, int64_t K, int cus, 
     *mt = t.mt;
     *nf = t.nf;
     *db = t.db;
+    *waves = t.nw;
     return GEMM_F16_NT_OK;
 }
 

@@ -76,10 +76,10 @@ constexpr int64_t kSMajorMinBytes = int64_t(32) << 20;
 
 // LDS of one workgroup: the waves' 4 KiB transposition buffers during the
 // k loop, then (after a barrier) the waves' partial sums.
-template <int MT, int NF>
+template <int MT, int NF, int NW = kWaves>
 constexpr int lds_bytes()
 {
-    constexpr int red = kWaves * MT * NF * 64 * 16, tb = kWaves * 4096;
+    constexpr int red = NW * MT * NF * 64 * 16, tb = NW * 4096;
     return red > tb ? red : tb;
 }
 
@@ -89,12 +89,12 @@ constexpr int lds_bytes()
 // same code as without the option; measured on MI355X, a run-time choice
 // made the 32 x 32 tile's loop twice as slow, 15.5 -> 30.8 us on 256 x
 // 1024 x 8192).
-template <int MT, int NF, int DB, bool TRANS, bool SMAJ = false>
-__global__ __launch_bounds__(64 * kWaves) void skinny_kernel(const Args g)
+template <int MT, int NF, int DB, bool TRANS, bool SMAJ = false, int NW = kWaves>
+__global__ __launch_bounds__(64 * NW) void skinny_kernel(const Args g)
 {
     static_assert(DB == 1 || DB == 2, "one or two groups in flight");
     constexpr int NB = MT + NF;   // 16-row blocks: MT of S, then NF of L
-    __shared__ __attribute__((aligned(16))) char smem[lds_bytes<MT, NF>()];
+    __shared__ __attribute__((aligned(16))) char smem[lds_bytes<MT, NF, NW>()];
     const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int r16 = lane & 15, kq = lane >> 4;
     int64_t i0, j0;
@@ -127,7 +127,7 @@ __global__ __launch_bounds__(64 * kWaves) void skinny_kernel(const Args g)
     }
     // this wave's chunks [c0, c1): whole groups of 4 chunks inside K, then the rest
     const int64_t K = g.K, chunks = (K + 31) / 32;
-    const int64_t per = ((chunks + kWaves - 1) / kWaves + 3) / 4 * 4;
+    const int64_t per = ((chunks + NW - 1) / NW + 3) / 4 * 4;
     const int64_t c0 = w * per, c1 = c0 + per < chunks ? c0 + per : chunks;
     const int64_t cw = c1 < K / 32 ? c1 : K / 32;
     const int64_t groups = cw > c0 ? (cw - c0) / 4 : 0;
@@ -219,10 +219,10 @@ __global__ __launch_bounds__(64 * kWaves) void skinny_kernel(const Args g)
 #pragma unroll
         for (int f = 0; f < NF; ++f) red[(w * MT * NF + t * NF + f) * 64 + lane] = acc[t][f];
     __syncthreads();
-    for (int b = w; b < MT * NF; b += kWaves) {
+    for (int b = w; b < MT * NF; b += NW) {
         f32x4 sum = red[b * 64 + lane];
 #pragma unroll
-        for (int v = 1; v < kWaves; ++v) sum += red[(v * MT * NF + b) * 64 + lane];
+        for (int v = 1; v < NW; ++v) sum += red[(v * MT * NF + b) * 64 + lane];
         const int t = b / NF, f = b % NF;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
@@ -237,10 +237,17 @@ __global__ __launch_bounds__(64 * kWaves) void skinny_kernel(const Args g)
     }
 }
 
-// A workgroup tile: 16 * mt rows of S and 16 * nf rows of L, db groups in flight.
+// A workgroup tile: 16 * mt rows of S and 16 * nf rows of L, db groups in
+// flight, nw waves splitting K.
 struct Tile {
-    int mt, nf, db;
+    int mt, nf, db, nw = kWaves;
 };
+
+// The tiles of 64 L rows that run in the S-major order (when L is large
+// and takes more than one round).  Rung 13's 4-wave 64 x 64 tile keeps the
+// L-major order: measured on MI355X it ran 3-30% slower in the S-major one
+// (256 x 8192 x 8192 69.4 -> 77.2 us, 128 x 8192 x 8192 36.7 -> 42.5).
+inline bool smajor_tile(const Tile& t) { return t.nf == 4 && t.mt <= 3; }
 
 // Rung 12's tile: all of S (mt = ceil(S / 16)) and 16 or 32 rows of L.
 // 32 L rows ("wide") need every compute unit to get a workgroup; measured
@@ -266,34 +273,58 @@ inline Tile skinny_tile(int64_t s_rows, int64_t l_rows, int64_t K, int cus)
 }
 
 // Rung 13's tiles, and a model of their time in microseconds: a workgroup
-// streams (mt + nf) 16-row blocks of K elements at ~75 GB/s (one workgroup
-// per compute unit, latency-bound loads), rounds of workgroups over the
-// compute units, plus ~3 us of launch and reduction.  Fitted on MI355X over
-// 75 shapes of 128-2048 x 1024-14336 x 1024-14336 rows: on the 29 of them
-// where these tiles beat the ring kernels, the tile the model picks runs
-// within 2.3% of the best of 16 tiles on average (16% at worst).  (6 x 2
-// blocks, best on a few shapes, never has the smallest model: 3 x 4 has the
-// same workgroup count with fewer blocks.)
-constexpr Tile kTiles13[] = {{1, 1, 2}, {1, 2, 2}, {2, 2, 1}, {2, 4, 1}, {3, 4, 1}};
-constexpr double kBytesPerUsPerCu = 75e3;
+// streams (mt + nf) 16-row blocks of K elements at a rate of its own (one
+// workgroup per compute unit, latency-bound loads), rounds of workgroups
+// over the compute units, plus ~3 us of launch and reduction.  The 8-wave
+// tiles' ~75 GB/s was fitted on MI355X over 75 shapes of 128-2048 x
+// 1024-14336 x 1024-14336 rows: on the 29 of them where these tiles beat
+// the ring kernels, the tile the model picks runs within 2.3% of the best
+// of 16 tiles on average (16% at worst).  (6 x 2 blocks, best on a few
+// shapes, never has the smallest model: 3 x 4 has the same workgroup count
+// with fewer blocks.)
+//
+// Two tiles split K among 4 waves, each with a SIMD's whole register file:
+// 32 x 64 (~90 GB/s, taken only with more than one round of workgroups:
+// two of them fit on a compute unit, and in a single round the 8-wave form
+// splits each tile's K finer, 128 x 4096 x 4096 13.1 against 15.2 us), and
+// 64 x 64 (~65 GB/s: its 8 blocks per wave spill registers with 8 waves).
+// Measured on MI355X over 20 shapes of 128-1024 x 1024-8192 x 4096-28672
+// (interleaved, bitwise equal on integer operands) they make the model's
+// pick 1.067x faster (geometric mean) and within 1.2% of the best of the
+// seven tiles: 256 x 4096 x 4096 23.7 -> 21.1 us, 256 x 8192 x 8192 96.8 ->
+// 65.5, 128 x 8192 x 28672 171.3 -> 147.6, 1024 x 1024 x 8192 39.4 -> 37.3.
+struct Tile13 {
+    Tile t;
+    double bytes_per_us;
+    bool multi_round;   // only with more workgroups than compute units
+};
+constexpr Tile13 kTiles13[] = {{{1, 1, 2}, 75e3, false}, {{1, 2, 2}, 75e3, false}, {{2, 2, 1}, 75e3, false},
+                               {{2, 4, 1}, 75e3, false}, {{3, 4, 1}, 75e3, false}, {{2, 4, 1, 4}, 90e3, true},
+                               {{4, 4, 1, 4}, 65e3, false}};
 constexpr double kFixedUs = 3.0;
 
-inline double tile_model_us(int64_t s_rows, int64_t l_rows, int64_t K, int cus, const Tile& t)
+inline int64_t tile_workgroups(int64_t s_rows, int64_t l_rows, const Tile& t)
 {
-    const int64_t wgs = ((l_rows + 16 * t.nf - 1) / (16 * t.nf)) * ((s_rows + 16 * t.mt - 1) / (16 * t.mt));
-    const int64_t rounds = (wgs + cus - 1) / cus;
-    return (double)rounds * (double)(t.mt + t.nf) * 32.0 * (double)K / kBytesPerUsPerCu + kFixedUs;
+    return ((l_rows + 16 * t.nf - 1) / (16 * t.nf)) * ((s_rows + 16 * t.mt - 1) / (16 * t.mt));
 }
 
+inline double tile_model_us(int64_t s_rows, int64_t l_rows, int64_t K, int cus, const Tile13& c)
+{
+    const int64_t rounds = (tile_workgroups(s_rows, l_rows, c.t) + cus - 1) / cus;
+    return (double)rounds * (double)(c.t.mt + c.t.nf) * 32.0 * (double)K / c.bytes_per_us + kFixedUs;
+}
+
+// The tile with the smallest model (the first of the list on ties).
 inline Tile ksplit_tile(int64_t s_rows, int64_t l_rows, int64_t K, int cus, double* model_us)
 {
-    Tile best = kTiles13[0];
-    double bt = tile_model_us(s_rows, l_rows, K, cus, best);
-    for (const Tile& t : kTiles13) {
-        const double v = tile_model_us(s_rows, l_rows, K, cus, t);
+    Tile best = kTiles13[0].t;
+    double bt = tile_model_us(s_rows, l_rows, K, cus, kTiles13[0]);
+    for (const Tile13& c : kTiles13) {
+        if (c.multi_round && tile_workgroups(s_rows, l_rows, c.t) <= (int64_t)cus) continue;
+        const double v = tile_model_us(s_rows, l_rows, K, cus, c);
         if (v < bt) {
             bt = v;
-            best = t;
+            best = c.t;
         }
     }
     if (model_us) *model_us = bt;

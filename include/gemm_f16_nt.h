@@ -264,10 +264,12 @@ int gemm_f16_nt_splitk_plan(int64_t M, int64_t N, int64_t K, int cus, int64_t* m
 /* Host evaluation of the workgroup tile rung 12 or 13 (`rung`) launches for
  * an M x N x K product on a device with `cus` compute units, no HIP call:
  * 16 * *mt rows of the side with fewer rows (A on a tie), 16 * *nf rows of
- * the other, and *db groups of 128 k elements in flight per wave.  Returns
- * 0, GEMM_F16_NT_INVALID_ARG (another rung, M or N < 1, null outputs) or
+ * the other, *db groups of 128 k elements in flight per wave, and *waves
+ * waves (8, or 4 on two of rung 13's tiles) splitting K.  Returns 0,
+ * GEMM_F16_NT_INVALID_ARG (another rung, M or N < 1, null outputs) or
  * GEMM_F16_NT_UNSUPPORTED (a shape the rung does not take). */
-int gemm_f16_nt_ksplit_plan(int rung, int64_t M, int64_t N, int64_t K, int cus, int* mt, int* nf, int* db);
+int gemm_f16_nt_ksplit_plan(int rung, int64_t M, int64_t N, int64_t K, int cus, int* mt, int* nf, int* db,
+                            int* waves);
 
 #ifdef __cplusplus
 }

@@ -380,7 +380,8 @@ def test_splitk_workspace_sizes():
     ((128, 8192, 8192), (13, 128, 0)),        # rung 13's model at most 0.87 of the ring's
     ((256, 4096, 14336), (13, 256, 0)),
     ((1024, 1024, 8192), (13, 1024, 0)),
-    ((1024, 1024, 2048), (9, 1024, 0)),       # above 0.87: the ring
+    ((1024, 1024, 2048), (13, 1024, 0)),      # 4-wave 64 x 64 tiles (14.2 us against 15.9 on 128 x 128 tiles)
+    ((640, 4096, 4096), (9, 640, 0)),         # above 0.87: the ring
     ((384, 4096, 1024), (9, 384, 0)),
     ((384, 4096, 4096), (9, 384, 0)),         # rung 13 would take 3 rounds of workgroups
     ((64, 28672, 8192), (9, 64, 0)),          # ... and a large side re-read from HBM per round
@@ -431,7 +432,7 @@ def test_wide_top_rows_plan_invariants(M, N, K, cus):
     ((256, 256, 65536), 256, (0, 64)),        # ... where rung 13's per-workgroup K costs more
     ((256, 4096, 4096), 256, (0, 1)),         # rung 13 modeled faster than 8 slices (the plain entry keeps R9)
     ((128, 14336, 4096), 256, (0, 1)),        # R9's 112 tiles unsplit modeled faster than 4 slices
-    ((128, 8192, 8192), 256, (0, 8)),
+    ((128, 8192, 8192), 256, (0, 1)),         # rung 13's 4-wave 64 x 64 tiles modeled faster than 8 slices
     ((64, 1024, 8192), 256, (0, 1)),          # one small side: rung 12, unsplit
     ((16, 4096, 14336), 256, (0, 1)),
     ((1024, 1024, 8192), 256, (0, 16)),       # 16 tiles: slices of at least 8 steps
@@ -442,21 +443,25 @@ def test_splitk_plan(shape, cus, want):
 
 
 @pytest.mark.parametrize("rung,shape,cus,want", [
-    (12, (16, 4096, 14336), 256, (1, 1, 2)),      # 16 rows of S: one L block, two groups in flight
-    (12, (16, 14336, 8192), 256, (1, 1, 2)),      # ... also with 32-row L tiles on every CU, below K = 12288
-    (12, (16, 8192, 28672), 256, (1, 2, 1)),      # 32 L rows for every compute unit and a long K
-    (12, (4096, 32, 4096), 256, (2, 1, 1)),
-    (12, (32, 14336, 14336), 256, (2, 2, 1)),
-    (12, (64, 8192, 8192), 256, (4, 2, 1)),       # from 48 rows of S, 32 L rows whenever every CU gets them
-    (12, (64, 4096, 4096), 256, (4, 1, 1)),       # ... here they would not
-    (12, (96, 16384, 8192), 80, (6, 2, 1)),
-    (13, (256, 1024, 8192), 256, (2, 2, 1)),      # 512 workgroups of 32 x 32: 2 rounds of 4 blocks
-    (13, (128, 1024, 8192), 256, (1, 2, 2)),      # 256 of 16 x 32: one round of 3 blocks
-    (13, (128, 4096, 4096), 256, (2, 4, 1)),      # 256 of 32 x 64
-    (13, (300, 2000, 3000), 256, (3, 4, 1)),      # 224 of 48 x 64
-    (13, (100, 100, 1001), 256, (1, 1, 2)),
-    (13, (4096, 128, 4096), 256, (2, 4, 1)),      # S is the side with fewer rows, here B
-    (13, (128, 4096, 4096), 64, (3, 4, 1)),       # fewer compute units: larger tiles
+    (12, (16, 4096, 14336), 256, (1, 1, 2, 8)),      # 16 rows of S: one L block, two groups in flight
+    (12, (16, 14336, 8192), 256, (1, 1, 2, 8)),      # ... also with 32-row L tiles on every CU, below K = 12288
+    (12, (16, 8192, 28672), 256, (1, 2, 1, 8)),      # 32 L rows for every compute unit and a long K
+    (12, (4096, 32, 4096), 256, (2, 1, 1, 8)),
+    (12, (32, 14336, 14336), 256, (2, 2, 1, 8)),
+    (12, (64, 8192, 8192), 256, (4, 2, 1, 8)),       # from 48 rows of S, 32 L rows whenever every CU gets them
+    (12, (64, 4096, 4096), 256, (4, 1, 1, 8)),       # ... here they would not
+    (12, (96, 16384, 8192), 80, (6, 2, 1, 8)),
+    (13, (256, 1024, 8192), 256, (2, 2, 1, 8)),      # 512 workgroups of 32 x 32: 2 rounds of 4 blocks
+    (13, (128, 1024, 8192), 256, (1, 2, 2, 8)),      # 256 of 16 x 32: one round of 3 blocks
+    (13, (128, 4096, 4096), 256, (2, 4, 1, 8)),      # 256 of 32 x 64
+    (13, (300, 2000, 3000), 256, (3, 4, 1, 8)),      # 224 of 48 x 64
+    (13, (100, 100, 1001), 256, (1, 1, 2, 8)),
+    (13, (4096, 128, 4096), 256, (2, 4, 1, 8)),      # S is the side with fewer rows, here B
+    (13, (256, 4096, 4096), 256, (4, 4, 1, 4)),      # 256 of 64 x 64 on 4 waves: 8 blocks at ~65 GB/s
+    (13, (128, 8192, 28672), 256, (4, 4, 1, 4)),
+    (13, (130, 6000, 1001), 256, (2, 4, 1, 4)),      # 1,125 of 32 x 64: 4 waves pay with several rounds
+    (13, (6000, 130, 3000), 256, (2, 4, 1, 4)),
+    (13, (128, 4096, 4096), 64, (4, 4, 1, 4)),       # fewer compute units: larger tiles (4 waves)
 ])
 def test_ksplit_plan(rung, shape, cus, want):
     """The workgroup tile of rungs 12 and 13, as the host evaluates it."""
@@ -464,32 +469,40 @@ def test_ksplit_plan(rung, shape, cus, want):
 
 
 def test_ksplit_plan_model_choice():
-    """Rung 13's tile is the one with the fewest rounds of workgroups times
-    blocks per workgroup (each round streams (mt + nf) 16-row blocks of K
-    per workgroup), the first of the list on ties."""
-    tiles = [(1, 1, 2), (1, 2, 2), (2, 2, 1), (2, 4, 1), (3, 4, 1)]
+    """Rung 13's tile is the one with the smallest model, the first of the
+    list on ties: rounds of workgroups times the bytes each streams ((mt +
+    nf) 16-row blocks of K), over the tile's rate, plus 3 us; the 4-wave
+    32 x 64 tile only with more workgroups than compute units."""
+    tiles = [((1, 1, 2, 8), 75e3, False), ((1, 2, 2, 8), 75e3, False), ((2, 2, 1, 8), 75e3, False),
+             ((2, 4, 1, 8), 75e3, False), ((3, 4, 1, 8), 75e3, False), ((2, 4, 1, 4), 90e3, True),
+             ((4, 4, 1, 4), 65e3, False)]
     for (M, N, K) in [(256, 1024, 8192), (97, 4096, 4096), (1000, 1000, 1001), (300, 2000, 3000), (700, 130, 1001),
-                      (5000, 5000, 64), (129, 129, 129)]:
+                      (5000, 5000, 64), (129, 129, 129), (256, 4096, 4096), (1024, 1024, 8192), (130, 6000, 1001),
+                      (512, 4096, 14336), (128, 8192, 8192)]:
         for cus in (64, 256, 304):
             s, l = min(M, N), max(M, N)
-
-            def cost(t):
+            best, bt = None, None
+            for t, rate, multi in tiles:
                 wgs = -(-l // (16 * t[1])) * -(-s // (16 * t[0]))
-                return -(-wgs // cus) * (t[0] + t[1])
-            want = min(tiles, key=cost)
-            assert g.ksplit_plan(13, M, N, K, cus) == want, (M, N, K, cus)
+                if multi and wgs <= cus:
+                    continue
+                v = float(-(-wgs // cus)) * float(t[0] + t[1]) * 32.0 * float(K) / rate + 3.0
+                if bt is None or v < bt:
+                    best, bt = t, v
+            assert g.ksplit_plan(13, M, N, K, cus) == best, (M, N, K, cus)
 
 
 def test_ksplit_plan_errors():
     L = g.lib()
     x = ctypes.c_int()
     p = ctypes.byref(x)
-    assert L.gemm_f16_nt_ksplit_plan(11, 64, 64, 64, 256, p, p, p) == g.INVALID_ARG
-    assert L.gemm_f16_nt_ksplit_plan(13, 0, 64, 64, 256, p, p, p) == g.INVALID_ARG
-    assert L.gemm_f16_nt_ksplit_plan(13, 64, 64, 64, 0, p, p, p) == g.INVALID_ARG
-    assert L.gemm_f16_nt_ksplit_plan(13, 64, 64, 64, 256, None, p, p) == g.INVALID_ARG
-    assert L.gemm_f16_nt_ksplit_plan(12, 97, 97, 4096, 256, p, p, p) == g.UNSUPPORTED
-    assert L.gemm_f16_nt_ksplit_plan(13, 64, 64, 7, 256, p, p, p) == g.UNSUPPORTED
+    assert L.gemm_f16_nt_ksplit_plan(11, 64, 64, 64, 256, p, p, p, p) == g.INVALID_ARG
+    assert L.gemm_f16_nt_ksplit_plan(13, 0, 64, 64, 256, p, p, p, p) == g.INVALID_ARG
+    assert L.gemm_f16_nt_ksplit_plan(13, 64, 64, 64, 0, p, p, p, p) == g.INVALID_ARG
+    assert L.gemm_f16_nt_ksplit_plan(13, 64, 64, 64, 256, None, p, p, p) == g.INVALID_ARG
+    assert L.gemm_f16_nt_ksplit_plan(13, 64, 64, 64, 256, p, p, p, None) == g.INVALID_ARG
+    assert L.gemm_f16_nt_ksplit_plan(12, 97, 97, 4096, 256, p, p, p, p) == g.UNSUPPORTED
+    assert L.gemm_f16_nt_ksplit_plan(13, 64, 64, 7, 256, p, p, p, p) == g.UNSUPPORTED
 
 
 @pytest.mark.parametrize("M,N,K", [(6144, 6144, 6144), (4352, 4352, 4096), (4500, 4352, 4096), (7168, 7168, 4096),
@@ -562,7 +575,7 @@ def test_rung13_only_where_tiles_are_few():
     applies; its tile always keeps every workgroup's blocks within the
     instantiated set.  (The split-K entry may still prefer slices there:
     with a workspace, long K on a tiny output splits better.)"""
-    tiles13 = {(1, 1, 2), (1, 2, 2), (2, 2, 1), (2, 4, 1), (3, 4, 1)}
+    tiles13 = {(1, 1, 2, 8), (1, 2, 2, 8), (2, 2, 1, 8), (2, 4, 1, 8), (3, 4, 1, 8), (2, 4, 1, 4), (4, 4, 1, 4)}
     for cus in (80, 256, 304):
         for M in (97, 128, 200, 256, 384, 512, 768, 1024, 1536, 2048, 4096, 8192):
             for N in (128, 1024, 2048, 4096, 8192, 14336, 28672):

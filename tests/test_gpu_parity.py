@@ -1197,9 +1197,11 @@ def _cus():
 # one shape per tile of rung 13 (16*mt rows of the side with fewer rows by
 # 16*nf of the other), both sides over 96 rows, either orientation, ragged
 # tile rows and columns, K with a crossing chunk and K % 8 != 0
-KSPLIT = [((100, 100, 1001), (1, 1, 2)), ((260, 250, 1001), (1, 2, 2)), ((1000, 130, 1001), (2, 2, 1)),
-          ((130, 2100, 2056), (2, 4, 1)), ((333, 1500, 1001), (3, 4, 1)), ((2100, 130, 4095), (2, 4, 1)),
-          ((300, 2000, 3000), (3, 4, 1)), ((97, 97, 8), (1, 1, 2)), ((140, 700, 40), None)]
+KSPLIT = [((100, 100, 1001), (1, 1, 2, 8)), ((260, 250, 1001), (1, 2, 2, 8)), ((1000, 130, 1001), (2, 2, 1, 8)),
+          ((130, 2100, 2056), (2, 4, 1, 8)), ((333, 1500, 1001), (3, 4, 1, 8)), ((2100, 130, 4095), (2, 4, 1, 8)),
+          ((300, 2000, 3000), (3, 4, 1, 8)), ((97, 97, 8), (1, 1, 2, 8)), ((140, 700, 40), None),
+          ((130, 6000, 1001), (2, 4, 1, 4)), ((6000, 130, 1001), (2, 4, 1, 4)), ((260, 3000, 1001), (4, 4, 1, 4)),
+          ((3000, 260, 1001), (4, 4, 1, 4)), ((200, 4096, 4096), (4, 4, 1, 4))]
 
 
 @pytest.mark.parametrize("shape,tile", KSPLIT, ids=lambda s: "x".join(map(str, s)) if s else "any")
@@ -1221,7 +1223,8 @@ def test_ksplit_parity(shape, tile):
         assert np.array_equal(host_bits(D0), host_bits(D))
 
 
-@pytest.mark.parametrize("shape", [(256, 1024, 8192), (4096, 130, 2040), (300, 2000, 1000)], ids=lambda s: "x".join(map(str, s)))
+@pytest.mark.parametrize("shape", [(256, 1024, 8192), (4096, 130, 2040), (300, 2000, 1000), (130, 6000, 1001),
+                                   (3000, 260, 1001)], ids=lambda s: "x".join(map(str, s)))
 def test_ksplit_exact_pins(shape):
     """Small integers: every fp32 partial sum and the waves' total are
     exact, so rung 13 equals the oracle bit for bit; all-ones gives K."""
@@ -1287,20 +1290,21 @@ def test_splitk_entry_takes_rung13_or_one_launch_where_modeled_faster():
         assert_parity(got[rows, cols], want, K, f"split-K entry {M}x{N}x{K}")
 
 
-@pytest.mark.parametrize("shape", [(130, 17000, 1001), (17000, 130, 1001)], ids=lambda s: "x".join(map(str, s)))
+@pytest.mark.parametrize("shape", [(130, 17000, 1001), (17000, 130, 1001), (130, 6000, 3000), (6000, 130, 3000)],
+                         ids=lambda s: "x".join(map(str, s)))
 def test_ksplit_s_major_parity(shape):
     """Rung 13 in its S-major tile order (64-row L tiles, an L side over 32
     MiB, more than one round of workgroups): every output against the
     oracle into NaN-poisoned D, either operand as S, bitwise repeatable."""
     M, N, K = shape
-    mt, nf, db = g.ksplit_plan(13, M, N, K, _cus())
+    mt, nf, db, nw = g.ksplit_plan(13, M, N, K, _cus())
     s_rows, l_rows = min(M, N), max(M, N)
     wgs = -(-l_rows // (16 * nf)) * -(-s_rows // (16 * mt))
-    assert nf == 4 and l_rows * K * 2 > 32 << 20 and wgs > _cus() and g.plan(M, N, K, _cus())[0] == 13
+    assert nf == 4 and mt <= 3 and l_rows * K * 2 > 32 << 20 and wgs > _cus() and g.plan(M, N, K, _cus())[0] == 13
     A, B = rand_case(M, N, K, 7700 + M)
     ref, _ = oracle.gemm_nt(A, B)
     dA, dB = dev(A), dev(B)
-    say(f"[gpu] rung 13 S-major {M}x{N}x{K} tile={(mt, nf, db)} workgroups={wgs}")
+    say(f"[gpu] rung 13 S-major {M}x{N}x{K} tile={(mt, nf, db, nw)} workgroups={wgs}")
     got = host_bits(run(13, dA, dB, poisoned(M, N)))
     assert_parity(got, ref, K, f"rung 13 S-major {shape}")
     assert np.array_equal(host_bits(run(0, dA, dB, poisoned(M, N))), got)
